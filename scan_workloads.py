@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the device-wide prefix scan.
+
+This module only draws random numbers and names the workloads. It holds none of
+the scan's arithmetic, and it is the one piece of code that both the oracle side
+(tests, CPU baseline) and the HIP side (tests, bench, smoke) use, so that both
+see the same input array.
+
+Generator: numpy PCG64 through ``numpy.random.default_rng(seed)``. The pages give
+no generator; only seeds, sizes and value distributions are fixed by the
+workloads below, and parity does not depend on the choice because both sides
+consume the same array.
+
+Workloads (sizes, dtypes, distributions and scan kinds of the measured
+configurations):
+  C1  N = 4096          int32   uniform integers 0..9        inclusive, seed 0
+  C2  N = 2^20          float32 uniform [-1, 1)              inclusive, seed 1
+  C3  N = 2^26          uint32  uniform over [0, 2^32)       inclusive, seed 2
+  C4  N = 2^28          float32 uniform [0, 1), in place     exclusive, seed 3
+  C5  N = 2^30 - 12345  int32   Bernoulli(0.5) 0/1 flags     exclusive, seed 4
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    n: int
+    dtype: str          # "int32" | "uint32" | "float32"
+    dist: str           # key of DISTRIBUTIONS
+    seed: int
+    exclusive: bool
+    in_place: bool
+    description: str
+
+    @property
+    def itemsize(self) -> int:
+        return 4
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes a scan must move at minimum: read n elements, write n."""
+        return 2 * self.n * self.itemsize
+
+
+WORKLOADS = {
+    "C1": Workload("C1", 4096, "int32", "int_0_9", 0, False, False,
+                   "inclusive + scan, N=4096 int32 uniform integers 0..9, seed 0"),
+    "C2": Workload("C2", 1 << 20, "float32", "f32_pm1", 1, False, False,
+                   "inclusive + scan, N=2^20 fp32 uniform [-1,1), seed 1"),
+    "C3": Workload("C3", 1 << 26, "uint32", "u32_full", 2, False, False,
+                   "inclusive + scan mod 2^32, N=2^26 uint32 uniform over [0,2^32), seed 2"),
+    "C4": Workload("C4", 1 << 28, "float32", "f32_01", 3, True, True,
+                   "exclusive + scan in place, N=2^28 fp32 uniform [0,1), seed 3"),
+    "C5": Workload("C5", (1 << 30) - 12345, "int32", "flags_half", 4, True, False,
+                   "exclusive + scan, N=2^30-12345 int32 0/1 flags Bernoulli(0.5), seed 4"),
+}
+
+
+def _int_0_9(rng, n):
+    return rng.integers(0, 10, size=n, dtype=np.int32)
+
+
+def _f32_pm1(rng, n):
+    # uniform on [-1, 1): draw fp32 in [0, 1) and map affinely (exact in fp32
+    # up to one rounding of 2u - 1)
+    u = rng.random(n, dtype=np.float32)
+    return (u * np.float32(2.0) - np.float32(1.0)).astype(np.float32, copy=False)
+
+
+def _u32_full(rng, n):
+    return rng.integers(0, 1 << 32, size=n, dtype=np.uint32)
+
+
+def _f32_01(rng, n):
+    return rng.random(n, dtype=np.float32)
+
+
+def _flags_half(rng, n):
+    return rng.integers(0, 2, size=n, dtype=np.int32)
+
+
+def _i32_full(rng, n):
+    return rng.integers(-(1 << 31), 1 << 31, size=n, dtype=np.int32)
+
+
+def _f32_normal(rng, n):
+    return rng.standard_normal(n, dtype=np.float32)
+
+
+DISTRIBUTIONS = {
+    "int_0_9": _int_0_9,
+    "f32_pm1": _f32_pm1,
+    "u32_full": _u32_full,
+    "f32_01": _f32_01,
+    "flags_half": _flags_half,
+    "i32_full": _i32_full,
+    "f32_normal": _f32_normal,
+}
+
+# default distribution per dtype for ad-hoc parity cases
+DEFAULT_DIST = {"int32": "i32_full", "uint32": "u32_full", "float32": "f32_pm1"}
+
+
+def generate(dist: str, n: int, seed: int) -> np.ndarray:
+    """Draw ``n`` values of distribution ``dist`` from PCG64(seed)."""
+    rng = np.random.default_rng(seed)
+    return DISTRIBUTIONS[dist](rng, int(n))
+
+
+def generate_workload(w: Workload) -> np.ndarray:
+    return generate(w.dist, w.n, w.seed)
+
+
+def random_input(dtype: str, n: int, seed: int) -> np.ndarray:
+    return generate(DEFAULT_DIST[dtype], n, seed)

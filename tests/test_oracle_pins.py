@@ -1,0 +1,292 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+- values the pages print: the 16-element worked examples of the PMPP 11.3
+  (hierarchical scan) and 11.2 (three-phase coarsened scan) notes, and the
+  premise of Fig 6 of the decoupled look-back paper (tests/golden/);
+- the exclusive definition (identity first, then the inclusive shifted by one),
+  as the smarter.xin RTX 4090 scan notes state it in their section on
+  inclusive/exclusive conversion;
+- closed forms (constant and arithmetic inputs, with the modulo-2^32 wrap);
+- a witness that fp32 inputs are accumulated in fp64;
+- O(n^2) brute force on small n with exact Python integers / math.fsum;
+- numpy's cumsum, an independent library routine, on the seeded workloads.
+
+The last test plants plausible mistakes in copies of the oracle's C source,
+compiles each copy with gcc on the CPU and checks that every mutant fails at
+least one of the pins above.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import scan_workloads as wl
+from golden_io import read_golden
+
+M32 = 0xFFFFFFFF
+
+
+def _golden_checks(lib, fname, fail):
+    g = read_golden(fname)
+    x = np.array(g["input"], dtype=np.int32)
+    b = g["block_size"]
+    incl = lib.scan_u32(x, exclusive=False)
+    excl = lib.scan_u32(x, exclusive=True)
+    if incl.tolist() != g["inclusive"]:
+        fail(f"{fname}: inclusive")
+    # the scanned block sums are the final values at the block ends
+    if incl[b - 1::b].tolist() != g["scanned_block_sums"]:
+        fail(f"{fname}: block-end values")
+    # step 1 of the example: each block scanned on its own
+    for k in range(len(g["block_sums"])):
+        local = lib.scan_u32(x[k * b:(k + 1) * b], exclusive=False)
+        if local.tolist() != g["block_local_inclusive"][k * b:(k + 1) * b]:
+            fail(f"{fname}: block {k} local scan")
+        if int(local[-1]) != g["block_sums"][k]:
+            fail(f"{fname}: block {k} sum")
+    # step 2: scanning the block sums gives the scanned block sums
+    s = lib.scan_u32(np.array(g["block_sums"], dtype=np.int32))
+    if s.tolist() != g["scanned_block_sums"]:
+        fail(f"{fname}: scan of block sums")
+    # exclusive: identity first, then the inclusive result shifted by one
+    if excl.tolist() != [0] + g["inclusive"][:-1]:
+        fail(f"{fname}: exclusive")
+    # the fp32 oracle gives the same integers (small exact values)
+    yf, sf = lib.scan_f32(x.astype(np.float32))
+    if yf.tolist() != [float(v) for v in g["inclusive"]]:
+        fail(f"{fname}: fp32 inclusive")
+    if sf.tolist() != [float(v) for v in g["inclusive"]]:   # inputs are >= 0
+        fail(f"{fname}: fp32 running |x|")
+    yfe, _ = lib.scan_f32(x.astype(np.float32), exclusive=True)
+    if yfe.tolist() != [0.0] + [float(v) for v in g["inclusive"][:-1]]:
+        fail(f"{fname}: fp32 exclusive")
+
+
+def _fig6_checks(lib, fail):
+    g = read_golden("decoupled_lookback_fig6.txt")
+    p, s = g["partitions"], g["partition_sum"]
+    rng = np.random.default_rng(6)
+    # partitions of 5 elements whose values are non-negative and sum to s
+    parts = []
+    for _ in range(p):
+        cut = np.sort(rng.integers(0, s + 1, size=4))
+        parts.append(np.diff(np.concatenate([[0], cut, [s]])))
+    x = np.concatenate(parts).astype(np.int32)
+    incl = lib.scan_u32(x)
+    if incl[4::5].tolist() != [s * (t + 1) for t in range(p)]:
+        fail("fig6: inclusive prefix at partition ends")
+
+
+def _closed_form_checks(lib, fail):
+    n = 1000
+    ones = np.ones(n, dtype=np.int32)
+    if lib.scan_u32(ones).tolist() != list(range(1, n + 1)):
+        fail("ones inclusive")
+    if lib.scan_u32(ones, exclusive=True).tolist() != list(range(n)):
+        fail("ones exclusive")
+    c = np.full(n, 7, dtype=np.uint32)
+    if lib.scan_u32(c).tolist() != [7 * (i + 1) for i in range(n)]:
+        fail("constant inclusive")
+    # arithmetic input x[i] = i; the sums pass 2^32 and wrap
+    n = 100_000
+    ar = np.arange(n, dtype=np.uint32)
+    want = [(i * (i + 1) // 2) & M32 for i in range(n)]
+    if lib.scan_u32(ar).tolist() != want:
+        fail("arithmetic inclusive mod 2^32")
+    want_ex = [(i * (i - 1) // 2) & M32 for i in range(n)]
+    if lib.scan_u32(ar, exclusive=True).tolist() != want_ex:
+        fail("arithmetic exclusive mod 2^32")
+    # int32 is the same bits
+    got = lib.scan_u32(ar.view(np.int32)).view(np.uint32).tolist()
+    if got != want:
+        fail("arithmetic int32 bits")
+    # wrap at the boundary
+    if lib.scan_u32(np.array([M32, 1, 5], dtype=np.uint32)).tolist() != [M32, 0, 5]:
+        fail("uint32 wrap")
+    imax = np.array([2**31 - 1, 1, 1], dtype=np.int32)
+    if lib.scan_u32(imax).tolist() != [2**31 - 1, -2**31, -2**31 + 1]:
+        fail("int32 wrap")
+    # fp32 closed form, exact in fp64
+    h = np.full(n, 0.5, dtype=np.float32)
+    y, s = lib.scan_f32(h)
+    if not np.array_equal(y, 0.5 * np.arange(1, n + 1)):
+        fail("fp32 constant inclusive")
+    ye, se = lib.scan_f32(h, exclusive=True)
+    if not np.array_equal(ye, 0.5 * np.arange(n)):
+        fail("fp32 constant exclusive")
+    # the running |x| covers element i itself, for both scan kinds
+    neg = np.full(10, -1.0, dtype=np.float32)
+    y, s = lib.scan_f32(neg)
+    if y.tolist() != [-float(i) for i in range(1, 11)] or s.tolist() != [float(i) for i in range(1, 11)]:
+        fail("fp32 negative constant / running |x|")
+    _, se = lib.scan_f32(neg, exclusive=True)
+    if se.tolist() != [float(i) for i in range(1, 11)]:
+        fail("fp32 exclusive running |x|")
+    mixed = np.array([3.0, -2.0, 0.5], dtype=np.float32)
+    y, s = lib.scan_f32(mixed)
+    if y.tolist() != [3.0, 1.0, 1.5] or s.tolist() != [3.0, 5.0, 5.5]:
+        fail("fp32 mixed signs")
+
+
+def _fp64_witness_checks(lib, fail):
+    # 2^24 + 1 is not an fp32 number; an fp32 accumulator would stall at 2^24
+    x = np.array([2.0**24, 1.0, 1.0, 1.0], dtype=np.float32)
+    y, _ = lib.scan_f32(x)
+    if y.tolist() != [2.0**24, 2.0**24 + 1, 2.0**24 + 2, 2.0**24 + 3]:
+        fail("fp64 accumulation (inclusive)")
+    ye, _ = lib.scan_f32(x, exclusive=True)
+    if ye.tolist() != [0.0, 2.0**24, 2.0**24 + 1, 2.0**24 + 2]:
+        fail("fp64 accumulation (exclusive)")
+
+
+def _brute_force_checks(lib, fail):
+    rng = np.random.default_rng(123)
+    for n in (1, 2, 3, 17, 64, 65, 300):
+        x = rng.integers(-(2**31), 2**31, size=n, dtype=np.int64).astype(np.int32)
+        xs = [int(v) for v in x]
+        want = [sum(xs[:i + 1]) & M32 for i in range(n)]
+        want_ex = [sum(xs[:i]) & M32 for i in range(n)]
+        if lib.scan_u32(x).view(np.uint32).tolist() != want:
+            fail(f"brute force int32 inclusive n={n}")
+        if lib.scan_u32(x, exclusive=True).view(np.uint32).tolist() != want_ex:
+            fail(f"brute force int32 exclusive n={n}")
+        # dyadic fp32 inputs: every partial sum is exact in fp64, so the fp64
+        # running sum must equal the correctly rounded (= exact) fsum
+        f = (rng.integers(-1024, 1025, size=n) / 1024.0).astype(np.float32)
+        fl = [float(v) for v in f]
+        y, s = lib.scan_f32(f)
+        if y.tolist() != [math.fsum(fl[:i + 1]) for i in range(n)]:
+            fail(f"brute force fp32 inclusive n={n}")
+        if s.tolist() != [math.fsum(abs(v) for v in fl[:i + 1]) for i in range(n)]:
+            fail(f"brute force fp32 running |x| n={n}")
+        ye, _ = lib.scan_f32(f, exclusive=True)
+        if ye.tolist() != [math.fsum(fl[:i]) for i in range(n)]:
+            fail(f"brute force fp32 exclusive n={n}")
+
+
+def pin_failures(lib) -> list:
+    """Run every pin against an oracle library; return the names that fail."""
+    failures = []
+    fail = failures.append
+    for fname in ("pmpp_11_3_hierarchical_example.txt", "pmpp_11_2_coarsened_example.txt"):
+        _golden_checks(lib, fname, fail)
+    _fig6_checks(lib, fail)
+    _closed_form_checks(lib, fail)
+    _fp64_witness_checks(lib, fail)
+    _brute_force_checks(lib, fail)
+    return failures
+
+
+@pytest.fixture(scope="module")
+def lib():
+    oracle.build(force=False)
+    return oracle.OracleLib(oracle.LIBRARY)
+
+
+def test_golden_examples(lib):
+    failures = []
+    for fname in ("pmpp_11_3_hierarchical_example.txt", "pmpp_11_2_coarsened_example.txt"):
+        _golden_checks(lib, fname, failures.append)
+    _fig6_checks(lib, failures.append)
+    assert failures == []
+
+
+def test_closed_forms(lib):
+    failures = []
+    _closed_form_checks(lib, failures.append)
+    assert failures == []
+
+
+def test_fp64_accumulation(lib):
+    failures = []
+    _fp64_witness_checks(lib, failures.append)
+    assert failures == []
+
+
+def test_brute_force(lib):
+    failures = []
+    _brute_force_checks(lib, failures.append)
+    assert failures == []
+
+
+def test_empty_and_in_place(lib):
+    e = np.zeros(0, dtype=np.int32)
+    assert lib.scan_u32(e).size == 0
+    assert lib.scan_f32(np.zeros(0, dtype=np.float32))[0].size == 0
+    x = wl.random_input("uint32", 5000, 9)
+    want = lib.scan_u32(x.copy(), exclusive=True)
+    lib.scan_u32(x, exclusive=True, out=x)
+    assert np.array_equal(x, want)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_numpy_cumsum_on_workloads(lib, name):
+    w = wl.WORKLOADS[name]
+    x = wl.generate_workload(w)
+    if w.dtype == "float32":
+        y, s = lib.scan_f32(x, exclusive=w.exclusive)
+        c = np.cumsum(x.astype(np.float64))
+        want = np.concatenate([[0.0], c[:-1]]) if w.exclusive else c
+        assert np.array_equal(y, want)          # both are sequential fp64 sums
+        assert np.array_equal(s, np.cumsum(np.abs(x.astype(np.float64))))
+    else:
+        y = lib.scan_u32(x, exclusive=w.exclusive)
+        c = np.cumsum(x.astype(np.int64)) & M32
+        want = np.concatenate([[0], c[:-1]]) if w.exclusive else c
+        assert np.array_equal(y.view(np.uint32).astype(np.int64), want)
+
+
+@pytest.mark.parametrize("dtype", ["int32", "uint32", "float32"])
+def test_exclusive_is_shifted_inclusive(lib, dtype):
+    x = wl.random_input(dtype, 100_003, 5)
+    if dtype == "float32":
+        inc, _ = lib.scan_f32(x)
+        exc, _ = lib.scan_f32(x, exclusive=True)
+        assert exc[0] == 0.0
+        assert np.array_equal(exc[1:], inc[:-1])
+    else:
+        inc = lib.scan_u32(x)
+        exc = lib.scan_u32(x, exclusive=True)
+        assert exc[0] == 0
+        assert np.array_equal(exc[1:], inc[:-1])
+        # the last inclusive value is the total modulo 2^32
+        assert int(inc[-1]) & M32 == int(np.sum(x.astype(np.int64))) & M32
+
+
+# Plausible mistakes planted in copies of the oracle's C source: (label, text
+# to find, replacement). Each mutant must fail at least one pin.
+MUTANTS = [
+    ("inclusive stores before adding",
+     "running += xi;\n            y[i] = running;", "y[i] = running;\n            running += xi;"),
+    ("exclusive stores after adding",
+     "y[i] = running;\n            running += xi;", "running += xi;\n            y[i] = running;"),
+    ("fp32 accumulator", "double running = 0.0;", "float running = 0.0f;"),
+    ("running |x| without abs", "running_abs += fabs(xi);", "running_abs += xi;"),
+    ("running |x| excludes element i",
+     "running_abs += fabs(xi);\n            sabs[i] = running_abs;",
+     "sabs[i] = running_abs;\n            running_abs += fabs(xi);"),
+    ("loop skips element 0", "for (size_t i = 0; i < n; ++i) {", "for (size_t i = 1; i < n; ++i) {"),
+    ("wrong sign", "running += xi;", "running -= xi;"),
+    ("reversed index", "uint32_t xi = x[i];", "uint32_t xi = x[n - 1 - i];"),
+    ("stale element", "double xi = (double)x[i];", "double xi = (double)x[i > 0 ? i - 1 : 0];"),
+]
+
+
+@pytest.mark.parametrize("label,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistakes(tmp_path, label, old, new):
+    with open(oracle.SOURCE, encoding="utf-8") as f:
+        src = f.read()
+    assert old in src, f"mutant '{label}' no longer matches the oracle source"
+    mutated = src.replace(old, new, 1)
+    csrc = os.path.join(tmp_path, "mutant.c")
+    with open(csrc, "w", encoding="utf-8") as f:
+        f.write(mutated)
+    so = oracle.compile_source(csrc, os.path.join(tmp_path, "libmutant.so"))
+    mutant = oracle.OracleLib(so)
+    assert pin_failures(mutant), f"no pin catches the planted mistake: {label}"
+
+
+def test_real_oracle_passes_every_pin(lib):
+    assert pin_failures(lib) == []
