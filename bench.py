@@ -1,0 +1,303 @@
+"""Benchmark of the device-wide + scan on one MI355X.
+
+Default: the headline workload, an exclusive + scan in place of N = 2^28 fp32
+values uniform in [0, 1) (seed 3), through scan_exclusive (the single-pass
+decoupled look-back kernel). Prints ONE JSON line on stdout:
+  value        scan GB/s = 2 * N * 4 bytes / mean step time
+  roofline     the scan kernel against the 8 TB/s HBM peak
+  memcpy       a same-run device-to-device hipMemcpyAsync of N * 4 bytes,
+               counted the same way (2 * N * 4 bytes)
+  cpu_baseline the sequential CPU oracle on the same input (1 host core)
+
+Step protocol: before every step (untimed) the input is restored from a
+pristine device copy and the caches (L2, MALL) are flushed by reading a 1 GiB
+buffer; a step is one scan call bracketed by HIP events on the stream the
+library launches on. The call is a single kernel launch, so the event time is
+the kernel's launch duration.
+
+Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained,
+--order relaxed|acq_rel, --tile-shape K, --nontemporal, --no-cpu-baseline,
+--all (extra JSON lines for every workload and variant on stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import scan_workloads as wl  # noqa: E402
+
+METRIC = "scan GB/s (2n·sizeof(T)/time) at N=2^28 fp32; % of HBM peak & of D2D memcpy"
+HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_c4.json")
+VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2}
+ORDERS = {"relaxed": 0, "acq_rel": 1}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    """Hash of the HIP sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "device_wide_prefix_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """hipMemcpyAsync through the HIP runtime (the memcpy reference)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_int, ctypes.c_void_p]
+        self.lib.hipMemcpyAsync.restype = ctypes.c_int
+
+    def memcpy_d2d(self, dst: int, src: int, nbytes: int, stream: int):
+        rc = self.lib.hipMemcpyAsync(dst, src, nbytes, 3, stream)  # hipMemcpyDeviceToDevice
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
+
+
+def time_steps(fn, prepare, steps: int, warmup: int):
+    """Run warmup + steps; each step: prepare() untimed, then fn() between two
+    events on the current stream. Returns per-step milliseconds."""
+    import torch
+    times = []
+    for i in range(warmup + steps):
+        prepare()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        if i >= warmup:
+            times.append(a.elapsed_time(b))
+    torch.cuda.synchronize()
+    return times
+
+
+def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool, steps: int, warmup: int,
+                 with_memcpy: bool, x_host=None):
+    import torch
+    import device_wide_prefix_amd as dws
+
+    x = wl.generate_workload(w) if x_host is None else x_host
+    tdtype = torch.float32 if w.dtype == "float32" else torch.int32
+    host = torch.from_numpy(x if w.dtype != "uint32" else x.view(np.int32))
+    pristine = host.to("cuda")
+    work = torch.empty_like(pristine)
+    out = work if w.in_place else torch.empty_like(pristine)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    code = {"int32": dws.INT32, "uint32": dws.UINT32, "float32": dws.FLOAT32}[w.dtype]
+    stream = torch.cuda.current_stream().cuda_stream
+    dws.reserve(w.n)
+    opt = dws.DwsOptions(variant, order, shape, int(nt))
+    default = variant == 0 and order == 0 and shape == 0 and not nt
+    entry = dws.scan_exclusive_ptr if w.exclusive else dws.scan_inclusive_ptr
+
+    def prepare():
+        work.copy_(pristine)
+        flush.sum()        # read-only flush: leaves clean lines, no write-back later
+
+    def scan():
+        if default:
+            st = entry(work.data_ptr(), out.data_ptr(), w.n, code, stream)
+        else:
+            st = dws.scan_ex_ptr(work.data_ptr(), out.data_ptr(), w.n, code, w.exclusive, opt, stream)
+        if st != dws.OK:
+            raise RuntimeError(f"scan failed: {dws.status_string(st)}")
+
+    times = time_steps(scan, prepare, steps, warmup)
+    result = {"times_ms": times}
+
+    # property checks that hold at any size (no oracle here)
+    y = out.cpu().numpy()
+    if w.dtype == "uint32":
+        y = y.view(np.uint32)
+    if w.dtype == "float32":
+        tot = float(np.sum(x, dtype=np.float64))
+        last = float(y[-1]) + (float(x[-1]) if w.exclusive else 0.0)
+        sabs = float(np.sum(np.abs(x), dtype=np.float64))
+        ok = abs(last - tot) <= 1e-4 * sabs + 1e-6
+        if w.exclusive:
+            ok = ok and float(y[0]) == 0.0
+        if np.all(x >= 0):
+            ok = ok and bool(np.all(np.diff(y) >= 0))
+    else:
+        tot = int(np.sum(x.astype(np.int64))) & 0xFFFFFFFF
+        last = (int(y[-1].view(np.uint32) if w.dtype == "int32" else y[-1]) +
+                (int(x[-1].view(np.uint32) if w.dtype == "int32" else x[-1]) if w.exclusive else 0)) & 0xFFFFFFFF
+        ok = last == tot and (not w.exclusive or int(y[0]) == 0)
+        if w.dtype == "int32" and w.dist == "flags_half":
+            ok = ok and bool(np.all(np.diff(y.astype(np.int64)) >= 0))
+    result["property_check"] = bool(ok)
+
+    if with_memcpy:
+        hip = Hip()
+        dst = torch.empty_like(pristine)
+        nbytes = w.n * 4
+
+        def memcpy():
+            hip.memcpy_d2d(dst.data_ptr(), work.data_ptr(), nbytes, stream)
+
+        result["memcpy_times_ms"] = time_steps(memcpy, prepare, steps, warmup)
+        del dst
+    del pristine, work, out, flush
+    torch.cuda.empty_cache()
+    return result
+
+
+def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
+    """The sequential oracle on the same input, timed on one host core, repeated
+    until about budget_s seconds of CPU work (the oracle is one loop: 1 thread)."""
+    import oracle
+    reps = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        if w.dtype == "float32":
+            oracle.scan_f32(x, exclusive=w.exclusive, want_sabs=False)
+        else:
+            oracle.scan_u32(x, exclusive=w.exclusive)
+        reps.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(reps) >= 50:
+            break
+    med = float(np.median(reps))
+    return {"value": round(w.algorithmic_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full {w.name} input (N={w.n}), {len(reps)} repetitions, median "
+                      f"{med * 1e3:.1f} ms; host has {os.cpu_count()} logical CPUs"}
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch from the stored rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def summarize(w, res, variant_name, args):
+    times = res["times_ms"]
+    mean_ms = float(np.mean(times))
+    gbps = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
+    out = {"workload": w.name, "variant": variant_name, "ms_mean": mean_ms, "ms_min": float(np.min(times)),
+           "ms_median": float(np.median(times)), "gbps": gbps, "property_check": res["property_check"]}
+    if "memcpy_times_ms" in res:
+        mc = float(np.mean(res["memcpy_times_ms"]))
+        out["memcpy_ms_mean"] = mc
+        out["memcpy_gbps"] = w.algorithmic_bytes / (mc * 1e-3) / 1e9
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--variant", default="single_pass", choices=sorted(VARIANTS))
+    ap.add_argument("--order", default="relaxed", choices=sorted(ORDERS))
+    ap.add_argument("--tile-shape", type=int, default=0)
+    ap.add_argument("--nontemporal", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also measure every workload and variant (stderr)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the scan runs on a "
+              "single device; see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import device_wide_prefix_amd as dws
+    dws.load_library()
+
+    w = wl.WORKLOADS[args.workload]
+    log(f"generating {w.description}")
+    x = wl.generate_workload(w)
+    variant = VARIANTS[args.variant]
+    res = run_workload(w, variant, ORDERS[args.order], args.tile_shape, args.nontemporal, args.steps,
+                       args.warmup, with_memcpy=True, x_host=x)
+    s = summarize(w, res, args.variant, args)
+    log(json.dumps(s))
+    if not s["property_check"]:
+        log("WARNING: property check of the scan output failed")
+
+    mean_ms = s["ms_mean"]
+    achieved = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
+    traffic = traffic_for_current_kernel() if (variant == 0 and args.workload == "C4" and args.order == "relaxed"
+                                               and args.tile_shape == 0 and not args.nontemporal) else None
+    line = {
+        "metric": METRIC,
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "int32": "int32", "uint32": "uint32"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.description, "n": w.n, "element": w.dtype,
+                   "scan": "exclusive" if w.exclusive else "inclusive", "in_place": w.in_place,
+                   "seed": w.seed, "variant": args.variant, "memory_order": args.order,
+                   "tile_shape": args.tile_shape, "nontemporal": bool(args.nontemporal),
+                   "parallelism": "single GPU"},
+        "frac_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
+        "memcpy_gbps": round(s["memcpy_gbps"], 2),
+        "frac_memcpy": round(achieved / s["memcpy_gbps"], 4),
+        "ms_min": round(s["ms_min"], 5),
+        "ms_median": round(s["ms_median"], 5),
+        "property_check": s["property_check"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(w, x)
+
+    if args.all:
+        for name in ("C1", "C2", "C3", "C4", "C5"):
+            wk = wl.WORKLOADS[name]
+            xk = wl.generate_workload(wk)
+            for vname, v in VARIANTS.items():
+                r = run_workload(wk, v, 0, 0, False, max(5, args.steps // 2), 3, with_memcpy=(v == 0), x_host=xk)
+                log("ALL " + json.dumps(summarize(wk, r, vname, args)))
+            del xk
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,269 @@
+"""Python binding of libdws_scan.so, the gfx950 device-wide + prefix scan.
+
+Argument marshalling only: every step of the scan runs in the library's HIP
+kernels. torch supplies device buffers and the current stream. There is no CPU
+fallback; if the library is not built, importing the binding's functions raises.
+
+    scan_inclusive(x, out=None)            -> out
+    scan_exclusive(x, out=None)            -> out      (out may be x: in place)
+    scan_ex(x, out=None, exclusive=False, variant=..., memory_order=...,
+            tile_shape=0, nontemporal=False) -> out
+    scan_debug(x, out, tile_elems, ...)    -> descriptor words (numpy uint64)
+    watchdog_trips()                       -> int
+    selftest_wave(x)                       -> (incl, shift)
+The C entry points take raw device pointers; the *_ptr functions expose them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libdws_scan.so")
+
+# dws_status
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_MISALIGNED, ERR_HIP, ERR_OOM = range(7)
+# dws_dtype
+INT32, UINT32, FLOAT32 = 0, 1, 2
+# dws_variant
+SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED = 0, 1, 2
+# dws_memory_order
+ORDER_RELAXED, ORDER_ACQ_REL = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
+    "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
+    "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
+)
+
+
+class ScanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class DwsOptions(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("memory_order", ctypes.c_int),
+                ("tile_shape", ctypes.c_int), ("nontemporal", ctypes.c_int)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libdws_scan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m device_wide_prefix_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, ci, cu = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
+    for name in ("scan_inclusive", "scan_exclusive"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, sz, ci, vp]
+        f.restype = ci
+    lib.dws_scan_ex.argtypes = [vp, vp, sz, ci, ci, ctypes.POINTER(DwsOptions), vp]
+    lib.dws_scan_ex.restype = ci
+    lib.dws_status_string.argtypes = [ci]
+    lib.dws_status_string.restype = ctypes.c_char_p
+    lib.dws_version.restype = ci
+    lib.dws_num_tile_shapes.restype = ci
+    lib.dws_tile_elems.argtypes = [ci, ci]
+    lib.dws_tile_elems.restype = cu
+    lib.dws_tile_threads.argtypes = [ci, ci]
+    lib.dws_tile_threads.restype = cu
+    lib.dws_reserve.argtypes = [sz, vp]
+    lib.dws_reserve.restype = ci
+    lib.dws_release_workspaces.restype = ci
+    lib.dws_watchdog_trips.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
+    lib.dws_watchdog_trips.restype = ci
+    lib.dws_scan_debug.argtypes = [vp, vp, sz, ci, ci, ci, cu, cu, cu, cu,
+                                   ctypes.POINTER(ctypes.c_ulonglong), vp]
+    lib.dws_scan_debug.restype = ci
+    lib.dws_selftest_wave.argtypes = [vp, vp, vp, sz, ci, vp]
+    lib.dws_selftest_wave.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().dws_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise ScanError(status, what)
+
+
+# ---- raw-pointer entry points (same names as the C ABI, plus _ptr) --------
+
+def scan_inclusive_ptr(d_in: int, d_out: int, n: int, dtype: int, stream: int = 0) -> int:
+    return load_library().scan_inclusive(d_in, d_out, n, dtype, stream)
+
+
+def scan_exclusive_ptr(d_in: int, d_out: int, n: int, dtype: int, stream: int = 0) -> int:
+    return load_library().scan_exclusive(d_in, d_out, n, dtype, stream)
+
+
+def scan_ex_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,
+                options: DwsOptions | None, stream: int = 0) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    return load_library().dws_scan_ex(d_in, d_out, n, dtype, int(bool(exclusive)), opt, stream)
+
+
+# ---- torch-tensor entry points --------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.int32: INT32, torch.float32: FLOAT32}
+    u32 = getattr(torch, "uint32", None)
+    if u32 is not None:
+        codes[u32] = UINT32
+    if t.dtype not in codes:
+        raise TypeError(f"scan supports int32, uint32 and float32 tensors, got {t.dtype}")
+    return codes[t.dtype]
+
+
+def _prepare(x, out):
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("scan expects a GPU tensor (there is no CPU path)")
+    if not x.is_contiguous():
+        raise ValueError("input tensor must be contiguous")
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous() or \
+            out.device != x.device:
+        raise ValueError("out must be a contiguous tensor with the dtype, size and device of x")
+    return code, out
+
+
+def _stream(x, stream):
+    import torch
+    if stream is not None:
+        return int(stream)
+    return int(torch.cuda.current_stream(x.device).cuda_stream)
+
+
+def scan_inclusive(x, out=None, stream=None):
+    """Inclusive + scan of a contiguous GPU tensor; returns ``out``."""
+    code, out = _prepare(x, out)
+    with _device_of(x):
+        _check(scan_inclusive_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, _stream(x, stream)),
+               "scan_inclusive")
+    return out
+
+
+def scan_exclusive(x, out=None, stream=None):
+    """Exclusive + scan of a contiguous GPU tensor; returns ``out`` (may be x)."""
+    code, out = _prepare(x, out)
+    with _device_of(x):
+        _check(scan_exclusive_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, _stream(x, stream)),
+               "scan_exclusive")
+    return out
+
+
+def scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=ORDER_RELAXED,
+            tile_shape=0, nontemporal=False, stream=None):
+    """Scan with explicit options (variant, descriptor memory order, tile shape,
+    non-temporal memory access); returns ``out``."""
+    code, out = _prepare(x, out)
+    opt = DwsOptions(int(variant), int(memory_order), int(tile_shape), int(bool(nontemporal)))
+    with _device_of(x):
+        _check(scan_ex_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, opt,
+                           _stream(x, stream)), "dws_scan_ex")
+    return out
+
+
+def scan_debug(x, out, tile_elems, exclusive=False, variant=SINGLE_PASS, delay_every=0,
+               delay_phase=0, delay_ticks=0, want_descriptors=True, stream=None):
+    """Run the protocol-inspection kernel (one wavefront per tile of
+    ``tile_elems`` <= 64 elements). Returns the final descriptor words as a numpy
+    uint64 array (synchronises) or None."""
+    import numpy as np
+    code, out = _prepare(x, out)
+    n = x.numel()
+    num_tiles = max(1, -(-n // int(tile_elems))) if n else 0
+    desc = None
+    ptr = None
+    if want_descriptors and n:
+        desc = np.zeros(num_tiles, dtype=np.uint64)
+        ptr = desc.ctypes.data_as(ctypes.POINTER(ctypes.c_ulonglong))
+    with _device_of(x):
+        _check(load_library().dws_scan_debug(x.data_ptr(), out.data_ptr(), n, code, int(bool(exclusive)),
+                                             int(variant), int(tile_elems), int(delay_every),
+                                             int(delay_phase), int(delay_ticks), ptr, _stream(x, stream)),
+               "dws_scan_debug")
+    return desc
+
+
+def watchdog_trips() -> int:
+    v = ctypes.c_ulonglong(0)
+    _check(load_library().dws_watchdog_trips(ctypes.byref(v)), "dws_watchdog_trips")
+    return int(v.value)
+
+
+def selftest_wave(x, stream=None):
+    """Apply the kernels' wave64 primitives to each group of 64 elements of x:
+    returns (in-wave inclusive scan, previous-lane value)."""
+    import torch
+    code, _ = _prepare(x, None)
+    if x.numel() % 64:
+        raise ValueError("selftest_wave needs a multiple of 64 elements")
+    incl = torch.empty_like(x)
+    shift = torch.empty_like(x)
+    with _device_of(x):
+        _check(load_library().dws_selftest_wave(x.data_ptr(), incl.data_ptr(), shift.data_ptr(),
+                                                x.numel() // 64, code, _stream(x, stream)),
+               "dws_selftest_wave")
+    return incl, shift
+
+
+def reserve(n: int, stream=None, device=None):
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    with torch.cuda.device(dev):
+        s = int(torch.cuda.current_stream(dev).cuda_stream) if stream is None else int(stream)
+        _check(load_library().dws_reserve(int(n), s), "dws_reserve")
+
+
+def release_workspaces():
+    _check(load_library().dws_release_workspaces(), "dws_release_workspaces")
+
+
+def tile_elems(tile_shape: int = 0, aligned: bool = True) -> int:
+    return int(load_library().dws_tile_elems(int(tile_shape), int(bool(aligned))))
+
+
+def tile_threads(tile_shape: int = 0, aligned: bool = True) -> int:
+    return int(load_library().dws_tile_threads(int(tile_shape), int(bool(aligned))))
+
+
+def num_tile_shapes() -> int:
+    return int(load_library().dws_num_tile_shapes())
+
+
+class _device_of:
+    """Make x's device current for the C call (the library works on the
+    current HIP device)."""
+
+    def __init__(self, x):
+        self.x = x
+        self.ctx = None
+
+    def __enter__(self):
+        import torch
+        self.ctx = torch.cuda.device(self.x.device)
+        self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        self.ctx.__exit__(*exc)
+        return False

@@ -1,0 +1,459 @@
+// C ABI of the scan library: argument validation, per-(device, stream)
+// workspaces and dispatch to the kernel launchers. Declarations and the full
+// contract are in include/dws_scan.h.
+#include "dws_scan.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "dws_internal.h"
+
+namespace {
+
+using namespace dws;
+
+constexpr size_t kElemBytes = 4;
+constexpr uint64_t kMinDescSlots = 1u << 16;
+constexpr unsigned kMaxDebugDelayTicks = 50000000u;  // 0.5 s of the 100 MHz clock
+constexpr uint64_t kMaxGridThreads = (1ull << 32) - 1ull;
+
+struct Workspace {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    std::mutex mu;
+    void* ctl = nullptr;          // counter + watchdog (kCtlBytes)
+    uint64_t* desc = nullptr;     // descriptor slots
+    uint64_t desc_slots = 0;
+    void* partials = nullptr;     // reduce-then-scan partials (kRtsMaxGroups x 4 B)
+    uint64_t draws_launches = 0;  // launches that used the counter since the last clear
+
+    unsigned long long* counter() const
+    {
+        return reinterpret_cast<unsigned long long*>(static_cast<char*>(ctl) + kCtlCounterOffset);
+    }
+    unsigned int* watchdog() const
+    {
+        return reinterpret_cast<unsigned int*>(static_cast<char*>(ctl) + kCtlWatchdogOffset);
+    }
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>> g_workspaces;
+std::map<int, int> g_cu_count;
+
+dws_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return DWS_OK;
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return DWS_ERR_OOM;
+    return DWS_ERR_HIP;
+}
+
+bool valid_dtype(int d) { return d == DWS_INT32 || d == DWS_UINT32 || d == DWS_FLOAT32; }
+
+// All checks that need no HIP call. n == 0 is accepted with any pointers.
+dws_status validate(const void* in, const void* out, size_t n, int dtype)
+{
+    if (!valid_dtype(dtype)) return DWS_ERR_INVALID_ARG;
+    if (n == 0) return DWS_OK;
+    if (in == nullptr || out == nullptr) return DWS_ERR_INVALID_ARG;
+    if (n > DWS_MAX_ELEMENTS) return DWS_ERR_UNSUPPORTED;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(in);
+    const uintptr_t b = reinterpret_cast<uintptr_t>(out);
+    if ((a % kElemBytes) != 0 || (b % kElemBytes) != 0) return DWS_ERR_MISALIGNED;
+    const uintptr_t bytes = (uintptr_t)n * kElemBytes;
+    if (a + bytes < a || b + bytes < b) return DWS_ERR_INVALID_ARG;
+    if (a != b && a < b + bytes && b < a + bytes) return DWS_ERR_OVERLAP;
+    return DWS_OK;
+}
+
+int kind_of(int dtype) { return dtype == DWS_FLOAT32 ? kKindF32 : kKindU32; }
+
+bool aligned16(const void* in, const void* out)
+{
+    return ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15u) == 0;
+}
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Workspace of (current device, stream), created on first use.
+dws_status get_workspace(hipStream_t stream, Workspace** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e);
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto key = std::make_pair(dev, stream);
+    auto it = g_workspaces.find(key);
+    if (it != g_workspaces.end()) {
+        *out = it->second.get();
+        return DWS_OK;
+    }
+    auto ws = std::make_unique<Workspace>();
+    ws->device = dev;
+    ws->stream = stream;
+    e = hipMalloc(&ws->ctl, kCtlBytes);
+    if (e != hipSuccess) return from_hip(e);
+    e = hipMalloc(&ws->partials, (size_t)kRtsMaxGroups * kElemBytes);
+    if (e != hipSuccess) {
+        (void)hipFree(ws->ctl);
+        return from_hip(e);
+    }
+    e = launch_workspace_init(nullptr, 0, ws->counter(), ws->watchdog(), stream);
+    if (e != hipSuccess) {
+        (void)hipFree(ws->ctl);
+        (void)hipFree(ws->partials);
+        return from_hip(e);
+    }
+    *out = ws.get();
+    g_workspaces.emplace(key, std::move(ws));
+    return DWS_OK;
+}
+
+// Grow the descriptor array to at least `slots` (call with ws->mu held). A new
+// array is cleared by a kernel on the workspace's stream; the old one is freed
+// once the stream has drained, since kernels in flight may still use it.
+dws_status ensure_desc(Workspace* ws, uint64_t slots)
+{
+    if (slots <= ws->desc_slots) return DWS_OK;
+    uint64_t want = std::max<uint64_t>({slots, ws->desc_slots * 2, kMinDescSlots});
+    if (ws->desc != nullptr) {
+        hipError_t e = hipStreamSynchronize(ws->stream);
+        if (e != hipSuccess) return from_hip(e);
+        (void)hipFree(ws->desc);
+        ws->desc = nullptr;
+        ws->desc_slots = 0;
+    }
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, want * sizeof(uint64_t));
+    if (e != hipSuccess) return from_hip(e);
+    // fresh zeroed descriptors and a re-armed counter (epoch 1)
+    e = launch_workspace_init(static_cast<uint64_t*>(p), want, ws->counter(), nullptr, ws->stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return from_hip(e);
+    }
+    ws->desc = static_cast<uint64_t*>(p);
+    ws->desc_slots = want;
+    ws->draws_launches = 0;
+    return DWS_OK;
+}
+
+// Before a launch that draws from the counter: once the epoch would wrap,
+// clear every descriptor so no word of an old call can carry the new epoch.
+dws_status before_draw_launch(Workspace* ws)
+{
+    if (ws->draws_launches + 1 >= (uint64_t)kEpochMax) {
+        hipError_t e = launch_workspace_init(ws->desc, ws->desc_slots, ws->counter(), nullptr, ws->stream);
+        if (e != hipSuccess) return from_hip(e);
+        ws->draws_launches = 0;
+    }
+    return DWS_OK;
+}
+
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_cu_count.find(dev);
+    if (it != g_cu_count.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cu_count[dev] = cus;
+    return cus;
+}
+
+dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
+                           const dws_options& o, hipStream_t stream)
+{
+    const bool aligned = aligned16(in, out);
+    // non-temporal access is a hint, built for the aligned default shape only
+    const bool nt = o.nontemporal != 0 && aligned;
+    if (!single_pass_available(o.tile_shape, aligned, o.memory_order, mode, nt)) return DWS_ERR_UNSUPPORTED;
+    const uint64_t tile = single_pass_tile_elems(o.tile_shape, aligned);
+    const uint64_t threads = single_pass_threads(o.tile_shape, aligned);
+    const uint64_t num_tiles = ceil_div(n, tile);
+    if (num_tiles > 0xffffffffull || num_tiles * threads > kMaxGridThreads) return DWS_ERR_UNSUPPORTED;
+
+    SinglePassArgs a{};
+    a.in = in;
+    a.out = out;
+    a.n = n;
+    a.kind = kind_of(dtype);
+    a.exclusive = excl;
+    a.aligned = aligned;
+    a.shape = o.tile_shape;
+    a.order = o.memory_order;
+    a.mode = mode;
+    a.nontemporal = nt;
+    a.num_tiles = (uint32_t)num_tiles;
+    if (num_tiles == 1) {
+        // one tile: no predecessors, no descriptors, no counter
+        return from_hip(launch_single_pass(a, stream));
+    }
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_desc(ws, num_tiles);
+    if (s != DWS_OK) return s;
+    s = before_draw_launch(ws);
+    if (s != DWS_OK) return s;
+    a.desc = ws->desc;
+    a.counter = ws->counter();
+    a.watchdog = ws->watchdog();
+    s = from_hip(launch_single_pass(a, stream));
+    if (s == DWS_OK) ++ws->draws_launches;
+    return s;
+}
+
+dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hipStream_t stream)
+{
+    const bool aligned = aligned16(in, out);
+    const uint64_t tile = rts_tile_elems(aligned);
+    const uint64_t num_tiles = ceil_div(n, tile);
+    if (num_tiles > 0xffffffffull) return DWS_ERR_UNSUPPORTED;
+    uint64_t groups = std::min<uint64_t>({num_tiles, (uint64_t)cu_count() * 8u, (uint64_t)kRtsMaxGroups});
+    const uint64_t tpg = ceil_div(num_tiles, groups);
+    groups = ceil_div(num_tiles, tpg);
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    RtsArgs a{};
+    a.in = in;
+    a.out = out;
+    a.n = n;
+    a.kind = kind_of(dtype);
+    a.exclusive = excl;
+    a.aligned = aligned;
+    a.partials = ws->partials;
+    a.num_tiles = (uint32_t)num_tiles;
+    a.groups = (uint32_t)groups;
+    a.tiles_per_group = (uint32_t)tpg;
+    return from_hip(launch_rts(a, stream));
+}
+
+dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclusive, const dws_options* opt,
+                      hipStream_t stream)
+{
+    try {
+        dws_options o{};
+        if (opt != nullptr) o = *opt;
+        if (o.variant < DWS_VARIANT_SINGLE_PASS || o.variant > DWS_VARIANT_CHAINED) return DWS_ERR_INVALID_ARG;
+        if (o.memory_order != DWS_ORDER_RELAXED && o.memory_order != DWS_ORDER_ACQ_REL)
+            return DWS_ERR_INVALID_ARG;
+        if (o.tile_shape < 0 || o.tile_shape >= kNumShapes) return DWS_ERR_INVALID_ARG;
+        if (o.nontemporal != 0 && o.nontemporal != 1) return DWS_ERR_INVALID_ARG;
+        dws_status s = validate(in, out, n, dtype);
+        if (s != DWS_OK || n == 0) return s;
+        const bool excl = exclusive != 0;
+        switch (o.variant) {
+        case DWS_VARIANT_REDUCE_THEN_SCAN:
+            if (o.tile_shape != 0 || o.nontemporal != 0) return DWS_ERR_UNSUPPORTED;
+            return run_rts(in, out, n, dtype, excl, stream);
+        case DWS_VARIANT_CHAINED:
+            return run_single_pass(in, out, n, dtype, excl, kModeChained, o, stream);
+        default:
+            return run_single_pass(in, out, n, dtype, excl, kModeDecoupled, o, stream);
+        }
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+dws_status scan_inclusive(const void* d_in, void* d_out, size_t n, dws_dtype dtype, hipStream_t stream)
+{
+    return scan_entry(d_in, d_out, n, (int)dtype, 0, nullptr, stream);
+}
+
+dws_status scan_exclusive(const void* d_in, void* d_out, size_t n, dws_dtype dtype, hipStream_t stream)
+{
+    return scan_entry(d_in, d_out, n, (int)dtype, 1, nullptr, stream);
+}
+
+dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive,
+                       const dws_options* opt, hipStream_t stream)
+{
+    return scan_entry(d_in, d_out, n, (int)dtype, exclusive, opt, stream);
+}
+
+const char* dws_status_string(dws_status status)
+{
+    switch (status) {
+    case DWS_OK: return "ok";
+    case DWS_ERR_INVALID_ARG: return "invalid argument";
+    case DWS_ERR_UNSUPPORTED: return "unsupported size or option combination";
+    case DWS_ERR_OVERLAP: return "input and output overlap without being identical";
+    case DWS_ERR_MISALIGNED: return "pointer not aligned to the 4-byte element size";
+    case DWS_ERR_HIP: return "HIP runtime error";
+    case DWS_ERR_OOM: return "out of device memory";
+    }
+    return "unknown status";
+}
+
+int dws_version(void) { return DWS_VERSION; }
+
+int dws_num_tile_shapes(void) { return kNumShapes; }
+
+unsigned dws_tile_elems(int tile_shape, int aligned)
+{
+    return single_pass_tile_elems(tile_shape, aligned != 0);
+}
+
+unsigned dws_tile_threads(int tile_shape, int aligned)
+{
+    return single_pass_threads(tile_shape, aligned != 0);
+}
+
+dws_status dws_reserve(size_t n, hipStream_t stream)
+{
+    try {
+        if (n > DWS_MAX_ELEMENTS) return DWS_ERR_UNSUPPORTED;
+        Workspace* ws = nullptr;
+        dws_status s = get_workspace(stream, &ws);
+        if (s != DWS_OK) return s;
+        uint32_t min_tile = 0xffffffffu;
+        for (int i = 0; i < kNumShapes; ++i)
+            min_tile = std::min(min_tile, std::min(single_pass_tile_elems(i, true), single_pass_tile_elems(i, false)));
+        std::lock_guard<std::mutex> lock(ws->mu);
+        return ensure_desc(ws, ceil_div(std::max<uint64_t>(n, 1), min_tile));
+    } catch (...) {
+        return DWS_ERR_OOM;
+    }
+}
+
+dws_status dws_release_workspaces(void)
+{
+    try {
+        std::lock_guard<std::mutex> lock(g_mu);
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        dws_status result = DWS_OK;
+        for (auto& kv : g_workspaces) {
+            Workspace* ws = kv.second.get();
+            if (hipSetDevice(ws->device) != hipSuccess) {
+                result = DWS_ERR_HIP;
+                continue;
+            }
+            if (hipDeviceSynchronize() != hipSuccess) result = DWS_ERR_HIP;
+            if (ws->desc) (void)hipFree(ws->desc);
+            if (ws->partials) (void)hipFree(ws->partials);
+            if (ws->ctl) (void)hipFree(ws->ctl);
+        }
+        g_workspaces.clear();
+        (void)hipSetDevice(cur);
+        return result;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_watchdog_trips(unsigned long long* trips)
+{
+    if (trips == nullptr) return DWS_ERR_INVALID_ARG;
+    try {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return from_hip(e);
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return from_hip(e);
+        unsigned long long total = 0;
+        std::lock_guard<std::mutex> lock(g_mu);
+        for (auto& kv : g_workspaces) {
+            if (kv.first.first != dev) continue;
+            unsigned int v = 0;
+            e = hipMemcpy(&v, kv.second->watchdog(), sizeof(v), hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return from_hip(e);
+            total += v;
+        }
+        *trips = total;
+        return DWS_OK;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive, int variant,
+                          unsigned tile_elems, unsigned delay_every, unsigned delay_phase, unsigned delay_ticks,
+                          unsigned long long* h_desc, hipStream_t stream)
+{
+    try {
+        if (variant != DWS_VARIANT_SINGLE_PASS && variant != DWS_VARIANT_CHAINED) return DWS_ERR_INVALID_ARG;
+        if (tile_elems == 0 || tile_elems > kDebugMaxTile) return DWS_ERR_INVALID_ARG;
+        if (delay_ticks > kMaxDebugDelayTicks) return DWS_ERR_INVALID_ARG;
+        if (delay_every != 0 && delay_phase >= delay_every) return DWS_ERR_INVALID_ARG;
+        dws_status s = validate(d_in, d_out, n, (int)dtype);
+        if (s != DWS_OK || n == 0) return s;
+        const uint64_t num_tiles = ceil_div(n, tile_elems);
+        if (num_tiles > 0x7fffffffull || num_tiles * 64ull > kMaxGridThreads) return DWS_ERR_UNSUPPORTED;
+        Workspace* ws = nullptr;
+        s = get_workspace(stream, &ws);
+        if (s != DWS_OK) return s;
+        std::lock_guard<std::mutex> lock(ws->mu);
+        s = ensure_desc(ws, num_tiles);
+        if (s != DWS_OK) return s;
+        s = before_draw_launch(ws);
+        if (s != DWS_OK) return s;
+        DebugArgs a{};
+        a.in = d_in;
+        a.out = d_out;
+        a.n = n;
+        a.kind = kind_of((int)dtype);
+        a.exclusive = exclusive != 0;
+        a.mode = variant == DWS_VARIANT_CHAINED ? kModeChained : kModeDecoupled;
+        a.tile_elems = tile_elems;
+        a.delay_every = delay_every;
+        a.delay_phase = delay_phase;
+        a.delay_ticks = delay_ticks;
+        a.desc = ws->desc;
+        a.counter = ws->counter();
+        a.watchdog = ws->watchdog();
+        a.num_tiles = (uint32_t)num_tiles;
+        s = from_hip(launch_debug(a, stream));
+        if (s != DWS_OK) return s;
+        if (num_tiles > 1) ++ws->draws_launches;
+        if (h_desc != nullptr) {
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return from_hip(e);
+            if (num_tiles > 1) {
+                e = hipMemcpy(h_desc, ws->desc, num_tiles * sizeof(uint64_t), hipMemcpyDeviceToHost);
+                if (e != hipSuccess) return from_hip(e);
+            } else {
+                h_desc[0] = 0;   // a single tile publishes nothing
+            }
+        }
+        return DWS_OK;
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_selftest_wave(const void* d_in, void* d_incl, void* d_shift, size_t n_waves, dws_dtype dtype,
+                             hipStream_t stream)
+{
+    if (!valid_dtype((int)dtype)) return DWS_ERR_INVALID_ARG;
+    if (n_waves == 0) return DWS_OK;
+    if (d_in == nullptr || d_incl == nullptr || d_shift == nullptr) return DWS_ERR_INVALID_ARG;
+    if (n_waves > 0xffffffffull / 64ull) return DWS_ERR_UNSUPPORTED;
+    return from_hip(launch_wave_selftest(d_in, d_incl, d_shift, n_waves, kind_of((int)dtype), stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,347 @@
+// Device primitives of the gfx950 scan kernels: wavefront (wave64) scans on
+// DPP, tile loads/stores, the packed tile descriptor and the look-back.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dws_protocol.h"
+
+namespace dws {
+
+// ---------------------------------------------------------------------------
+// Element traits. Both 32-bit integer types run as uint32_t (wrapping adds are
+// the same bits for int32 and uint32), fp32 runs as float.
+// ---------------------------------------------------------------------------
+template <class T> struct Elem;
+
+template <> struct Elem<uint32_t> {
+    static __device__ __forceinline__ uint32_t bits(uint32_t v) { return v; }
+    static __device__ __forceinline__ uint32_t from(uint32_t b) { return b; }
+    // value a disabled DPP lane contributes: the identity of +
+    static constexpr uint32_t kDppOld = 0u;
+};
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ uint32_t bits(float v) { return __float_as_uint(v); }
+    static __device__ __forceinline__ float from(uint32_t b) { return __uint_as_float(b); }
+    // -0.0 is the exact identity of IEEE addition (x + -0.0 == x for all x,
+    // +0.0 included); it also lets the compiler fold the DPP move into the add
+    static constexpr uint32_t kDppOld = 0x80000000u;
+};
+
+// ---------------------------------------------------------------------------
+// Wavefront primitives on DPP. A wave64 is four rows of 16 lanes.
+// ---------------------------------------------------------------------------
+enum : int {
+    kDppRowShr1 = 0x111,
+    kDppRowShr2 = 0x112,
+    kDppRowShr4 = 0x114,
+    kDppRowShr8 = 0x118,
+    kDppWaveShr1 = 0x138,   // whole-wave shift by one lane
+    kDppRowBcast15 = 0x142, // lane 15 of each row -> the next row
+    kDppRowBcast31 = 0x143, // lane 31 -> rows 2 and 3
+};
+
+template <int CTRL, int ROW_MASK, bool ZERO_OUT_OF_ROW, class T>
+__device__ __forceinline__ T dpp_read(T v)
+{
+    return Elem<T>::from((uint32_t)__builtin_amdgcn_update_dpp(
+        (int)Elem<T>::kDppOld, (int)Elem<T>::bits(v), CTRL, ROW_MASK, 0xf, ZERO_OUT_OF_ROW));
+}
+
+// Inclusive + scan over the 64 lanes in lane order. Within each row a
+// Kogge-Stone doubling (shifts 1, 2, 4, 8; lanes shifted in from outside the
+// row read 0), then the row totals are carried forward: row 1 and row 3 add
+// the last lane of the row before them, rows 2 and 3 add lane 31.
+template <class T>
+__device__ __forceinline__ T wave_inclusive_scan(T v)
+{
+    v = v + dpp_read<kDppRowShr1, 0xf, true>(v);
+    v = v + dpp_read<kDppRowShr2, 0xf, true>(v);
+    v = v + dpp_read<kDppRowShr4, 0xf, true>(v);
+    v = v + dpp_read<kDppRowShr8, 0xf, true>(v);
+    v = v + dpp_read<kDppRowBcast15, 0xa, false>(v);
+    v = v + dpp_read<kDppRowBcast31, 0xc, false>(v);
+    return v;
+}
+
+// Value held by the previous lane; lane 0 gets 0 (+0.0 for fp32).
+template <class T>
+__device__ __forceinline__ T wave_shift_up1(T v)
+{
+    return Elem<T>::from((uint32_t)__builtin_amdgcn_update_dpp(
+        0, (int)Elem<T>::bits(v), kDppWaveShr1, 0xf, 0xf, true));
+}
+
+template <class T>
+__device__ __forceinline__ T wave_read_lane(T v, int lane)
+{
+    return Elem<T>::from((uint32_t)__builtin_amdgcn_readlane((int)Elem<T>::bits(v), lane));
+}
+
+template <class T>
+__device__ __forceinline__ T wave_sum(T v)
+{
+    return wave_read_lane(wave_inclusive_scan(v), 63);
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+// ---------------------------------------------------------------------------
+// Tile I/O. A tile is W wave segments; a wave segment is CHUNKS chunks of
+// 64 * VEC consecutive elements, and lane l holds elements [l*VEC, l*VEC+VEC)
+// of every chunk. Each load instruction of a wave therefore reads 64*VEC*4
+// contiguous bytes (1 KiB for dwordx4): fully coalesced, no LDS transpose.
+// ---------------------------------------------------------------------------
+template <class T, int VEC> struct Vec { typedef T type __attribute__((ext_vector_type(VEC))); };
+template <class T> struct Vec<T, 1> { typedef T type; };
+
+template <class T, int VEC, int CHUNKS, bool NT>
+__device__ __forceinline__ void load_segment(const T* in, uint64_t seg_base, uint64_t n,
+                                             bool full, int lane, T (&x)[CHUNKS][VEC])
+{
+    typedef typename Vec<T, VEC>::type V;
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            const V* p = reinterpret_cast<const V*>(in + seg_base + (uint64_t)(c * 64 * VEC + lane * VEC));
+            V v;
+            if constexpr (NT) v = __builtin_nontemporal_load(p);
+            else v = *p;
+            if constexpr (VEC == 1) {
+                x[c][0] = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) x[c][e] = v[e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint64_t i = seg_base + (uint64_t)(c * 64 * VEC + lane * VEC + e);
+                x[c][e] = (i < n) ? in[i] : T(0);   // identity past the end
+            }
+        }
+    }
+}
+
+template <class T, int VEC, int CHUNKS, bool NT>
+__device__ __forceinline__ void store_segment(T* out, uint64_t seg_base, uint64_t n,
+                                              bool full, int lane, const T (&y)[CHUNKS][VEC])
+{
+    typedef typename Vec<T, VEC>::type V;
+    if (full) {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            V* p = reinterpret_cast<V*>(out + seg_base + (uint64_t)(c * 64 * VEC + lane * VEC));
+            V v;
+            if constexpr (VEC == 1) {
+                v = y[c][0];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[e] = y[c][e];
+            }
+            if constexpr (NT) __builtin_nontemporal_store(v, p);
+            else *p = v;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint64_t i = seg_base + (uint64_t)(c * 64 * VEC + lane * VEC + e);
+                if (i < n) out[i] = y[c][e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scan of one wave segment held in registers (three-phase coarsened scan of the
+// PMPP 11.2 notes, with wave scans in place of the block-wide phase 2):
+//   lane_total[c]  serial sum of the lane's VEC elements of chunk c
+//   lane_excl[c]   sum of the lower lanes' totals of chunk c (in-wave scan)
+//   chunk_pre[c]   sum of the wave's chunks before c (uniform)
+//   returns        the wave segment total (uniform)
+// ---------------------------------------------------------------------------
+template <class T, int VEC, int CHUNKS>
+__device__ __forceinline__ T scan_segment(const T (&x)[CHUNKS][VEC], T (&lane_excl)[CHUNKS],
+                                          T (&chunk_pre)[CHUNKS])
+{
+    T incl[CHUNKS];
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        T s = x[c][0];
+#pragma unroll
+        for (int e = 1; e < VEC; ++e) s = s + x[c][e];
+        incl[c] = wave_inclusive_scan(s);
+    }
+    T running = T(0);
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        lane_excl[c] = wave_shift_up1(incl[c]);
+        chunk_pre[c] = running;
+        running = running + wave_read_lane(incl[c], 63);
+    }
+    return running;
+}
+
+// Seeded serial finish of a wave segment: every element gets seed + the sum of
+// everything before it in the segment (exclusive) or up to and including it
+// (inclusive). Exclusive values are formed directly, never as inclusive - x.
+template <class T, bool EXCL, int VEC, int CHUNKS>
+__device__ __forceinline__ void finish_segment(const T (&x)[CHUNKS][VEC], const T (&lane_excl)[CHUNKS],
+                                               const T (&chunk_pre)[CHUNKS], T seed, T (&y)[CHUNKS][VEC])
+{
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        T s = (seed + chunk_pre[c]) + lane_excl[c];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (EXCL) {
+                y[c][e] = s;
+                s = s + x[c][e];
+            } else {
+                s = s + x[c][e];
+                y[c][e] = s;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tile descriptors (Merrill & Garland, sections 4.1 and 4.4): one 64-bit word
+// per tile holding the status flag and a single value field, written and read
+// as one device-scope atomic, so status and value are always seen together.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t desc_pack(uint32_t epoch, uint32_t status, uint32_t value_bits)
+{
+    return ((uint64_t)((epoch << kDescStatusBits) | status) << 32) | value_bits;
+}
+
+// Status of a descriptor word for the current epoch; words written by an
+// earlier call (another epoch) or never written read as X.
+__device__ __forceinline__ uint32_t desc_status(uint64_t d, uint32_t epoch)
+{
+    const uint32_t hi = (uint32_t)(d >> 32);
+    return ((hi >> kDescStatusBits) == epoch) ? (hi & kDescStatusMask) : kStatusX;
+}
+
+template <int ORDER>
+__device__ __forceinline__ uint64_t desc_load(const uint64_t* p)
+{
+    if constexpr (ORDER == kOrderAcqRel)
+        return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int ORDER>
+__device__ __forceinline__ void desc_store(uint64_t* p, uint64_t w)
+{
+    if constexpr (ORDER == kOrderAcqRel)
+        __hip_atomic_store(p, w, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Draw the next tile index and the call's epoch from the 64-bit counter
+// ([63:32] epoch, [31:0] draws) with one device-scope atomic (dynamic tile
+// index assignment, PMPP 11.3 notes; "virtual processors" in section 4.4 of the
+// Merrill & Garland notes): the holder of tile t knows tiles 0..t-1 were drawn
+// by workgroups that are already running, so waiting on them cannot deadlock.
+// The draw of the last tile re-arms the counter for the next call on the same
+// workspace: draws back to 0, epoch + 1. Call from one lane.
+__device__ __forceinline__ void draw_tile(unsigned long long* counter, uint32_t num_draws,
+                                          uint32_t& tile, uint32_t& epoch)
+{
+    const unsigned long long old =
+        __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tile = (uint32_t)old;
+    epoch = (uint32_t)(old >> 32);
+    if (tile == num_draws - 1u) {
+        const uint32_t next = (epoch >= kEpochMax) ? 1u : epoch + 1u;
+        __hip_atomic_store(counter, (unsigned long long)next << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Decoupled look-back by one whole wavefront (section 4.4, parallelized
+// look-back): lane l inspects the descriptor of tile hi - l, so each step
+// covers 64 predecessors. If any of the lanes up to and including the nearest
+// P is still X, the window is polled again. Otherwise those lanes' values are
+// summed into the running exclusive prefix (aggregates of the A lanes plus the
+// inclusive prefix of the nearest P); with a P the look-back ends, without one
+// the window slides back by 64. Indices below 0 read as P with value 0, so the
+// walk always ends at tile 0 at the latest. Returns the exclusive prefix of
+// `tile` (uniform). A wait longer than kWatchdogTicks counts one trip in
+// *watchdog and returns the incomplete prefix instead of hanging. Call with the
+// whole wave active.
+template <class T, int ORDER>
+__device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t epoch,
+                               unsigned int* watchdog)
+{
+    const int lane = lane_id();
+    const uint64_t lane_bit = 1ull << lane;
+    T prefix = T(0);
+    int64_t hi = (int64_t)tile - 1;
+    const uint64_t t0 = realtime();
+    for (;;) {
+        const int64_t idx = hi - lane;
+        const uint64_t d = (idx >= 0) ? desc_load<ORDER>(desc + idx) : desc_pack(epoch, kStatusP, 0u);
+        const uint32_t st = desc_status(d, epoch);
+        const uint64_t has_p = __builtin_amdgcn_ballot_w64(st == kStatusP);
+        const uint64_t has_x = __builtin_amdgcn_ballot_w64(st == kStatusX);
+        // lanes 0 .. nearest P inclusive; all 64 lanes when no P is in view
+        const uint64_t need = has_p ? (has_p ^ (has_p - 1ull)) : ~0ull;
+        if ((has_x & need) == 0ull) {
+            const T v = (need & lane_bit) ? Elem<T>::from((uint32_t)d) : T(0);
+            prefix = prefix + wave_sum(v);
+            if (has_p) return prefix;
+            hi -= 64;
+            continue;
+        }
+        if (realtime() - t0 > kWatchdogTicks) {
+            if (lane == 0) atomicAdd(watchdog, 1u);
+            return prefix;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Chained scan (section 3.2, Fig 4): wait for the immediate predecessor's
+// inclusive prefix only. Lane 0 polls; the result is broadcast to the wave.
+template <class T, int ORDER>
+__device__ T lookback_chained(const uint64_t* desc, uint32_t tile, uint32_t epoch,
+                             unsigned int* watchdog)
+{
+    uint32_t bits = 0u;
+    if (lane_id() == 0) {
+        const uint64_t t0 = realtime();
+        for (;;) {
+            const uint64_t d = desc_load<ORDER>(desc + (tile - 1u));
+            if (desc_status(d, epoch) == kStatusP) {
+                bits = (uint32_t)d;
+                break;
+            }
+            if (realtime() - t0 > kWatchdogTicks) {
+                atomicAdd(watchdog, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    return Elem<T>::from((uint32_t)__builtin_amdgcn_readfirstlane((int)bits));
+}
+
+}  // namespace dws

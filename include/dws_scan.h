@@ -1,0 +1,213 @@
+/*
+ * dws_scan.h — device-wide + prefix scan (inclusive / exclusive) for AMD
+ * Instinct MI355X (gfx950), single pass with decoupled look-back.
+ *
+ * What is computed (the plain definition of a prefix sum):
+ *   inclusive  y[i] = x[0] + ... + x[i]
+ *   exclusive  y[0] = 0,  y[i] = x[0] + ... + x[i-1]
+ * Definition: CUDA-Operators-6-Cumsum, section 1 (Cumsum theory); the
+ * exclusive form and its identity first element: the smarter.xin RTX 4090 scan
+ * notes, section on converting between inclusive and exclusive scans.
+ * How: one kernel launch in which every workgroup scans one tile, publishes its
+ * aggregate, then determines its exclusive prefix by looking back over
+ * predecessor tiles' descriptors (Merrill & Garland, "Single-pass Parallel
+ * Prefix Scan with Decoupled Look-back", sections 4.1 and 4.4). It moves about
+ * 2n elements through memory (section A1 of the same notes).
+ *
+ * Element types and arithmetic:
+ *   DWS_INT32, DWS_UINT32  wrap modulo 2^32 (int32 is two's complement, so both
+ *                          give identical bits); results are deterministic.
+ *   DWS_FLOAT32            IEEE fp32 additions, round to nearest even; the order
+ *                          of additions depends on run-time scheduling, so bits
+ *                          may differ from run to run (section A6 of the same
+ *                          notes) while staying within a few ulps of the exact
+ *                          prefix relative to the running sum of |x|.
+ *
+ * Pointers: d_in and d_out are DEVICE pointers on the current HIP device, owned
+ * by the caller, each holding n contiguous 4-byte elements. d_out == d_in
+ * (in place) is allowed; any other overlap is rejected. Pointers must be 4-byte
+ * aligned; 16-byte alignment of both selects the vector (dwordx4) path, other
+ * alignments a scalar-load path with the same results.
+ *
+ * Streams and ownership: every call is asynchronous on `stream` (0 = the
+ * default stream of the current device) and returns after enqueue. The library
+ * keeps one small workspace per (device, stream): descriptors (8 bytes per
+ * tile), a tile counter and, for the reduce-then-scan variant, a partials
+ * array. It is allocated and cleared on the first multi-tile call on that
+ * stream (which therefore must not be under graph capture; dws_reserve can
+ * create it ahead of time) and reused by later calls, which the stream orders.
+ * Calls on different streams never share a workspace. Host threads may call
+ * concurrently. dws_release_workspaces frees every workspace.
+ *
+ * Errors: argument checks run before any HIP call and enqueue nothing. No C++
+ * exception crosses this interface.
+ */
+#ifndef DWS_SCAN_H
+#define DWS_SCAN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DWS_VERSION 1
+
+typedef enum dws_status {
+    DWS_OK = 0,
+    DWS_ERR_INVALID_ARG = 1,   /* null pointer with n > 0, bad enum or option */
+    DWS_ERR_UNSUPPORTED = 2,   /* n above DWS_MAX_ELEMENTS */
+    DWS_ERR_OVERLAP = 3,       /* d_in and d_out overlap without being equal */
+    DWS_ERR_MISALIGNED = 4,    /* a pointer is not 4-byte aligned */
+    DWS_ERR_HIP = 5,           /* a HIP runtime call failed */
+    DWS_ERR_OOM = 6            /* workspace allocation failed */
+} dws_status;
+
+typedef enum dws_dtype {
+    DWS_INT32 = 0,
+    DWS_UINT32 = 1,
+    DWS_FLOAT32 = 2
+} dws_dtype;
+
+/* Largest supported element count (2^35). */
+#define DWS_MAX_ELEMENTS (((size_t)1) << 35)
+
+/*
+ * Inclusive + scan of n elements: d_out[i] = d_in[0] + ... + d_in[i].
+ * Single-pass decoupled look-back (Merrill & Garland, section 4.1). n == 0 is a
+ * no-op returning DWS_OK.
+ */
+dws_status scan_inclusive(const void* d_in, void* d_out, size_t n,
+                          dws_dtype dtype, hipStream_t stream);
+
+/*
+ * Exclusive + scan of n elements: d_out[0] = 0, d_out[i] = d_in[0] + ... +
+ * d_in[i-1] (smarter.xin RTX 4090 scan notes, inclusive/exclusive section). The
+ * exclusive values are produced directly, not by subtracting x from an
+ * inclusive result. Same contract as scan_inclusive.
+ */
+dws_status scan_exclusive(const void* d_in, void* d_out, size_t n,
+                          dws_dtype dtype, hipStream_t stream);
+
+/* Global strategy selected by dws_options.variant. */
+typedef enum dws_variant {
+    /* one pass, decoupled look-back: ~2n traffic (Merrill & Garland, 4.1) */
+    DWS_VARIANT_SINGLE_PASS = 0,
+    /* three kernels: reduce G chunks, scan the G partials, seeded scan of
+     * each chunk: ~3n traffic (same notes, section 3.2, Fig 3; G is the
+     * number of co-resident workgroups, CUDA-Operators-6-Cumsum section 1.2) */
+    DWS_VARIANT_REDUCE_THEN_SCAN = 1,
+    /* one pass, each tile waits for its immediate predecessor's inclusive
+     * prefix: ~2n traffic, serial signal chain (same notes, section 3.2,
+     * Fig 4; PMPP 11.3 notes, single-pass domino scan with adjacent
+     * synchronisation) */
+    DWS_VARIANT_CHAINED = 2
+} dws_variant;
+
+/* Ordering of descriptor stores and loads. The descriptor packs status and
+ * value in one 64-bit word, so a relaxed device-scope atomic suffices for the
+ * protocol (Merrill & Garland, section 4.4, fence-free descriptor updates);
+ * release/acquire is available for comparison. */
+typedef enum dws_memory_order {
+    DWS_ORDER_RELAXED = 0,
+    DWS_ORDER_ACQ_REL = 1
+} dws_memory_order;
+
+typedef struct dws_options {
+    int variant;        /* dws_variant; default DWS_VARIANT_SINGLE_PASS */
+    int memory_order;   /* dws_memory_order; default DWS_ORDER_RELAXED */
+    int tile_shape;     /* 0 = default (256 threads x 16 elements); other
+                           indices < dws_num_tile_shapes() select other tile
+                           shapes of the single-pass kernel, for sweeps */
+    int nontemporal;    /* 1 = non-temporal (streaming) loads and stores */
+} dws_options;
+
+/*
+ * Scan with explicit options. opt == NULL (or a zeroed struct) means all
+ * defaults; exclusive != 0 selects the exclusive scan. Unknown values give
+ * DWS_ERR_INVALID_ARG. Built combinations (others give DWS_ERR_UNSUPPORTED):
+ *   single pass: any tile_shape with relaxed order; tile_shape 0 also with
+ *                release/acquire, and with nontemporal (relaxed);
+ *   chained:     tile_shape 0, either order;
+ *   reduce-then-scan: tile_shape 0, nontemporal 0 (memory_order ignored).
+ * Pointers that are not both 16-byte aligned use the scalar-load kernel of
+ * tile_shape 0 whatever tile_shape asks for, and ignore nontemporal.
+ */
+dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                       int exclusive, const dws_options* opt, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dws_status_string(dws_status status);
+
+/* Library version (DWS_VERSION). */
+int dws_version(void);
+
+/* ---- tile geometry (host only, no HIP call) ---------------------------- */
+
+/* Number of tile shapes of the single-pass kernel (index 0 is the default). */
+int dws_num_tile_shapes(void);
+
+/*
+ * Elements per tile for a tile shape and alignment class (aligned != 0: both
+ * pointers 16-byte aligned). Returns 0 for an unknown shape.
+ */
+unsigned dws_tile_elems(int tile_shape, int aligned);
+
+/* Threads per workgroup of a tile shape (0 for an unknown shape). */
+unsigned dws_tile_threads(int tile_shape, int aligned);
+
+/* ---- workspace ---------------------------------------------------------- */
+
+/*
+ * Create (or grow) the workspace of `stream` on the current device so that
+ * scans of up to n elements with any option need no further allocation.
+ */
+dws_status dws_reserve(size_t n, hipStream_t stream);
+
+/* Synchronise the device and free every workspace the library holds. */
+dws_status dws_release_workspaces(void);
+
+/* ---- diagnostics (tests and benchmarks) --------------------------------- */
+
+/*
+ * Number of look-back waits on the current device that exceeded the safety
+ * limit (about two seconds) since the library was loaded. A correct run keeps
+ * it at 0; when it trips, the waiting tile proceeds with an incomplete prefix
+ * rather than hang, so that run's output is wrong. Synchronous.
+ */
+dws_status dws_watchdog_trips(unsigned long long* trips);
+
+/*
+ * Protocol inspection kernel: the same descriptor protocol and look-back as
+ * the single-pass scan, but with one wavefront per tile and a run-time tile
+ * size of 1..64 elements, so that small inputs exercise many tiles and
+ * look-back windows. Tiles whose index t satisfies t % delay_every ==
+ * delay_phase (delay_every > 0) wait delay_ticks ticks of the 100 MHz
+ * real-time counter before publishing their aggregate, which forces their
+ * successors to observe the X and A states. If h_desc != NULL, the call
+ * synchronises the stream and copies the num_tiles = ceil(n / tile_elems)
+ * final descriptor words to host memory h_desc: bits 63..34 epoch, 33..32
+ * status (0 X, 1 A, 2 P), 31..0 value bits (the tile's inclusive prefix once
+ * P). With variant == DWS_VARIANT_CHAINED the look-back window is one tile.
+ */
+dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                          int exclusive, int variant, unsigned tile_elems,
+                          unsigned delay_every, unsigned delay_phase,
+                          unsigned delay_ticks, unsigned long long* h_desc,
+                          hipStream_t stream);
+
+/*
+ * Wavefront primitive check: for each group of 64 elements g, writes the
+ * in-wave inclusive scan to d_incl and the value of the previous lane (0 in
+ * lane 0) to d_shift, exactly as the scan kernels compute them.
+ * n_waves groups of 64 elements; dtype DWS_UINT32/DWS_INT32/DWS_FLOAT32.
+ */
+dws_status dws_selftest_wave(const void* d_in, void* d_incl, void* d_shift,
+                             size_t n_waves, dws_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWS_SCAN_H */

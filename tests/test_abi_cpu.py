@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+public header declares, and rejects bad arguments before any HIP call (so these
+run without a GPU; no scan is computed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import device_wide_prefix_amd as dws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dws_scan.h")
+
+
+def declared_functions():
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dws.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return dws.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string"):
+        assert required in names
+    assert set(names) == set(dws.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in dws_scan.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dws_version() == 1
+    for code in range(7):
+        s = dws.status_string(code)
+        assert isinstance(s, str) and s
+    assert dws.status_string(0) == "ok"
+    assert dws.status_string(99) == "unknown status"
+
+
+def test_tile_geometry(lib):
+    n = dws.num_tile_shapes()
+    assert n >= 1
+    assert dws.tile_elems(0, True) == 4096
+    assert dws.tile_threads(0, True) == 256
+    assert dws.tile_elems(0, False) == 4096
+    for s in range(n):
+        e, t = dws.tile_elems(s, True), dws.tile_threads(s, True)
+        assert e > 0 and t % 64 == 0 and e % (t * 4) == 0
+        # unaligned pointers fall back to the default shape's scalar kernel
+        assert dws.tile_elems(s, False) == 4096
+    assert dws.tile_elems(n, True) == 0
+    assert dws.tile_elems(-1, True) == 0
+
+
+FAKE = 0x10000  # never dereferenced: validation fails or passes before any HIP call
+
+
+@pytest.mark.parametrize("fn", ["scan_inclusive", "scan_exclusive"])
+def test_validation(lib, fn):
+    f = getattr(lib, fn)
+    # n == 0 is a no-op, even with null pointers
+    assert f(None, None, 0, dws.INT32, None) == dws.OK
+    assert f(None, FAKE, 10, dws.INT32, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, None, 10, dws.FLOAT32, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, 7, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, -1, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE + 2, FAKE + 4096, 10, dws.UINT32, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, FAKE + 4097, 10, dws.UINT32, None) == dws.ERR_MISALIGNED
+    # partial overlap in either direction; exact aliasing is allowed (not run here)
+    assert f(FAKE, FAKE + 4, 10, dws.INT32, None) == dws.ERR_OVERLAP
+    assert f(FAKE + 36, FAKE, 10, dws.INT32, None) == dws.ERR_OVERLAP
+    # too large
+    assert f(FAKE, FAKE + (1 << 40), (1 << 35) + 1, dws.INT32, None) == dws.ERR_UNSUPPORTED
+    # address range wraps around
+    assert f(2**64 - 16, FAKE, 100, dws.INT32, None) == dws.ERR_INVALID_ARG
+
+
+def test_option_validation(lib):
+    def call(**kw):
+        o = dws.DwsOptions(kw.get("variant", 0), kw.get("order", 0), kw.get("shape", 0), kw.get("nt", 0))
+        return lib.dws_scan_ex(FAKE, FAKE + (1 << 20), 1 << 16, dws.FLOAT32, 1, ctypes.byref(o), None)
+    assert call(variant=3) == dws.ERR_INVALID_ARG
+    assert call(variant=-1) == dws.ERR_INVALID_ARG
+    assert call(order=2) == dws.ERR_INVALID_ARG
+    assert call(shape=dws.num_tile_shapes()) == dws.ERR_INVALID_ARG
+    assert call(nt=2) == dws.ERR_INVALID_ARG
+    # combinations that are not built
+    assert call(shape=1, order=dws.ORDER_ACQ_REL) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.CHAINED, shape=2) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.REDUCE_THEN_SCAN, nt=1) == dws.ERR_UNSUPPORTED
+    # options are validated before the arguments: n == 0 with bad options
+    o = dws.DwsOptions(9, 0, 0, 0)
+    assert lib.dws_scan_ex(None, None, 0, dws.INT32, 0, ctypes.byref(o), None) == dws.ERR_INVALID_ARG
+    assert lib.dws_scan_ex(None, None, 0, dws.INT32, 0, None, None) == dws.OK
+
+
+def test_debug_and_selftest_validation(lib):
+    d = lib.dws_scan_debug
+    assert d(FAKE, FAKE + 4096, 16, dws.INT32, 0, 0, 0, 0, 0, 0, None, None) == dws.ERR_INVALID_ARG
+    assert d(FAKE, FAKE + 4096, 16, dws.INT32, 0, 0, 65, 0, 0, 0, None, None) == dws.ERR_INVALID_ARG
+    assert d(FAKE, FAKE + 4096, 16, dws.INT32, 0, 1, 4, 0, 0, 0, None, None) == dws.ERR_INVALID_ARG
+    assert d(FAKE, FAKE + 4096, 16, dws.INT32, 0, 0, 4, 3, 3, 0, None, None) == dws.ERR_INVALID_ARG
+    assert d(FAKE, FAKE + 4096, 16, dws.INT32, 0, 0, 4, 0, 0, 10**9, None, None) == dws.ERR_INVALID_ARG
+    assert d(FAKE, FAKE + 4, 16, dws.INT32, 0, 0, 4, 0, 0, 0, None, None) == dws.ERR_OVERLAP
+    assert d(None, None, 0, dws.INT32, 0, 0, 4, 0, 0, 0, None, None) == dws.OK
+    s = lib.dws_selftest_wave
+    assert s(None, None, None, 0, dws.INT32, None) == dws.OK
+    assert s(None, FAKE, FAKE, 1, dws.INT32, None) == dws.ERR_INVALID_ARG
+    assert s(FAKE, FAKE, FAKE, 1, 5, None) == dws.ERR_INVALID_ARG
+    assert lib.dws_watchdog_trips(None) == dws.ERR_INVALID_ARG
+    assert lib.dws_reserve((1 << 35) + 1, None) == dws.ERR_UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    x = torch.arange(10, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        dws.scan_inclusive(x)
+    with pytest.raises(TypeError):
+        dws.scan_exclusive(x.float())

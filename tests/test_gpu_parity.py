@@ -1,0 +1,374 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle,
+element by element on the same seeded inputs.
+
+Bar: 32-bit integers bit-exact (modulo 2^32); fp32 within
+1e-4 * sum_{j<=i}|x_j| + 1e-6 of the fp64 oracle. Where several fp32 results
+are correct (the order of additions depends on scheduling), the tolerance is the
+check; the descriptors' statuses and epochs, which are unique, are compared
+exactly.
+"""
+import numpy as np
+import pytest
+
+import device_wide_prefix_amd as dws
+import oracle
+import scan_workloads as wl
+from golden_io import read_golden
+from gpu_util import (check, check_chunked, decode_desc, from_device, note, run, to_device)
+
+pytestmark = pytest.mark.gpu
+
+TILE = 4096
+DTYPES = ["int32", "uint32", "float32"]
+
+
+def _roundtrip(x, dtype, exclusive, in_place=False, offset=0, **opts):
+    import torch
+    store, xd = to_device(x, extra_front=offset)
+    if in_place:
+        out = xd
+    else:
+        ostore = torch.empty(x.size + offset, dtype=xd.dtype, device="cuda")
+        out = ostore[offset:]
+    run(xd, out, x.size, dtype, exclusive, **opts)
+    return from_device(out, dtype)
+
+
+# ---------------------------------------------------------------------------
+# wavefront primitives
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["uint32", "float32"])
+def test_wave_primitives_lane_layout(gpu, dtype):
+    import torch
+    note(f"selftest_wave {dtype}")
+    waves = 257
+    if dtype == "uint32":
+        x = wl.generate("u32_full", waves * 64, 11)
+    else:
+        # small integers: every partial sum is exact in fp32
+        x = wl.generate("int_0_9", waves * 64, 11).astype(np.float32) - 4.0
+    _, xd = to_device(x)
+    incl, shift = dws.selftest_wave(xd)
+    incl = from_device(incl, dtype).reshape(waves, 64)
+    shift = from_device(shift, dtype).reshape(waves, 64)
+    xr = x.reshape(waves, 64)
+    if dtype == "uint32":
+        want = (np.cumsum(xr.astype(np.uint64), axis=1) & 0xFFFFFFFF).astype(np.uint32)
+    else:
+        want = np.cumsum(xr.astype(np.float64), axis=1).astype(np.float32)
+    assert np.array_equal(incl, want)
+    want_shift = np.concatenate([np.zeros((waves, 1), dtype=xr.dtype), xr[:, :-1]], axis=1)
+    assert np.array_equal(shift, want_shift)
+
+
+# ---------------------------------------------------------------------------
+# sizes around tile and wave boundaries, all dtypes, both kinds
+# ---------------------------------------------------------------------------
+EDGE_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, TILE - 1, TILE, TILE + 1,
+              2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 65 * TILE - 3,
+              1_000_003]
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_edge_sizes(gpu, dtype, exclusive):
+    for n in EDGE_SIZES:
+        note(f"edge dtype={dtype} excl={exclusive} n={n}")
+        x = wl.random_input(dtype, n, seed=n)
+        y = _roundtrip(x, dtype, exclusive)
+        check(x, y, dtype, exclusive, label=f"n={n}")
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_in_place(gpu, dtype, exclusive):
+    for n in (5, 3 * TILE + 5, 1_000_003):
+        note(f"in-place dtype={dtype} excl={exclusive} n={n}")
+        x = wl.random_input(dtype, n, seed=7 + n)
+        y = _roundtrip(x, dtype, exclusive, in_place=True)
+        check(x, y, dtype, exclusive, label=f"in-place n={n}")
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_unaligned_pointers(gpu, dtype, exclusive):
+    # 4-byte aligned but not 16-byte aligned: the scalar-load kernel
+    for off in (1, 2, 3):
+        for n in (TILE - 1, 5 * TILE + 7, 300_001):
+            note(f"unaligned off={off} dtype={dtype} excl={exclusive} n={n}")
+            x = wl.random_input(dtype, n, seed=100 * off + n)
+            y = _roundtrip(x, dtype, exclusive, offset=off)
+            check(x, y, dtype, exclusive, label=f"offset {off} n={n}")
+            y = _roundtrip(x, dtype, exclusive, in_place=True, offset=off)
+            check(x, y, dtype, exclusive, label=f"in-place offset {off} n={n}")
+
+
+def test_input_aligned_output_unaligned(gpu):
+    import torch
+    n = 10 * TILE + 9
+    x = wl.random_input("int32", n, seed=3)
+    _, xd = to_device(x)
+    ostore = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    out = ostore[1:]
+    run(xd, out, n, "int32", False)
+    check(x, from_device(out, "int32"), "int32", False)
+
+
+# ---------------------------------------------------------------------------
+# comparison variants, tile shapes, descriptor memory order, non-temporal
+# ---------------------------------------------------------------------------
+VARIANT_SIZES = [1, TILE - 1, TILE + 1, 3 * TILE + 7, (1 << 20) + 3, 64 * 3 * TILE + 11]
+
+
+@pytest.mark.parametrize("variant", [dws.REDUCE_THEN_SCAN, dws.CHAINED], ids=["rts", "chained"])
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_comparison_variants(gpu, dtype, exclusive, variant):
+    for n in VARIANT_SIZES:
+        for in_place in (False, True):
+            note(f"variant={variant} dtype={dtype} excl={exclusive} n={n} in_place={in_place}")
+            x = wl.random_input(dtype, n, seed=n + variant)
+            y = _roundtrip(x, dtype, exclusive, in_place=in_place, variant=variant)
+            check(x, y, dtype, exclusive, label=f"variant {variant} n={n}")
+    # unaligned
+    n = 5 * TILE + 3
+    x = wl.random_input(dtype, n, seed=99)
+    y = _roundtrip(x, dtype, exclusive, offset=1, variant=variant)
+    check(x, y, dtype, exclusive, label=f"variant {variant} unaligned")
+
+
+def test_tile_shapes(gpu):
+    for shape in range(dws.num_tile_shapes()):
+        t = dws.tile_elems(shape, True)
+        for dtype in ("uint32", "float32"):
+            for exclusive in (False, True):
+                for n in (t - 1, 5 * t + 3, (1 << 21) + 1):
+                    note(f"shape={shape} dtype={dtype} excl={exclusive} n={n}")
+                    x = wl.random_input(dtype, n, seed=shape * 1000 + n)
+                    y = _roundtrip(x, dtype, exclusive, shape=shape)
+                    check(x, y, dtype, exclusive, label=f"shape {shape} n={n}")
+
+
+@pytest.mark.parametrize("opts", [dict(order=dws.ORDER_ACQ_REL), dict(nt=1),
+                                  dict(variant=dws.CHAINED, order=dws.ORDER_ACQ_REL)],
+                         ids=["acq_rel", "nontemporal", "chained_acq_rel"])
+def test_order_and_nontemporal(gpu, opts):
+    for dtype in DTYPES:
+        for exclusive in (False, True):
+            for n in (TILE + 1, (1 << 20) + 5, 40 * TILE):
+                note(f"opts={opts} dtype={dtype} excl={exclusive} n={n}")
+                x = wl.random_input(dtype, n, seed=n + 5)
+                y = _roundtrip(x, dtype, exclusive, in_place=exclusive, **opts)
+                check(x, y, dtype, exclusive, label=f"{opts} n={n}")
+    x = wl.random_input("float32", 3 * TILE + 1, seed=1)
+    y = _roundtrip(x, "float32", True, offset=1, **opts)   # non-temporal is a hint; unaligned ignores it
+    check(x, y, "float32", True)
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked examples and Fig 6, through the protocol-inspection kernel
+# ---------------------------------------------------------------------------
+def _debug(x, dtype, exclusive, tile_elems, variant=dws.SINGLE_PASS, **kw):
+    import torch
+    _, xd = to_device(x)
+    out = torch.empty_like(xd)
+    desc = dws.scan_debug(xd, out, tile_elems, exclusive=exclusive, variant=variant, **kw)
+    return from_device(out, dtype), desc
+
+
+@pytest.mark.parametrize("fname", ["pmpp_11_3_hierarchical_example.txt", "pmpp_11_2_coarsened_example.txt"])
+@pytest.mark.parametrize("variant", [dws.SINGLE_PASS, dws.CHAINED], ids=["lookback", "chained"])
+def test_page_worked_example(gpu, fname, variant):
+    g = read_golden(fname)
+    x = np.array(g["input"], dtype=np.int32)
+    note(f"worked example {fname} variant={variant}")
+    y, desc = _debug(x, "int32", False, g["block_size"], variant=variant)
+    assert y.tolist() == g["inclusive"]
+    epoch, status, value = decode_desc(desc)
+    assert status.tolist() == [2] * len(g["block_sums"])          # every tile ends P
+    assert len(set(epoch.tolist())) == 1 and epoch[0] > 0
+    assert value.view(np.int32).tolist() == g["scanned_block_sums"]  # S' of the example
+    ye, _ = _debug(x, "int32", True, g["block_size"], variant=variant)
+    assert ye.tolist() == [0] + g["inclusive"][:-1]
+    # the same example through the production kernel (one tile)
+    assert _roundtrip(x, "int32", False).tolist() == g["inclusive"]
+
+
+def test_fig6_snapshot_premise(gpu):
+    g = read_golden("decoupled_lookback_fig6.txt")
+    p, s = g["partitions"], g["partition_sum"]
+    rng = np.random.default_rng(6)
+    parts = [np.diff(np.concatenate([[0], np.sort(rng.integers(0, s + 1, size=4)), [s]])) for _ in range(p)]
+    x = np.concatenate(parts).astype(np.int32)
+    for delay_every in (0, 2, 3):
+        note(f"fig6 delay_every={delay_every}")
+        y, desc = _debug(x, "int32", False, 5, delay_every=delay_every, delay_phase=1 if delay_every else 0,
+                         delay_ticks=200_000)
+        check(x, y, "int32", False)
+        _, status, value = decode_desc(desc)
+        assert status.tolist() == [2] * p
+        assert value.view(np.int32).tolist() == [s * (t + 1) for t in range(p)]
+
+
+# ---------------------------------------------------------------------------
+# look-back protocol under stress: many small tiles, delayed publications
+# ---------------------------------------------------------------------------
+STRESS = [
+    # (tile_elems, n, delay_every, delay_phase, delay_ticks)
+    (1, 70_001, 0, 0, 0),
+    (3, 200_003, 0, 0, 0),
+    (64, 1_000_000, 0, 0, 0),
+    (7, 100_000, 97, 13, 20_000),     # 0.2 ms stalls before publishing A
+    (64, 640_000, 1001, 0, 200_000),  # tile 0 and every 1001st stall 2 ms
+    (2, 40_000, 5, 4, 2_000),
+]
+
+
+@pytest.mark.parametrize("variant", [dws.SINGLE_PASS, dws.CHAINED], ids=["lookback", "chained"])
+@pytest.mark.parametrize("dtype", ["uint32", "float32"])
+def test_lookback_protocol_stress(gpu, dtype, variant):
+    for tile_elems, n, every, phase, ticks in STRESS:
+        if variant == dws.CHAINED and ticks * max(1, n // max(every, 1) // tile_elems) > 50_000_000:
+            continue  # a serial chain would sum every stall; keep the case short
+        for exclusive in (False, True):
+            note(f"stress dtype={dtype} variant={variant} tile={tile_elems} n={n} delay={every}/{phase}/{ticks}")
+            x = wl.random_input(dtype, n, seed=tile_elems * 7 + n)
+            y, desc = _debug(x, dtype, exclusive, tile_elems, variant=variant, delay_every=every,
+                             delay_phase=phase, delay_ticks=ticks)
+            check(x, y, dtype, exclusive, label=f"stress tile={tile_elems} n={n}")
+            epoch, status, value = decode_desc(desc)
+            num_tiles = -(-n // tile_elems)
+            assert status.size == num_tiles
+            assert np.all(status == 2), "every tile must end with an inclusive prefix (P)"
+            assert np.all(epoch == epoch[0]) and epoch[0] > 0
+            ends = np.minimum(np.arange(1, num_tiles + 1) * tile_elems, n) - 1
+            if dtype == "uint32":
+                ref = oracle.scan_u32(x)
+                assert np.array_equal(value, ref[ends])
+            else:
+                ref, sabs = oracle.scan_f32(x)
+                got = value.view(np.float32).astype(np.float64)
+                assert np.all(np.abs(got - ref[ends]) <= 1e-4 * sabs[ends] + 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# repeated calls (epochs), several streams, determinism, special values
+# ---------------------------------------------------------------------------
+def test_repeated_calls_same_stream(gpu):
+    import torch
+    rng = np.random.default_rng(42)
+    sizes = [int(v) for v in rng.integers(1, 40 * TILE, size=30)] + [TILE + 1] * 5 + [1 << 20] * 3
+    for k, n in enumerate(sizes):
+        dtype = DTYPES[k % 3]
+        exclusive = bool(k & 1)
+        note(f"repeat k={k} n={n} dtype={dtype}")
+        x = wl.random_input(dtype, n, seed=k)
+        y = _roundtrip(x, dtype, exclusive, in_place=(k % 4 == 0))
+        check(x, y, dtype, exclusive, label=f"call {k}")
+    # many back-to-back calls without host synchronisation in between
+    x = wl.random_input("int32", 9 * TILE + 1, seed=5)
+    _, xd = to_device(x)
+    outs = [torch.empty_like(xd) for _ in range(50)]
+    for o in outs:
+        run(xd, o, x.size, "int32", False)
+    ref = oracle.scan_i32(x)
+    for o in outs:
+        assert np.array_equal(from_device(o, "int32"), ref)
+
+
+def test_concurrent_streams(gpu):
+    import torch
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    cases = []
+    for k, s in enumerate(streams):
+        n = (k + 1) * 37 * TILE + k
+        x = wl.random_input("uint32", n, seed=200 + k)
+        _, xd = to_device(x)
+        out = torch.empty_like(xd)
+        cases.append((x, xd, out, s))
+    torch.cuda.synchronize()
+    note("concurrent streams")
+    for rep in range(3):
+        for x, xd, out, s in cases:
+            with torch.cuda.stream(s):
+                run(xd, out, x.size, "uint32", rep == 1)
+        torch.cuda.synchronize()
+        for x, xd, out, s in cases:
+            check(x, from_device(out, "uint32"), "uint32", rep == 1, label="stream")
+
+
+def test_integer_results_are_deterministic(gpu):
+    n = 1 << 24
+    x = wl.random_input("int32", n, seed=8)
+    a = _roundtrip(x, "int32", True)
+    b = _roundtrip(x, "int32", True)
+    assert np.array_equal(a, b)
+    check(x, a, "int32", True)
+
+
+def test_special_values(gpu):
+    n = 3 * TILE + 11
+    cases = [
+        ("int32", np.full(n, 2**31 - 1, dtype=np.int32)),          # wraps every other element
+        ("uint32", np.full(n, 0xFFFFFFFF, dtype=np.uint32)),        # y[i] = -(i+1) mod 2^32
+        ("int32", np.full(n, -1, dtype=np.int32)),
+        ("float32", np.zeros(n, dtype=np.float32)),
+        ("float32", np.ones(n, dtype=np.float32)),
+        ("float32", wl.generate("f32_normal", 1 << 20, 3) * np.float32(1e3)),
+        ("float32", np.full(n, -0.25, dtype=np.float32)),
+    ]
+    for dtype, x in cases:
+        for exclusive in (False, True):
+            note(f"special dtype={dtype} excl={exclusive} first={x[0]!r}")
+            y = _roundtrip(x, dtype, exclusive)
+            check(x, y, dtype, exclusive)
+    # closed forms, exactly
+    ones = np.ones(n, dtype=np.float32)
+    assert np.array_equal(_roundtrip(ones, "float32", False), np.arange(1, n + 1, dtype=np.float32))
+    assert np.array_equal(_roundtrip(ones, "float32", True), np.arange(n, dtype=np.float32))
+    y = _roundtrip(np.full(n, 0xFFFFFFFF, dtype=np.uint32), "uint32", False)
+    assert np.array_equal(y.astype(np.int64), (-(np.arange(1, n + 1, dtype=np.int64))) & 0xFFFFFFFF)
+
+
+def test_errors_enqueue_nothing(gpu):
+    import torch
+    x = torch.arange(1000, dtype=torch.int32, device="cuda")
+    before = x.clone()
+    st = dws.scan_inclusive_ptr(x.data_ptr(), x.data_ptr() + 4, 999, dws.INT32,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == dws.ERR_OVERLAP
+    torch.cuda.synchronize()
+    assert torch.equal(x, before)
+    with pytest.raises(dws.ScanError):
+        dws.scan_ex(x, variant=7)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark
+# times (default options through scan_inclusive / scan_exclusive)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_workload_full_size(gpu, name):
+    import torch
+    w = wl.WORKLOADS[name]
+    note(f"workload {name}: {w.description}")
+    x = wl.generate_workload(w)
+    store, xd = to_device(x)
+    out = xd if w.in_place else torch.empty_like(xd)
+    if w.dtype == "uint32":
+        run(xd, out, x.size, "uint32", w.exclusive)
+    else:
+        (dws.scan_exclusive if w.exclusive else dws.scan_inclusive)(xd, out=out)
+    torch.cuda.synchronize()
+    y = from_device(out, w.dtype)
+    del store, xd, out
+    worst = check_chunked(x, y, w.dtype, w.exclusive, label=name)
+    note(f"workload {name}: parity ok, max fp32 tolerance ratio {worst:.3g}")
+    if name == "C5":
+        # stream-compaction offsets: the exclusive scan of 0/1 flags ends at
+        # popcount - last flag
+        assert int(y[-1]) + int(x[-1]) == int(x.sum(dtype=np.int64))
+
+
+def test_zz_watchdog_never_tripped(gpu):
+    assert dws.watchdog_trips() == 0
