@@ -141,8 +141,8 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
         ok = abs(last - tot) <= 1e-4 * sabs + 1e-6
         if w.exclusive:
             ok = ok and float(y[0]) == 0.0
-        if np.all(x >= 0):
-            ok = ok and bool(np.all(np.diff(y) >= 0))
+        # (no monotonicity check: fp32 prefixes reached through different
+        # rounding paths may step back by an ulp where x[i] is below the ulp)
     else:
         tot = int(np.sum(x.astype(np.int64))) & 0xFFFFFFFF
         last = (int(y[-1].view(np.uint32) if w.dtype == "int32" else y[-1]) +

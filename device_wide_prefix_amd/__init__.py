@@ -75,9 +75,9 @@ def load_library():
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
     lib.dws_num_tile_shapes.restype = ci
-    lib.dws_tile_elems.argtypes = [ci, ci]
+    lib.dws_tile_elems.argtypes = [ci, sz, ci]
     lib.dws_tile_elems.restype = cu
-    lib.dws_tile_threads.argtypes = [ci, ci]
+    lib.dws_tile_threads.argtypes = [ci, sz, ci]
     lib.dws_tile_threads.restype = cu
     lib.dws_reserve.argtypes = [sz, vp]
     lib.dws_reserve.restype = ci
@@ -239,12 +239,14 @@ def release_workspaces():
     _check(load_library().dws_release_workspaces(), "dws_release_workspaces")
 
 
-def tile_elems(tile_shape: int = 0, aligned: bool = True) -> int:
-    return int(load_library().dws_tile_elems(int(tile_shape), int(bool(aligned))))
+def tile_elems(tile_shape: int = 0, n: int = 1 << 28, aligned: bool = True) -> int:
+    """Elements per tile the single-pass kernel uses (tile_shape 0 = automatic
+    choice for n)."""
+    return int(load_library().dws_tile_elems(int(tile_shape), int(n), int(bool(aligned))))
 
 
-def tile_threads(tile_shape: int = 0, aligned: bool = True) -> int:
-    return int(load_library().dws_tile_threads(int(tile_shape), int(bool(aligned))))
+def tile_threads(tile_shape: int = 0, n: int = 1 << 28, aligned: bool = True) -> int:
+    return int(load_library().dws_tile_threads(int(tile_shape), int(n), int(bool(aligned))))
 
 
 def num_tile_shapes() -> int:

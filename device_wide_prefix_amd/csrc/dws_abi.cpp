@@ -176,29 +176,29 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
                            const dws_options& o, hipStream_t stream)
 {
     const bool aligned = aligned16(in, out);
-    // non-temporal access is a hint, built for the aligned default shape only
+    // non-temporal access is a hint, built for aligned pointers only
     const bool nt = o.nontemporal != 0 && aligned;
-    if (!single_pass_available(o.tile_shape, aligned, o.memory_order, mode, nt)) return DWS_ERR_UNSUPPORTED;
-    const uint64_t tile = single_pass_tile_elems(o.tile_shape, aligned);
-    const uint64_t threads = single_pass_threads(o.tile_shape, aligned);
-    const uint64_t num_tiles = ceil_div(n, tile);
-    if (num_tiles > 0xffffffffull || num_tiles * threads > kMaxGridThreads) return DWS_ERR_UNSUPPORTED;
+    const int shape = resolve_shape(o.tile_shape, n, aligned);
+    if (shape < 0) return DWS_ERR_INVALID_ARG;
+    const int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt);
+    if (cfg < 0) return DWS_ERR_UNSUPPORTED;
+    const TileShape ts = cfg_shape(kCfgs[cfg]);
+    const uint64_t num_tiles = ceil_div(n, (uint64_t)ts.elems());
+    if (num_tiles > 0xffffffffull || num_tiles * (uint64_t)ts.threads > kMaxGridThreads) return DWS_ERR_UNSUPPORTED;
 
-    SinglePassArgs a{};
-    a.in = in;
-    a.out = out;
-    a.n = n;
-    a.kind = kind_of(dtype);
-    a.exclusive = excl;
-    a.aligned = aligned;
-    a.shape = o.tile_shape;
-    a.order = o.memory_order;
-    a.mode = mode;
-    a.nontemporal = nt;
-    a.num_tiles = (uint32_t)num_tiles;
+    SinglePassParams p{};
+    p.in = in;
+    p.out = out;
+    p.n = n;
+    p.num_tiles = (uint32_t)num_tiles;
+    const bool f32 = kind_of(dtype) == kKindF32;
+    auto launch = [&]() {
+        return f32 ? launch_single_pass_typed<float>(cfg, excl, p, stream)
+                   : launch_single_pass_typed<uint32_t>(cfg, excl, p, stream);
+    };
     if (num_tiles == 1) {
         // one tile: no predecessors, no descriptors, no counter
-        return from_hip(launch_single_pass(a, stream));
+        return from_hip(launch());
     }
     Workspace* ws = nullptr;
     dws_status s = get_workspace(stream, &ws);
@@ -208,10 +208,10 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     if (s != DWS_OK) return s;
     s = before_draw_launch(ws);
     if (s != DWS_OK) return s;
-    a.desc = ws->desc;
-    a.counter = ws->counter();
-    a.watchdog = ws->watchdog();
-    s = from_hip(launch_single_pass(a, stream));
+    p.desc = ws->desc;
+    p.counter = ws->counter();
+    p.watchdog = ws->watchdog();
+    s = from_hip(launch());
     if (s == DWS_OK) ++ws->draws_launches;
     return s;
 }
@@ -219,7 +219,7 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
 dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hipStream_t stream)
 {
     const bool aligned = aligned16(in, out);
-    const uint64_t tile = rts_tile_elems(aligned);
+    const uint64_t tile = kRtsTileElems;
     const uint64_t num_tiles = ceil_div(n, tile);
     if (num_tiles > 0xffffffffull) return DWS_ERR_UNSUPPORTED;
     uint64_t groups = std::min<uint64_t>({num_tiles, (uint64_t)cu_count() * 8u, (uint64_t)kRtsMaxGroups});
@@ -252,7 +252,7 @@ dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclus
         if (o.variant < DWS_VARIANT_SINGLE_PASS || o.variant > DWS_VARIANT_CHAINED) return DWS_ERR_INVALID_ARG;
         if (o.memory_order != DWS_ORDER_RELAXED && o.memory_order != DWS_ORDER_ACQ_REL)
             return DWS_ERR_INVALID_ARG;
-        if (o.tile_shape < 0 || o.tile_shape >= kNumShapes) return DWS_ERR_INVALID_ARG;
+        if (o.tile_shape < 0 || o.tile_shape > kNumShapes) return DWS_ERR_INVALID_ARG;
         if (o.nontemporal != 0 && o.nontemporal != 1) return DWS_ERR_INVALID_ARG;
         dws_status s = validate(in, out, n, dtype);
         if (s != DWS_OK || n == 0) return s;
@@ -309,16 +309,26 @@ const char* dws_status_string(dws_status status)
 
 int dws_version(void) { return DWS_VERSION; }
 
-int dws_num_tile_shapes(void) { return kNumShapes; }
+int dws_num_tile_shapes(void) { return kNumShapes + 1; }
 
-unsigned dws_tile_elems(int tile_shape, int aligned)
+static int shape_for(int tile_shape, size_t n, int aligned)
 {
-    return single_pass_tile_elems(tile_shape, aligned != 0);
+    if (tile_shape < 0 || tile_shape > kNumShapes) return -1;
+    return resolve_shape(tile_shape, n, aligned != 0);
 }
 
-unsigned dws_tile_threads(int tile_shape, int aligned)
+unsigned dws_tile_elems(int tile_shape, size_t n, int aligned)
 {
-    return single_pass_threads(tile_shape, aligned != 0);
+    const int s = shape_for(tile_shape, n, aligned);
+    if (s < 0) return 0;
+    return (unsigned)(aligned ? kShapes[s] : scalar_shape(kShapes[s])).elems();
+}
+
+unsigned dws_tile_threads(int tile_shape, size_t n, int aligned)
+{
+    const int s = shape_for(tile_shape, n, aligned);
+    if (s < 0) return 0;
+    return (unsigned)kShapes[s].threads;
 }
 
 dws_status dws_reserve(size_t n, hipStream_t stream)
@@ -329,8 +339,7 @@ dws_status dws_reserve(size_t n, hipStream_t stream)
         dws_status s = get_workspace(stream, &ws);
         if (s != DWS_OK) return s;
         uint32_t min_tile = 0xffffffffu;
-        for (int i = 0; i < kNumShapes; ++i)
-            min_tile = std::min(min_tile, std::min(single_pass_tile_elems(i, true), single_pass_tile_elems(i, false)));
+        for (int i = 0; i < kNumShapes; ++i) min_tile = std::min(min_tile, (uint32_t)kShapes[i].elems());
         std::lock_guard<std::mutex> lock(ws->mu);
         return ensure_desc(ws, ceil_div(std::max<uint64_t>(n, 1), min_tile));
     } catch (...) {

@@ -126,11 +126,7 @@ __global__ void __launch_bounds__(BLOCK)
     }
 }
 
-uint32_t rts_tile_elems(bool aligned)
-{
-    (void)aligned;
-    return 4096u;
-}
+static_assert(kRtsThreads * 16 == (int)kRtsTileElems, "reduce-then-scan tiles are 256 threads x 16 elements");
 
 template <class T, bool EXCL, int VEC, int CHUNKS>
 static hipError_t launch_rts_typed(const RtsArgs& a, hipStream_t stream)
@@ -226,7 +222,7 @@ __global__ void __launch_bounds__(64) k_debug(DebugParams p)
             if constexpr (MODE == kModeDecoupled) {
                 if (lane == 0)
                     desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
-                prefix = lookback_decoupled<T, kOrderRelaxed>(p.desc, tile, epoch, p.watchdog);
+                prefix = lookback_decoupled<T, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
             } else {
                 prefix = lookback_chained<T, kOrderRelaxed>(p.desc, tile, epoch, p.watchdog);
             }

@@ -277,17 +277,25 @@ __device__ __forceinline__ void draw_tile(unsigned long long* counter, uint32_t 
 }
 
 // Decoupled look-back by one whole wavefront (section 4.4, parallelized
-// look-back): lane l inspects the descriptor of tile hi - l, so each step
-// covers 64 predecessors. If any of the lanes up to and including the nearest
-// P is still X, the window is polled again. Otherwise those lanes' values are
-// summed into the running exclusive prefix (aggregates of the A lanes plus the
+// look-back), widened to K slots per lane: slot j of lane l inspects the
+// descriptor of tile hi - (64 j + l), so one poll covers 64 K predecessors with
+// K independent loads per lane in flight at once. The nearest P is the lowest
+// lane of the lowest slot that holds one. If any descriptor from tile - 1 back
+// to that P (or back through the whole window when there is none) is still X,
+// the window is polled again. Otherwise those descriptors' values are summed
+// into the running exclusive prefix (aggregates of the A tiles plus the
 // inclusive prefix of the nearest P); with a P the look-back ends, without one
-// the window slides back by 64. Indices below 0 read as P with value 0, so the
-// walk always ends at tile 0 at the latest. Returns the exclusive prefix of
+// the window slides back by 64 K. Indices below 0 read as P with value 0, so
+// the walk ends at tile 0 at the latest. Returns the exclusive prefix of
 // `tile` (uniform). A wait longer than kWatchdogTicks counts one trip in
 // *watchdog and returns the incomplete prefix instead of hanging. Call with the
 // whole wave active.
-template <class T, int ORDER>
+//
+// Why K > 1: a tile publishes P only after its own look-back, so if one poll
+// of latency L covers W predecessors, P can advance by at most W tiles per L.
+// Tiles arriving faster than W / L fall further and further behind the last
+// P and need ever more polls; W = 64 K keeps W / L above the tile rate.
+template <class T, int ORDER, int K>
 __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t epoch,
                                unsigned int* watchdog)
 {
@@ -297,18 +305,44 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
     int64_t hi = (int64_t)tile - 1;
     const uint64_t t0 = realtime();
     for (;;) {
-        const int64_t idx = hi - lane;
-        const uint64_t d = (idx >= 0) ? desc_load<ORDER>(desc + idx) : desc_pack(epoch, kStatusP, 0u);
-        const uint32_t st = desc_status(d, epoch);
-        const uint64_t has_p = __builtin_amdgcn_ballot_w64(st == kStatusP);
-        const uint64_t has_x = __builtin_amdgcn_ballot_w64(st == kStatusX);
-        // lanes 0 .. nearest P inclusive; all 64 lanes when no P is in view
-        const uint64_t need = has_p ? (has_p ^ (has_p - 1ull)) : ~0ull;
-        if ((has_x & need) == 0ull) {
-            const T v = (need & lane_bit) ? Elem<T>::from((uint32_t)d) : T(0);
+        uint64_t d[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t idx = hi - (int64_t)(j * 64 + lane);
+            d[j] = (idx >= 0) ? desc_load<ORDER>(desc + idx) : desc_pack(epoch, kStatusP, 0u);
+        }
+        uint64_t has_p[K], has_x[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint32_t st = desc_status(d[j], epoch);
+            has_p[j] = __builtin_amdgcn_ballot_w64(st == kStatusP);
+            has_x[j] = __builtin_amdgcn_ballot_w64(st == kStatusX);
+        }
+        // slot of the nearest P (K if none) and the lanes needed in it
+        int jp = K;
+#pragma unroll
+        for (int j = K - 1; j >= 0; --j)
+            if (has_p[j]) jp = j;
+        bool blocked = false;
+        uint64_t need_p = 0ull;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (j < jp && has_x[j]) blocked = true;
+            if (j == jp) {
+                need_p = has_p[j] ^ (has_p[j] - 1ull);   // lanes 0 .. lowest P
+                if (has_x[j] & need_p) blocked = true;
+            }
+        }
+        if (!blocked) {
+            T v = T(0);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const uint64_t need = (j < jp) ? ~0ull : ((j == jp) ? need_p : 0ull);
+                if (need & lane_bit) v = v + Elem<T>::from((uint32_t)d[j]);
+            }
             prefix = prefix + wave_sum(v);
-            if (has_p) return prefix;
-            hi -= 64;
+            if (jp < K) return prefix;
+            hi -= 64 * K;
             continue;
         }
         if (realtime() - t0 > kWatchdogTicks) {

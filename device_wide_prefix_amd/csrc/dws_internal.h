@@ -15,29 +15,28 @@ constexpr size_t kCtlBytes = 256;
 constexpr size_t kCtlCounterOffset = 0;
 constexpr size_t kCtlWatchdogOffset = 128;
 
-struct SinglePassArgs {
+// Kernel arguments of the single-pass scan.
+struct SinglePassParams {
     const void* in;
     void* out;
     uint64_t n;
-    int kind;              // kKindU32 / kKindF32
-    bool exclusive;
-    bool aligned;          // both pointers 16-byte aligned
-    int shape;             // index into kAlignedShapes
-    int order;             // kOrderRelaxed / kOrderAcqRel
-    int mode;              // kModeDecoupled / kModeChained
-    bool nontemporal;
     uint64_t* desc;        // >= num_tiles slots (unused when num_tiles == 1)
     unsigned long long* counter;
     unsigned int* watchdog;
     uint32_t num_tiles;
 };
 
-// Whether a single-pass kernel with these compile-time parameters is built.
-bool single_pass_available(int shape, bool aligned, int order, int mode, bool nontemporal);
-// Elements per tile and threads per workgroup of the kernel the launcher uses.
-uint32_t single_pass_tile_elems(int shape, bool aligned);
-uint32_t single_pass_threads(int shape, bool aligned);
-hipError_t launch_single_pass(const SinglePassArgs& a, hipStream_t stream);
+// Launch built configuration `cfg` (index into kCfgs) for element type T
+// (uint32_t or float; instantiated in dws_sp_u32.hip / dws_sp_f32.hip).
+template <class T>
+hipError_t launch_single_pass_typed(int cfg, bool exclusive, const SinglePassParams& p, hipStream_t stream);
+
+// Shape index (into kShapes) used for an option value (0 = automatic) and n.
+// Pointers that are not both 16-byte aligned use the scalar-load version of
+// the shape, or of the automatic shape if that one is not built.
+int resolve_shape(int option_shape, uint64_t n, bool aligned);
+// Index into kCfgs of the kernel for these parameters, or -1 if not built.
+int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal);
 
 struct RtsArgs {
     const void* in;
@@ -51,7 +50,7 @@ struct RtsArgs {
     uint32_t groups;
     uint32_t tiles_per_group;
 };
-uint32_t rts_tile_elems(bool aligned);
+constexpr uint32_t kRtsTileElems = 4096u;
 hipError_t launch_rts(const RtsArgs& a, hipStream_t stream);
 
 struct DebugArgs {

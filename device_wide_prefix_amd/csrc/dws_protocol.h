@@ -35,7 +35,8 @@ constexpr int kKindU32 = 0;
 constexpr int kKindF32 = 1;
 
 // Tile shapes of the single-pass kernel: threads per workgroup, elements per
-// load (4 = one dwordx4 per lane) and loads per lane.
+// load (4 = one dwordx4 per lane, 1 = scalar loads for pointers that are not
+// 16-byte aligned) and loads per lane.
 struct TileShape {
     int threads;
     int vec;
@@ -43,18 +44,72 @@ struct TileShape {
     constexpr int elems() const { return threads * vec * chunks; }
 };
 
-// index 0 is the default; the unaligned path uses VEC 1 with the same tile size
-constexpr TileShape kAlignedShapes[] = {
-    {256, 4, 4},    // 4096 elements (16 KiB)
-    {256, 4, 8},    // 8192
-    {512, 4, 4},    // 8192
-    {512, 4, 8},    // 16384
-    {1024, 4, 4},   // 16384
-    {128, 4, 8},    // 4096
+// Explicit shapes (option tile_shape = index + 1; tile_shape 0 is automatic).
+// Large tiles matter on this GPU: every tile costs one draw on the single
+// tile counter and a look-back wait for its slowest predecessor, during which
+// the workgroup holds its registers without loading. 32K-65K-element tiles
+// keep enough bytes in flight to run at memory speed.
+constexpr TileShape kShapes[] = {
+    {256, 4, 4},     // 0:  4096 elements (16 KiB)
+    {256, 4, 8},     // 1:  8192
+    {512, 4, 8},     // 2:  16384
+    {1024, 4, 4},    // 3:  16384
+    {1024, 4, 8},    // 4:  32768
+    {1024, 4, 16},   // 5:  65536 (256 KiB)
 };
-constexpr int kNumShapes = (int)(sizeof(kAlignedShapes) / sizeof(kAlignedShapes[0]));
+constexpr int kNumShapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
 
-constexpr TileShape unaligned_shape(const TileShape& s) { return TileShape{s.threads, 1, s.vec * s.chunks}; }
+// Automatic shape, from a size sweep on MI355X (fp32, exclusive, in place):
+// the best tile grows with n as long as every CU still gets tiles.
+constexpr uint64_t kAutoHugeMin = (uint64_t)1 << 24;    // 65536-element tiles
+constexpr uint64_t kAutoLargeMin = (uint64_t)1 << 22;   // 32768
+constexpr uint64_t kAutoMediumMin = (uint64_t)1 << 20;  // 16384 (512 threads)
+
+constexpr int auto_shape(uint64_t n)
+{
+    return n >= kAutoHugeMin ? 5 : (n >= kAutoLargeMin ? 4 : (n >= kAutoMediumMin ? 2 : 0));
+}
+
+constexpr TileShape scalar_shape(const TileShape& s) { return TileShape{s.threads, 1, s.vec * s.chunks}; }
+
+// Look-back width: descriptors per lane per poll (64 * K per poll).
+constexpr int kLookbackSlots = 4;
+
+// Built single-pass kernel configurations. Shape index into kShapes; vec 1
+// means the scalar-load version of that shape.
+struct KernelCfg {
+    int shape, vec, order, mode;
+    bool nt;
+};
+
+#define DWS_AUTO_SHAPES(VEC, ORDER, MODE, NT) \
+    {0, VEC, ORDER, MODE, NT}, {2, VEC, ORDER, MODE, NT}, {4, VEC, ORDER, MODE, NT}, {5, VEC, ORDER, MODE, NT}
+
+constexpr KernelCfg kCfgs[] = {
+    // decoupled look-back, relaxed descriptor atomics: every shape, and the
+    // scalar-load versions of the automatic shapes
+    {1, 4, kOrderRelaxed, kModeDecoupled, false},
+    {3, 4, kOrderRelaxed, kModeDecoupled, false},
+    DWS_AUTO_SHAPES(4, kOrderRelaxed, kModeDecoupled, false),
+    DWS_AUTO_SHAPES(1, kOrderRelaxed, kModeDecoupled, false),
+    // release/acquire descriptors
+    DWS_AUTO_SHAPES(4, kOrderAcqRel, kModeDecoupled, false),
+    DWS_AUTO_SHAPES(1, kOrderAcqRel, kModeDecoupled, false),
+    // non-temporal loads and stores (aligned pointers only)
+    DWS_AUTO_SHAPES(4, kOrderRelaxed, kModeDecoupled, true),
+    // chained scan
+    DWS_AUTO_SHAPES(4, kOrderRelaxed, kModeChained, false),
+    DWS_AUTO_SHAPES(1, kOrderRelaxed, kModeChained, false),
+    DWS_AUTO_SHAPES(4, kOrderAcqRel, kModeChained, false),
+    DWS_AUTO_SHAPES(1, kOrderAcqRel, kModeChained, false),
+};
+#undef DWS_AUTO_SHAPES
+constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
+
+constexpr TileShape cfg_shape(const KernelCfg& c)
+{
+    return c.vec == 4 ? kShapes[c.shape] : scalar_shape(kShapes[c.shape]);
+}
 
 // Reduce-then-scan: at most this many chunks (one partial each).
 constexpr uint32_t kRtsMaxGroups = 4096u;

@@ -17,22 +17,14 @@
 //   5. every element gets prefix + wave prefix + chunk/lane prefix + its
 //      serial in-lane prefix, and the tile is stored. The whole tile is in
 //      registers before the first store, so d_out == d_in is safe.
+#pragma once
+
 #include <utility>
 
 #include "dws_device.hpp"
 #include "dws_internal.h"
 
 namespace dws {
-
-struct SinglePassParams {
-    const void* in;
-    void* out;
-    uint64_t n;
-    uint64_t* desc;
-    unsigned long long* counter;
-    unsigned int* watchdog;
-    uint32_t num_tiles;
-};
 
 template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT>
 __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
@@ -95,7 +87,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)
                         desc_store<ORDER>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
-                    prefix = lookback_decoupled<T, ORDER>(p.desc, tile, epoch, p.watchdog);
+                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
@@ -115,109 +107,37 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Built kernel configurations.
+// Launch of built configuration `cfg` (index into kCfgs) for element type T.
+// Each element type is instantiated in its own translation unit.
 // ---------------------------------------------------------------------------
-struct KernelCfg {
-    int threads, vec, chunks, order, mode;
-    bool nt;
-};
-
-constexpr KernelCfg kCfgs[] = {
-    // decoupled look-back, relaxed descriptor atomics: every aligned shape
-    {kAlignedShapes[0].threads, 4, kAlignedShapes[0].chunks, kOrderRelaxed, kModeDecoupled, false},
-    {kAlignedShapes[1].threads, 4, kAlignedShapes[1].chunks, kOrderRelaxed, kModeDecoupled, false},
-    {kAlignedShapes[2].threads, 4, kAlignedShapes[2].chunks, kOrderRelaxed, kModeDecoupled, false},
-    {kAlignedShapes[3].threads, 4, kAlignedShapes[3].chunks, kOrderRelaxed, kModeDecoupled, false},
-    {kAlignedShapes[4].threads, 4, kAlignedShapes[4].chunks, kOrderRelaxed, kModeDecoupled, false},
-    {kAlignedShapes[5].threads, 4, kAlignedShapes[5].chunks, kOrderRelaxed, kModeDecoupled, false},
-    // default shape: unaligned (scalar loads), release/acquire, non-temporal
-    {256, 1, 16, kOrderRelaxed, kModeDecoupled, false},
-    {256, 4, 4, kOrderAcqRel, kModeDecoupled, false},
-    {256, 1, 16, kOrderAcqRel, kModeDecoupled, false},
-    {256, 4, 4, kOrderRelaxed, kModeDecoupled, true},
-    // chained scan
-    {256, 4, 4, kOrderRelaxed, kModeChained, false},
-    {256, 4, 4, kOrderAcqRel, kModeChained, false},
-    {256, 1, 16, kOrderRelaxed, kModeChained, false},
-    {256, 1, 16, kOrderAcqRel, kModeChained, false},
-};
-constexpr size_t kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
-
-static_assert(kAlignedShapes[0].threads == 256 && kAlignedShapes[0].vec == 4 &&
-                  kAlignedShapes[0].chunks == 4,
-              "the unaligned and comparison kernels assume the default shape 256 x 4 x 4");
-
-static TileShape shape_of(int shape, bool aligned)
-{
-    const TileShape s = kAlignedShapes[shape];
-    // unaligned pointers always take the default shape with scalar loads
-    return aligned ? s : unaligned_shape(kAlignedShapes[0]);
-}
-
-static int find_cfg(int shape, bool aligned, int order, int mode, bool nt)
-{
-    if (shape < 0 || shape >= kNumShapes) return -1;
-    const TileShape s = shape_of(shape, aligned);
-    for (size_t i = 0; i < kNumCfgs; ++i) {
-        const KernelCfg& c = kCfgs[i];
-        if (c.threads == s.threads && c.vec == s.vec && c.chunks == s.chunks && c.order == order &&
-            c.mode == mode && c.nt == nt)
-            return (int)i;
-    }
-    return -1;
-}
-
-bool single_pass_available(int shape, bool aligned, int order, int mode, bool nontemporal)
-{
-    return find_cfg(shape, aligned, order, mode, nontemporal) >= 0;
-}
-
-uint32_t single_pass_tile_elems(int shape, bool aligned)
-{
-    if (shape < 0 || shape >= kNumShapes) return 0;
-    return (uint32_t)shape_of(shape, aligned).elems();
-}
-
-uint32_t single_pass_threads(int shape, bool aligned)
-{
-    if (shape < 0 || shape >= kNumShapes) return 0;
-    return (uint32_t)shape_of(shape, aligned).threads;
-}
-
-template <class T, bool EXCL, size_t I>
-static hipError_t launch_typed(const SinglePassParams& p, hipStream_t stream)
+template <class T, bool EXCL, int I>
+static hipError_t launch_cfg(const SinglePassParams& p, hipStream_t stream)
 {
     constexpr KernelCfg c = kCfgs[I];
+    constexpr TileShape s = cfg_shape(c);
     const void* fn = reinterpret_cast<const void*>(
-        &k_single_pass<T, EXCL, c.threads, c.vec, c.chunks, c.order, c.mode, c.nt>);
+        &k_single_pass<T, EXCL, s.threads, s.vec, s.chunks, c.order, c.mode, c.nt>);
     SinglePassParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(c.threads), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(s.threads), args, 0, stream);
 }
 
-template <size_t I>
-static hipError_t launch_cfg(const SinglePassArgs& a, hipStream_t stream)
-{
-    const SinglePassParams p{a.in, a.out, a.n, a.desc, a.counter, a.watchdog, a.num_tiles};
-    if (a.kind == kKindF32)
-        return a.exclusive ? launch_typed<float, true, I>(p, stream) : launch_typed<float, false, I>(p, stream);
-    return a.exclusive ? launch_typed<uint32_t, true, I>(p, stream) : launch_typed<uint32_t, false, I>(p, stream);
-}
-
-template <size_t... I>
-static hipError_t dispatch(int idx, const SinglePassArgs& a, hipStream_t stream, std::index_sequence<I...>)
+template <class T, int... I>
+static hipError_t dispatch_cfg(int cfg, bool exclusive, const SinglePassParams& p, hipStream_t stream,
+                               std::integer_sequence<int, I...>)
 {
     hipError_t r = hipErrorInvalidValue;
-    (void)((idx == (int)I ? (r = launch_cfg<I>(a, stream), true) : false) || ...);
+    (void)((cfg == I ? (r = exclusive ? launch_cfg<T, true, I>(p, stream) : launch_cfg<T, false, I>(p, stream),
+                        true)
+                     : false) ||
+           ...);
     return r;
 }
 
-hipError_t launch_single_pass(const SinglePassArgs& a, hipStream_t stream)
+template <class T>
+hipError_t launch_single_pass_typed(int cfg, bool exclusive, const SinglePassParams& p, hipStream_t stream)
 {
-    const int idx = find_cfg(a.shape, a.aligned, a.order, a.mode, a.nontemporal);
-    if (idx < 0) return hipErrorInvalidValue;
-    if (a.num_tiles == 0u) return hipSuccess;
-    return dispatch(idx, a, stream, std::make_index_sequence<kNumCfgs>{});
+    return dispatch_cfg<T>(cfg, exclusive, p, stream, std::make_integer_sequence<int, kNumCfgs>{});
 }
 
 }  // namespace dws

@@ -117,9 +117,11 @@ typedef enum dws_memory_order {
 typedef struct dws_options {
     int variant;        /* dws_variant; default DWS_VARIANT_SINGLE_PASS */
     int memory_order;   /* dws_memory_order; default DWS_ORDER_RELAXED */
-    int tile_shape;     /* 0 = default (256 threads x 16 elements); other
-                           indices < dws_num_tile_shapes() select other tile
-                           shapes of the single-pass kernel, for sweeps */
+    int tile_shape;     /* 0 = automatic (by n: 65536-element tiles from
+                           2^24 elements, 32768 from 2^22, 16384 from 2^20,
+                           else 4096);
+                           1 .. dws_num_tile_shapes()-1 force one shape of
+                           the single-pass kernel, for sweeps */
     int nontemporal;    /* 1 = non-temporal (streaming) loads and stores */
 } dws_options;
 
@@ -127,12 +129,14 @@ typedef struct dws_options {
  * Scan with explicit options. opt == NULL (or a zeroed struct) means all
  * defaults; exclusive != 0 selects the exclusive scan. Unknown values give
  * DWS_ERR_INVALID_ARG. Built combinations (others give DWS_ERR_UNSUPPORTED):
- *   single pass: any tile_shape with relaxed order; tile_shape 0 also with
- *                release/acquire, and with nontemporal (relaxed);
- *   chained:     tile_shape 0, either order;
+ *   single pass: every tile_shape with relaxed order; the automatically
+ *                chosen shapes also with release/acquire and with
+ *                nontemporal (relaxed);
+ *   chained:     the automatically chosen shapes, either order;
  *   reduce-then-scan: tile_shape 0, nontemporal 0 (memory_order ignored).
- * Pointers that are not both 16-byte aligned use the scalar-load kernel of
- * tile_shape 0 whatever tile_shape asks for, and ignore nontemporal.
+ * Pointers that are not both 16-byte aligned use scalar loads; a forced
+ * shape without a scalar-load kernel then falls back to the automatic one,
+ * and nontemporal is ignored.
  */
 dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                        int exclusive, const dws_options* opt, hipStream_t stream);
@@ -145,17 +149,18 @@ int dws_version(void);
 
 /* ---- tile geometry (host only, no HIP call) ---------------------------- */
 
-/* Number of tile shapes of the single-pass kernel (index 0 is the default). */
+/* Number of tile_shape option values (0 = automatic, then forced shapes). */
 int dws_num_tile_shapes(void);
 
 /*
- * Elements per tile for a tile shape and alignment class (aligned != 0: both
- * pointers 16-byte aligned). Returns 0 for an unknown shape.
+ * Elements per tile the single-pass kernel uses for a tile_shape option value,
+ * n elements and an alignment class (aligned != 0: both pointers 16-byte
+ * aligned). Returns 0 for an unknown shape.
  */
-unsigned dws_tile_elems(int tile_shape, int aligned);
+unsigned dws_tile_elems(int tile_shape, size_t n, int aligned);
 
-/* Threads per workgroup of a tile shape (0 for an unknown shape). */
-unsigned dws_tile_threads(int tile_shape, int aligned);
+/* Threads per workgroup for the same arguments (0 for an unknown shape). */
+unsigned dws_tile_threads(int tile_shape, size_t n, int aligned);
 
 /* ---- workspace ---------------------------------------------------------- */
 

@@ -51,18 +51,24 @@ def test_version_and_status_strings(lib):
 
 
 def test_tile_geometry(lib):
-    n = dws.num_tile_shapes()
-    assert n >= 1
-    assert dws.tile_elems(0, True) == 4096
-    assert dws.tile_threads(0, True) == 256
-    assert dws.tile_elems(0, False) == 4096
-    for s in range(n):
-        e, t = dws.tile_elems(s, True), dws.tile_threads(s, True)
+    n_opts = dws.num_tile_shapes()
+    assert n_opts >= 2
+    # automatic choice by n
+    for n, tile, threads in ((1 << 28, 65536, 1024), (1 << 24, 65536, 1024), ((1 << 24) - 1, 32768, 1024),
+                             (1 << 22, 32768, 1024), ((1 << 22) - 1, 16384, 512), (1 << 20, 16384, 512),
+                             ((1 << 20) - 1, 4096, 256), (1, 4096, 256)):
+        assert dws.tile_elems(0, n, True) == tile, n
+        assert dws.tile_threads(0, n, True) == threads, n
+    # the scalar-load kernels keep the element count of their shape
+    for n in (1, 1 << 21, 1 << 28):
+        assert dws.tile_elems(0, n, False) == dws.tile_elems(0, n, True)
+    for s in range(1, n_opts):
+        e, t = dws.tile_elems(s, 1 << 28, True), dws.tile_threads(s, 1 << 28, True)
         assert e > 0 and t % 64 == 0 and e % (t * 4) == 0
-        # unaligned pointers fall back to the default shape's scalar kernel
-        assert dws.tile_elems(s, False) == 4096
-    assert dws.tile_elems(n, True) == 0
-    assert dws.tile_elems(-1, True) == 0
+        # a forced shape without a scalar-load kernel falls back to automatic
+        assert dws.tile_elems(s, 1 << 28, False) in (e, dws.tile_elems(0, 1 << 28, True))
+    assert dws.tile_elems(n_opts, 100, True) == 0
+    assert dws.tile_elems(-1, 100, True) == 0
 
 
 FAKE = 0x10000  # never dereferenced: validation fails or passes before any HIP call
@@ -96,10 +102,15 @@ def test_option_validation(lib):
     assert call(variant=-1) == dws.ERR_INVALID_ARG
     assert call(order=2) == dws.ERR_INVALID_ARG
     assert call(shape=dws.num_tile_shapes()) == dws.ERR_INVALID_ARG
+    assert call(shape=-1) == dws.ERR_INVALID_ARG
     assert call(nt=2) == dws.ERR_INVALID_ARG
     # combinations that are not built
-    assert call(shape=1, order=dws.ORDER_ACQ_REL) == dws.ERR_UNSUPPORTED
-    assert call(variant=dws.CHAINED, shape=2) == dws.ERR_UNSUPPORTED
+    # forced shapes 2 (256 x 32) and 4 (1024 x 16) are built for the relaxed
+    # single pass only
+    assert call(shape=2, order=dws.ORDER_ACQ_REL) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.CHAINED, shape=4) == dws.ERR_UNSUPPORTED
+    assert call(shape=4, nt=1) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.REDUCE_THEN_SCAN, shape=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.REDUCE_THEN_SCAN, nt=1) == dws.ERR_UNSUPPORTED
     # options are validated before the arguments: n == 0 with bad options
     o = dws.DwsOptions(9, 0, 0, 0)

@@ -64,9 +64,14 @@ def test_wave_primitives_lane_layout(gpu, dtype):
 # ---------------------------------------------------------------------------
 # sizes around tile and wave boundaries, all dtypes, both kinds
 # ---------------------------------------------------------------------------
+# sizes around wave and tile boundaries of every automatic tile size: 4096
+# below 2^20, 16384 from 2^20, 32768 from 2^22, 65536 from 2^24
+M, L, H = 16384, 32768, 65536
 EDGE_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, TILE - 1, TILE, TILE + 1,
-              2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 65 * TILE - 3,
-              1_000_003]
+              2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 255 * TILE + 3,
+              (1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 20) + M - 1, 150 * M + 7,
+              (1 << 22) - 1, 1 << 22, (1 << 22) + 1, (1 << 22) + L + 1, 301 * L - 5,
+              (1 << 24) - 1, 1 << 24, (1 << 24) + 1, (1 << 24) + H + 3, 301 * H - 7]
 
 
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
@@ -94,7 +99,7 @@ def test_in_place(gpu, dtype, exclusive):
 def test_unaligned_pointers(gpu, dtype, exclusive):
     # 4-byte aligned but not 16-byte aligned: the scalar-load kernel
     for off in (1, 2, 3):
-        for n in (TILE - 1, 5 * TILE + 7, 300_001):
+        for n in (TILE - 1, 5 * TILE + 7, 300_001, (1 << 20) + 9, (1 << 22) + 5, (1 << 24) + 3):
             note(f"unaligned off={off} dtype={dtype} excl={exclusive} n={n}")
             x = wl.random_input(dtype, n, seed=100 * off + n)
             y = _roundtrip(x, dtype, exclusive, offset=off)
@@ -117,7 +122,7 @@ def test_input_aligned_output_unaligned(gpu):
 # ---------------------------------------------------------------------------
 # comparison variants, tile shapes, descriptor memory order, non-temporal
 # ---------------------------------------------------------------------------
-VARIANT_SIZES = [1, TILE - 1, TILE + 1, 3 * TILE + 7, (1 << 20) + 3, 64 * 3 * TILE + 11]
+VARIANT_SIZES = [1, TILE - 1, TILE + 1, 3 * TILE + 7, (1 << 20) + 3, (1 << 22) + 11, (1 << 24) + 5]
 
 
 @pytest.mark.parametrize("variant", [dws.REDUCE_THEN_SCAN, dws.CHAINED], ids=["rts", "chained"])
@@ -138,8 +143,8 @@ def test_comparison_variants(gpu, dtype, exclusive, variant):
 
 
 def test_tile_shapes(gpu):
-    for shape in range(dws.num_tile_shapes()):
-        t = dws.tile_elems(shape, True)
+    for shape in range(1, dws.num_tile_shapes()):
+        t = dws.tile_elems(shape, 1 << 28, True)
         for dtype in ("uint32", "float32"):
             for exclusive in (False, True):
                 for n in (t - 1, 5 * t + 3, (1 << 21) + 1):
@@ -155,7 +160,7 @@ def test_tile_shapes(gpu):
 def test_order_and_nontemporal(gpu, opts):
     for dtype in DTYPES:
         for exclusive in (False, True):
-            for n in (TILE + 1, (1 << 20) + 5, 40 * TILE):
+            for n in (TILE + 1, 40 * TILE, (1 << 20) + 5, (1 << 22) + 3, (1 << 24) + 9):
                 note(f"opts={opts} dtype={dtype} excl={exclusive} n={n}")
                 x = wl.random_input(dtype, n, seed=n + 5)
                 y = _roundtrip(x, dtype, exclusive, in_place=exclusive, **opts)
