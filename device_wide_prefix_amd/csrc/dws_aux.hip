@@ -25,17 +25,16 @@ __global__ void __launch_bounds__(BLOCK)
     constexpr uint32_t TILE = W * SEG;
     __shared__ T s_wave[W];
     const int lane = lane_id();
-    const int wave = (int)(threadIdx.x >> 6);
+    const int wave = (int)uniform(threadIdx.x >> 6);
     const uint32_t g = blockIdx.x;
     const uint32_t t0 = g * tiles_per_group;
     const uint32_t t1 = min(t0 + tiles_per_group, num_tiles);
 
     T acc = T(0);
     for (uint32_t t = t0; t < t1; ++t) {
-        const uint64_t tile_base = (uint64_t)t * TILE;
-        const bool full = tile_base + TILE <= n;
+        const uint64_t seg_first = (uint64_t)t * TILE + (uint64_t)wave * SEG;
         T x[CHUNKS][VEC];
-        load_segment<T, VEC, CHUNKS, false>(in, tile_base + (uint64_t)wave * SEG, n, full, lane, x);
+        load_segment<T, VEC, CHUNKS, false>(make_rsrc(in + seg_first, valid_bytes(seg_first, SEG, n)), lane, x);
 #pragma unroll
         for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
@@ -95,7 +94,7 @@ __global__ void __launch_bounds__(BLOCK)
     // passed the barrier of tile i+1, i.e. finished reading tile i's totals
     __shared__ T s_wave[2][W];
     const int lane = lane_id();
-    const int wave = (int)(threadIdx.x >> 6);
+    const int wave = (int)uniform(threadIdx.x >> 6);
     const uint32_t g = blockIdx.x;
     const uint32_t t0 = g * tiles_per_group;
     const uint32_t t1 = min(t0 + tiles_per_group, num_tiles);
@@ -103,13 +102,11 @@ __global__ void __launch_bounds__(BLOCK)
     T seed = prefixes[g];
     uint32_t it = 0;
     for (uint32_t t = t0; t < t1; ++t, ++it) {
-        const uint64_t tile_base = (uint64_t)t * TILE;
-        const uint64_t seg_base = tile_base + (uint64_t)wave * SEG;
-        const bool full = tile_base + TILE <= n;
+        const uint64_t seg_first = (uint64_t)t * TILE + (uint64_t)wave * SEG;
+        const uint32_t valid = valid_bytes(seg_first, SEG, n);
         T x[CHUNKS][VEC];
-        load_segment<T, VEC, CHUNKS, false>(in, seg_base, n, full, lane, x);
-        T lane_excl[CHUNKS], chunk_pre[CHUNKS];
-        const T seg_total = scan_segment<T, VEC, CHUNKS>(x, lane_excl, chunk_pre);
+        load_segment<T, VEC, CHUNKS, false>(make_rsrc(in + seg_first, valid), lane, x);
+        const T seg_total = scan_segment_local<T, EXCL, VEC, CHUNKS>(x);
         T* buf = s_wave[it & 1u];
         if (lane == 0) buf[wave] = seg_total;
         __syncthreads();
@@ -119,9 +116,8 @@ __global__ void __launch_bounds__(BLOCK)
             if (w == wave) wave_pre = agg;
             agg = agg + buf[w];
         }
-        T y[CHUNKS][VEC];
-        finish_segment<T, EXCL, VEC, CHUNKS>(x, lane_excl, chunk_pre, seed + wave_pre, y);
-        store_segment<T, VEC, CHUNKS, false>(out, seg_base, n, full, lane, y);
+        add_seed<T, VEC, CHUNKS>(x, seed + wave_pre);
+        store_segment<T, VEC, CHUNKS, false>(make_rsrc(out + seg_first, valid), lane, x);
         seed = seed + agg;
     }
 }

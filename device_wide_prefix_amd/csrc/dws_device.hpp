@@ -94,127 +94,139 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v)
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 
 // ---------------------------------------------------------------------------
-// Tile I/O. A tile is W wave segments; a wave segment is CHUNKS chunks of
-// 64 * VEC consecutive elements, and lane l holds elements [l*VEC, l*VEC+VEC)
-// of every chunk. Each load instruction of a wave therefore reads 64*VEC*4
-// contiguous bytes (1 KiB for dwordx4): fully coalesced, no LDS transpose.
+// Tile I/O through buffer resources. A tile is W wave segments; a wave segment
+// is CHUNKS chunks of 64 * VEC consecutive elements, and lane l holds elements
+// [l*VEC, l*VEC+VEC) of every chunk. Each load instruction of a wave therefore
+// reads 64*VEC*4 contiguous bytes (1 KiB for dwordx4): fully coalesced, no LDS
+// transpose.
+//
+// Each wave addresses its segment through a buffer resource that starts at the
+// segment's first element (a uniform 64-bit base in SGPRs) with num_records =
+// the segment's valid bytes. gfx950 range checks raw buffer accesses per dword:
+// dwords past num_records load as 0 (the identity, which pads a ragged last
+// tile) and are not stored. So full and ragged tiles share one path, and a lane
+// needs a single 32-bit offset register.
 // ---------------------------------------------------------------------------
-template <class T, int VEC> struct Vec { typedef T type __attribute__((ext_vector_type(VEC))); };
-template <class T> struct Vec<T, 1> { typedef T type; };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <class T, int VEC, int CHUNKS, bool NT>
-__device__ __forceinline__ void load_segment(const T* in, uint64_t seg_base, uint64_t n,
-                                             bool full, int lane, T (&x)[CHUNKS][VEC])
+// Third descriptor dword for raw 32-bit buffer access on the gfx9 family.
+constexpr int kBufferRsrcFlags = 0x00020000;
+// Cache-policy bit of buffer instructions for a non-temporal (streaming) access.
+constexpr int kBufferNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t valid_bytes)
 {
-    typedef typename Vec<T, VEC>::type V;
-    if (full) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)valid_bytes,
+                                             kBufferRsrcFlags);
+}
+
+// Valid bytes of the `len` elements starting at element `first` of an array of
+// n elements (first < n is not required: past the end gives 0).
+__device__ __forceinline__ uint32_t valid_bytes(uint64_t first, uint32_t len, uint64_t n)
+{
+    const uint64_t left = first < n ? n - first : 0u;
+    return (uint32_t)((left < len ? left : len) * 4u);
+}
+
+// Lane l of chunk c reads/writes the VEC elements at byte offset
+// 4 * (64 VEC c + VEC l) of the wave segment: the lane part is the only
+// per-lane offset; the chunk part is an immediate or scalar offset.
+template <class T, int VEC, int CHUNKS, bool NT>
+__device__ __forceinline__ void load_segment(__amdgpu_buffer_rsrc_t r, int lane, T (&x)[CHUNKS][VEC])
+{
+    static_assert(VEC == 1 || VEC == 4, "dword or dwordx4 accesses");
+    constexpr int aux = NT ? kBufferNonTemporal : 0;
+    const int voff = lane * VEC * 4;
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) {
-            const V* p = reinterpret_cast<const V*>(in + seg_base + (uint64_t)(c * 64 * VEC + lane * VEC));
-            V v;
-            if constexpr (NT) v = __builtin_nontemporal_load(p);
-            else v = *p;
-            if constexpr (VEC == 1) {
-                x[c][0] = v;
-            } else {
+    for (int c = 0; c < CHUNKS; ++c) {
+        if constexpr (VEC == 4) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, c * 64 * VEC * 4, aux);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) x[c][e] = v[e];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint64_t i = seg_base + (uint64_t)(c * 64 * VEC + lane * VEC + e);
-                x[c][e] = (i < n) ? in[i] : T(0);   // identity past the end
-            }
+            for (int e = 0; e < 4; ++e) x[c][e] = Elem<T>::from(v[e]);
+        } else {
+            x[c][0] = Elem<T>::from(__builtin_amdgcn_raw_buffer_load_b32(r, voff, c * 64 * VEC * 4, aux));
         }
     }
 }
 
 template <class T, int VEC, int CHUNKS, bool NT>
-__device__ __forceinline__ void store_segment(T* out, uint64_t seg_base, uint64_t n,
-                                              bool full, int lane, const T (&y)[CHUNKS][VEC])
+__device__ __forceinline__ void store_segment(__amdgpu_buffer_rsrc_t r, int lane, const T (&y)[CHUNKS][VEC])
 {
-    typedef typename Vec<T, VEC>::type V;
-    if (full) {
+    constexpr int aux = NT ? kBufferNonTemporal : 0;
+    const int voff = lane * VEC * 4;
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) {
-            V* p = reinterpret_cast<V*>(out + seg_base + (uint64_t)(c * 64 * VEC + lane * VEC));
-            V v;
-            if constexpr (VEC == 1) {
-                v = y[c][0];
-            } else {
+    for (int c = 0; c < CHUNKS; ++c) {
+        if constexpr (VEC == 4) {
+            u32x4 v;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) v[e] = y[c][e];
-            }
-            if constexpr (NT) __builtin_nontemporal_store(v, p);
-            else *p = v;
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint64_t i = seg_base + (uint64_t)(c * 64 * VEC + lane * VEC + e);
-                if (i < n) out[i] = y[c][e];
-            }
+            for (int e = 0; e < 4; ++e) v[e] = Elem<T>::bits(y[c][e]);
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, c * 64 * VEC * 4, aux);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(Elem<T>::bits(y[c][0]), r, voff, c * 64 * VEC * 4, aux);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Scan of one wave segment held in registers (three-phase coarsened scan of the
-// PMPP 11.2 notes, with wave scans in place of the block-wide phase 2):
-//   lane_total[c]  serial sum of the lane's VEC elements of chunk c
-//   lane_excl[c]   sum of the lower lanes' totals of chunk c (in-wave scan)
-//   chunk_pre[c]   sum of the wave's chunks before c (uniform)
-//   returns        the wave segment total (uniform)
+// Scan of one wave segment held in registers, in place (three-phase coarsened
+// scan of the PMPP 11.2 notes, with wave scans in place of the block-wide
+// phase 2). For each chunk c, each lane
+//   1. replaces its VEC elements by their in-lane prefix sums (exclusive or
+//      inclusive) and keeps the lane total;
+//   2. gets the sum of the lower lanes' totals (wave64 DPP scan) and the sum
+//      of the wave's earlier chunks (uniform), and adds both to its elements.
+// Afterwards every element holds its prefix inside the wave segment; the
+// segment total is returned (uniform). Nothing but the tile stays live for the
+// look-back, and the finish is one uniform add per element. Exclusive values
+// are formed directly, never as inclusive - x.
 // ---------------------------------------------------------------------------
-template <class T, int VEC, int CHUNKS>
-__device__ __forceinline__ T scan_segment(const T (&x)[CHUNKS][VEC], T (&lane_excl)[CHUNKS],
-                                          T (&chunk_pre)[CHUNKS])
+template <class T, bool EXCL, int VEC, int CHUNKS>
+__device__ __forceinline__ T scan_segment_local(T (&x)[CHUNKS][VEC])
 {
-    T incl[CHUNKS];
+    T running = T(0);   // sum of the wave's chunks before c
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
-        T s = x[c][0];
+        T lane_total = T(0);
 #pragma unroll
-        for (int e = 1; e < VEC; ++e) s = s + x[c][e];
-        incl[c] = wave_inclusive_scan(s);
-    }
-    T running = T(0);
+        for (int e = 0; e < VEC; ++e) {
+            const T xe = x[c][e];
+            if constexpr (EXCL) {
+                x[c][e] = lane_total;
+                lane_total = lane_total + xe;
+            } else {
+                lane_total = lane_total + xe;
+                x[c][e] = lane_total;
+            }
+        }
+        const T incl = wave_inclusive_scan(lane_total);
+        const T offset = running + wave_shift_up1(incl);
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        lane_excl[c] = wave_shift_up1(incl[c]);
-        chunk_pre[c] = running;
-        running = running + wave_read_lane(incl[c], 63);
+        for (int e = 0; e < VEC; ++e) x[c][e] = offset + x[c][e];
+        running = running + wave_read_lane(incl, 63);
     }
     return running;
 }
 
-// Seeded serial finish of a wave segment: every element gets seed + the sum of
-// everything before it in the segment (exclusive) or up to and including it
-// (inclusive). Exclusive values are formed directly, never as inclusive - x.
-template <class T, bool EXCL, int VEC, int CHUNKS>
-__device__ __forceinline__ void finish_segment(const T (&x)[CHUNKS][VEC], const T (&lane_excl)[CHUNKS],
-                                               const T (&chunk_pre)[CHUNKS], T seed, T (&y)[CHUNKS][VEC])
+// Keep every element materialised in a VGPR here. Without it the compiler
+// sinks the segment-offset adds past the look-back to their single use and
+// keeps the offsets alive (spilling them) across it. Emits no instruction.
+template <class T, int VEC, int CHUNKS>
+__device__ __forceinline__ void pin_in_registers(T (&x)[CHUNKS][VEC])
 {
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        T s = (seed + chunk_pre[c]) + lane_excl[c];
+    for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            if constexpr (EXCL) {
-                y[c][e] = s;
-                s = s + x[c][e];
-            } else {
-                s = s + x[c][e];
-                y[c][e] = s;
-            }
-        }
-    }
+        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(x[c][e]));
+}
+
+// Add the segment's seed (everything before the wave segment) to every element.
+template <class T, int VEC, int CHUNKS>
+__device__ __forceinline__ void add_seed(T (&x)[CHUNKS][VEC], T seed)
+{
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[c][e] = seed + x[c][e];
 }
 
 // ---------------------------------------------------------------------------

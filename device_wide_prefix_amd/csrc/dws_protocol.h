@@ -70,10 +70,34 @@ constexpr int auto_shape(uint64_t n)
     return n >= kAutoHugeMin ? 5 : (n >= kAutoLargeMin ? 4 : (n >= kAutoMediumMin ? 2 : 0));
 }
 
-constexpr TileShape scalar_shape(const TileShape& s) { return TileShape{s.threads, 1, s.vec * s.chunks}; }
+// Scalar-load version of a shape: one element per load, at most 16 loads per
+// lane (each load is one wave scan; more would spill registers).
+constexpr TileShape scalar_shape(const TileShape& s)
+{
+    return TileShape{s.threads, 1, s.vec * s.chunks < 16 ? s.vec * s.chunks : 16};
+}
 
-// Look-back width: descriptors per lane per poll (64 * K per poll).
+// Occupancy asked of the compiler: waves per SIMD such that two 1024-thread
+// workgroups (or the equivalent) fit per CU, i.e. at most 64 VGPRs, whenever
+// the tile data (elements per lane) leaves room for it; otherwise 4 waves per
+// SIMD (one 1024-thread workgroup, up to 128 VGPRs).
+constexpr int waves_per_eu_target(int threads, int elems_per_lane)
+{
+    return (elems_per_lane <= 32) ? 8 : (threads >= 1024 ? 4 : 4);
+}
+
+// Look-back width: descriptors per lane per poll (64 * K per poll). P can
+// advance by at most 64 K tiles per poll latency (~0.8 us measured), so small
+// tiles, which arrive fast, need K = 4; from 16K-element tiles on, 64 tiles
+// per poll already outpace the memory system and K = 1 keeps registers free.
+#ifndef DWS_LOOKBACK_SLOTS_LARGE
+#define DWS_LOOKBACK_SLOTS_LARGE 1
+#endif
 constexpr int kLookbackSlots = 4;
+constexpr int lookback_slots(uint32_t tile_elems)
+{
+    return tile_elems >= 16384u ? DWS_LOOKBACK_SLOTS_LARGE : kLookbackSlots;
+}
 
 // Built single-pass kernel configurations. Shape index into kShapes; vec 1
 // means the scalar-load version of that shape.

@@ -27,7 +27,8 @@
 namespace dws {
 
 template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT>
-__global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(waves_per_eu_target(BLOCK, VEC * CHUNKS))))
+k_single_pass(SinglePassParams p)
 {
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
@@ -37,7 +38,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     __shared__ T s_prefix;
 
     const int lane = lane_id();
-    const int wave = (int)(threadIdx.x >> 6);
+    const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
 
     uint32_t tile = 0u, epoch = 0u;
@@ -59,15 +60,14 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
         }
     }
 
-    const uint64_t tile_base = (uint64_t)tile * TILE;
-    const uint64_t seg_base = tile_base + (uint64_t)wave * SEG;
-    const bool full = tile_base + TILE <= p.n;
+    const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
+    const uint32_t seg_valid = valid_bytes(seg_first, SEG, p.n);
 
     T x[CHUNKS][VEC];
-    load_segment<T, VEC, CHUNKS, NT>(static_cast<const T*>(p.in), seg_base, p.n, full, lane, x);
+    load_segment<T, VEC, CHUNKS, NT>(make_rsrc(static_cast<const T*>(p.in) + seg_first, seg_valid), lane, x);
 
-    T lane_excl[CHUNKS], chunk_pre[CHUNKS];
-    const T seg_total = scan_segment<T, VEC, CHUNKS>(x, lane_excl, chunk_pre);
+    const T seg_total = scan_segment_local<T, EXCL, VEC, CHUNKS>(x);
+    pin_in_registers<T, VEC, CHUNKS>(x);
 
     if (lane == 0) s_wave[wave] = seg_total;
     __syncthreads();
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)
                         desc_store<ORDER>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
-                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
+                    prefix = lookback_decoupled<T, ORDER, lookback_slots(TILE)>(p.desc, tile, epoch, p.watchdog);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
@@ -101,9 +101,8 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     __syncthreads();
     const T seed = s_prefix + wave_pre;
 
-    T y[CHUNKS][VEC];
-    finish_segment<T, EXCL, VEC, CHUNKS>(x, lane_excl, chunk_pre, seed, y);
-    store_segment<T, VEC, CHUNKS, NT>(static_cast<T*>(p.out), seg_base, p.n, full, lane, y);
+    add_seed<T, VEC, CHUNKS>(x, seed);
+    store_segment<T, VEC, CHUNKS, NT>(make_rsrc(static_cast<T*>(p.out) + seg_first, seg_valid), lane, x);
 }
 
 // ---------------------------------------------------------------------------

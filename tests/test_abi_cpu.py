@@ -59,14 +59,18 @@ def test_tile_geometry(lib):
                              ((1 << 20) - 1, 4096, 256), (1, 4096, 256)):
         assert dws.tile_elems(0, n, True) == tile, n
         assert dws.tile_threads(0, n, True) == threads, n
-    # the scalar-load kernels keep the element count of their shape
-    for n in (1, 1 << 21, 1 << 28):
-        assert dws.tile_elems(0, n, False) == dws.tile_elems(0, n, True)
+    # the scalar-load kernels keep the threads of their shape and at most 16
+    # elements per lane
+    for n in (1, 1 << 21, 1 << 23, 1 << 28):
+        t = dws.tile_threads(0, n, True)
+        assert dws.tile_threads(0, n, False) == t
+        assert dws.tile_elems(0, n, False) == min(dws.tile_elems(0, n, True), 16 * t)
     for s in range(1, n_opts):
         e, t = dws.tile_elems(s, 1 << 28, True), dws.tile_threads(s, 1 << 28, True)
         assert e > 0 and t % 64 == 0 and e % (t * 4) == 0
-        # a forced shape without a scalar-load kernel falls back to automatic
-        assert dws.tile_elems(s, 1 << 28, False) in (e, dws.tile_elems(0, 1 << 28, True))
+        # unaligned: the scalar-load version of the forced shape, or of the
+        # automatic shape when the forced one has none
+        assert dws.tile_elems(s, 1 << 28, False) in (min(e, 16 * t), dws.tile_elems(0, 1 << 28, False))
     assert dws.tile_elems(n_opts, 100, True) == 0
     assert dws.tile_elems(-1, 100, True) == 0
 
