@@ -77,27 +77,11 @@ constexpr TileShape scalar_shape(const TileShape& s)
     return TileShape{s.threads, 1, s.vec * s.chunks < 16 ? s.vec * s.chunks : 16};
 }
 
-// Occupancy asked of the compiler: waves per SIMD such that two 1024-thread
-// workgroups (or the equivalent) fit per CU, i.e. at most 64 VGPRs, whenever
-// the tile data (elements per lane) leaves room for it; otherwise 4 waves per
-// SIMD (one 1024-thread workgroup, up to 128 VGPRs).
-constexpr int waves_per_eu_target(int threads, int elems_per_lane)
-{
-    return (elems_per_lane <= 32) ? 8 : (threads >= 1024 ? 4 : 4);
-}
-
 // Look-back width: descriptors per lane per poll (64 * K per poll). P can
-// advance by at most 64 K tiles per poll latency (~0.8 us measured), so small
-// tiles, which arrive fast, need K = 4; from 16K-element tiles on, 64 tiles
-// per poll already outpace the memory system and K = 1 keeps registers free.
-#ifndef DWS_LOOKBACK_SLOTS_LARGE
-#define DWS_LOOKBACK_SLOTS_LARGE 1
-#endif
+// advance by at most 64 K tiles per poll latency (~0.8 us measured); with
+// fewer slots the walk back to the last P grows (measured: K = 4 beats K = 1
+// by 6% at 32K-element tiles and by 1% at 64K).
 constexpr int kLookbackSlots = 4;
-constexpr int lookback_slots(uint32_t tile_elems)
-{
-    return tile_elems >= 16384u ? DWS_LOOKBACK_SLOTS_LARGE : kLookbackSlots;
-}
 
 // Built single-pass kernel configurations. Shape index into kShapes; vec 1
 // means the scalar-load version of that shape.

@@ -27,8 +27,7 @@
 namespace dws {
 
 template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT>
-__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(waves_per_eu_target(BLOCK, VEC * CHUNKS))))
-k_single_pass(SinglePassParams p)
+__global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
 {
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
@@ -87,7 +86,7 @@ k_single_pass(SinglePassParams p)
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)
                         desc_store<ORDER>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
-                    prefix = lookback_decoupled<T, ORDER, lookback_slots(TILE)>(p.desc, tile, epoch, p.watchdog);
+                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
