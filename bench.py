@@ -152,6 +152,20 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
             ok = ok and bool(np.all(np.diff(y.astype(np.int64)) >= 0))
     result["property_check"] = bool(ok)
 
+    if w.dtype != "uint32" and variant == 0 and order == 0 and shape == 0 and not nt:
+        # one instrumented run: where a tile's time goes (100 MHz stamps)
+        prepare()
+        torch.cuda.synchronize()
+        _, st = dws.scan_profiled(work, out=out, exclusive=w.exclusive)
+        torch.cuda.synchronize()
+        st = st.cpu().numpy().astype(np.int64)
+        life = (st[:, 4] - st[:, 0]).astype(np.float64)
+        phases = {"draw": st[:, 1] - st[:, 0], "load_and_local_scan": st[:, 2] - st[:, 1],
+                  "lookback": st[:, 3] - st[:, 2], "finish_and_store_issue": st[:, 4] - st[:, 3]}
+        result["lookback_stall_share"] = float((st[:, 3] - st[:, 2]).sum() / life.sum())
+        result["phase_mean_us"] = {k: round(float(v.mean()) * 0.01, 3) for k, v in phases.items()}
+        result["tiles"] = int(st.shape[0])
+
     if with_memcpy:
         hip = Hip()
         dst = torch.empty_like(pristine)
@@ -206,6 +220,9 @@ def summarize(w, res, variant_name, args):
     gbps = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
     out = {"workload": w.name, "variant": variant_name, "ms_mean": mean_ms, "ms_min": float(np.min(times)),
            "ms_median": float(np.median(times)), "gbps": gbps, "property_check": res["property_check"]}
+    for key in ("lookback_stall_share", "phase_mean_us", "tiles"):
+        if key in res:
+            out[key] = res[key]
     if "memcpy_times_ms" in res:
         mc = float(np.mean(res["memcpy_times_ms"]))
         out["memcpy_ms_mean"] = mc
@@ -281,6 +298,8 @@ def main():
         "property_check": s["property_check"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "lookback_stall_share": s.get("lookback_stall_share"),
+        "tile_phase_mean_us": s.get("phase_mean_us"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

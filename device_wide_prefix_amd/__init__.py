@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
+    "dws_scan_profiled",
 )
 
 
@@ -87,6 +88,8 @@ def load_library():
     lib.dws_scan_debug.argtypes = [vp, vp, sz, ci, ci, ci, cu, cu, cu, cu,
                                    ctypes.POINTER(ctypes.c_ulonglong), vp]
     lib.dws_scan_debug.restype = ci
+    lib.dws_scan_profiled.argtypes = [vp, vp, sz, ci, ci, vp, sz, ctypes.POINTER(cu), vp]
+    lib.dws_scan_profiled.restype = ci
     lib.dws_selftest_wave.argtypes = [vp, vp, vp, sz, ci, vp]
     lib.dws_selftest_wave.restype = ci
     _lib = lib
@@ -203,6 +206,33 @@ def scan_debug(x, out, tile_elems, exclusive=False, variant=SINGLE_PASS, delay_e
                                              int(delay_phase), int(delay_ticks), ptr, _stream(x, stream)),
                "dws_scan_debug")
     return desc
+
+
+STAMPS_PER_TILE = 5
+STAMP_NAMES = ("start", "drawn", "aggregate_published", "prefix_known", "stores_issued")
+
+
+def profiled_num_tiles(n: int) -> int:
+    t = ctypes.c_uint(0)
+    _check(load_library().dws_scan_profiled(None, None, int(n), INT32, 0, None, 0, ctypes.byref(t), None),
+           "dws_scan_profiled")
+    return int(t.value)
+
+
+def scan_profiled(x, out=None, exclusive=False, stream=None):
+    """Instrumented single-pass scan. Returns (out, stamps) where stamps is a
+    (num_tiles, 5) int64 GPU tensor of 100 MHz real-time counter values:
+    start, drawn, aggregate published, prefix known, stores issued."""
+    import torch
+    code, out = _prepare(x, out)
+    tiles = profiled_num_tiles(x.numel())
+    stamps = torch.zeros((max(tiles, 1), STAMPS_PER_TILE), dtype=torch.int64, device=x.device)
+    t = ctypes.c_uint(0)
+    with _device_of(x):
+        _check(load_library().dws_scan_profiled(x.data_ptr(), out.data_ptr(), x.numel(), code, int(bool(exclusive)),
+                                                stamps.data_ptr(), stamps.numel(), ctypes.byref(t),
+                                                _stream(x, stream)), "dws_scan_profiled")
+    return out, stamps[:tiles]
 
 
 def watchdog_trips() -> int:

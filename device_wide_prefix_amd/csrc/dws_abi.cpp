@@ -173,14 +173,14 @@ int cu_count()
 }
 
 dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
-                           const dws_options& o, hipStream_t stream)
+                           const dws_options& o, hipStream_t stream, unsigned long long* stamps = nullptr)
 {
     const bool aligned = aligned16(in, out);
     // non-temporal access is a hint, built for aligned pointers only
     const bool nt = o.nontemporal != 0 && aligned;
     const int shape = resolve_shape(o.tile_shape, n, aligned);
     if (shape < 0) return DWS_ERR_INVALID_ARG;
-    const int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt);
+    const int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt, stamps != nullptr);
     if (cfg < 0) return DWS_ERR_UNSUPPORTED;
     const TileShape ts = cfg_shape(kCfgs[cfg]);
     const uint64_t num_tiles = ceil_div(n, (uint64_t)ts.elems());
@@ -191,6 +191,7 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     p.out = out;
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
+    p.stamps = stamps;
     const bool f32 = kind_of(dtype) == kKindF32;
     auto launch = [&]() {
         return f32 ? launch_single_pass_typed<float>(cfg, excl, p, stream)
@@ -448,6 +449,36 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
             }
         }
         return DWS_OK;
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive,
+                             unsigned long long* d_stamps, size_t stamps_capacity, unsigned* num_tiles,
+                             hipStream_t stream)
+{
+    try {
+        if (!valid_dtype((int)dtype)) return DWS_ERR_INVALID_ARG;
+        if (n == 0) {
+            if (num_tiles != nullptr) *num_tiles = 0;
+            return DWS_OK;
+        }
+        if (n > DWS_MAX_ELEMENTS) return DWS_ERR_UNSUPPORTED;
+        const int shape = auto_shape(n);
+        const uint64_t tiles = ceil_div(n, (uint64_t)kShapes[shape].elems());
+        if (tiles > 0xffffffffull) return DWS_ERR_UNSUPPORTED;
+        if (num_tiles != nullptr) *num_tiles = (unsigned)tiles;
+        if (d_stamps == nullptr) return DWS_OK;   // size query
+        if (stamps_capacity < tiles * kStampsPerTile) return DWS_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(d_stamps) & 7u) != 0) return DWS_ERR_MISALIGNED;
+        dws_status s = validate(d_in, d_out, n, (int)dtype);
+        if (s != DWS_OK) return s;
+        if (!aligned16(d_in, d_out)) return DWS_ERR_UNSUPPORTED;
+        dws_options o{};
+        return run_single_pass(d_in, d_out, n, (int)dtype, exclusive != 0, kModeDecoupled, o, stream, d_stamps);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

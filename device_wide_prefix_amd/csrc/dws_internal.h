@@ -23,6 +23,7 @@ struct SinglePassParams {
     uint64_t* desc;        // >= num_tiles slots (unused when num_tiles == 1)
     unsigned long long* counter;
     unsigned int* watchdog;
+    unsigned long long* stamps;   // kStampsPerTile per tile (instrumented kernels only)
     uint32_t num_tiles;
 };
 
@@ -36,7 +37,7 @@ hipError_t launch_single_pass_typed(int cfg, bool exclusive, const SinglePassPar
 // the shape, or of the automatic shape if that one is not built.
 int resolve_shape(int option_shape, uint64_t n, bool aligned);
 // Index into kCfgs of the kernel for these parameters, or -1 if not built.
-int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal);
+int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal, bool instr = false);
 
 struct RtsArgs {
     const void* in;

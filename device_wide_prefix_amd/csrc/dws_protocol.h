@@ -88,6 +88,7 @@ constexpr int kLookbackSlots = 4;
 struct KernelCfg {
     int shape, vec, order, mode;
     bool nt;
+    bool instr = false;   // records per-tile phase time stamps (measurement build)
 };
 
 #define DWS_AUTO_SHAPES(VEC, ORDER, MODE, NT) \
@@ -110,6 +111,11 @@ constexpr KernelCfg kCfgs[] = {
     DWS_AUTO_SHAPES(1, kOrderRelaxed, kModeChained, false),
     DWS_AUTO_SHAPES(4, kOrderAcqRel, kModeChained, false),
     DWS_AUTO_SHAPES(1, kOrderAcqRel, kModeChained, false),
+    // instrumented (time stamps), aligned automatic shapes
+    {0, 4, kOrderRelaxed, kModeDecoupled, false, true},
+    {2, 4, kOrderRelaxed, kModeDecoupled, false, true},
+    {4, 4, kOrderRelaxed, kModeDecoupled, false, true},
+    {5, 4, kOrderRelaxed, kModeDecoupled, false, true},
 };
 #undef DWS_AUTO_SHAPES
 constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
@@ -124,5 +130,9 @@ constexpr uint32_t kRtsMaxGroups = 4096u;
 
 // Protocol-inspection kernel: one wavefront per tile of 1..64 elements.
 constexpr uint32_t kDebugMaxTile = 64u;
+
+// Instrumented scan: 64-bit time stamps per tile (start, drawn, aggregate
+// published, prefix known, stores issued).
+constexpr uint32_t kStampsPerTile = 5u;
 
 }  // namespace dws

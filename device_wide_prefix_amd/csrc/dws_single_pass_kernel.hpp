@@ -26,9 +26,11 @@
 
 namespace dws {
 
-template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT>
+template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT, bool INSTR>
 __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
 {
+    uint64_t stamp[kStampsPerTile] = {};
+    if constexpr (INSTR) stamp[0] = realtime();
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
@@ -58,6 +60,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
             return;
         }
     }
+    if constexpr (INSTR) stamp[1] = realtime();
 
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t seg_valid = valid_bytes(seg_first, SEG, p.n);
@@ -70,6 +73,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
 
     if (lane == 0) s_wave[wave] = seg_total;
     __syncthreads();
+    if constexpr (INSTR) stamp[2] = realtime();
     T wave_pre = T(0), agg = T(0);
 #pragma unroll
     for (int w = 0; w < W; ++w) {
@@ -98,10 +102,18 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
         if (lane == 0) s_prefix = prefix;
     }
     __syncthreads();
+    if constexpr (INSTR) stamp[3] = realtime();
     const T seed = s_prefix + wave_pre;
 
     add_seed<T, VEC, CHUNKS>(x, seed);
     store_segment<T, VEC, CHUNKS, NT>(make_rsrc(static_cast<T*>(p.out) + seg_first, seg_valid), lane, x);
+    if constexpr (INSTR) {
+        stamp[4] = realtime();
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (uint32_t i = 0; i < kStampsPerTile; ++i) p.stamps[(uint64_t)tile * kStampsPerTile + i] = stamp[i];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -114,7 +126,7 @@ static hipError_t launch_cfg(const SinglePassParams& p, hipStream_t stream)
     constexpr KernelCfg c = kCfgs[I];
     constexpr TileShape s = cfg_shape(c);
     const void* fn = reinterpret_cast<const void*>(
-        &k_single_pass<T, EXCL, s.threads, s.vec, s.chunks, c.order, c.mode, c.nt>);
+        &k_single_pass<T, EXCL, s.threads, s.vec, s.chunks, c.order, c.mode, c.nt, c.instr>);
     SinglePassParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(s.threads), args, 0, stream);

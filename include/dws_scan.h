@@ -203,6 +203,23 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
                           hipStream_t stream);
 
 /*
+ * Instrumented single-pass scan, for measuring where a tile's time goes. Same
+ * result as scan_inclusive / scan_exclusive with the automatic tile shape
+ * (relaxed descriptors; both pointers must be 16-byte aligned, else
+ * DWS_ERR_UNSUPPORTED). In addition, for every tile t it writes five 64-bit
+ * stamps of the 100 MHz real-time counter to the DEVICE buffer
+ * d_stamps[5t .. 5t+4]: workgroup start, tile index drawn, aggregate
+ * published (tile loaded and scanned), exclusive prefix known (look-back
+ * done), stores issued. *num_tiles (if not NULL) receives the tile count;
+ * with d_stamps == NULL the call only reports it. stamps_capacity is the
+ * number of 64-bit words at d_stamps (at least 5 per tile). Asynchronous.
+ */
+dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                             int exclusive, unsigned long long* d_stamps,
+                             size_t stamps_capacity, unsigned* num_tiles,
+                             hipStream_t stream);
+
+/*
  * Wavefront primitive check: for each group of 64 elements g, writes the
  * in-wave inclusive scan to d_incl and the value of the previous lane (0 in
  * lane 0) to d_shift, exactly as the scan kernels compute them.

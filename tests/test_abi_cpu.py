@@ -139,6 +139,23 @@ def test_debug_and_selftest_validation(lib):
     assert lib.dws_reserve((1 << 35) + 1, None) == dws.ERR_UNSUPPORTED
 
 
+def test_profiled_size_query_and_validation(lib):
+    # size query: no pointers, no HIP call
+    assert dws.profiled_num_tiles(0) == 0
+    assert dws.profiled_num_tiles(1) == 1
+    assert dws.profiled_num_tiles(1 << 28) == (1 << 28) // dws.tile_elems(0, 1 << 28, True)
+    assert dws.profiled_num_tiles((1 << 28) + 1) == (1 << 28) // dws.tile_elems(0, 1 << 28, True) + 1
+    f = lib.dws_scan_profiled
+    t = ctypes.c_uint(0)
+    assert f(FAKE, FAKE + (1 << 20), 1 << 16, 9, 0, None, 0, ctypes.byref(t), None) == dws.ERR_INVALID_ARG
+    # too small a stamp buffer, misaligned stamps, overlap, unaligned data
+    tiles = dws.profiled_num_tiles(1 << 16)
+    assert f(FAKE, FAKE + (1 << 20), 1 << 16, dws.INT32, 0, FAKE + (1 << 24), 5 * tiles - 1, None, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + (1 << 20), 1 << 16, dws.INT32, 0, FAKE + (1 << 24) + 4, 5 * tiles, None, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, FAKE + 4, 1 << 16, dws.INT32, 0, FAKE + (1 << 24), 5 * tiles, None, None) == dws.ERR_OVERLAP
+    assert f(FAKE + 4, FAKE + (1 << 20), 1 << 16, dws.INT32, 0, FAKE + (1 << 24), 5 * tiles, None, None) == dws.ERR_UNSUPPORTED
+
+
 def test_binding_refuses_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     x = torch.arange(10, dtype=torch.int32)

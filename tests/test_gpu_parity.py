@@ -375,5 +375,22 @@ def test_workload_full_size(gpu, name):
         assert int(y[-1]) + int(x[-1]) == int(x.sum(dtype=np.int64))
 
 
+@pytest.mark.parametrize("n", [5, (1 << 20) + 3, (1 << 24) + 77])
+def test_profiled_scan(gpu, n):
+    import torch
+    for dtype in ("int32", "float32"):
+        for exclusive in (False, True):
+            note(f"profiled dtype={dtype} excl={exclusive} n={n}")
+            x = wl.random_input(dtype, n, seed=n + 3)
+            _, xd = to_device(x)
+            out, stamps = dws.scan_profiled(xd, exclusive=exclusive)
+            torch.cuda.synchronize()
+            check(x, from_device(out, dtype), dtype, exclusive, label="profiled")
+            st = stamps.cpu().numpy()
+            assert st.shape == (dws.profiled_num_tiles(n), 5)
+            assert np.all(st > 0), "every tile writes its stamps"
+            assert np.all(np.diff(st, axis=1) >= 0), "phases are in order within a tile"
+
+
 def test_zz_watchdog_never_tripped(gpu):
     assert dws.watchdog_trips() == 0
