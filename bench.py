@@ -15,7 +15,7 @@ buffer; a step is one scan call bracketed by HIP events on the stream the
 library launches on. The call is a single kernel launch, so the event time is
 the kernel's launch duration.
 
-Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained,
+Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained|scan_then_propagate,
 --order relaxed|acq_rel, --tile-shape K, --nontemporal, --no-cpu-baseline,
 --all (extra JSON lines for every workload and variant on stderr).
 """
@@ -41,7 +41,7 @@ METRIC = "scan GB/s (2n·sizeof(T)/time) at N=2^28 fp32; % of HBM peak & of D2D 
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_c4.json")
-VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2}
+VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2, "scan_then_propagate": 3}
 ORDERS = {"relaxed": 0, "acq_rel": 1}
 
 

@@ -26,7 +26,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_MISALIGNED, ERR_HIP, ERR_
 # dws_dtype
 INT32, UINT32, FLOAT32 = 0, 1, 2
 # dws_variant
-SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED = 0, 1, 2
+SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED, SCAN_THEN_PROPAGATE = 0, 1, 2, 3
 # dws_memory_order
 ORDER_RELAXED, ORDER_ACQ_REL = 0, 1
 
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
-    "dws_scan_profiled",
+    "dws_scan_profiled", "dws_select_flagged",
 )
 
 
@@ -90,6 +90,8 @@ def load_library():
     lib.dws_scan_debug.restype = ci
     lib.dws_scan_profiled.argtypes = [vp, vp, sz, ci, ci, vp, sz, ctypes.POINTER(cu), vp]
     lib.dws_scan_profiled.restype = ci
+    lib.dws_select_flagged.argtypes = [vp, vp, vp, sz, ci, vp, vp]
+    lib.dws_select_flagged.restype = ci
     lib.dws_selftest_wave.argtypes = [vp, vp, vp, sz, ci, vp]
     lib.dws_selftest_wave.restype = ci
     _lib = lib
@@ -233,6 +235,30 @@ def scan_profiled(x, out=None, exclusive=False, stream=None):
                                                 stamps.data_ptr(), stamps.numel(), ctypes.byref(t),
                                                 _stream(x, stream)), "dws_scan_profiled")
     return out, stamps[:tiles]
+
+
+def select_flagged_ptr(d_in: int, d_flags: int, d_out: int, n: int, dtype: int, d_count: int,
+                      stream: int = 0) -> int:
+    return load_library().dws_select_flagged(d_in, d_flags, d_out, n, dtype, d_count, stream)
+
+
+def select_flagged(x, flags, out=None, count=None, stream=None):
+    """Stream compaction: the elements of x whose int32 flag is non-zero, in
+    order, written to out[:count]. Returns (out, count) with count a one-element
+    int64 GPU tensor (no synchronisation). out may be x (in place)."""
+    import torch
+    code, out = _prepare(x, out)
+    if not isinstance(flags, torch.Tensor) or flags.dtype != torch.int32 or \
+            flags.numel() != x.numel() or not flags.is_contiguous() or flags.device != x.device:
+        raise ValueError("flags must be a contiguous int32 tensor with the size and device of x")
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=x.device)
+    if count.dtype != torch.int64 or count.numel() < 1 or count.device != x.device:
+        raise ValueError("count must be an int64 tensor on the device of x")
+    with _device_of(x):
+        _check(select_flagged_ptr(x.data_ptr(), flags.data_ptr(), out.data_ptr(), x.numel(), code,
+                                  count.data_ptr(), _stream(x, stream)), "dws_select_flagged")
+    return out, count
 
 
 def watchdog_trips() -> int:

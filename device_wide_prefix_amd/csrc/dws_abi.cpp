@@ -33,6 +33,8 @@ struct Workspace {
     uint64_t* desc = nullptr;     // descriptor slots
     uint64_t desc_slots = 0;
     void* partials = nullptr;     // reduce-then-scan partials (kRtsMaxGroups x 4 B)
+    void* stp = nullptr;          // scan-then-propagate tile sums (all levels)
+    uint64_t stp_elems = 0;
     uint64_t draws_launches = 0;  // launches that used the counter since the last clear
 
     unsigned long long* counter() const
@@ -244,13 +246,52 @@ dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hi
     return from_hip(launch_rts(a, stream));
 }
 
+// Grow the scan-then-propagate scratch (call with ws->mu held).
+dws_status ensure_stp(Workspace* ws, uint64_t elems)
+{
+    if (elems <= ws->stp_elems) return DWS_OK;
+    const uint64_t want = std::max<uint64_t>({elems, ws->stp_elems * 2, 1024});
+    if (ws->stp != nullptr) {
+        hipError_t e = hipStreamSynchronize(ws->stream);
+        if (e != hipSuccess) return from_hip(e);
+        (void)hipFree(ws->stp);
+        ws->stp = nullptr;
+        ws->stp_elems = 0;
+    }
+    hipError_t e = hipMalloc(&ws->stp, want * kElemBytes);
+    if (e != hipSuccess) return from_hip(e);
+    ws->stp_elems = want;
+    return DWS_OK;
+}
+
+dws_status run_stp(const void* in, void* out, size_t n, int dtype, bool excl, hipStream_t stream)
+{
+    StpArgs a{};
+    a.in = in;
+    a.out = out;
+    a.n = n;
+    a.kind = kind_of(dtype);
+    a.exclusive = excl;
+    const uint64_t need = stp_scratch_elems(n);
+    if (need == 0) return from_hip(launch_stp(a, stream));
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_stp(ws, need);
+    if (s != DWS_OK) return s;
+    a.scratch = ws->stp;
+    a.scratch_elems = ws->stp_elems;
+    return from_hip(launch_stp(a, stream));
+}
+
 dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclusive, const dws_options* opt,
                       hipStream_t stream)
 {
     try {
         dws_options o{};
         if (opt != nullptr) o = *opt;
-        if (o.variant < DWS_VARIANT_SINGLE_PASS || o.variant > DWS_VARIANT_CHAINED) return DWS_ERR_INVALID_ARG;
+        if (o.variant < DWS_VARIANT_SINGLE_PASS || o.variant > DWS_VARIANT_SCAN_THEN_PROPAGATE) return DWS_ERR_INVALID_ARG;
         if (o.memory_order != DWS_ORDER_RELAXED && o.memory_order != DWS_ORDER_ACQ_REL)
             return DWS_ERR_INVALID_ARG;
         if (o.tile_shape < 0 || o.tile_shape > kNumShapes) return DWS_ERR_INVALID_ARG;
@@ -264,6 +305,9 @@ dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclus
             return run_rts(in, out, n, dtype, excl, stream);
         case DWS_VARIANT_CHAINED:
             return run_single_pass(in, out, n, dtype, excl, kModeChained, o, stream);
+        case DWS_VARIANT_SCAN_THEN_PROPAGATE:
+            if (o.tile_shape != 0 || o.nontemporal != 0) return DWS_ERR_UNSUPPORTED;
+            return run_stp(in, out, n, dtype, excl, stream);
         default:
             return run_single_pass(in, out, n, dtype, excl, kModeDecoupled, o, stream);
         }
@@ -364,6 +408,7 @@ dws_status dws_release_workspaces(void)
             if (hipDeviceSynchronize() != hipSuccess) result = DWS_ERR_HIP;
             if (ws->desc) (void)hipFree(ws->desc);
             if (ws->partials) (void)hipFree(ws->partials);
+            if (ws->stp) (void)hipFree(ws->stp);
             if (ws->ctl) (void)hipFree(ws->ctl);
         }
         g_workspaces.clear();
@@ -479,6 +524,59 @@ dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype 
         if (!aligned16(d_in, d_out)) return DWS_ERR_UNSUPPORTED;
         dws_options o{};
         return run_single_pass(d_in, d_out, n, (int)dtype, exclusive != 0, kModeDecoupled, o, stream, d_stamps);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out, size_t n, dws_dtype dtype,
+                              unsigned long long* d_count, hipStream_t stream)
+{
+    try {
+        if (!valid_dtype((int)dtype)) return DWS_ERR_INVALID_ARG;
+        if (d_count == nullptr) return DWS_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(d_count) & 7u) != 0) return DWS_ERR_MISALIGNED;
+        if (n > kSelectMaxElems) return DWS_ERR_UNSUPPORTED;
+        if (n > 0) {
+            dws_status s = validate(d_in, d_out, n, (int)dtype);
+            if (s != DWS_OK) return s;
+            s = validate(d_flags, d_flags, n, DWS_INT32);
+            if (s != DWS_OK) return s;
+            const uintptr_t f = reinterpret_cast<uintptr_t>(d_flags), o = reinterpret_cast<uintptr_t>(d_out);
+            const uintptr_t c = reinterpret_cast<uintptr_t>(d_count), bytes = (uintptr_t)n * kElemBytes;
+            // the flags are read by later tiles while earlier ones write: no overlap with the output
+            if (f < o + bytes && o < f + bytes) return DWS_ERR_OVERLAP;
+            if ((c < o + bytes && o < c + 8) || (c < f + bytes && f < c + 8)) return DWS_ERR_OVERLAP;
+            const uintptr_t i = reinterpret_cast<uintptr_t>(d_in);
+            if (c < i + bytes && i < c + 8) return DWS_ERR_OVERLAP;
+        }
+        SelectArgs a{};
+        a.in = d_in;
+        a.flags = d_flags;
+        a.out = d_out;
+        a.n = n;
+        a.count = d_count;
+        a.aligned = ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out) |
+                      reinterpret_cast<uintptr_t>(d_flags)) & 15u) == 0;
+        const uint64_t tiles = n == 0 ? 0 : ceil_div(n, select_tile_elems(n, a.aligned));
+        a.num_tiles = (uint32_t)tiles;
+        if (tiles <= 1) return from_hip(launch_select(a, stream));
+        Workspace* ws = nullptr;
+        dws_status s = get_workspace(stream, &ws);
+        if (s != DWS_OK) return s;
+        std::lock_guard<std::mutex> lock(ws->mu);
+        s = ensure_desc(ws, tiles);
+        if (s != DWS_OK) return s;
+        s = before_draw_launch(ws);
+        if (s != DWS_OK) return s;
+        a.desc = ws->desc;
+        a.counter = ws->counter();
+        a.watchdog = ws->watchdog();
+        s = from_hip(launch_select(a, stream));
+        if (s == DWS_OK) ++ws->draws_launches;
+        return s;
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

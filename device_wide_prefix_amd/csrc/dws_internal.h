@@ -54,6 +54,39 @@ struct RtsArgs {
 constexpr uint32_t kRtsTileElems = 4096u;
 hipError_t launch_rts(const RtsArgs& a, hipStream_t stream);
 
+// Scan-then-propagate: per-tile scans, recursive scan of the tile sums,
+// propagation of the scanned sums (dws_stp.hip).
+struct StpArgs {
+    const void* in;
+    void* out;
+    uint64_t n;
+    int kind;
+    bool exclusive;
+    void* scratch;          // >= stp_scratch_elems(n) elements (16-byte aligned)
+    uint64_t scratch_elems;
+};
+constexpr uint32_t kStpTileElems = 4096u;
+uint64_t stp_scratch_elems(uint64_t n);
+hipError_t launch_stp(const StpArgs& a, hipStream_t stream);
+
+// Stream compaction by flags (dws_select.hip).
+struct SelectArgs {
+    const void* in;
+    const void* flags;
+    void* out;
+    uint64_t n;
+    bool aligned;            // in, flags and out all 16-byte aligned
+    uint64_t* desc;
+    unsigned long long* counter;
+    unsigned int* watchdog;
+    unsigned long long* count;
+    uint32_t num_tiles;
+};
+constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
+constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
+uint32_t select_tile_elems(uint64_t n, bool aligned);
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
 struct DebugArgs {
     const void* in;
     void* out;

@@ -1,0 +1,176 @@
+// Fused stream compaction (select by flags) on the single-pass decoupled
+// look-back: Merrill & Garland, section 4.4 (in-place compaction behaviour:
+// scatter offsets come from a prefix sum of 0/1 flags, and the look-back's
+// signalling guarantees every predecessor has read its input before a tile
+// writes, so the output may overwrite the input) and section A5 (select-if
+// fused with the scan, no extra pass).
+//
+// Per tile (one workgroup, dynamic tile index, same descriptor protocol and
+// workspace as the scan):
+//   1. load the values and the flags of the tile (coalesced, in registers);
+//   2. exclusive scan of the 0/1 flags in the tile -> each element's rank
+//      among the tile's selected elements, and the tile's selected count;
+//   3. publish {A, count}, look back over predecessors' counts -> the number
+//      of selected elements before the tile, publish {P, prefix + count};
+//   4. every selected element is stored to out[prefix + rank]. The stores go
+//      through a buffer resource based at out + prefix whose range is the
+//      tile's count; unselected elements get an offset past that range, which
+//      the hardware drops, so the scatter needs no branch.
+// Writes of tile t land in [prefix_t, prefix_t + count_t), below the end of
+// tile t, and start only after every earlier tile has published (so has read
+// its input): in place is safe.
+#include "dws_device.hpp"
+#include "dws_internal.h"
+
+namespace dws {
+
+struct SelectParams {
+    const uint32_t* in;
+    const uint32_t* flags;
+    uint32_t* out;
+    uint64_t n;
+    uint64_t* desc;
+    unsigned long long* counter;
+    unsigned int* watchdog;
+    unsigned long long* count;
+    uint32_t num_tiles;
+};
+
+// Byte offset far past any tile's range (at most 4 * 32768 bytes): the
+// buffer range check drops the store. Offset plus store size stays below 2^32.
+constexpr uint32_t kDroppedOffset = 0x80000000u;
+
+template <int BLOCK, int VEC, int CHUNKS>
+__global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
+{
+    static_assert(VEC * CHUNKS <= 32, "one selection bit per element in a 32-bit mask");
+    constexpr int W = BLOCK / 64;
+    constexpr uint32_t SEG = 64u * VEC * CHUNKS;
+    constexpr uint32_t TILE = W * SEG;
+    __shared__ uint32_t s_draw[2];
+    __shared__ uint32_t s_wave[W];
+    __shared__ uint32_t s_prefix;
+
+    const int lane = lane_id();
+    const int wave = (int)uniform(threadIdx.x >> 6);
+    const bool multi = p.num_tiles > 1u;
+
+    uint32_t tile = 0u, epoch = 0u;
+    if (multi) {
+        if (threadIdx.x == 0) {
+            uint32_t t, e;
+            draw_tile(p.counter, p.num_tiles, t, e);
+            s_draw[0] = t;
+            s_draw[1] = e;
+        }
+        __syncthreads();
+        tile = uniform(s_draw[0]);
+        epoch = uniform(s_draw[1]);
+        if (tile >= p.num_tiles) {   // counter not re-armed: never index past the grid
+            if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
+            return;
+        }
+    }
+
+    const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
+    const uint32_t seg_valid = valid_bytes(seg_first, SEG, p.n);
+    uint32_t x[CHUNKS][VEC], r[CHUNKS][VEC];
+    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
+
+    // selection bits, then ranks (exclusive scan of the 0/1 flags) in place
+    uint32_t selected = 0u;
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t bit = r[c][e] != 0u ? 1u : 0u;
+            selected |= bit << (c * VEC + e);
+            r[c][e] = bit;
+        }
+    const uint32_t seg_count = scan_segment_local<uint32_t, true, VEC, CHUNKS>(r);
+    pin_in_registers<uint32_t, VEC, CHUNKS>(x);
+    pin_in_registers<uint32_t, VEC, CHUNKS>(r);
+
+    if (lane == 0) s_wave[wave] = seg_count;
+    __syncthreads();
+    uint32_t wave_pre = 0u, count = 0u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        if (w == wave) wave_pre = count;
+        count += s_wave[w];
+    }
+
+    if (wave == 0) {
+        uint32_t prefix = 0u;
+        if (multi) {
+            if (tile == 0u) {
+                if (lane == 0) desc_store<kOrderRelaxed>(p.desc, desc_pack(epoch, kStatusP, count));
+            } else {
+                if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, count));
+                prefix = lookback_decoupled<uint32_t, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch,
+                                                                                     p.watchdog);
+                if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusP, prefix + count));
+            }
+        }
+        if (lane == 0) s_prefix = prefix;
+    }
+    __syncthreads();
+    const uint32_t prefix = uniform(s_prefix);
+
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.out + prefix, count * 4u);
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const bool sel = (selected >> (c * VEC + e)) & 1u;
+            const uint32_t off = sel ? (wave_pre + r[c][e]) * 4u : kDroppedOffset;
+            __builtin_amdgcn_raw_buffer_store_b32(x[c][e], rout, (int)off, 0, 0);
+        }
+    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.count = (unsigned long long)prefix + count;
+}
+
+__global__ void __launch_bounds__(64) k_store_count(unsigned long long* count, unsigned long long v)
+{
+    if (threadIdx.x == 0) *count = v;
+}
+
+struct SelectShape {
+    int threads, vec, chunks;
+    constexpr uint32_t elems() const { return (uint32_t)(threads * vec * chunks); }
+};
+constexpr SelectShape kSelectLarge{1024, 4, 8};   // 32768 elements
+constexpr SelectShape kSelectSmall{256, 4, 4};    // 4096
+constexpr SelectShape kSelectScalar{256, 1, 16};  // 4096, pointers not 16-byte aligned
+
+static SelectShape select_shape(uint64_t n, bool aligned)
+{
+    if (!aligned) return kSelectScalar;
+    return n >= kSelectLargeMin ? kSelectLarge : kSelectSmall;
+}
+
+uint32_t select_tile_elems(uint64_t n, bool aligned) { return select_shape(n, aligned).elems(); }
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
+{
+    if (a.n == 0) {
+        unsigned long long* c = a.count;
+        unsigned long long zero = 0ull;
+        void* args[] = {&c, &zero};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&k_store_count), dim3(1), dim3(64), args, 0, stream);
+    }
+    const SelectShape s = select_shape(a.n, a.aligned);
+    SelectParams p{static_cast<const uint32_t*>(a.in), static_cast<const uint32_t*>(a.flags),
+                   static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles};
+    void* args[] = {&p};
+    const void* fn = nullptr;
+    if (!a.aligned)
+        fn = reinterpret_cast<const void*>(&k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks>);
+    else if (s.threads == kSelectLarge.threads)
+        fn = reinterpret_cast<const void*>(&k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks>);
+    else
+        fn = reinterpret_cast<const void*>(&k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks>);
+    return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
+}
+
+}  // namespace dws

@@ -102,7 +102,12 @@ typedef enum dws_variant {
      * prefix: ~2n traffic, serial signal chain (same notes, section 3.2,
      * Fig 4; PMPP 11.3 notes, single-pass domino scan with adjacent
      * synchronisation) */
-    DWS_VARIANT_CHAINED = 2
+    DWS_VARIANT_CHAINED = 2,
+    /* three steps, recursively: scan every tile on its own, scan the tile
+     * sums, add each tile's scanned predecessor sum to its elements: ~4n
+     * traffic (PMPP 11.3 notes, hierarchical scan; CUDA-Operators-6-Cumsum
+     * section 2, recursive form; Merrill & Garland section 3.2) */
+    DWS_VARIANT_SCAN_THEN_PROPAGATE = 3
 } dws_variant;
 
 /* Ordering of descriptor stores and loads. The descriptor packs status and
@@ -133,13 +138,32 @@ typedef struct dws_options {
  *                chosen shapes also with release/acquire and with
  *                nontemporal (relaxed);
  *   chained:     the automatically chosen shapes, either order;
- *   reduce-then-scan: tile_shape 0, nontemporal 0 (memory_order ignored).
+ *   reduce-then-scan, scan-then-propagate: tile_shape 0, nontemporal 0
+ *                (memory_order ignored).
  * Pointers that are not both 16-byte aligned use scalar loads; a forced
  * shape without a scalar-load kernel then falls back to the automatic one,
  * and nontemporal is ignored.
  */
 dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                        int exclusive, const dws_options* opt, hipStream_t stream);
+
+/*
+ * Stream compaction (select by flags), fused with the single-pass scan
+ * (Merrill & Garland, section 4.4, in-place compaction; section A5): copies,
+ * in order, every d_in[i] whose flag d_flags[i] (32-bit integer) is non-zero
+ * to d_out[0 .. count) and writes count to the DEVICE word *d_count (64-bit,
+ * 8-byte aligned). The values are moved as 32-bit words whatever dtype says
+ * (dtype is checked, not used). d_out == d_in (in place) is allowed: a tile
+ * writes only after every earlier tile has read its input. d_flags may equal
+ * d_in when d_out does not (selects the non-zero words); the flags, the count
+ * word and the output must not overlap otherwise (DWS_ERR_OVERLAP). d_out
+ * elements at and past count are left unchanged. n must be below 2^32
+ * (DWS_ERR_UNSUPPORTED): counts travel in 32-bit descriptor values. n == 0
+ * writes count 0. Asynchronous on `stream`; same workspace as the scans.
+ */
+dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out, size_t n,
+                              dws_dtype dtype, unsigned long long* d_count,
+                              hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* dws_status_string(dws_status status);

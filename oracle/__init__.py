@@ -13,6 +13,7 @@ Functions:
     scan_i32                -> alias of scan_u32
     scan_f32(x, exclusive)  -> (y fp64, sabs fp64)
     scan(x, exclusive)      -> dispatch on x.dtype
+    select_flagged(x, flags) -> the x[i] with flags[i] != 0, in order
 """
 from __future__ import annotations
 
@@ -65,6 +66,8 @@ class OracleLib:
         lib.oracle_scan_u32.restype = ctypes.c_int
         lib.oracle_scan_f32.argtypes = [vp, sz, vp, vp, ctypes.c_int]
         lib.oracle_scan_f32.restype = ctypes.c_int
+        lib.oracle_select_flagged.argtypes = [vp, vp, sz, vp]
+        lib.oracle_select_flagged.restype = sz
         self._lib = lib
         self.path = path
 
@@ -99,6 +102,18 @@ class OracleLib:
         return y, s
 
 
+    def select_flagged(self, x: np.ndarray, flags: np.ndarray) -> np.ndarray:
+        """Elements of x (any 4-byte dtype, moved as bits) whose int32 flag is
+        non-zero, in order."""
+        x = np.ascontiguousarray(x)
+        flags = np.ascontiguousarray(flags, dtype=np.int32)
+        if x.itemsize != 4 or x.shape != flags.shape:
+            raise ValueError("x must hold 4-byte elements, one flag each")
+        out = np.empty_like(x)
+        cnt = self._lib.oracle_select_flagged(_ptr(x), _ptr(flags), x.size, _ptr(out))
+        return out[:cnt]
+
+
 _default: OracleLib | None = None
 
 
@@ -120,6 +135,10 @@ scan_i32 = scan_u32
 
 def scan_f32(x, exclusive=False, want_sabs=True):
     return _oracle().scan_f32(x, exclusive, want_sabs)
+
+
+def select_flagged(x, flags):
+    return _oracle().select_flagged(x, flags)
 
 
 def scan(x: np.ndarray, exclusive: bool = False):

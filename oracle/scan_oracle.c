@@ -36,7 +36,9 @@
  * the PMPP 11.3 and 11.2 notes (tests/golden/), closed forms (constant and
  * arithmetic inputs), modular wrap cases, an fp64-accumulation witness,
  * O(n^2) brute force on small n and numpy's cumsum as an independent library
- * routine.
+ * routine. The compaction is pinned by closed forms (all, none, every other),
+ * brute force against a list comprehension, the scatter to exclusive prefix
+ * offsets and numpy's boolean-mask indexing.
  */
 #include <stddef.h>
 #include <stdint.h>
@@ -96,4 +98,24 @@ int oracle_scan_f32(const float* x, size_t n, double* y, double* sabs, int exclu
         }
     }
     return 0;
+}
+
+/*
+ * Stream compaction by flags: appends, in input order, every x[i] whose flag
+ * is non-zero to out and returns how many were appended. This is the plain
+ * definition of the select operation that Merrill & Garland (section 4.4,
+ * in-place compaction) build from a prefix sum of 0/1 flags: selected element
+ * i lands at the number of selected elements before it. out may be x itself
+ * (the write index never passes the read index).
+ */
+size_t oracle_select_flagged(const uint32_t* x, const int32_t* flags, size_t n, uint32_t* out)
+{
+    size_t count = 0;
+    for (size_t i = 0; i < n; ++i) {
+        if (flags[i] != 0) {
+            out[count] = x[i];
+            ++count;
+        }
+    }
+    return count;
 }

@@ -17,6 +17,9 @@ configurations):
   C3  N = 2^26          uint32  uniform over [0, 2^32)       inclusive, seed 2
   C4  N = 2^28          float32 uniform [0, 1), in place     exclusive, seed 3
   C5  N = 2^30 - 12345  int32   Bernoulli(0.5) 0/1 flags     exclusive, seed 4
+
+Stream compaction (select by flags) reuses C5's flags as the selection and
+draws the values to move as uniform int32 with seed 5 (SELECT_VALUE_SEED).
 """
 from __future__ import annotations
 
@@ -58,6 +61,9 @@ WORKLOADS = {
     "C5": Workload("C5", (1 << 30) - 12345, "int32", "flags_half", 4, True, False,
                    "exclusive + scan, N=2^30-12345 int32 0/1 flags Bernoulli(0.5), seed 4"),
 }
+
+
+SELECT_VALUE_SEED = 5
 
 
 def _int_0_9(rng, n):
@@ -103,6 +109,19 @@ DISTRIBUTIONS = {
 
 # default distribution per dtype for ad-hoc parity cases
 DEFAULT_DIST = {"int32": "i32_full", "uint32": "u32_full", "float32": "f32_pm1"}
+
+
+def selection_flags(n: int, density: float, seed: int, any_nonzero: bool = False) -> np.ndarray:
+    """int32 selection flags, each non-zero with probability ``density``
+    (Bernoulli from PCG64(seed)). Non-zero flags are 1, or with
+    ``any_nonzero`` a uniform non-zero int32 (negative values included)."""
+    rng = np.random.default_rng(seed)
+    on = rng.random(int(n)) < density
+    if not any_nonzero:
+        return on.astype(np.int32)
+    v = rng.integers(-(1 << 31), 1 << 31, size=int(n), dtype=np.int64)
+    v[v == 0] = 1
+    return np.where(on, v, 0).astype(np.int32)
 
 
 def generate(dist: str, n: int, seed: int) -> np.ndarray:

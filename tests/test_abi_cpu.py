@@ -102,7 +102,7 @@ def test_option_validation(lib):
     def call(**kw):
         o = dws.DwsOptions(kw.get("variant", 0), kw.get("order", 0), kw.get("shape", 0), kw.get("nt", 0))
         return lib.dws_scan_ex(FAKE, FAKE + (1 << 20), 1 << 16, dws.FLOAT32, 1, ctypes.byref(o), None)
-    assert call(variant=3) == dws.ERR_INVALID_ARG
+    assert call(variant=4) == dws.ERR_INVALID_ARG
     assert call(variant=-1) == dws.ERR_INVALID_ARG
     assert call(order=2) == dws.ERR_INVALID_ARG
     assert call(shape=dws.num_tile_shapes()) == dws.ERR_INVALID_ARG
@@ -116,6 +116,8 @@ def test_option_validation(lib):
     assert call(shape=4, nt=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.REDUCE_THEN_SCAN, shape=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.REDUCE_THEN_SCAN, nt=1) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.SCAN_THEN_PROPAGATE, shape=1) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.SCAN_THEN_PROPAGATE, nt=1) == dws.ERR_UNSUPPORTED
     # options are validated before the arguments: n == 0 with bad options
     o = dws.DwsOptions(9, 0, 0, 0)
     assert lib.dws_scan_ex(None, None, 0, dws.INT32, 0, ctypes.byref(o), None) == dws.ERR_INVALID_ARG
@@ -163,3 +165,35 @@ def test_binding_refuses_cpu_tensors(lib):
         dws.scan_inclusive(x)
     with pytest.raises(TypeError):
         dws.scan_exclusive(x.float())
+
+
+def test_select_validation(lib):
+    f = lib.dws_select_flagged
+    cnt = FAKE + (1 << 24)
+    n = 1000
+    # bad dtype, missing or misaligned count word
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, 9, cnt, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, None, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, cnt + 4, None) == dws.ERR_MISALIGNED
+    # null data pointers, misaligned elements
+    assert f(None, FAKE + 8192, FAKE + 16384, n, dws.INT32, cnt, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, None, FAKE + 16384, n, dws.INT32, cnt, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 8192, None, n, dws.INT32, cnt, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 8194, FAKE + 16384, n, dws.INT32, cnt, None) == dws.ERR_MISALIGNED
+    # flags overlapping the output (the flags must survive the writes)
+    assert f(FAKE, FAKE + 8192, FAKE + 8192, n, dws.INT32, cnt, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + 8192, FAKE + 8192 + 400, n, dws.INT32, cnt, None) == dws.ERR_OVERLAP
+    # partial overlap of input and output
+    assert f(FAKE, FAKE + 16384, FAKE + 4, n, dws.INT32, cnt, None) == dws.ERR_OVERLAP
+    # the count word inside the input, the flags or the output
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, FAKE + 8, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, FAKE + 8192 + 8, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, FAKE + 16384 + 3992, None) == dws.ERR_OVERLAP
+    # counts travel in 32-bit descriptor values
+    assert f(FAKE, FAKE + (1 << 36), FAKE + (2 << 36), 1 << 32, dws.INT32, cnt, None) == dws.ERR_UNSUPPORTED
+
+
+def test_select_binding_checks_flags(lib):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        dws.select_flagged(torch.arange(10, dtype=torch.int32), torch.ones(10, dtype=torch.int32))

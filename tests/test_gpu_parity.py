@@ -122,10 +122,12 @@ def test_input_aligned_output_unaligned(gpu):
 # ---------------------------------------------------------------------------
 # comparison variants, tile shapes, descriptor memory order, non-temporal
 # ---------------------------------------------------------------------------
-VARIANT_SIZES = [1, TILE - 1, TILE + 1, 3 * TILE + 7, (1 << 20) + 3, (1 << 22) + 11, (1 << 24) + 5]
+VARIANT_SIZES = [1, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, TILE * TILE + 1, (1 << 20) + 3, (1 << 22) + 11,
+                 (1 << 24) + 5]
 
 
-@pytest.mark.parametrize("variant", [dws.REDUCE_THEN_SCAN, dws.CHAINED], ids=["rts", "chained"])
+@pytest.mark.parametrize("variant", [dws.REDUCE_THEN_SCAN, dws.CHAINED, dws.SCAN_THEN_PROPAGATE],
+                         ids=["rts", "chained", "stp"])
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_comparison_variants(gpu, dtype, exclusive, variant):
@@ -390,6 +392,146 @@ def test_profiled_scan(gpu, n):
             assert st.shape == (dws.profiled_num_tiles(n), 5)
             assert np.all(st > 0), "every tile writes its stamps"
             assert np.all(np.diff(st, axis=1) >= 0), "phases are in order within a tile"
+
+
+# ---------------------------------------------------------------------------
+# stream compaction (select by flags) fused with the single-pass scan
+# ---------------------------------------------------------------------------
+SEL_TILE_LARGE = 32768
+SELECT_SIZES = [0, 1, 2, 63, 64, 65, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, 1_000_003,
+                (1 << 22) - 1, 1 << 22, (1 << 22) + 1, (1 << 22) + SEL_TILE_LARGE + 5, 129 * SEL_TILE_LARGE - 3]
+DENSITIES = [0.0, 0.01, 0.5, 0.99, 1.0]
+SENTINEL = -0x21524111   # 0xdeadbeef as int32
+
+
+def _select(x, flags, in_place=False, offset=0):
+    """Run dws_select_flagged; returns (out as numpy over all n, count)."""
+    import torch
+    n = x.size
+    _, xd = to_device(x, extra_front=offset)
+    _, fd = to_device(flags, extra_front=offset)
+    if in_place:
+        out = xd
+    else:
+        ostore = torch.full((n + offset,), SENTINEL, dtype=torch.int32, device="cuda")
+        out = ostore[offset:]
+    count = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    st = dws.select_flagged_ptr(xd.data_ptr(), fd.data_ptr(), out.data_ptr(), n, dws.INT32,
+                                count.data_ptr(), stream)
+    assert st == dws.OK, dws.status_string(st)
+    return from_device(out, "int32"), int(count.item())
+
+
+def _check_select(x, flags, got, cnt, in_place, label):
+    want = oracle.select_flagged(x, flags)
+    assert cnt == want.size, f"{label}: count {cnt} != {want.size}"
+    if not np.array_equal(got[:cnt], want):
+        i = int(np.flatnonzero(got[:cnt] != want)[0])
+        raise AssertionError(f"{label}: mismatch at {i}/{cnt}: gpu {got[i]} ref {want[i]}")
+    # past the count the output is untouched: the sentinel, or (in place) the input
+    rest = x[cnt:] if in_place else np.full(x.size - cnt, SENTINEL, dtype=np.int32)
+    assert np.array_equal(got[cnt:], rest), f"{label}: output changed past the count"
+
+
+@pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
+@pytest.mark.parametrize("density", DENSITIES)
+def test_select_sizes_and_densities(gpu, density, in_place):
+    for n in SELECT_SIZES:
+        note(f"select n={n} density={density} in_place={in_place}")
+        x = wl.generate("i32_full", n, seed=n + 1)
+        flags = wl.selection_flags(n, density, seed=n + 2, any_nonzero=(n % 2 == 1))
+        got, cnt = _select(x, flags, in_place=in_place)
+        _check_select(x, flags, got, cnt, in_place, f"n={n} d={density}")
+
+
+def test_select_unaligned(gpu):
+    for off in (1, 3):
+        for n in (TILE - 1, 5 * TILE + 7, (1 << 22) + 9):
+            for in_place in (False, True):
+                note(f"select unaligned off={off} n={n} in_place={in_place}")
+                x = wl.generate("i32_full", n, seed=n + off)
+                flags = wl.selection_flags(n, 0.3, seed=n + off + 1)
+                got, cnt = _select(x, flags, in_place=in_place, offset=off)
+                _check_select(x, flags, got, cnt, in_place, f"offset {off} n={n}")
+
+
+def test_select_flags_are_the_input(gpu):
+    # d_flags == d_in: keeps the non-zero words
+    import torch
+    n = 3 * SEL_TILE_LARGE + 11 + (1 << 22)
+    note(f"select flags=input n={n}")
+    x = wl.generate("flags_half", n, seed=9) * wl.generate("i32_full", n, seed=10)
+    _, xd = to_device(x)
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, cnt = dws.select_flagged(xd, xd, out=out, count=cnt)
+    c = int(cnt.item())
+    assert np.array_equal(from_device(out, "int32")[:c], x[x != 0])
+
+
+def test_select_float_bits_and_binding(gpu):
+    import torch
+    n = 50_001
+    note(f"select float bits n={n}")
+    x = wl.generate("f32_normal", n, seed=12)
+    x[::7] = -0.0
+    x[5] = np.inf
+    x[6] = np.nan
+    flags = wl.selection_flags(n, 0.5, seed=13)
+    xd = torch.from_numpy(x).cuda()
+    fd = torch.from_numpy(flags).cuda()
+    out, cnt = dws.select_flagged(xd, fd)
+    c = int(cnt.item())
+    want = oracle.select_flagged(x, flags)
+    assert c == want.size
+    assert np.array_equal(out[:c].cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_select_repeated_and_streams(gpu):
+    # the descriptor epoch protocol is shared with the scans: interleave them
+    import torch
+    n = (1 << 22) + 77
+    x = wl.generate("i32_full", n, seed=21)
+    flags = wl.selection_flags(n, 0.5, seed=22)
+    want = oracle.select_flagged(x, flags)
+    _, xd = to_device(x)
+    _, fd = to_device(flags)
+    s2 = torch.cuda.Stream()
+    for rep in range(6):
+        note(f"select repeat {rep}")
+        out = torch.empty_like(xd)
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        stream = s2 if rep % 2 else None
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                dws.select_flagged(xd, fd, out=out, count=cnt)
+                y = dws.scan_exclusive(fd)
+            torch.cuda.current_stream().wait_stream(stream)
+        else:
+            dws.select_flagged(xd, fd, out=out, count=cnt)
+            y = dws.scan_exclusive(fd)
+        torch.cuda.synchronize()
+        c = int(cnt.item())
+        assert c == want.size
+        assert np.array_equal(out[:c].cpu().numpy(), want)
+        check(flags, from_device(y, "int32"), "int32", True, label=f"interleaved scan {rep}")
+
+
+def test_select_full_size(gpu):
+    # C5's flags select from uniform int32 values, in place
+    w = wl.WORKLOADS["C5"]
+    note(f"select full size n={w.n}")
+    flags = wl.generate_workload(w)
+    x = wl.generate("i32_full", w.n, seed=wl.SELECT_VALUE_SEED)
+    got, cnt = _select(x, flags, in_place=True)
+    want = oracle.select_flagged(x, flags)
+    assert cnt == want.size
+    for s in range(0, cnt, 1 << 26):
+        e = slice(s, min(s + (1 << 26), cnt))
+        assert np.array_equal(got[e], want[e]), f"mismatch in [{s}, {e.stop})"
+    assert np.array_equal(got[cnt:], x[cnt:])
 
 
 def test_zz_watchdog_never_tripped(gpu):

@@ -166,6 +166,45 @@ def _brute_force_checks(lib, fail):
             fail(f"brute force fp32 exclusive n={n}")
 
 
+def _select_checks(lib, fail):
+    rng = np.random.default_rng(77)
+    # closed forms
+    x = np.arange(1000, dtype=np.uint32)
+    if lib.select_flagged(x, np.ones(1000, np.int32)).tolist() != x.tolist():
+        fail("select all")
+    if lib.select_flagged(x, np.zeros(1000, np.int32)).size != 0:
+        fail("select none")
+    alt = (np.arange(1000) % 2 == 0).astype(np.int32)
+    if lib.select_flagged(x, alt).tolist() != list(range(0, 1000, 2)):
+        fail("select even positions")
+    # any non-zero flag selects, negative ones included
+    f = np.array([0, -1, 5, 0, 2**31 - 1, -(2**31)], dtype=np.int32)
+    if lib.select_flagged(np.arange(6, dtype=np.uint32), f).tolist() != [1, 2, 4, 5]:
+        fail("select non-zero flags")
+    # brute force against a Python list comprehension, and the scatter form:
+    # selected element i lands at the exclusive prefix sum of the 0/1 flags
+    for n in (1, 2, 7, 64, 65, 300):
+        xs = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        fl = rng.integers(-2, 3, size=n).astype(np.int32)
+        got = lib.select_flagged(xs, fl)
+        if got.tolist() != [int(v) for v, g in zip(xs, fl) if g != 0]:
+            fail(f"select brute force n={n}")
+        excl = lib.scan_u32((fl != 0).astype(np.int32), exclusive=True)
+        scat = np.zeros(int(np.count_nonzero(fl)), dtype=np.uint32)
+        dest = excl[fl != 0].astype(np.int64)
+        if dest.size and (dest.min() < 0 or dest.max() >= scat.size):
+            fail(f"select scatter offsets out of range n={n}")
+            continue
+        scat[dest] = xs[fl != 0]
+        if not np.array_equal(got, scat):
+            fail(f"select vs scatter to exclusive offsets n={n}")
+    # float bits are moved unchanged
+    fx = np.array([1.5, -0.0, np.inf, 3.25], dtype=np.float32)
+    got = lib.select_flagged(fx, np.array([1, 1, 1, 0], np.int32))
+    if got.view(np.uint32).tolist() != fx[:3].view(np.uint32).tolist():
+        fail("select float bits")
+
+
 def pin_failures(lib) -> list:
     """Run every pin against an oracle library; return the names that fail."""
     failures = []
@@ -176,6 +215,7 @@ def pin_failures(lib) -> list:
     _closed_form_checks(lib, fail)
     _fp64_witness_checks(lib, fail)
     _brute_force_checks(lib, fail)
+    _select_checks(lib, fail)
     return failures
 
 
@@ -209,6 +249,20 @@ def test_brute_force(lib):
     failures = []
     _brute_force_checks(lib, failures.append)
     assert failures == []
+
+
+def test_select_flagged(lib):
+    failures = []
+    _select_checks(lib, failures.append)
+    assert failures == []
+    # numpy's boolean indexing as an independent routine, on a C5-like input
+    x = np.arange(1 << 20, dtype=np.uint32)
+    flags = wl.generate("flags_half", 1 << 20, 4)
+    assert np.array_equal(lib.select_flagged(x, flags), x[flags != 0])
+    # in place
+    y = x.copy()
+    out = lib._lib.oracle_select_flagged(y.ctypes.data, flags.ctypes.data, y.size, y.ctypes.data)
+    assert np.array_equal(y[:out], x[flags != 0])
 
 
 def test_empty_and_in_place(lib):
@@ -271,6 +325,9 @@ MUTANTS = [
     ("wrong sign", "running += xi;", "running -= xi;"),
     ("reversed index", "uint32_t xi = x[i];", "uint32_t xi = x[n - 1 - i];"),
     ("stale element", "double xi = (double)x[i];", "double xi = (double)x[i > 0 ? i - 1 : 0];"),
+    ("select tests sign", "if (flags[i] != 0) {", "if (flags[i] > 0) {"),
+    ("select drops the last element", "for (size_t i = 0; i < n; ++i) {\n        if (flags[i]", "for (size_t i = 0; i + 1 < n; ++i) {\n        if (flags[i]"),
+    ("select writes past the slot", "out[count] = x[i];\n            ++count;", "++count;\n            out[count - 1 + (count > 1)] = x[i];"),
 ]
 
 
