@@ -17,7 +17,9 @@ the kernel's launch duration.
 
 Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained|scan_then_propagate,
 --order relaxed|acq_rel, --tile-shape K, --nontemporal, --no-cpu-baseline,
---all (extra JSON lines for every workload and variant on stderr).
+--all (extra JSON lines for every workload and variant on stderr), --sweep
+(N = 2^10..2^30, every variant and memcpy, cold and warm caches; stderr),
+--select (stream compaction on the 2^30-12345 flag workload; stderr).
 """
 from __future__ import annotations
 
@@ -43,21 +45,27 @@ FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_c4.json")
 VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2, "scan_then_propagate": 3}
 ORDERS = {"relaxed": 0, "acq_rel": 1}
+TILE_INDEX = {"auto": 0, "drawn": 1, "dispatch": 2}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
-    """Hash of the HIP sources, to tell whether stored counters still apply."""
+# the sources the fp32 single-pass kernel is compiled from
+SINGLE_PASS_SOURCES = ("dws_device.hpp", "dws_internal.h", "dws_protocol.h", "dws_single_pass_kernel.hpp",
+                       "dws_sp_f32.hip")
+
+
+def kernel_source_sha(names=SINGLE_PASS_SOURCES) -> str:
+    """Hash of the sources a kernel is built from, to tell whether stored
+    counters still apply to it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "device_wide_prefix_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in sorted(names):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -97,7 +105,8 @@ def time_steps(fn, prepare, steps: int, warmup: int):
 
 
 def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool, steps: int, warmup: int,
-                 with_memcpy: bool, x_host=None):
+                 with_memcpy: bool, x_host=None, instrument: bool = True, flush_caches: bool = True,
+                 tile_index: int = 0):
     import torch
     import device_wide_prefix_amd as dws
 
@@ -111,13 +120,14 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
     code = {"int32": dws.INT32, "uint32": dws.UINT32, "float32": dws.FLOAT32}[w.dtype]
     stream = torch.cuda.current_stream().cuda_stream
     dws.reserve(w.n)
-    opt = dws.DwsOptions(variant, order, shape, int(nt))
-    default = variant == 0 and order == 0 and shape == 0 and not nt
+    opt = dws.DwsOptions(variant, order, shape, int(nt), tile_index)
+    default = variant == 0 and order == 0 and shape == 0 and not nt and tile_index == 0
     entry = dws.scan_exclusive_ptr if w.exclusive else dws.scan_inclusive_ptr
 
     def prepare():
         work.copy_(pristine)
-        flush.sum()        # read-only flush: leaves clean lines, no write-back later
+        if flush_caches:
+            flush.sum()    # read-only flush: leaves clean lines, no write-back later
 
     def scan():
         if default:
@@ -152,7 +162,7 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
             ok = ok and bool(np.all(np.diff(y.astype(np.int64)) >= 0))
     result["property_check"] = bool(ok)
 
-    if w.dtype != "uint32" and variant == 0 and order == 0 and shape == 0 and not nt:
+    if instrument and w.dtype != "uint32" and default:
         # one instrumented run: where a tile's time goes (100 MHz stamps)
         prepare()
         torch.cuda.synchronize()
@@ -160,7 +170,7 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
         torch.cuda.synchronize()
         st = st.cpu().numpy().astype(np.int64)
         life = (st[:, 4] - st[:, 0]).astype(np.float64)
-        phases = {"draw": st[:, 1] - st[:, 0], "load_and_local_scan": st[:, 2] - st[:, 1],
+        phases = {"tile_index": st[:, 1] - st[:, 0], "load_and_local_scan": st[:, 2] - st[:, 1],
                   "lookback": st[:, 3] - st[:, 2], "finish_and_store_issue": st[:, 4] - st[:, 3]}
         result["lookback_stall_share"] = float((st[:, 3] - st[:, 2]).sum() / life.sum())
         result["phase_mean_us"] = {k: round(float(v.mean()) * 0.01, 3) for k, v in phases.items()}
@@ -179,6 +189,84 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
     del pristine, work, out, flush
     torch.cuda.empty_cache()
     return result
+
+
+SWEEP_EXPONENTS = range(10, 31)
+
+
+def run_sweep(steps: int, warmup: int):
+    """Exclusive in-place fp32 scan (the headline workload's kind) at N = 2^10 ..
+    2^30, every variant, against a same-size device-to-device memcpy; cold
+    (caches flushed before each step) and warm (no flush). Inputs are prefixes
+    of one seeded draw. One JSON line per (N, variant, cache state) on stderr."""
+    w_big = wl.WORKLOADS["C4"]
+    x_all = wl.generate(w_big.dist, 1 << max(SWEEP_EXPONENTS), w_big.seed)
+    rows = []
+    for k in SWEEP_EXPONENTS:
+        n = 1 << k
+        w = wl.Workload(f"sweep_2^{k}", n, "float32", w_big.dist, w_big.seed, True, True,
+                        f"exclusive + scan in place, N=2^{k} fp32 uniform [0,1) (prefix of the seed-3 draw)")
+        x = x_all[:n]
+        for cold in (True, False):
+            for vname, v in VARIANTS.items():
+                r = run_workload(w, v, 0, 0, False, steps, warmup, with_memcpy=(v == 0), x_host=x,
+                                 instrument=False, flush_caches=cold)
+                row = summarize(w, r, vname, None)
+                row["cache"] = "cold" if cold else "warm"
+                row["n"] = n
+                log("SWEEP " + json.dumps(row))
+                rows.append(row)
+    return rows
+
+
+def run_select(steps: int, warmup: int, in_place: bool):
+    """Stream compaction: C5's 0/1 flags (Bernoulli 0.5, seed 4) select from
+    uniform int32 values (seed 5). Algorithmic bytes = read values and flags
+    (8 n) + write the selected values (4 count). Also times torch.masked_select
+    on the same data (its output size needs a host synchronisation)."""
+    import torch
+    import device_wide_prefix_amd as dws
+    w = wl.WORKLOADS["C5"]
+    n = w.n
+    flags = torch.from_numpy(wl.generate_workload(w)).to("cuda")
+    vals = torch.from_numpy(wl.generate("i32_full", n, wl.SELECT_VALUE_SEED)).to("cuda")
+    work = torch.empty_like(vals)
+    out = work if in_place else torch.empty_like(vals)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    dws.reserve(n)
+
+    def prepare():
+        work.copy_(vals)
+        flush.sum()
+
+    def select():
+        st = dws.select_flagged_ptr(work.data_ptr(), flags.data_ptr(), out.data_ptr(), n, dws.INT32,
+                                    cnt.data_ptr(), stream)
+        if st != dws.OK:
+            raise RuntimeError(f"select failed: {dws.status_string(st)}")
+
+    times = time_steps(select, prepare, steps, warmup)
+    count = int(cnt.item())
+    mask = flags != 0
+    ok = count == int(mask.sum().item())
+    ok = ok and bool(torch.equal(out[:count], vals[mask]))
+    algo = 8 * n + 4 * count
+    mean = float(np.mean(times))
+    row = {"op": "select_flagged", "n": n, "in_place": in_place, "count": count, "ms_mean": mean,
+           "ms_min": float(np.min(times)), "gbps": algo / (mean * 1e-3) / 1e9,
+           "frac_hbm_peak": algo / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, "property_check": ok}
+
+    def torch_select():
+        torch.masked_select(work, mask)
+
+    tt = time_steps(torch_select, prepare, max(3, steps // 2), 2)
+    row["torch_masked_select_ms_mean"] = float(np.mean(tt))
+    row["speedup_vs_torch_masked_select"] = float(np.mean(tt)) / mean
+    del flags, vals, work, out, flush, mask
+    torch.cuda.empty_cache()
+    return row
 
 
 def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
@@ -240,8 +328,13 @@ def main():
     ap.add_argument("--order", default="relaxed", choices=sorted(ORDERS))
     ap.add_argument("--tile-shape", type=int, default=0)
     ap.add_argument("--nontemporal", action="store_true")
+    ap.add_argument("--tile-index", default="auto", choices=sorted(TILE_INDEX))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also measure every workload and variant (stderr)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also sweep N = 2^10..2^30 for every variant against memcpy (stderr)")
+    ap.add_argument("--select", action="store_true",
+                    help="also measure stream compaction on the 2^30-12345 flag workload (stderr)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -262,7 +355,7 @@ def main():
     x = wl.generate_workload(w)
     variant = VARIANTS[args.variant]
     res = run_workload(w, variant, ORDERS[args.order], args.tile_shape, args.nontemporal, args.steps,
-                       args.warmup, with_memcpy=True, x_host=x)
+                       args.warmup, with_memcpy=True, x_host=x, tile_index=TILE_INDEX[args.tile_index])
     s = summarize(w, res, args.variant, args)
     log(json.dumps(s))
     if not s["property_check"]:
@@ -271,7 +364,8 @@ def main():
     mean_ms = s["ms_mean"]
     achieved = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
     traffic = traffic_for_current_kernel() if (variant == 0 and args.workload == "C4" and args.order == "relaxed"
-                                               and args.tile_shape == 0 and not args.nontemporal) else None
+                                               and args.tile_shape == 0 and not args.nontemporal
+                                               and args.tile_index == "auto") else None
     line = {
         "metric": METRIC,
         "value": round(achieved, 2),
@@ -289,6 +383,7 @@ def main():
                    "scan": "exclusive" if w.exclusive else "inclusive", "in_place": w.in_place,
                    "seed": w.seed, "variant": args.variant, "memory_order": args.order,
                    "tile_shape": args.tile_shape, "nontemporal": bool(args.nontemporal),
+                   "tile_index": args.tile_index,
                    "parallelism": "single GPU"},
         "frac_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
         "memcpy_gbps": round(s["memcpy_gbps"], 2),
@@ -314,6 +409,12 @@ def main():
                 r = run_workload(wk, v, 0, 0, False, max(5, args.steps // 2), 3, with_memcpy=(v == 0), x_host=xk)
                 log("ALL " + json.dumps(summarize(wk, r, vname, args)))
             del xk
+
+    if args.sweep:
+        run_sweep(max(5, args.steps // 2), 3)
+    if args.select:
+        for in_place in (False, True):
+            log("SELECT " + json.dumps(run_select(args.steps, args.warmup, in_place)))
 
     print(json.dumps(line), flush=True)
 

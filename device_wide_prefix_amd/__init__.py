@@ -29,6 +29,8 @@ INT32, UINT32, FLOAT32 = 0, 1, 2
 SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED, SCAN_THEN_PROPAGATE = 0, 1, 2, 3
 # dws_memory_order
 ORDER_RELAXED, ORDER_ACQ_REL = 0, 1
+# dws_tile_index
+TILE_AUTO, TILE_DRAWN, TILE_DISPATCH = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
@@ -46,7 +48,8 @@ class ScanError(RuntimeError):
 
 class DwsOptions(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("memory_order", ctypes.c_int),
-                ("tile_shape", ctypes.c_int), ("nontemporal", ctypes.c_int)]
+                ("tile_shape", ctypes.c_int), ("nontemporal", ctypes.c_int),
+                ("tile_index", ctypes.c_int)]
 
 
 _lib = None
@@ -177,11 +180,11 @@ def scan_exclusive(x, out=None, stream=None):
 
 
 def scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=ORDER_RELAXED,
-            tile_shape=0, nontemporal=False, stream=None):
+            tile_shape=0, nontemporal=False, tile_index=TILE_AUTO, stream=None):
     """Scan with explicit options (variant, descriptor memory order, tile shape,
-    non-temporal memory access); returns ``out``."""
+    non-temporal memory access, tile index source); returns ``out``."""
     code, out = _prepare(x, out)
-    opt = DwsOptions(int(variant), int(memory_order), int(tile_shape), int(bool(nontemporal)))
+    opt = DwsOptions(int(variant), int(memory_order), int(tile_shape), int(bool(nontemporal)), int(tile_index))
     with _device_of(x):
         _check(scan_ex_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, opt,
                            _stream(x, stream)), "dws_scan_ex")
@@ -211,7 +214,7 @@ def scan_debug(x, out, tile_elems, exclusive=False, variant=SINGLE_PASS, delay_e
 
 
 STAMPS_PER_TILE = 5
-STAMP_NAMES = ("start", "drawn", "aggregate_published", "prefix_known", "stores_issued")
+STAMP_NAMES = ("start", "tile_index_known", "aggregate_published", "prefix_known", "stores_issued")
 
 
 def profiled_num_tiles(n: int) -> int:
@@ -224,7 +227,7 @@ def profiled_num_tiles(n: int) -> int:
 def scan_profiled(x, out=None, exclusive=False, stream=None):
     """Instrumented single-pass scan. Returns (out, stamps) where stamps is a
     (num_tiles, 5) int64 GPU tensor of 100 MHz real-time counter values:
-    start, drawn, aggregate published, prefix known, stores issued."""
+    start, tile index known, aggregate published, prefix known, stores issued."""
     import torch
     code, out = _prepare(x, out)
     tiles = profiled_num_tiles(x.numel())

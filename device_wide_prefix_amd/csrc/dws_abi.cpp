@@ -35,7 +35,7 @@ struct Workspace {
     void* partials = nullptr;     // reduce-then-scan partials (kRtsMaxGroups x 4 B)
     void* stp = nullptr;          // scan-then-propagate tile sums (all levels)
     uint64_t stp_elems = 0;
-    uint64_t draws_launches = 0;  // launches that used the counter since the last clear
+    uint32_t epoch = 0;           // descriptor epoch of the last launch (0: none since the clear)
 
     unsigned long long* counter() const
     {
@@ -136,7 +136,7 @@ dws_status ensure_desc(Workspace* ws, uint64_t slots)
     void* p = nullptr;
     hipError_t e = hipMalloc(&p, want * sizeof(uint64_t));
     if (e != hipSuccess) return from_hip(e);
-    // fresh zeroed descriptors and a re-armed counter (epoch 1)
+    // fresh zeroed descriptors (all X for every epoch) and a zero counter
     e = launch_workspace_init(static_cast<uint64_t*>(p), want, ws->counter(), nullptr, ws->stream);
     if (e != hipSuccess) {
         (void)hipFree(p);
@@ -144,19 +144,22 @@ dws_status ensure_desc(Workspace* ws, uint64_t slots)
     }
     ws->desc = static_cast<uint64_t*>(p);
     ws->desc_slots = want;
-    ws->draws_launches = 0;
+    ws->epoch = 0;
     return DWS_OK;
 }
 
-// Before a launch that draws from the counter: once the epoch would wrap,
-// clear every descriptor so no word of an old call can carry the new epoch.
-dws_status before_draw_launch(Workspace* ws)
+// The descriptor epoch of the next launch on the workspace (call with ws->mu
+// held). Every launch gets a new one, so descriptors left by earlier launches
+// read as X; once the epochs are used up, every descriptor is cleared first,
+// so no word of an old launch can carry a reused epoch.
+dws_status next_epoch(Workspace* ws, uint32_t* epoch)
 {
-    if (ws->draws_launches + 1 >= (uint64_t)kEpochMax) {
+    if (ws->epoch >= kEpochMax) {
         hipError_t e = launch_workspace_init(ws->desc, ws->desc_slots, ws->counter(), nullptr, ws->stream);
         if (e != hipSuccess) return from_hip(e);
-        ws->draws_launches = 0;
+        ws->epoch = 0;
     }
+    *epoch = ++ws->epoch;
     return DWS_OK;
 }
 
@@ -182,7 +185,12 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     const bool nt = o.nontemporal != 0 && aligned;
     const int shape = resolve_shape(o.tile_shape, n, aligned);
     if (shape < 0) return DWS_ERR_INVALID_ARG;
-    const int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt, stamps != nullptr);
+    // automatic: the workgroup index below kAutoDrawnMin elements where that
+    // kernel is built (relaxed decoupled look-back, no non-temporal access)
+    int tile_index = o.tile_index == DWS_TILE_DISPATCH ? kTileDispatch : kTileDrawn;
+    if (o.tile_index == DWS_TILE_AUTO && mode == kModeDecoupled && o.memory_order == DWS_ORDER_RELAXED && !nt)
+        tile_index = auto_tile_index(n);
+    const int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt, tile_index, stamps != nullptr);
     if (cfg < 0) return DWS_ERR_UNSUPPORTED;
     const TileShape ts = cfg_shape(kCfgs[cfg]);
     const uint64_t num_tiles = ceil_div(n, (uint64_t)ts.elems());
@@ -209,14 +217,12 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     std::lock_guard<std::mutex> lock(ws->mu);
     s = ensure_desc(ws, num_tiles);
     if (s != DWS_OK) return s;
-    s = before_draw_launch(ws);
+    s = next_epoch(ws, &p.epoch);
     if (s != DWS_OK) return s;
     p.desc = ws->desc;
     p.counter = ws->counter();
     p.watchdog = ws->watchdog();
-    s = from_hip(launch());
-    if (s == DWS_OK) ++ws->draws_launches;
-    return s;
+    return from_hip(launch());
 }
 
 dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hipStream_t stream)
@@ -296,6 +302,9 @@ dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclus
             return DWS_ERR_INVALID_ARG;
         if (o.tile_shape < 0 || o.tile_shape > kNumShapes) return DWS_ERR_INVALID_ARG;
         if (o.nontemporal != 0 && o.nontemporal != 1) return DWS_ERR_INVALID_ARG;
+        if (o.tile_index < DWS_TILE_AUTO || o.tile_index > DWS_TILE_DISPATCH) return DWS_ERR_INVALID_ARG;
+        if (o.tile_index != DWS_TILE_AUTO && o.variant != DWS_VARIANT_SINGLE_PASS && o.variant != DWS_VARIANT_CHAINED)
+            return DWS_ERR_UNSUPPORTED;
         dws_status s = validate(in, out, n, dtype);
         if (s != DWS_OK || n == 0) return s;
         const bool excl = exclusive != 0;
@@ -463,9 +472,9 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
         std::lock_guard<std::mutex> lock(ws->mu);
         s = ensure_desc(ws, num_tiles);
         if (s != DWS_OK) return s;
-        s = before_draw_launch(ws);
-        if (s != DWS_OK) return s;
         DebugArgs a{};
+        s = next_epoch(ws, &a.epoch);
+        if (s != DWS_OK) return s;
         a.in = d_in;
         a.out = d_out;
         a.n = n;
@@ -482,7 +491,6 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
         a.num_tiles = (uint32_t)num_tiles;
         s = from_hip(launch_debug(a, stream));
         if (s != DWS_OK) return s;
-        if (num_tiles > 1) ++ws->draws_launches;
         if (h_desc != nullptr) {
             hipError_t e = hipStreamSynchronize(stream);
             if (e != hipSuccess) return from_hip(e);
@@ -569,14 +577,12 @@ dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out
         std::lock_guard<std::mutex> lock(ws->mu);
         s = ensure_desc(ws, tiles);
         if (s != DWS_OK) return s;
-        s = before_draw_launch(ws);
+        s = next_epoch(ws, &a.epoch);
         if (s != DWS_OK) return s;
         a.desc = ws->desc;
         a.counter = ws->counter();
         a.watchdog = ws->watchdog();
-        s = from_hip(launch_select(a, stream));
-        if (s == DWS_OK) ++ws->draws_launches;
-        return s;
+        return from_hip(launch_select(a, stream));
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

@@ -181,7 +181,7 @@ struct DebugParams {
     uint64_t* desc;
     unsigned long long* counter;
     unsigned int* watchdog;
-    uint32_t num_tiles, tile_elems, delay_every, delay_phase, delay_ticks;
+    uint32_t num_tiles, tile_elems, delay_every, delay_phase, delay_ticks, epoch;
 };
 
 template <class T, bool EXCL, int MODE>
@@ -189,13 +189,13 @@ __global__ void __launch_bounds__(64) k_debug(DebugParams p)
 {
     const int lane = lane_id();
     const bool multi = p.num_tiles > 1u;
-    uint32_t tile = 0u, epoch = 0u;
+    const uint32_t epoch = p.epoch;
+    uint32_t tile = 0u;
     if (multi) {
-        uint32_t t = 0u, e = 0u;
-        if (lane == 0) draw_tile(p.counter, p.num_tiles, t, e);
+        uint32_t t = 0u;
+        if (lane == 0) t = draw_tile(p.counter, p.num_tiles);
         tile = uniform(t);
-        epoch = uniform(e);
-        if (tile >= p.num_tiles) {   // counter not re-armed: never index past the grid
+        if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
             if (lane == 0) atomicAdd(p.watchdog, 1u);
             return;
         }
@@ -245,7 +245,7 @@ hipError_t launch_debug(const DebugArgs& a, hipStream_t stream)
     if (a.num_tiles == 0u) return hipSuccess;
     if (a.tile_elems == 0u || a.tile_elems > kDebugMaxTile) return hipErrorInvalidValue;
     const DebugParams p{a.in, a.out, a.n, a.desc, a.counter, a.watchdog, a.num_tiles,
-                        a.tile_elems, a.delay_every, a.delay_phase, a.delay_ticks};
+                        a.tile_elems, a.delay_every, a.delay_phase, a.delay_ticks, a.epoch};
     const bool ch = a.mode == kModeChained;
     if (a.kind == kKindF32) {
         if (a.exclusive)

@@ -267,25 +267,20 @@ __device__ __forceinline__ void desc_store(uint64_t* p, uint64_t w)
 
 __device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
-// Draw the next tile index and the call's epoch from the 64-bit counter
-// ([63:32] epoch, [31:0] draws) with one device-scope atomic (dynamic tile
-// index assignment, PMPP 11.3 notes; "virtual processors" in section 4.4 of the
-// Merrill & Garland notes): the holder of tile t knows tiles 0..t-1 were drawn
-// by workgroups that are already running, so waiting on them cannot deadlock.
-// The draw of the last tile re-arms the counter for the next call on the same
-// workspace: draws back to 0, epoch + 1. Call from one lane.
-__device__ __forceinline__ void draw_tile(unsigned long long* counter, uint32_t num_draws,
-                                          uint32_t& tile, uint32_t& epoch)
+// Draw the next tile index from the workspace counter with one device-scope
+// atomic (dynamic tile index assignment, PMPP 11.3 notes; "virtual processors"
+// in section 4.4 of the Merrill & Garland notes): the holder of tile t knows
+// tiles 0..t-1 were drawn by workgroups that are already running, so waiting
+// on them cannot deadlock. The draw of the last tile puts the counter back to
+// 0 for the next call on the same workspace (every other draw of the call has
+// happened by then). Call from one lane.
+__device__ __forceinline__ uint32_t draw_tile(unsigned long long* counter, uint32_t num_draws)
 {
-    const unsigned long long old =
-        __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tile = (uint32_t)old;
-    epoch = (uint32_t)(old >> 32);
-    if (tile == num_draws - 1u) {
-        const uint32_t next = (epoch >= kEpochMax) ? 1u : epoch + 1u;
-        __hip_atomic_store(counter, (unsigned long long)next << 32, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const uint32_t tile =
+        (uint32_t)__hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tile == num_draws - 1u)
+        __hip_atomic_store(counter, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return tile;
 }
 
 // Decoupled look-back by one whole wavefront (section 4.4, parallelized

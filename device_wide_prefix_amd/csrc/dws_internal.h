@@ -25,6 +25,7 @@ struct SinglePassParams {
     unsigned int* watchdog;
     unsigned long long* stamps;   // kStampsPerTile per tile (instrumented kernels only)
     uint32_t num_tiles;
+    uint32_t epoch;               // descriptor epoch of this call (1 .. kEpochMax)
 };
 
 // Launch built configuration `cfg` (index into kCfgs) for element type T
@@ -37,7 +38,8 @@ hipError_t launch_single_pass_typed(int cfg, bool exclusive, const SinglePassPar
 // the shape, or of the automatic shape if that one is not built.
 int resolve_shape(int option_shape, uint64_t n, bool aligned);
 // Index into kCfgs of the kernel for these parameters, or -1 if not built.
-int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal, bool instr = false);
+int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal,
+                         int tile_index = kTileDrawn, bool instr = false);
 
 struct RtsArgs {
     const void* in;
@@ -81,6 +83,7 @@ struct SelectArgs {
     unsigned int* watchdog;
     unsigned long long* count;
     uint32_t num_tiles;
+    uint32_t epoch;
 };
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
 constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
@@ -100,6 +103,7 @@ struct DebugArgs {
     unsigned long long* counter;
     unsigned int* watchdog;
     uint32_t num_tiles;
+    uint32_t epoch;
 };
 hipError_t launch_debug(const DebugArgs& a, hipStream_t stream);
 

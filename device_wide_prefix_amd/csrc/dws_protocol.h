@@ -10,7 +10,9 @@ namespace dws {
 // Status codes follow the three states of the decoupled look-back
 // (Merrill & Garland, section 4.1): X no information, A aggregate available,
 // P inclusive prefix available. A word whose epoch is not the current call's
-// reads as X, so a zeroed array (epoch 0, never used) is all-X.
+// reads as X, so a zeroed array (epoch 0, never used) is all-X. The host gives
+// every launch on a workspace the next epoch, which replaces the separate
+// descriptor-initialisation step of section 4.1 (step 1).
 constexpr uint32_t kStatusX = 0u;
 constexpr uint32_t kStatusA = 1u;
 constexpr uint32_t kStatusP = 2u;
@@ -18,8 +20,9 @@ constexpr uint32_t kDescStatusBits = 2u;
 constexpr uint32_t kDescStatusMask = 3u;
 constexpr uint32_t kEpochMax = (1u << 30) - 1u;  // epochs run 1 .. kEpochMax
 
-// Tile counter word: [63:32] epoch, [31:0] draws made in the current call.
-constexpr uint64_t kCounterInit = (uint64_t)1 << 32;  // epoch 1, no draws
+// Tile counter word: draws made in the current call (the last draw of a call
+// puts it back to 0).
+constexpr uint64_t kCounterInit = 0ull;
 
 // Look-back safety limit: 2 s of the 100 MHz real-time counter.
 constexpr uint64_t kWatchdogTicks = 200000000ull;
@@ -29,6 +32,16 @@ constexpr int kOrderAcqRel = 1;
 
 constexpr int kModeDecoupled = 0;
 constexpr int kModeChained = 1;
+
+// Where a workgroup's tile index comes from. kTileDrawn: one atomic add on
+// the workspace counter per workgroup, in the order workgroups start running
+// (PMPP 11.3 notes, dynamic block index). kTileDispatch: the workgroup index
+// itself, relying on the dispatcher starting workgroups in index order within
+// each XCD, so every tile a workgroup waits on has been started before it. No
+// atomic, but the guarantee is the hardware's, not the protocol's; a wait that
+// outlives the watchdog still ends.
+constexpr int kTileDrawn = 0;
+constexpr int kTileDispatch = 1;
 
 // Element kinds the kernels are built for (int32 runs as u32).
 constexpr int kKindU32 = 0;
@@ -59,16 +72,25 @@ constexpr TileShape kShapes[] = {
 };
 constexpr int kNumShapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
 
-// Automatic shape, from a size sweep on MI355X (fp32, exclusive, in place):
-// the best tile grows with n as long as every CU still gets tiles.
+// Automatic shape and tile index source, from a sweep of every shape with
+// both sources at n = 2^16 .. 2^28 on MI355X (fp32, exclusive, in place,
+// caches flushed): the best tile grows with n as long as every CU still gets
+// tiles. Below 2^25 elements (at most a few hundred tiles) the workgroup
+// index is the better tile index: no atomic on the critical path. From 2^25
+// the drawn index wins by 2-11%: many workgroups run one after another on
+// each CU, and a drawn index follows the order in which they really start,
+// so a tile rarely waits on a predecessor that started after it.
 constexpr uint64_t kAutoHugeMin = (uint64_t)1 << 24;    // 65536-element tiles
-constexpr uint64_t kAutoLargeMin = (uint64_t)1 << 22;   // 32768
+constexpr uint64_t kAutoLargeMin = (uint64_t)1 << 23;   // 32768
 constexpr uint64_t kAutoMediumMin = (uint64_t)1 << 20;  // 16384 (512 threads)
+constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 25;   // drawn tile index from here
 
 constexpr int auto_shape(uint64_t n)
 {
     return n >= kAutoHugeMin ? 5 : (n >= kAutoLargeMin ? 4 : (n >= kAutoMediumMin ? 2 : 0));
 }
+
+constexpr int auto_tile_index(uint64_t n) { return n >= kAutoDrawnMin ? kTileDrawn : kTileDispatch; }
 
 // Scalar-load version of a shape: one element per load, at most 16 loads per
 // lane (each load is one wave scan; more would spill registers).
@@ -88,11 +110,13 @@ constexpr int kLookbackSlots = 4;
 struct KernelCfg {
     int shape, vec, order, mode;
     bool nt;
+    int tile_index = kTileDrawn;
     bool instr = false;   // records per-tile phase time stamps (measurement build)
 };
 
 #define DWS_AUTO_SHAPES(VEC, ORDER, MODE, NT) \
     {0, VEC, ORDER, MODE, NT}, {2, VEC, ORDER, MODE, NT}, {4, VEC, ORDER, MODE, NT}, {5, VEC, ORDER, MODE, NT}
+#define DWS_DISPATCH(SHAPE, VEC) {SHAPE, VEC, kOrderRelaxed, kModeDecoupled, false, kTileDispatch}
 
 constexpr KernelCfg kCfgs[] = {
     // decoupled look-back, relaxed descriptor atomics: every shape, and the
@@ -111,13 +135,22 @@ constexpr KernelCfg kCfgs[] = {
     DWS_AUTO_SHAPES(1, kOrderRelaxed, kModeChained, false),
     DWS_AUTO_SHAPES(4, kOrderAcqRel, kModeChained, false),
     DWS_AUTO_SHAPES(1, kOrderAcqRel, kModeChained, false),
-    // instrumented (time stamps), aligned automatic shapes
-    {0, 4, kOrderRelaxed, kModeDecoupled, false, true},
-    {2, 4, kOrderRelaxed, kModeDecoupled, false, true},
-    {4, 4, kOrderRelaxed, kModeDecoupled, false, true},
-    {5, 4, kOrderRelaxed, kModeDecoupled, false, true},
+    // tile index = workgroup index: every shape aligned, automatic shapes
+    // with scalar loads
+    DWS_DISPATCH(0, 4), DWS_DISPATCH(1, 4), DWS_DISPATCH(2, 4), DWS_DISPATCH(3, 4), DWS_DISPATCH(4, 4),
+    DWS_DISPATCH(5, 4), DWS_DISPATCH(0, 1), DWS_DISPATCH(2, 1), DWS_DISPATCH(4, 1), DWS_DISPATCH(5, 1),
+    // instrumented (time stamps), aligned automatic shapes, both sources
+    {0, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
+    {2, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
+    {4, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
+    {5, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
+    {0, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
+    {2, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
+    {4, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
+    {5, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
 };
 #undef DWS_AUTO_SHAPES
+#undef DWS_DISPATCH
 constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
 
 constexpr TileShape cfg_shape(const KernelCfg& c)
@@ -131,7 +164,7 @@ constexpr uint32_t kRtsMaxGroups = 4096u;
 // Protocol-inspection kernel: one wavefront per tile of 1..64 elements.
 constexpr uint32_t kDebugMaxTile = 64u;
 
-// Instrumented scan: 64-bit time stamps per tile (start, drawn, aggregate
+// Instrumented scan: 64-bit time stamps per tile (start, tile index known, aggregate
 // published, prefix known, stores issued).
 constexpr uint32_t kStampsPerTile = 5u;
 

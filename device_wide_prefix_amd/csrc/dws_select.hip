@@ -34,6 +34,7 @@ struct SelectParams {
     unsigned int* watchdog;
     unsigned long long* count;
     uint32_t num_tiles;
+    uint32_t epoch;
 };
 
 // Byte offset far past any tile's range (at most 4 * 32768 bytes): the
@@ -47,26 +48,21 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
-    __shared__ uint32_t s_draw[2];
+    __shared__ uint32_t s_draw;
     __shared__ uint32_t s_wave[W];
     __shared__ uint32_t s_prefix;
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
+    const uint32_t epoch = p.epoch;
 
-    uint32_t tile = 0u, epoch = 0u;
+    uint32_t tile = 0u;
     if (multi) {
-        if (threadIdx.x == 0) {
-            uint32_t t, e;
-            draw_tile(p.counter, p.num_tiles, t, e);
-            s_draw[0] = t;
-            s_draw[1] = e;
-        }
+        if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
         __syncthreads();
-        tile = uniform(s_draw[0]);
-        epoch = uniform(s_draw[1]);
-        if (tile >= p.num_tiles) {   // counter not re-armed: never index past the grid
+        tile = uniform(s_draw);
+        if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
             if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
             return;
         }
@@ -161,7 +157,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     }
     const SelectShape s = select_shape(a.n, a.aligned);
     SelectParams p{static_cast<const uint32_t*>(a.in), static_cast<const uint32_t*>(a.flags),
-                   static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles};
+                   static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
+                   a.epoch};
     void* args[] = {&p};
     const void* fn = nullptr;
     if (!a.aligned)

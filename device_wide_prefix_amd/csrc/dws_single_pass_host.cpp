@@ -18,13 +18,14 @@ int resolve_shape(int option_shape, uint64_t n, bool aligned)
     return s;
 }
 
-int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal, bool instr)
+int find_single_pass_cfg(int shape, bool aligned, int order, int mode, bool nontemporal, int tile_index,
+                         bool instr)
 {
     const int vec = aligned ? 4 : 1;
     for (int i = 0; i < kNumCfgs; ++i) {
         const KernelCfg& c = kCfgs[i];
         if (c.shape == shape && c.vec == vec && c.order == order && c.mode == mode && c.nt == nontemporal &&
-            c.instr == instr)
+            c.tile_index == tile_index && c.instr == instr)
             return i;
     }
     return -1;

@@ -3,9 +3,11 @@
 // Look-back", section 4.1 steps and section 4.4 adaptations), and the chained
 // scan that waits on the immediate predecessor only (section 3.2, Fig 4).
 //
-// One workgroup per tile; the kernel is the whole call (no init launch):
-//   1. lane 0 draws (tile, epoch) from the workspace counter (dynamic tile
-//      index, PMPP 11.3 notes);
+// One workgroup per tile; the kernel is the whole call (no init launch: the
+// host hands every call a new descriptor epoch):
+//   1. lane 0 draws the tile index from the workspace counter (dynamic tile
+//      index, PMPP 11.3 notes), or the tile is the workgroup index
+//      (TILE_INDEX == kTileDispatch);
 //   2. every wave loads its segment of the tile with coalesced vector loads,
 //      CHUNKS x VEC elements per lane kept in registers (thread coarsening,
 //      PMPP 11.2 notes);
@@ -26,7 +28,8 @@
 
 namespace dws {
 
-template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT, bool INSTR>
+template <class T, bool EXCL, int BLOCK, int VEC, int CHUNKS, int ORDER, int MODE, bool NT, int TILE_INDEX,
+          bool INSTR>
 __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
 {
     uint64_t stamp[kStampsPerTile] = {};
@@ -34,30 +37,29 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
-    __shared__ uint32_t s_draw[2];
+    __shared__ uint32_t s_draw;
     __shared__ T s_wave[W];
     __shared__ T s_prefix;
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
+    const uint32_t epoch = p.epoch;
 
-    uint32_t tile = 0u, epoch = 0u;
+    uint32_t tile = 0u;
     if (multi) {
-        if (threadIdx.x == 0) {
-            uint32_t t, e;
-            draw_tile(p.counter, p.num_tiles, t, e);
-            s_draw[0] = t;
-            s_draw[1] = e;
-        }
-        __syncthreads();
-        tile = uniform(s_draw[0]);
-        epoch = uniform(s_draw[1]);
-        // a counter that was not re-armed would hand out indices past the
-        // grid; never touch memory with them (counts as a watchdog trip)
-        if (tile >= p.num_tiles) {
-            if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
-            return;
+        if constexpr (TILE_INDEX == kTileDispatch) {
+            tile = blockIdx.x;
+        } else {
+            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            __syncthreads();
+            tile = uniform(s_draw);
+            // a counter that was not put back to 0 would hand out indices past
+            // the grid; never touch memory with them (counts as a watchdog trip)
+            if (tile >= p.num_tiles) {
+                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
+                return;
+            }
         }
     }
     if constexpr (INSTR) stamp[1] = realtime();
@@ -126,7 +128,7 @@ static hipError_t launch_cfg(const SinglePassParams& p, hipStream_t stream)
     constexpr KernelCfg c = kCfgs[I];
     constexpr TileShape s = cfg_shape(c);
     const void* fn = reinterpret_cast<const void*>(
-        &k_single_pass<T, EXCL, s.threads, s.vec, s.chunks, c.order, c.mode, c.nt, c.instr>);
+        &k_single_pass<T, EXCL, s.threads, s.vec, s.chunks, c.order, c.mode, c.nt, c.tile_index, c.instr>);
     SinglePassParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(s.threads), args, 0, stream);

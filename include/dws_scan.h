@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DWS_VERSION 1
+#define DWS_VERSION 2
 
 typedef enum dws_status {
     DWS_OK = 0,
@@ -119,15 +119,33 @@ typedef enum dws_memory_order {
     DWS_ORDER_ACQ_REL = 1
 } dws_memory_order;
 
+/* Where a tile's index comes from in the single-pass and chained kernels. */
+typedef enum dws_tile_index {
+    /* the library's choice: DWS_TILE_DISPATCH below 2^25 elements for the
+     * relaxed single pass without non-temporal access, else DWS_TILE_DRAWN */
+    DWS_TILE_AUTO = 0,
+    /* one atomic add on a device-wide counter per workgroup, in the order the
+     * workgroups start (PMPP 11.3 notes, dynamic block index; Merrill &
+     * Garland, section 4.4): a tile only ever waits on tiles whose
+     * workgroups are running, whatever order the hardware starts them in */
+    DWS_TILE_DRAWN = 1,
+    /* the workgroup index itself: no atomic per tile, relying on the GPU
+     * starting the workgroups of each XCD in index order. A look-back wait
+     * that still outlives the watchdog (about two seconds) ends and is
+     * counted by dws_watchdog_trips() */
+    DWS_TILE_DISPATCH = 2
+} dws_tile_index;
+
 typedef struct dws_options {
     int variant;        /* dws_variant; default DWS_VARIANT_SINGLE_PASS */
     int memory_order;   /* dws_memory_order; default DWS_ORDER_RELAXED */
     int tile_shape;     /* 0 = automatic (by n: 65536-element tiles from
-                           2^24 elements, 32768 from 2^22, 16384 from 2^20,
+                           2^24 elements, 32768 from 2^23, 16384 from 2^20,
                            else 4096);
                            1 .. dws_num_tile_shapes()-1 force one shape of
                            the single-pass kernel, for sweeps */
     int nontemporal;    /* 1 = non-temporal (streaming) loads and stores */
+    int tile_index;     /* dws_tile_index; default DWS_TILE_AUTO */
 } dws_options;
 
 /*
@@ -138,8 +156,10 @@ typedef struct dws_options {
  *                chosen shapes also with release/acquire and with
  *                nontemporal (relaxed);
  *   chained:     the automatically chosen shapes, either order;
- *   reduce-then-scan, scan-then-propagate: tile_shape 0, nontemporal 0
- *                (memory_order ignored).
+ *   reduce-then-scan, scan-then-propagate: tile_shape 0, nontemporal 0,
+ *                tile_index 0 (memory_order ignored);
+ *   DWS_TILE_DISPATCH: single pass with relaxed order, every tile_shape,
+ *                nontemporal 0.
  * Pointers that are not both 16-byte aligned use scalar loads; a forced
  * shape without a scalar-load kernel then falls back to the automatic one,
  * and nontemporal is ignored.
@@ -228,11 +248,11 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
 
 /*
  * Instrumented single-pass scan, for measuring where a tile's time goes. Same
- * result as scan_inclusive / scan_exclusive with the automatic tile shape
- * (relaxed descriptors; both pointers must be 16-byte aligned, else
- * DWS_ERR_UNSUPPORTED). In addition, for every tile t it writes five 64-bit
- * stamps of the 100 MHz real-time counter to the DEVICE buffer
- * d_stamps[5t .. 5t+4]: workgroup start, tile index drawn, aggregate
+ * result as scan_inclusive / scan_exclusive with the automatic tile shape and
+ * tile index source (relaxed descriptors; both pointers must be 16-byte
+ * aligned, else DWS_ERR_UNSUPPORTED). In addition, for every tile t it writes
+ * five 64-bit stamps of the 100 MHz real-time counter to the DEVICE buffer
+ * d_stamps[5t .. 5t+4]: workgroup start, tile index known, aggregate
  * published (tile loaded and scanned), exclusive prefix known (look-back
  * done), stores issued. *num_tiles (if not NULL) receives the tile count;
  * with d_stamps == NULL the call only reports it. stamps_capacity is the

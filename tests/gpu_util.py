@@ -47,15 +47,15 @@ def from_device(t, dtype: str) -> np.ndarray:
     return a
 
 
-def run(x_dev, out_dev, n: int, dtype: str, exclusive: bool, variant=0, order=0, shape=0, nt=0):
+def run(x_dev, out_dev, n: int, dtype: str, exclusive: bool, variant=0, order=0, shape=0, nt=0, tile_index=0):
     """Call dws_scan_ex on raw device pointers on torch's current stream."""
     import torch
     stream = torch.cuda.current_stream().cuda_stream
-    if variant == 0 and order == 0 and shape == 0 and nt == 0:
+    if variant == 0 and order == 0 and shape == 0 and nt == 0 and tile_index == 0:
         f = dws.scan_exclusive_ptr if exclusive else dws.scan_inclusive_ptr
         st = f(x_dev.data_ptr(), out_dev.data_ptr(), n, CODE[dtype], stream)
     else:
-        opt = dws.DwsOptions(variant, order, shape, nt)
+        opt = dws.DwsOptions(variant, order, shape, nt, tile_index)
         st = dws.scan_ex_ptr(x_dev.data_ptr(), out_dev.data_ptr(), n, CODE[dtype], exclusive, opt, stream)
     assert st == dws.OK, f"scan returned {st}: {dws.status_string(st)}"
 

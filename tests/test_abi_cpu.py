@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dws_version() == 1
+    assert lib.dws_version() == 2
     for code in range(7):
         s = dws.status_string(code)
         assert isinstance(s, str) and s
@@ -55,7 +55,7 @@ def test_tile_geometry(lib):
     assert n_opts >= 2
     # automatic choice by n
     for n, tile, threads in ((1 << 28, 65536, 1024), (1 << 24, 65536, 1024), ((1 << 24) - 1, 32768, 1024),
-                             (1 << 22, 32768, 1024), ((1 << 22) - 1, 16384, 512), (1 << 20, 16384, 512),
+                             (1 << 23, 32768, 1024), ((1 << 23) - 1, 16384, 512), (1 << 20, 16384, 512),
                              ((1 << 20) - 1, 4096, 256), (1, 4096, 256)):
         assert dws.tile_elems(0, n, True) == tile, n
         assert dws.tile_threads(0, n, True) == threads, n
@@ -100,7 +100,8 @@ def test_validation(lib, fn):
 
 def test_option_validation(lib):
     def call(**kw):
-        o = dws.DwsOptions(kw.get("variant", 0), kw.get("order", 0), kw.get("shape", 0), kw.get("nt", 0))
+        o = dws.DwsOptions(kw.get("variant", 0), kw.get("order", 0), kw.get("shape", 0), kw.get("nt", 0),
+                           kw.get("tile_index", 0))
         return lib.dws_scan_ex(FAKE, FAKE + (1 << 20), 1 << 16, dws.FLOAT32, 1, ctypes.byref(o), None)
     assert call(variant=4) == dws.ERR_INVALID_ARG
     assert call(variant=-1) == dws.ERR_INVALID_ARG
@@ -118,6 +119,15 @@ def test_option_validation(lib):
     assert call(variant=dws.REDUCE_THEN_SCAN, nt=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.SCAN_THEN_PROPAGATE, shape=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.SCAN_THEN_PROPAGATE, nt=1) == dws.ERR_UNSUPPORTED
+    # tile index source: 0..2; dispatch order is built for the relaxed single
+    # pass without non-temporal access
+    assert call(tile_index=3) == dws.ERR_INVALID_ARG
+    assert call(tile_index=-1) == dws.ERR_INVALID_ARG
+    assert call(variant=dws.REDUCE_THEN_SCAN, tile_index=dws.TILE_DRAWN) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.SCAN_THEN_PROPAGATE, tile_index=dws.TILE_DISPATCH) == dws.ERR_UNSUPPORTED
+    assert call(variant=dws.CHAINED, tile_index=dws.TILE_DISPATCH) == dws.ERR_UNSUPPORTED
+    assert call(tile_index=dws.TILE_DISPATCH, order=dws.ORDER_ACQ_REL) == dws.ERR_UNSUPPORTED
+    assert call(tile_index=dws.TILE_DISPATCH, nt=1) == dws.ERR_UNSUPPORTED
     # options are validated before the arguments: n == 0 with bad options
     o = dws.DwsOptions(9, 0, 0, 0)
     assert lib.dws_scan_ex(None, None, 0, dws.INT32, 0, ctypes.byref(o), None) == dws.ERR_INVALID_ARG

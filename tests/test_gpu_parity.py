@@ -64,14 +64,16 @@ def test_wave_primitives_lane_layout(gpu, dtype):
 # ---------------------------------------------------------------------------
 # sizes around tile and wave boundaries, all dtypes, both kinds
 # ---------------------------------------------------------------------------
-# sizes around wave and tile boundaries of every automatic tile size: 4096
-# below 2^20, 16384 from 2^20, 32768 from 2^22, 65536 from 2^24
+# sizes around wave and tile boundaries of every automatic tile size (4096
+# below 2^20, 16384 from 2^20, 32768 from 2^23, 65536 from 2^24) and around
+# the switch from workgroup-index tiles to drawn tiles at 2^25
 M, L, H = 16384, 32768, 65536
 EDGE_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, TILE - 1, TILE, TILE + 1,
               2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 255 * TILE + 3,
-              (1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 20) + M - 1, 150 * M + 7,
-              (1 << 22) - 1, 1 << 22, (1 << 22) + 1, (1 << 22) + L + 1, 301 * L - 5,
-              (1 << 24) - 1, 1 << 24, (1 << 24) + 1, (1 << 24) + H + 3, 301 * H - 7]
+              (1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 20) + M - 1, 150 * M + 7, (1 << 22) + 1,
+              (1 << 23) - 1, 1 << 23, (1 << 23) + 1, (1 << 23) + L + 1, 301 * L - 5,
+              (1 << 24) - 1, 1 << 24, (1 << 24) + 1, (1 << 24) + H + 3, 301 * H - 7,
+              (1 << 25) - 1, (1 << 25) + 1]
 
 
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
@@ -154,6 +156,57 @@ def test_tile_shapes(gpu):
                     x = wl.random_input(dtype, n, seed=shape * 1000 + n)
                     y = _roundtrip(x, dtype, exclusive, shape=shape)
                     check(x, y, dtype, exclusive, label=f"shape {shape} n={n}")
+
+
+@pytest.mark.parametrize("tile_index", [dws.TILE_DRAWN, dws.TILE_DISPATCH], ids=["drawn", "dispatch"])
+def test_tile_index_sources(gpu, tile_index):
+    # every shape with the tile index from the counter or the workgroup index,
+    # and the automatic shape across the size regimes, aligned and not
+    for shape in range(dws.num_tile_shapes()):
+        t = dws.tile_elems(shape, 1 << 28, True)
+        for dtype in ("int32", "float32"):
+            for n in (t + 1, 7 * t - 5, 300 * t + 3):
+                exclusive = n % 2 == 1
+                note(f"tile_index={tile_index} shape={shape} dtype={dtype} n={n}")
+                x = wl.random_input(dtype, n, seed=shape * 7 + n)
+                y = _roundtrip(x, dtype, exclusive, in_place=exclusive, shape=shape, tile_index=tile_index)
+                check(x, y, dtype, exclusive, label=f"tile_index {tile_index} shape {shape} n={n}")
+    for n in (TILE + 7, (1 << 20) + 5, (1 << 22) + 3, (1 << 24) + 9):
+        note(f"tile_index={tile_index} unaligned n={n}")
+        x = wl.random_input("uint32", n, seed=n)
+        y = _roundtrip(x, "uint32", False, offset=1, tile_index=tile_index)
+        check(x, y, "uint32", False, label=f"tile_index {tile_index} unaligned n={n}")
+
+
+def test_epochs_across_launch_kinds(gpu):
+    # drawn, dispatch-order, chained, compaction and debug launches share one
+    # workspace's descriptors; each must see only its own epoch
+    import torch
+    n = 40 * 65536 + 11
+    x = wl.random_input("int32", n, seed=4)
+    flags = wl.selection_flags(n, 0.5, seed=5)
+    want_sel = oracle.select_flagged(x, flags)
+    _, xd = to_device(x)
+    _, fd = to_device(flags)
+    for rep in range(4):
+        for kind in ("drawn", "dispatch", "chained", "select", "debug"):
+            note(f"epochs rep={rep} kind={kind}")
+            out = torch.empty_like(xd)
+            if kind == "select":
+                cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+                dws.select_flagged(xd, fd, out=out, count=cnt)
+                c = int(cnt.item())
+                assert c == want_sel.size and np.array_equal(out[:c].cpu().numpy(), want_sel)
+                continue
+            if kind == "debug":
+                m = 64 * 200 + 5
+                dws.scan_debug(xd[:m], out[:m], 64, want_descriptors=False)
+                check(x[:m], from_device(out[:m], "int32"), "int32", False, label="debug")
+                continue
+            opts = {"drawn": dict(tile_index=dws.TILE_DRAWN), "dispatch": dict(tile_index=dws.TILE_DISPATCH),
+                    "chained": dict(variant=dws.CHAINED)}[kind]
+            run(xd, out, n, "int32", rep % 2 == 1, **opts)
+            check(x, from_device(out, "int32"), "int32", rep % 2 == 1, label=f"{kind} rep {rep}")
 
 
 @pytest.mark.parametrize("opts", [dict(order=dws.ORDER_ACQ_REL), dict(nt=1),
