@@ -14,6 +14,11 @@ Functions:
     scan_f32(x, exclusive)  -> (y fp64, sabs fp64)
     scan(x, exclusive)      -> dispatch on x.dtype
     select_flagged(x, flags) -> the x[i] with flags[i] != 0, in order
+    scan_minmax(x, is_max, exclusive)        -> running max/min (int32 signed, uint32 unsigned)
+    scan_pair_sum_u32 / scan_affine_u32 / scan_segsum_u32(x, exclusive)
+                            -> (n, 2) uint32 pairs in, (n, 2) uint32 out
+    scan_pair_sum_i32_f32 / scan_segsum_i32_f32(x, exclusive)
+                            -> (int32 part, fp64 part, |fp| sum), pairs in as (n, 2) words
 """
 from __future__ import annotations
 
@@ -68,6 +73,15 @@ class OracleLib:
         lib.oracle_scan_f32.restype = ctypes.c_int
         lib.oracle_select_flagged.argtypes = [vp, vp, sz, vp]
         lib.oracle_select_flagged.restype = sz
+        ci = ctypes.c_int
+        lib.oracle_scan_minmax.argtypes = [vp, sz, vp, ci, ci, ci]
+        for name in ("oracle_scan_pair_sum_u32", "oracle_scan_affine_u32", "oracle_scan_segsum_u32"):
+            getattr(lib, name).argtypes = [vp, sz, vp, ci]
+        for name in ("oracle_scan_pair_sum_i32_f32", "oracle_scan_segsum_i32_f32"):
+            getattr(lib, name).argtypes = [vp, sz, vp, vp, vp, ci]
+        for name in ("oracle_scan_minmax", "oracle_scan_pair_sum_u32", "oracle_scan_affine_u32",
+                     "oracle_scan_segsum_u32", "oracle_scan_pair_sum_i32_f32", "oracle_scan_segsum_i32_f32"):
+            getattr(lib, name).restype = ci
         self._lib = lib
         self.path = path
 
@@ -114,6 +128,79 @@ class OracleLib:
         return out[:cnt]
 
 
+    # -- generic operators ---------------------------------------------------
+    # Pairs travel as (n, 2) uint32 arrays of bits: column 0 the first
+    # component, column 1 the second.
+
+    def scan_minmax(self, x: np.ndarray, is_max: bool, exclusive: bool = False) -> np.ndarray:
+        """Running max/min of int32 (signed) or uint32 (unsigned) values."""
+        x = np.ascontiguousarray(x)
+        if x.dtype not in (np.int32, np.uint32):
+            raise TypeError("scan_minmax wants int32 or uint32")
+        y = np.empty_like(x)
+        rc = self._lib.oracle_scan_minmax(_ptr(x), x.size, _ptr(y), int(x.dtype == np.int32), int(bool(is_max)),
+                                          int(bool(exclusive)))
+        if rc != 0:
+            raise RuntimeError("oracle_scan_minmax failed")
+        return y
+
+    def _pair_u32(self, name: str, x: np.ndarray, exclusive: bool) -> np.ndarray:
+        x = _as_pairs(x)
+        y = np.empty_like(x)
+        if getattr(self._lib, name)(_ptr(x), x.shape[0], _ptr(y), int(bool(exclusive))) != 0:
+            raise RuntimeError(f"{name} failed")
+        return y
+
+    def scan_pair_sum_u32(self, x, exclusive=False):
+        """Componentwise + of uint32 pairs, modulo 2^32; (n, 2) uint32."""
+        return self._pair_u32("oracle_scan_pair_sum_u32", x, exclusive)
+
+    def scan_affine_u32(self, x, exclusive=False):
+        """Composition of the affine maps v -> a v + b (mod 2^32), element
+        (a, b); returns the running (A, B) as (n, 2) uint32."""
+        return self._pair_u32("oracle_scan_affine_u32", x, exclusive)
+
+    def scan_segsum_u32(self, x, exclusive=False):
+        """Segmented + on (flag, value) uint32 pairs; (n, 2) uint32 of
+        (OR of flags so far, segment sum)."""
+        return self._pair_u32("oracle_scan_segsum_u32", x, exclusive)
+
+    def _pair_if(self, name: str, x: np.ndarray, exclusive: bool):
+        x = _as_pairs(x)
+        n = x.shape[0]
+        yi = np.empty(n, dtype=np.int32)
+        yf = np.empty(n, dtype=np.float64)
+        sa = np.empty(n, dtype=np.float64)
+        if getattr(self._lib, name)(_ptr(x), n, _ptr(yi), _ptr(yf), _ptr(sa), int(bool(exclusive))) != 0:
+            raise RuntimeError(f"{name} failed")
+        return yi, yf, sa
+
+    def scan_pair_sum_i32_f32(self, x, exclusive=False):
+        """Componentwise + of {int32, fp32} pairs: (int32 part, fp64 part,
+        running |fp part| over j <= i)."""
+        return self._pair_if("oracle_scan_pair_sum_i32_f32", x, exclusive)
+
+    def scan_segsum_i32_f32(self, x, exclusive=False):
+        """Segmented + on {int32 flag, fp32 value} pairs: (OR of flags so far,
+        fp64 segment sum, sum of |value| over the elements in that sum)."""
+        return self._pair_if("oracle_scan_segsum_i32_f32", x, exclusive)
+
+
+def _as_pairs(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.ndim != 2 or x.shape[1] != 2 or x.dtype.itemsize != 4:
+        raise ValueError("pairs are (n, 2) arrays of 4-byte words")
+    return x.view(np.uint32)
+
+
+def make_pairs(first: np.ndarray, second: np.ndarray) -> np.ndarray:
+    """(n, 2) uint32 bit array from two 4-byte columns (any 4-byte dtypes)."""
+    out = np.empty((first.size, 2), dtype=np.uint32)
+    out[:, 0] = np.ascontiguousarray(first).view(np.uint32)
+    out[:, 1] = np.ascontiguousarray(second).view(np.uint32)
+    return out
+
+
 _default: OracleLib | None = None
 
 
@@ -139,6 +226,30 @@ def scan_f32(x, exclusive=False, want_sabs=True):
 
 def select_flagged(x, flags):
     return _oracle().select_flagged(x, flags)
+
+
+def scan_minmax(x, is_max, exclusive=False):
+    return _oracle().scan_minmax(x, is_max, exclusive)
+
+
+def scan_pair_sum_u32(x, exclusive=False):
+    return _oracle().scan_pair_sum_u32(x, exclusive)
+
+
+def scan_affine_u32(x, exclusive=False):
+    return _oracle().scan_affine_u32(x, exclusive)
+
+
+def scan_segsum_u32(x, exclusive=False):
+    return _oracle().scan_segsum_u32(x, exclusive)
+
+
+def scan_pair_sum_i32_f32(x, exclusive=False):
+    return _oracle().scan_pair_sum_i32_f32(x, exclusive)
+
+
+def scan_segsum_i32_f32(x, exclusive=False):
+    return _oracle().scan_segsum_i32_f32(x, exclusive)
 
 
 def scan(x: np.ndarray, exclusive: bool = False):

@@ -38,11 +38,15 @@
  * O(n^2) brute force on small n and numpy's cumsum as an independent library
  * routine. The compaction is pinned by closed forms (all, none, every other),
  * brute force against a list comprehension, the scatter to exclusive prefix
- * offsets and numpy's boolean-mask indexing.
+ * offsets and numpy's boolean-mask indexing. The generic operators are pinned
+ * by numpy's maximum/minimum.accumulate and per-column cumsum, by running the
+ * affine recurrence directly from several start values, by brute-force
+ * segmented sums and by closed forms (a = 1, b = 0; all heads, no heads).
  */
 #include <stddef.h>
 #include <stdint.h>
 #include <math.h>
+#include <string.h>
 
 #define ORACLE_ABI_VERSION 1
 
@@ -118,4 +122,183 @@ size_t oracle_select_flagged(const uint32_t* x, const int32_t* flags, size_t n, 
         }
     }
     return count;
+}
+
+/*
+ * Generic associative operators (Merrill & Garland, section 4.2: the method
+ * only ever combines contiguous inputs or contiguous partial reductions, so
+ * the operator need not be commutative; section A4: 32-bit integers and
+ * {int32, fp32} pairs). Each function below is one sequential loop that folds
+ * the operator left to right, x[0] first, and writes the running value after
+ * (inclusive) or before (exclusive, identity first) element i. Pairs are two
+ * 32-bit words per element, interleaved: x[2i] first component, x[2i+1]
+ * second.
+ */
+
+/* Running max or min of 32-bit integers, signed or unsigned. The exclusive
+ * identity is the smallest (max) or largest (min) value of the type. */
+int oracle_scan_minmax(const uint32_t* x, size_t n, uint32_t* y, int is_signed, int is_max, int exclusive)
+{
+    if (n == 0) return 0;
+    if (x == NULL || y == NULL) return -1;
+    uint32_t running;
+    if (is_max) running = is_signed ? 0x80000000u : 0u;
+    else running = is_signed ? 0x7fffffffu : 0xffffffffu;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t xi = x[i];
+        int take;
+        if (is_signed) take = is_max ? ((int32_t)xi > (int32_t)running) : ((int32_t)xi < (int32_t)running);
+        else take = is_max ? (xi > running) : (xi < running);
+        if (exclusive) y[i] = running;
+        if (take) running = xi;
+        if (!exclusive) y[i] = running;
+    }
+    return 0;
+}
+
+static float word_as_float(uint32_t w)
+{
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+/* Componentwise + on {int32, fp32} pairs: the integer part wraps modulo 2^32,
+ * the fp32 part is accumulated in fp64 (returned as y_f) with the running
+ * absolute sum over j <= i (sabs, may be NULL), as for the fp32 scan. */
+int oracle_scan_pair_sum_i32_f32(const uint32_t* x, size_t n, uint32_t* y_int, double* y_f, double* sabs,
+                                 int exclusive)
+{
+    if (n == 0) return 0;
+    if (x == NULL || y_int == NULL || y_f == NULL) return -1;
+    uint32_t ri = 0u;
+    double rf = 0.0, ra = 0.0;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t xi = x[2 * i];
+        const double xf = (double)word_as_float(x[2 * i + 1]);
+        if (exclusive) {
+            y_int[i] = ri;
+            y_f[i] = rf;
+        }
+        ri += xi;
+        rf += xf;
+        if (!exclusive) {
+            y_int[i] = ri;
+            y_f[i] = rf;
+        }
+        ra += fabs(xf);
+        if (sabs != NULL) sabs[i] = ra;
+    }
+    return 0;
+}
+
+/* Componentwise + on pairs of uint32, modulo 2^32. */
+int oracle_scan_pair_sum_u32(const uint32_t* x, size_t n, uint32_t* y, int exclusive)
+{
+    if (n == 0) return 0;
+    if (x == NULL || y == NULL) return -1;
+    uint32_t r0 = 0u, r1 = 0u;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t x0 = x[2 * i], x1 = x[2 * i + 1];
+        if (exclusive) {
+            y[2 * i] = r0;
+            y[2 * i + 1] = r1;
+        }
+        r0 += x0;
+        r1 += x1;
+        if (!exclusive) {
+            y[2 * i] = r0;
+            y[2 * i + 1] = r1;
+        }
+    }
+    return 0;
+}
+
+/* Composition of affine maps modulo 2^32 (a non-commutative operator).
+ * Element (a, b) is the map v -> a v + b. The running value (A, B) is the
+ * composition of the maps of elements 0..i, applied in order, so that for any
+ * start value s the recurrence v_i = a_i v_{i-1} + b_i, v_{-1} = s, gives
+ * v_i = A_i s + B_i. Folding element (a, b) into (A, B) gives (a A, a B + b);
+ * the identity is (1, 0). */
+int oracle_scan_affine_u32(const uint32_t* x, size_t n, uint32_t* y, int exclusive)
+{
+    if (n == 0) return 0;
+    if (x == NULL || y == NULL) return -1;
+    uint32_t A = 1u, B = 0u;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t a = x[2 * i], b = x[2 * i + 1];
+        if (exclusive) {
+            y[2 * i] = A;
+            y[2 * i + 1] = B;
+        }
+        A = a * A;
+        B = a * B + b;
+        if (!exclusive) {
+            y[2 * i] = A;
+            y[2 * i + 1] = B;
+        }
+    }
+    return 0;
+}
+
+/* Segmented sum on (flag, value) pairs (a non-commutative operator): a
+ * non-zero flag starts a new segment, whose running value restarts at the
+ * element's own value; the flag part of the result is the bitwise OR of all
+ * flags so far. Identity (0, 0). The value is uint32 modulo 2^32 here. */
+int oracle_scan_segsum_u32(const uint32_t* x, size_t n, uint32_t* y, int exclusive)
+{
+    if (n == 0) return 0;
+    if (x == NULL || y == NULL) return -1;
+    uint32_t F = 0u, V = 0u;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t f = x[2 * i], v = x[2 * i + 1];
+        if (exclusive) {
+            y[2 * i] = F;
+            y[2 * i + 1] = V;
+        }
+        F |= f;
+        if (f != 0u) V = v;
+        else V += v;
+        if (!exclusive) {
+            y[2 * i] = F;
+            y[2 * i + 1] = V;
+        }
+    }
+    return 0;
+}
+
+/* Segmented sum on {int32 flag, fp32 value} pairs, the value accumulated in
+ * fp64. sabs[i] (may be NULL) is the sum of |value| over exactly the elements
+ * whose values make up y_f[i] (the current segment up to i, or up to i - 1 for
+ * the exclusive scan), which scales the fp32 tolerance. */
+int oracle_scan_segsum_i32_f32(const uint32_t* x, size_t n, uint32_t* y_flag, double* y_f, double* sabs,
+                               int exclusive)
+{
+    if (n == 0) return 0;
+    if (x == NULL || y_flag == NULL || y_f == NULL) return -1;
+    uint32_t F = 0u;
+    double V = 0.0, S = 0.0;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t f = x[2 * i];
+        const double v = (double)word_as_float(x[2 * i + 1]);
+        if (exclusive) {
+            y_flag[i] = F;
+            y_f[i] = V;
+            if (sabs != NULL) sabs[i] = S;
+        }
+        F |= f;
+        if (f != 0u) {
+            V = v;
+            S = fabs(v);
+        } else {
+            V += v;
+            S += fabs(v);
+        }
+        if (!exclusive) {
+            y_flag[i] = F;
+            y_f[i] = V;
+            if (sabs != NULL) sabs[i] = S;
+        }
+    }
+    return 0;
 }

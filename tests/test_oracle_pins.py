@@ -9,7 +9,10 @@
 - closed forms (constant and arithmetic inputs, with the modulo-2^32 wrap);
 - a witness that fp32 inputs are accumulated in fp64;
 - O(n^2) brute force on small n with exact Python integers / math.fsum;
-- numpy's cumsum, an independent library routine, on the seeded workloads.
+- numpy's cumsum, an independent library routine, on the seeded workloads;
+- for the generic operators: numpy's maximum/minimum.accumulate and per-column
+  cumsum, the affine recurrence run directly from several start values, and
+  brute-force segmented sums.
 
 The last test plants plausible mistakes in copies of the oracle's C source,
 compiles each copy with gcc on the CPU and checks that every mutant fails at
@@ -205,6 +208,155 @@ def _select_checks(lib, fail):
         fail("select float bits")
 
 
+def _minmax_checks(lib, fail):
+    rng = np.random.default_rng(31)
+    for dt, lo, hi in ((np.int32, -(2**31), 2**31), (np.uint32, 0, 2**32)):
+        info = np.iinfo(dt)
+        for n in (1, 2, 5, 64, 65, 1000):
+            x = rng.integers(lo, hi, size=n, dtype=np.int64).astype(dt)
+            xs = [int(v) for v in x]
+            for is_max, acc, ident in ((True, np.maximum, info.min), (False, np.minimum, info.max)):
+                y = lib.scan_minmax(x, is_max)
+                ye = lib.scan_minmax(x, is_max, exclusive=True)
+                # numpy's accumulate, an independent routine
+                if not np.array_equal(y, acc.accumulate(x)):
+                    fail(f"{dt.__name__} {'max' if is_max else 'min'} vs numpy n={n}")
+                # brute force over every prefix
+                f = max if is_max else min
+                if n <= 65 and y.tolist() != [f(xs[:i + 1]) for i in range(n)]:
+                    fail(f"{dt.__name__} {'max' if is_max else 'min'} brute force n={n}")
+                # exclusive: the type's extreme first, then the shifted inclusive
+                if ye.tolist() != [int(ident)] + y[:-1].tolist():
+                    fail(f"{dt.__name__} {'max' if is_max else 'min'} exclusive n={n}")
+    # signed and unsigned order differ on the top bit
+    x = np.array([1, 0x80000000, 5], dtype=np.uint32)
+    if lib.scan_minmax(x, True).tolist() != [1, 0x80000000, 0x80000000]:
+        fail("unsigned max order")
+    if lib.scan_minmax(x.view(np.int32), True).tolist() != [1, 1, 5]:
+        fail("signed max order")
+
+
+def _pair_sum_checks(lib, fail):
+    rng = np.random.default_rng(32)
+    for n in (1, 3, 64, 1000):
+        a = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        b = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        y = lib.scan_pair_sum_u32(oracle.make_pairs(a, b))
+        for col, v in ((0, a), (1, b)):
+            want = (np.cumsum(v.astype(np.uint64)) & M32).astype(np.uint32)
+            if not np.array_equal(y[:, col], want):
+                fail(f"pair sum u32 column {col} n={n}")
+        ye = lib.scan_pair_sum_u32(oracle.make_pairs(a, b), exclusive=True)
+        if ye[0].tolist() != [0, 0] or not np.array_equal(ye[1:], y[:-1]):
+            fail(f"pair sum u32 exclusive n={n}")
+        # {int32, fp32}: the int part against numpy's integer cumsum, the fp
+        # part against numpy's fp64 cumsum (both sequential)
+        ia = rng.integers(-(2**31), 2**31, size=n, dtype=np.int64).astype(np.int32)
+        fb = (rng.standard_normal(n)).astype(np.float32)
+        yi, yf, sa = lib.scan_pair_sum_i32_f32(oracle.make_pairs(ia, fb))
+        want_i = (np.cumsum(ia.astype(np.int64)) & M32).astype(np.uint32).view(np.int32)
+        if not np.array_equal(yi, want_i):
+            fail(f"pair sum i32 part n={n}")
+        if not np.array_equal(yf, np.cumsum(fb.astype(np.float64))):
+            fail(f"pair sum f32 part n={n}")
+        if not np.array_equal(sa, np.cumsum(np.abs(fb.astype(np.float64)))):
+            fail(f"pair sum running |f| n={n}")
+        yie, yfe, sae = lib.scan_pair_sum_i32_f32(oracle.make_pairs(ia, fb), exclusive=True)
+        if yie[0] != 0 or yfe[0] != 0.0 or not np.array_equal(yie[1:], yi[:-1]) or \
+                not np.array_equal(yfe[1:], yf[:-1]) or not np.array_equal(sae, sa):
+            fail(f"pair sum i32/f32 exclusive n={n}")
+
+
+def _affine_checks(lib, fail):
+    rng = np.random.default_rng(33)
+    for n in (1, 2, 7, 64, 500):
+        a = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        b = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        y = lib.scan_affine_u32(oracle.make_pairs(a, b))
+        ye = lib.scan_affine_u32(oracle.make_pairs(a, b), exclusive=True)
+        # the defining property: running the recurrence v = a v + b from any
+        # start s gives A_i s + B_i at every i (checked for three starts)
+        for s in (0, 1, int(rng.integers(0, 2**32))):
+            v = s
+            for i in range(n):
+                v = (int(a[i]) * v + int(b[i])) & M32
+                if v != (int(y[i, 0]) * s + int(y[i, 1])) & M32:
+                    fail(f"affine recurrence n={n} s={s} i={i}")
+                    break
+        if ye[0].tolist() != [1, 0] or not np.array_equal(ye[1:], y[:-1]):
+            fail(f"affine exclusive n={n}")
+        # a = 1: B is the prefix sum of b; b = 0: A is the prefix product of a
+        ones = np.ones(n, dtype=np.uint32)
+        y1 = lib.scan_affine_u32(oracle.make_pairs(ones, b))
+        if not np.array_equal(y1[:, 1], (np.cumsum(b.astype(np.uint64)) & M32).astype(np.uint32)) or \
+                not np.all(y1[:, 0] == 1):
+            fail(f"affine a=1 n={n}")
+        y0 = lib.scan_affine_u32(oracle.make_pairs(a, np.zeros(n, np.uint32)))
+        prod, want = 1, []
+        for v in a:
+            prod = (prod * int(v)) & M32
+            want.append(prod)
+        if y0[:, 0].tolist() != want or np.any(y0[:, 1] != 0):
+            fail(f"affine b=0 n={n}")
+    # order matters: the same two maps in the two orders
+    p = lib.scan_affine_u32(np.array([[2, 1], [3, 4]], dtype=np.uint32))[-1].tolist()
+    q = lib.scan_affine_u32(np.array([[3, 4], [2, 1]], dtype=np.uint32))[-1].tolist()
+    if p != [6, 7] or q != [6, 9]:
+        fail("affine composition order")
+
+
+def _segsum_checks(lib, fail):
+    rng = np.random.default_rng(34)
+    for n in (1, 2, 9, 64, 300):
+        flags = np.where(rng.random(n) < 0.2, rng.integers(1, 2**31, size=n), 0).astype(np.uint32)
+        vals = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        y = lib.scan_segsum_u32(oracle.make_pairs(flags, vals))
+        ye = lib.scan_segsum_u32(oracle.make_pairs(flags, vals), exclusive=True)
+        # brute force: the sum since the last head at or before i, and the OR
+        # of all flags up to i
+        for i in range(n):
+            h = max([j for j in range(i + 1) if flags[j] != 0], default=0)
+            v = sum(int(vals[j]) for j in range(h, i + 1)) & M32
+            f = 0
+            for j in range(i + 1):
+                f |= int(flags[j])
+            if [int(y[i, 0]), int(y[i, 1])] != [f, v]:
+                fail(f"segsum u32 brute force n={n} i={i}")
+                break
+        if ye[0].tolist() != [0, 0] or not np.array_equal(ye[1:], y[:-1]):
+            fail(f"segsum u32 exclusive n={n}")
+        # fp32 values (dyadic: every fp64 partial sum is exact), brute force
+        # with fsum, and the |value| sum over the same elements
+        fv = (rng.integers(-1024, 1025, size=n) / 64.0).astype(np.float32)
+        yfl, yf, sa = lib.scan_segsum_i32_f32(oracle.make_pairs(flags, fv))
+        yfle, yfe, sae = lib.scan_segsum_i32_f32(oracle.make_pairs(flags, fv), exclusive=True)
+        for i in range(n):
+            h = max([j for j in range(i + 1) if flags[j] != 0], default=0)
+            seg = [float(fv[j]) for j in range(h, i + 1)]
+            if yf[i] != math.fsum(seg) or sa[i] != math.fsum(abs(v) for v in seg):
+                fail(f"segsum f32 brute force n={n} i={i}")
+                break
+        if yfle[0] != 0 or yfe[0] != 0.0 or sae[0] != 0.0 or not np.array_equal(yfe[1:], yf[:-1]) or \
+                not np.array_equal(sae[1:], sa[:-1]) or not np.array_equal(yfle[1:], yfl[:-1]):
+            fail(f"segsum f32 exclusive n={n}")
+    # closed forms: every element a head gives the values back; no heads gives
+    # the plain prefix sum (numpy)
+    v = np.arange(1, 101, dtype=np.uint32)
+    if not np.array_equal(lib.scan_segsum_u32(oracle.make_pairs(np.ones(100, np.uint32), v))[:, 1], v):
+        fail("segsum all heads")
+    if not np.array_equal(lib.scan_segsum_u32(oracle.make_pairs(np.zeros(100, np.uint32), v))[:, 1],
+                          np.cumsum(v).astype(np.uint32)):
+        fail("segsum no heads")
+
+
+def _generic_checks(lib, fail):
+    for f in (_minmax_checks, _pair_sum_checks, _affine_checks, _segsum_checks):
+        try:
+            f(lib, fail)
+        except (IndexError, ValueError, RuntimeError) as e:   # a broken oracle may produce nonsense shapes
+            fail(f"{f.__name__}: {e}")
+
+
 def pin_failures(lib) -> list:
     """Run every pin against an oracle library; return the names that fail."""
     failures = []
@@ -216,6 +368,7 @@ def pin_failures(lib) -> list:
     _fp64_witness_checks(lib, fail)
     _brute_force_checks(lib, fail)
     _select_checks(lib, fail)
+    _generic_checks(lib, fail)
     return failures
 
 
@@ -263,6 +416,14 @@ def test_select_flagged(lib):
     y = x.copy()
     out = lib._lib.oracle_select_flagged(y.ctypes.data, flags.ctypes.data, y.size, y.ctypes.data)
     assert np.array_equal(y[:out], x[flags != 0])
+
+
+@pytest.mark.parametrize("checks", [_minmax_checks, _pair_sum_checks, _affine_checks, _segsum_checks],
+                         ids=["minmax", "pair_sum", "affine", "segsum"])
+def test_generic_operators(lib, checks):
+    failures = []
+    checks(lib, failures.append)
+    assert failures == []
 
 
 def test_empty_and_in_place(lib):
@@ -328,6 +489,17 @@ MUTANTS = [
     ("select tests sign", "if (flags[i] != 0) {", "if (flags[i] > 0) {"),
     ("select drops the last element", "for (size_t i = 0; i < n; ++i) {\n        if (flags[i]", "for (size_t i = 0; i + 1 < n; ++i) {\n        if (flags[i]"),
     ("select writes past the slot", "out[count] = x[i];\n            ++count;", "++count;\n            out[count - 1 + (count > 1)] = x[i];"),
+    ("max compares unsigned as signed", "else take = is_max ? (xi > running) : (xi < running);",
+     "else take = is_max ? ((int32_t)xi > (int32_t)running) : (xi < running);"),
+    ("min identity", "else running = is_signed ? 0x7fffffffu : 0xffffffffu;",
+     "else running = is_signed ? 0x7fffffffu : 0x7fffffffu;"),
+    ("pair sum drops the fp part", "        rf += xf;\n", "        rf = xf;\n"),
+    ("affine composed in the wrong order", "B = a * B + b;", "B = B + b * A;"),
+    ("affine uses the updated A", "        A = a * A;\n        B = a * B + b;", "        A = a * A;\n        B = A * B + b;"),
+    ("segsum does not restart", "if (f != 0u) V = v;", "if (f != 0u) V += v;"),
+    ("segsum flag not accumulated", "F |= f;", "F = f;"),
+    ("segsum fp restarts before the head", "            V = v;\n            S = fabs(v);",
+     "            V = 0.0;\n            S = 0.0;"),
 ]
 
 
