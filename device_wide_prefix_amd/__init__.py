@@ -24,7 +24,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libdws_scan.so")
 # dws_status
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_MISALIGNED, ERR_HIP, ERR_OOM = range(7)
 # dws_dtype
-INT32, UINT32, FLOAT32 = 0, 1, 2
+INT32, UINT32, FLOAT32, PAIR_I32_F32, PAIR_U32 = 0, 1, 2, 3, 4
+# dws_op
+OP_SUM, OP_MAX, OP_MIN, OP_AFFINE, OP_SEGMENTED_SUM = 0, 1, 2, 3, 4
 # dws_variant
 SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED, SCAN_THEN_PROPAGATE = 0, 1, 2, 3
 # dws_memory_order
@@ -36,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
-    "dws_scan_profiled", "dws_select_flagged",
+    "dws_scan_profiled", "dws_select_flagged", "dws_scan_op",
 )
 
 
@@ -93,6 +95,8 @@ def load_library():
     lib.dws_scan_debug.restype = ci
     lib.dws_scan_profiled.argtypes = [vp, vp, sz, ci, ci, vp, sz, ctypes.POINTER(cu), vp]
     lib.dws_scan_profiled.restype = ci
+    lib.dws_scan_op.argtypes = [vp, vp, sz, ci, ci, ci, vp]
+    lib.dws_scan_op.restype = ci
     lib.dws_select_flagged.argtypes = [vp, vp, vp, sz, ci, vp, vp]
     lib.dws_select_flagged.restype = ci
     lib.dws_selftest_wave.argtypes = [vp, vp, vp, sz, ci, vp]
@@ -238,6 +242,38 @@ def scan_profiled(x, out=None, exclusive=False, stream=None):
                                                 stamps.data_ptr(), stamps.numel(), ctypes.byref(t),
                                                 _stream(x, stream)), "dws_scan_profiled")
     return out, stamps[:tiles]
+
+
+def scan_op_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: bool, stream: int = 0) -> int:
+    return load_library().dws_scan_op(d_in, d_out, n, dtype, op, int(bool(exclusive)), stream)
+
+
+def scan_op(x, op, dtype=None, exclusive=False, out=None, stream=None):
+    """Scan of a contiguous GPU tensor under a generic operator (OP_*).
+
+    For the 32-bit types dtype defaults from the tensor. Pair types
+    (PAIR_I32_F32, PAIR_U32) take any contiguous tensor whose bytes hold the
+    pairs, e.g. an (n, 2) int32 tensor of bits; n is its byte size / 8.
+    Returns ``out`` (same shape and dtype as x; may be x)."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("scan_op expects a GPU tensor (there is no CPU path)")
+    if not x.is_contiguous():
+        raise ValueError("input tensor must be contiguous")
+    if dtype is None:
+        dtype = _dtype_code(x)
+    esize = 8 if dtype in (PAIR_I32_F32, PAIR_U32) else 4
+    nbytes = x.numel() * x.element_size()
+    if nbytes % esize:
+        raise ValueError(f"tensor of {nbytes} bytes does not hold whole {esize}-byte elements")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.numel() * out.element_size() != nbytes or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor of the same byte size on the device of x")
+    with _device_of(x):
+        _check(scan_op_ptr(x.data_ptr(), out.data_ptr(), nbytes // esize, int(dtype), int(op), exclusive,
+                           _stream(x, stream)), "dws_scan_op")
+    return out
 
 
 def select_flagged_ptr(d_in: int, d_flags: int, d_out: int, n: int, dtype: int, d_count: int,

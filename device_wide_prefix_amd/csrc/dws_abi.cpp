@@ -60,20 +60,26 @@ dws_status from_hip(hipError_t e)
 
 bool valid_dtype(int d) { return d == DWS_INT32 || d == DWS_UINT32 || d == DWS_FLOAT32; }
 
-// All checks that need no HIP call. n == 0 is accepted with any pointers.
-dws_status validate(const void* in, const void* out, size_t n, int dtype)
+// All checks on the data pointers that need no HIP call, for elements of
+// `esize` bytes. n == 0 is accepted with any pointers.
+dws_status validate_sized(const void* in, const void* out, size_t n, size_t esize)
 {
-    if (!valid_dtype(dtype)) return DWS_ERR_INVALID_ARG;
     if (n == 0) return DWS_OK;
     if (in == nullptr || out == nullptr) return DWS_ERR_INVALID_ARG;
     if (n > DWS_MAX_ELEMENTS) return DWS_ERR_UNSUPPORTED;
     const uintptr_t a = reinterpret_cast<uintptr_t>(in);
     const uintptr_t b = reinterpret_cast<uintptr_t>(out);
-    if ((a % kElemBytes) != 0 || (b % kElemBytes) != 0) return DWS_ERR_MISALIGNED;
-    const uintptr_t bytes = (uintptr_t)n * kElemBytes;
+    if ((a % esize) != 0 || (b % esize) != 0) return DWS_ERR_MISALIGNED;
+    const uintptr_t bytes = (uintptr_t)n * esize;
     if (a + bytes < a || b + bytes < b) return DWS_ERR_INVALID_ARG;
     if (a != b && a < b + bytes && b < a + bytes) return DWS_ERR_OVERLAP;
     return DWS_OK;
+}
+
+dws_status validate(const void* in, const void* out, size_t n, int dtype)
+{
+    if (!valid_dtype(dtype)) return DWS_ERR_INVALID_ARG;
+    return validate_sized(in, out, n, kElemBytes);
 }
 
 int kind_of(int dtype) { return dtype == DWS_FLOAT32 ? kKindF32 : kKindU32; }
@@ -327,9 +333,89 @@ dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclus
     }
 }
 
+// (operator, element type) -> kernel kind, or -1 where none is built.
+int op_kind(int dtype, int op)
+{
+    switch (op) {
+    case DWS_OP_MAX: return dtype == DWS_INT32 ? kOpMaxI32 : (dtype == DWS_UINT32 ? kOpMaxU32 : -1);
+    case DWS_OP_MIN: return dtype == DWS_INT32 ? kOpMinI32 : (dtype == DWS_UINT32 ? kOpMinU32 : -1);
+    case DWS_OP_SUM: return dtype == DWS_PAIR_I32_F32 ? kOpSumPairIF : (dtype == DWS_PAIR_U32 ? kOpSumPairU32 : -1);
+    case DWS_OP_AFFINE: return dtype == DWS_PAIR_U32 ? kOpAffineU32 : -1;
+    case DWS_OP_SEGMENTED_SUM:
+        return dtype == DWS_PAIR_I32_F32 ? kOpSegSumIF : (dtype == DWS_PAIR_U32 ? kOpSegSumU32 : -1);
+    default: return -1;
+    }
+}
+
+hipError_t launch_op_kind(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                          hipStream_t stream)
+{
+    switch (kind) {
+    case kOpMaxI32:
+    case kOpMaxU32:
+    case kOpMinI32:
+    case kOpMinU32: return launch_op_minmax(kind, exclusive, shape, tile_index, p, stream);
+    case kOpSumPairIF:
+    case kOpSumPairU32: return launch_op_pairsum(kind, exclusive, shape, tile_index, p, stream);
+    case kOpAffineU32: return launch_op_affine(kind, exclusive, shape, tile_index, p, stream);
+    case kOpSegSumIF:
+    case kOpSegSumU32: return launch_op_segsum(kind, exclusive, shape, tile_index, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl, hipStream_t stream)
+{
+    const int words = op_kind_words(kind);
+    const bool aligned = aligned16(in, out);
+    const int shape = op_auto_shape(n, aligned);
+    const int tile_index = (shape == kOpShapeLarge && n >= kAutoDrawnMin) ? kTileDrawn : kTileDispatch;
+    const uint64_t num_tiles = ceil_div(n, op_tile_elems(words, shape));
+    if (num_tiles > 0xffffffffull || num_tiles * op_tile_threads(shape) > kMaxGridThreads)
+        return DWS_ERR_UNSUPPORTED;
+    OpScanParams p{};
+    p.in = in;
+    p.out = out;
+    p.n = n;
+    p.num_tiles = (uint32_t)num_tiles;
+    if (num_tiles == 1) return from_hip(launch_op_kind(kind, excl, shape, tile_index, p, stream));
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_desc(ws, num_tiles * (uint64_t)words);
+    if (s != DWS_OK) return s;
+    s = next_epoch(ws, &p.epoch);
+    if (s != DWS_OK) return s;
+    p.desc = ws->desc;
+    p.counter = ws->counter();
+    p.watchdog = ws->watchdog();
+    return from_hip(launch_op_kind(kind, excl, shape, tile_index, p, stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_op op, int exclusive,
+                       hipStream_t stream)
+{
+    try {
+        if ((int)dtype < DWS_INT32 || (int)dtype > DWS_PAIR_U32) return DWS_ERR_INVALID_ARG;
+        if ((int)op < DWS_OP_SUM || (int)op > DWS_OP_SEGMENTED_SUM) return DWS_ERR_INVALID_ARG;
+        if (op == DWS_OP_SUM && valid_dtype((int)dtype))
+            return scan_entry(d_in, d_out, n, (int)dtype, exclusive, nullptr, stream);
+        const int kind = op_kind((int)dtype, (int)op);
+        if (kind < 0) return DWS_ERR_UNSUPPORTED;
+        const dws_status s = validate_sized(d_in, d_out, n, 4u * (size_t)op_kind_words(kind));
+        if (s != DWS_OK || n == 0) return s;
+        return run_scan_op(d_in, d_out, n, kind, exclusive != 0, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
 
 dws_status scan_inclusive(const void* d_in, void* d_out, size_t n, dws_dtype dtype, hipStream_t stream)
 {
@@ -392,10 +478,19 @@ dws_status dws_reserve(size_t n, hipStream_t stream)
         Workspace* ws = nullptr;
         dws_status s = get_workspace(stream, &ws);
         if (s != DWS_OK) return s;
-        uint32_t min_tile = 0xffffffffu;
-        for (int i = 0; i < kNumShapes; ++i) min_tile = std::min(min_tile, (uint32_t)kShapes[i].elems());
+        // the most descriptor slots any scan of n elements uses: the smallest
+        // single-pass tile, or the generic kernels' tiles times their words
+        const uint64_t m = std::max<uint64_t>(n, 1);
+        uint64_t slots = 0;
+        for (int i = 0; i < kNumShapes; ++i) slots = std::max(slots, ceil_div(m, (uint64_t)kShapes[i].elems()));
+        for (int w = 1; w <= 2; ++w)
+            for (int shape = kOpShapeSmall; shape <= kOpShapeUnaligned; ++shape)
+                slots = std::max(slots, ceil_div(m, op_tile_elems(w, shape)) * (uint64_t)w);
         std::lock_guard<std::mutex> lock(ws->mu);
-        return ensure_desc(ws, ceil_div(std::max<uint64_t>(n, 1), min_tile));
+        s = ensure_desc(ws, slots);
+        if (s != DWS_OK) return s;
+        const uint64_t stp = stp_scratch_elems(m);
+        return stp == 0 ? DWS_OK : ensure_stp(ws, stp);
     } catch (...) {
         return DWS_ERR_OOM;
     }

@@ -107,6 +107,59 @@ struct DebugArgs {
 };
 hipError_t launch_debug(const DebugArgs& a, hipStream_t stream);
 
+// Scan under a generic operator (dws_op_kernel.hpp). Kinds name an
+// (operator, element type) pair; pair elements are two 32-bit words.
+struct OpScanParams {
+    const void* in;
+    void* out;
+    uint64_t n;                   // elements
+    uint64_t* desc;               // >= words * num_tiles slots
+    unsigned long long* counter;
+    unsigned int* watchdog;
+    uint32_t num_tiles;
+    uint32_t epoch;
+};
+enum OpKind : int {
+    kOpMaxI32, kOpMaxU32, kOpMinI32, kOpMinU32,          // one word
+    kOpSumPairIF, kOpSumPairU32, kOpAffineU32, kOpSegSumIF, kOpSegSumU32,   // two words
+    kNumOpKinds
+};
+constexpr int op_kind_words(int kind) { return kind <= kOpMinU32 ? 1 : 2; }
+// Shapes (threads x words per load x loads per lane): small 256 x 4 x 4,
+// medium 512 x 4 x 8, large 1024 x 4 x 16, unaligned 256 x (one element) x 16.
+constexpr int kOpShapeSmall = 0;
+constexpr int kOpShapeMedium = 1;
+constexpr int kOpShapeLarge = 2;
+constexpr int kOpShapeUnaligned = 3;
+constexpr uint64_t kOpMediumMin = (uint64_t)1 << 20;
+constexpr uint64_t kOpLargeMin = (uint64_t)1 << 24;
+constexpr int op_auto_shape(uint64_t n, bool aligned)
+{
+    return !aligned ? kOpShapeUnaligned : (n >= kOpLargeMin ? kOpShapeLarge : (n >= kOpMediumMin ? kOpShapeMedium
+                                                                                                   : kOpShapeSmall));
+}
+constexpr uint32_t op_tile_elems(int words, int shape)
+{
+    return shape == kOpShapeSmall    ? 256u * (4u / words) * 4u
+           : shape == kOpShapeMedium ? 512u * (4u / words) * 8u
+           : shape == kOpShapeLarge  ? 1024u * (4u / words) * 16u
+                                     : 256u * 16u;
+}
+constexpr uint32_t op_tile_threads(int shape)
+{
+    return shape == kOpShapeMedium ? 512u : (shape == kOpShapeLarge ? 1024u : 256u);
+}
+// Only the large shape is built with a drawn tile index (used from
+// kAutoDrawnMin elements); the others take the workgroup index.
+hipError_t launch_op_minmax(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                            hipStream_t stream);
+hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                             hipStream_t stream);
+hipError_t launch_op_affine(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                            hipStream_t stream);
+hipError_t launch_op_segsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                            hipStream_t stream);
+
 // Zero `slots` descriptors and set the counter to kCounterInit and the
 // watchdog to 0 (a kernel, not a memset, so that it may sit in a graph).
 hipError_t launch_workspace_init(uint64_t* desc, uint64_t slots, unsigned long long* counter,

@@ -1,0 +1,14 @@
+// Composition of affine maps modulo 2^32 (first-order linear recurrences), a
+// non-commutative operator, on the generic-operator single-pass scan.
+#include "dws_op_kernel.hpp"
+
+namespace dws {
+
+hipError_t launch_op_affine(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                            hipStream_t stream)
+{
+    if (kind != kOpAffineU32) return hipErrorInvalidValue;
+    return launch_op_typed<OpAffineU32>(exclusive, shape, tile_index, p, stream);
+}
+
+}  // namespace dws

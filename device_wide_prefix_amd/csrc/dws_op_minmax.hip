@@ -1,0 +1,19 @@
+// Running max and min of 32-bit integers (signed and unsigned), on the
+// generic-operator single-pass scan.
+#include "dws_op_kernel.hpp"
+
+namespace dws {
+
+hipError_t launch_op_minmax(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                            hipStream_t stream)
+{
+    switch (kind) {
+    case kOpMaxI32: return launch_op_typed<OpMaxI32>(exclusive, shape, tile_index, p, stream);
+    case kOpMaxU32: return launch_op_typed<OpMaxU32>(exclusive, shape, tile_index, p, stream);
+    case kOpMinI32: return launch_op_typed<OpMinI32>(exclusive, shape, tile_index, p, stream);
+    case kOpMinU32: return launch_op_typed<OpMinU32>(exclusive, shape, tile_index, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dws

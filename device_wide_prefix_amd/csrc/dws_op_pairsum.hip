@@ -1,0 +1,17 @@
+// Componentwise + of {int32, fp32} and uint32 pairs, on the generic-operator
+// single-pass scan.
+#include "dws_op_kernel.hpp"
+
+namespace dws {
+
+hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                             hipStream_t stream)
+{
+    switch (kind) {
+    case kOpSumPairIF: return launch_op_typed<OpSumPairIF>(exclusive, shape, tile_index, p, stream);
+    case kOpSumPairU32: return launch_op_typed<OpSumPairU32>(exclusive, shape, tile_index, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dws

@@ -1,0 +1,17 @@
+// Segmented + on (flag, value) pairs, a non-commutative operator, on the
+// generic-operator single-pass scan.
+#include "dws_op_kernel.hpp"
+
+namespace dws {
+
+hipError_t launch_op_segsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+                            hipStream_t stream)
+{
+    switch (kind) {
+    case kOpSegSumIF: return launch_op_typed<OpSegSumIF>(exclusive, shape, tile_index, p, stream);
+    case kOpSegSumU32: return launch_op_typed<OpSegSumU32>(exclusive, shape, tile_index, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dws

@@ -32,10 +32,13 @@
  * Streams and ownership: every call is asynchronous on `stream` (0 = the
  * default stream of the current device) and returns after enqueue. The library
  * keeps one small workspace per (device, stream): descriptors (8 bytes per
- * tile), a tile counter and, for the reduce-then-scan variant, a partials
- * array. It is allocated and cleared on the first multi-tile call on that
- * stream (which therefore must not be under graph capture; dws_reserve can
- * create it ahead of time) and reused by later calls, which the stream orders.
+ * tile and 32-bit element word), a tile counter, a partials array for the
+ * reduce-then-scan variant and, allocated on its first use, the tile sums of
+ * the scan-then-propagate variant (about n / 4095 elements). It is allocated
+ * and cleared on the first multi-tile call on that stream (which therefore
+ * must not be under graph capture; dws_reserve can create it ahead of time)
+ * and reused by later calls, which the stream orders; a call that needs more
+ * descriptors than the workspace holds synchronises the stream and grows it.
  * Calls on different streams never share a workspace. Host threads may call
  * concurrently. dws_release_workspaces frees every workspace.
  *
@@ -57,9 +60,10 @@ extern "C" {
 typedef enum dws_status {
     DWS_OK = 0,
     DWS_ERR_INVALID_ARG = 1,   /* null pointer with n > 0, bad enum or option */
-    DWS_ERR_UNSUPPORTED = 2,   /* n above DWS_MAX_ELEMENTS */
+    DWS_ERR_UNSUPPORTED = 2,   /* n above a limit, or an option, operator or
+                                  type combination that is not built */
     DWS_ERR_OVERLAP = 3,       /* d_in and d_out overlap without being equal */
-    DWS_ERR_MISALIGNED = 4,    /* a pointer is not 4-byte aligned */
+    DWS_ERR_MISALIGNED = 4,    /* a pointer is not aligned to the element size */
     DWS_ERR_HIP = 5,           /* a HIP runtime call failed */
     DWS_ERR_OOM = 6            /* workspace allocation failed */
 } dws_status;
@@ -67,7 +71,12 @@ typedef enum dws_status {
 typedef enum dws_dtype {
     DWS_INT32 = 0,
     DWS_UINT32 = 1,
-    DWS_FLOAT32 = 2
+    DWS_FLOAT32 = 2,
+    /* 8-byte pairs, for dws_scan_op only: {int32, fp32} (Merrill & Garland,
+     * section A4, data types) and {uint32, uint32}; first component at the
+     * lower address */
+    DWS_PAIR_I32_F32 = 3,
+    DWS_PAIR_U32 = 4
 } dws_dtype;
 
 /* Largest supported element count (2^35). */
@@ -185,6 +194,44 @@ dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out
                               dws_dtype dtype, unsigned long long* d_count,
                               hipStream_t stream);
 
+/* Associative operators of dws_scan_op. The single pass only ever combines
+ * contiguous inputs or contiguous partial results, earlier operand first, so
+ * an operator need not be commutative (Merrill & Garland, section 4.2). */
+typedef enum dws_op {
+    /* +: int32/uint32 modulo 2^32 and fp32 (the scans above), and
+     * componentwise on both pair types */
+    DWS_OP_SUM = 0,
+    /* max / min: DWS_INT32 (signed order) and DWS_UINT32 (unsigned order);
+     * the exclusive scan starts with the type's lowest (max) or highest (min)
+     * value */
+    DWS_OP_MAX = 1,
+    DWS_OP_MIN = 2,
+    /* DWS_PAIR_U32 (a, b) is the map v -> a v + b modulo 2^32; element i of
+     * the inclusive result is (A, B) with v_i = A s + B for the recurrence
+     * v_i = a_i v_{i-1} + b_i, v_{-1} = s. Not commutative. Identity (1, 0). */
+    DWS_OP_AFFINE = 3,
+    /* (flag, value) pairs, DWS_PAIR_U32 or DWS_PAIR_I32_F32: a non-zero flag
+     * starts a new segment, the value part sums within the segment, the flag
+     * part is the OR of all flags so far. Not commutative. Identity (0, 0). */
+    DWS_OP_SEGMENTED_SUM = 4
+} dws_op;
+
+/*
+ * Inclusive (exclusive != 0: exclusive, identity first) scan of n elements of
+ * `dtype` under `op`, one single-pass launch with decoupled look-back. Built
+ * combinations: DWS_OP_SUM with every dtype (the 32-bit scalars take the
+ * scan_inclusive / scan_exclusive path), DWS_OP_MAX / DWS_OP_MIN with
+ * DWS_INT32 and DWS_UINT32, DWS_OP_AFFINE with DWS_PAIR_U32,
+ * DWS_OP_SEGMENTED_SUM with both pair types; others give
+ * DWS_ERR_UNSUPPORTED. Integer parts are exact; fp32 parts are rounded in an
+ * order that depends on scheduling. d_out == d_in is allowed. Pointers must
+ * be aligned to the element size (4 or 8 bytes); 16-byte aligned pointers
+ * take the vector-load kernels. Same workspace, errors and asynchrony as
+ * scan_inclusive.
+ */
+dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                       dws_op op, int exclusive, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* dws_status_string(dws_status status);
 
@@ -210,7 +257,8 @@ unsigned dws_tile_threads(int tile_shape, size_t n, int aligned);
 
 /*
  * Create (or grow) the workspace of `stream` on the current device so that
- * scans of up to n elements with any option need no further allocation.
+ * scans, compactions and generic-operator scans of up to n elements, with any
+ * variant or option, need no further allocation.
  */
 dws_status dws_reserve(size_t n, hipStream_t stream);
 

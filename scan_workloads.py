@@ -124,6 +124,49 @@ def selection_flags(n: int, density: float, seed: int, any_nonzero: bool = False
     return np.where(on, v, 0).astype(np.int32)
 
 
+OP_INPUTS = ("i32_full", "u32_full", "pair_i32_f32", "pair_u32", "affine_u32", "segsum_u32", "segsum_i32_f32")
+
+
+def op_input(kind: str, n: int, seed: int, head_density: float = 0.01) -> np.ndarray:
+    """Seeded inputs for the generic-operator scans. 32-bit kinds give (n,)
+    arrays; pair kinds give (n, 2) uint32 arrays of bits (column 0 the first
+    component):
+      pair_i32_f32    uniform int32, uniform [-1, 1) fp32
+      pair_u32        two uniform uint32
+      affine_u32      (a, b): a odd with probability 0.9 (else uniform), b
+                      uniform, so that most running products stay non-zero
+      segsum_u32      (flag, value): flag non-zero (uniform non-zero int32
+                      bits) with probability head_density, value uniform
+      segsum_i32_f32  the same flags, value uniform [-1, 1) fp32"""
+    rng = np.random.default_rng(seed)
+    n = int(n)
+    if kind == "i32_full":
+        return _i32_full(rng, n)
+    if kind == "u32_full":
+        return _u32_full(rng, n)
+    out = np.empty((n, 2), dtype=np.uint32)
+    if kind == "pair_i32_f32":
+        out[:, 0] = _i32_full(rng, n).view(np.uint32)
+        out[:, 1] = _f32_pm1(rng, n).view(np.uint32)
+    elif kind == "pair_u32":
+        out[:, 0] = _u32_full(rng, n)
+        out[:, 1] = _u32_full(rng, n)
+    elif kind == "affine_u32":
+        a = _u32_full(rng, n)
+        odd = rng.random(n) < 0.9
+        out[:, 0] = np.where(odd, a | np.uint32(1), a)
+        out[:, 1] = _u32_full(rng, n)
+    elif kind in ("segsum_u32", "segsum_i32_f32"):
+        heads = rng.random(n) < head_density
+        f = _u32_full(rng, n)
+        f[f == 0] = 1
+        out[:, 0] = np.where(heads, f, np.uint32(0))
+        out[:, 1] = _u32_full(rng, n) if kind == "segsum_u32" else _f32_pm1(rng, n).view(np.uint32)
+    else:
+        raise KeyError(kind)
+    return out
+
+
 def generate(dist: str, n: int, seed: int) -> np.ndarray:
     """Draw ``n`` values of distribution ``dist`` from PCG64(seed)."""
     rng = np.random.default_rng(seed)

@@ -207,3 +207,37 @@ def test_select_binding_checks_flags(lib):
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         dws.select_flagged(torch.arange(10, dtype=torch.int32), torch.ones(10, dtype=torch.int32))
+
+
+def test_scan_op_validation(lib):
+    f = lib.dws_scan_op
+    big = FAKE + (1 << 24)
+    # bad enums
+    assert f(FAKE, big, 10, 5, dws.OP_MAX, 0, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, big, 10, -1, dws.OP_MAX, 0, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, big, 10, dws.INT32, 5, 0, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, big, 10, dws.INT32, -1, 0, None) == dws.ERR_INVALID_ARG
+    # combinations that are not built
+    assert f(FAKE, big, 10, dws.FLOAT32, dws.OP_MAX, 0, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, big, 10, dws.PAIR_U32, dws.OP_MIN, 0, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, big, 10, dws.INT32, dws.OP_AFFINE, 0, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, big, 10, dws.PAIR_I32_F32, dws.OP_AFFINE, 0, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, big, 10, dws.FLOAT32, dws.OP_SEGMENTED_SUM, 0, None) == dws.ERR_UNSUPPORTED
+    # pointers: null, alignment to the element size, overlap, empty
+    assert f(None, big, 10, dws.PAIR_U32, dws.OP_AFFINE, 0, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE + 4, big, 10, dws.PAIR_U32, dws.OP_AFFINE, 0, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, big + 4, 10, dws.PAIR_I32_F32, dws.OP_SUM, 0, None) == dws.ERR_MISALIGNED
+    assert f(FAKE + 2, big, 10, dws.INT32, dws.OP_MAX, 0, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, FAKE + 8, 10, dws.PAIR_U32, dws.OP_SEGMENTED_SUM, 0, None) == dws.ERR_OVERLAP
+    assert f(FAKE + 72, FAKE, 10, dws.PAIR_U32, dws.OP_SEGMENTED_SUM, 0, None) == dws.ERR_OVERLAP
+    assert f(None, None, 0, dws.PAIR_U32, dws.OP_AFFINE, 1, None) == dws.OK
+    assert f(FAKE, big, (1 << 35) + 1, dws.PAIR_U32, dws.OP_AFFINE, 0, None) == dws.ERR_UNSUPPORTED
+    # + on the 32-bit types is the plain scan, with its checks
+    assert f(FAKE, FAKE + 4, 10, dws.INT32, dws.OP_SUM, 0, None) == dws.ERR_OVERLAP
+    assert f(None, None, 0, dws.FLOAT32, dws.OP_SUM, 0, None) == dws.OK
+
+
+def test_scan_op_binding_checks(lib):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        dws.scan_op(torch.zeros((4, 2), dtype=torch.int32), dws.OP_AFFINE, dws.PAIR_U32)
