@@ -19,7 +19,9 @@ Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained|scan_
 --order relaxed|acq_rel, --tile-shape K, --nontemporal, --no-cpu-baseline,
 --all (extra JSON lines for every workload and variant on stderr), --sweep
 (N = 2^10..2^30, every variant and memcpy, cold and warm caches; stderr),
---select (stream compaction on the 2^30-12345 flag workload; stderr).
+--select (stream compaction on the 2^30-12345 flag workload; stderr), --ops
+(generic-operator scans: max, min, {int32, fp32} pair sum, affine maps,
+segmented sum, on 1 GiB inputs; stderr).
 """
 from __future__ import annotations
 
@@ -269,6 +271,84 @@ def run_select(steps: int, warmup: int, in_place: bool):
     return row
 
 
+# name: (op, dtype, input kind, element bytes); every case reads and writes 1 GiB
+OP_CASES = {
+    "max_i32": (0x1, 0, "i32_full", 4),
+    "min_u32": (0x2, 1, "u32_full", 4),
+    "sum_pair_i32_f32": (0x0, 3, "pair_i32_f32", 8),
+    "affine_u32": (0x3, 4, "affine_u32", 8),
+    "segsum_i32_f32": (0x4, 3, "segsum_i32_f32", 8),
+}
+OP_BYTES = 1 << 31
+
+
+def op_property_check(name: str, x: np.ndarray, y: np.ndarray) -> bool:
+    """Checks that hold at any size (no oracle here)."""
+    if name == "max_i32":
+        return bool(np.all(np.diff(y.view(np.int32).astype(np.int64)) >= 0) and y.view(np.int32)[-1] == x.max())
+    if name == "min_u32":
+        return bool(np.all(np.diff(y.astype(np.int64)) <= 0) and y[-1] == x.min())
+    if name == "sum_pair_i32_f32":
+        tot_i = int(np.sum(x[:, 0].view(np.int32).astype(np.int64))) & 0xFFFFFFFF
+        f = x[:, 1].view(np.float32).astype(np.float64)
+        tot_f = float(f.sum())
+        return bool(int(y[-1, 0]) == tot_i and abs(float(y[-1:, 1].view(np.float32)[0]) - tot_f)
+                    <= 1e-4 * float(np.abs(f).sum()) + 1e-6)
+    if name == "affine_u32":
+        v, s = 7, 7
+        for i in range(2000):   # the recurrence, run directly, from start value 7
+            v = (int(x[i, 0]) * v + int(x[i, 1])) & 0xFFFFFFFF
+            if v != (int(y[i, 0]) * s + int(y[i, 1])) & 0xFFFFFFFF:
+                return False
+        return True
+    if name == "segsum_i32_f32":
+        heads = np.flatnonzero(x[:, 0] != 0)
+        return bool(np.array_equal(y[heads, 1], x[heads, 1]))   # a head restarts with its own value
+    return False
+
+
+def run_ops(steps: int, warmup: int):
+    """Generic-operator scans of 1 GiB of input (2^28 32-bit or 2^27 pair
+    elements), out of place, cold caches; GB/s counts 2 x the input bytes,
+    like the + scan, against a same-size memcpy. One OPS line per operator."""
+    import torch
+    import device_wide_prefix_amd as dws
+    rows = []
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+    for name, (op, dtype, kind, esize) in OP_CASES.items():
+        n = (OP_BYTES // 2) // esize
+        x = wl.op_input(kind, n, seed=11)
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int32).reshape(-1)).to("cuda")
+        out = torch.empty_like(xd)
+        dws.reserve(n)
+
+        def prepare():
+            flush.sum()
+
+        def scan():
+            st = dws.scan_op_ptr(xd.data_ptr(), out.data_ptr(), n, dtype, op, False, stream)
+            if st != dws.OK:
+                raise RuntimeError(f"{name}: {dws.status_string(st)}")
+
+        times = time_steps(scan, prepare, steps, warmup)
+        y = out.cpu().numpy().view(np.uint32).reshape(x.shape)
+        ok = op_property_check(name, x, y)
+        mc = time_steps(lambda: hip.memcpy_d2d(out.data_ptr(), xd.data_ptr(), n * esize, stream), prepare,
+                        steps, warmup)
+        mean, mcm = float(np.mean(times)), float(np.mean(mc))
+        row = {"op": name, "n": n, "element_bytes": esize, "ms_mean": mean, "ms_min": float(np.min(times)),
+               "gbps": 2 * n * esize / (mean * 1e-3) / 1e9, "memcpy_gbps": 2 * n * esize / (mcm * 1e-3) / 1e9,
+               "frac_memcpy": mcm / mean, "frac_hbm_peak": 2 * n * esize / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "property_check": ok}
+        log("OPS " + json.dumps(row))
+        rows.append(row)
+        del xd, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
     """The sequential oracle on the same input, timed on one host core, repeated
     until about budget_s seconds of CPU work (the oracle is one loop: 1 thread)."""
@@ -335,6 +415,8 @@ def main():
                     help="also sweep N = 2^10..2^30 for every variant against memcpy (stderr)")
     ap.add_argument("--select", action="store_true",
                     help="also measure stream compaction on the 2^30-12345 flag workload (stderr)")
+    ap.add_argument("--ops", action="store_true",
+                    help="also measure the generic-operator scans on 1 GiB inputs (stderr)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -412,6 +494,8 @@ def main():
 
     if args.sweep:
         run_sweep(max(5, args.steps // 2), 3)
+    if args.ops:
+        run_ops(args.steps, args.warmup)
     if args.select:
         for in_place in (False, True):
             log("SELECT " + json.dumps(run_select(args.steps, args.warmup, in_place)))
