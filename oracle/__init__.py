@@ -14,6 +14,9 @@ Functions:
     scan_f32(x, exclusive)  -> (y fp64, sabs fp64)
     scan(x, exclusive)      -> dispatch on x.dtype
     select_flagged(x, flags) -> the x[i] with flags[i] != 0, in order
+    partition_flagged(x, flags) -> (selected in order then rejected reversed, count)
+    reduce_by_key(keys, vals)   -> (unique keys, sums per run[, |value| sums per run])
+    run_length_encode(keys)     -> (unique keys, run lengths)
     scan_minmax(x, is_max, exclusive)        -> running max/min (int32 signed, uint32 unsigned)
     scan_pair_sum_u32 / scan_affine_u32 / scan_segsum_u32(x, exclusive)
                             -> (n, 2) uint32 pairs in, (n, 2) uint32 out
@@ -73,6 +76,14 @@ class OracleLib:
         lib.oracle_scan_f32.restype = ctypes.c_int
         lib.oracle_select_flagged.argtypes = [vp, vp, sz, vp]
         lib.oracle_select_flagged.restype = sz
+        lib.oracle_partition_flagged.argtypes = [vp, vp, sz, vp]
+        lib.oracle_partition_flagged.restype = sz
+        lib.oracle_reduce_by_key_u32.argtypes = [vp, vp, sz, vp, vp]
+        lib.oracle_reduce_by_key_u32.restype = sz
+        lib.oracle_reduce_by_key_f32.argtypes = [vp, vp, sz, vp, vp, vp]
+        lib.oracle_reduce_by_key_f32.restype = sz
+        lib.oracle_run_length_encode.argtypes = [vp, sz, vp, vp]
+        lib.oracle_run_length_encode.restype = sz
         ci = ctypes.c_int
         lib.oracle_scan_minmax.argtypes = [vp, sz, vp, ci, ci, ci]
         for name in ("oracle_scan_pair_sum_u32", "oracle_scan_affine_u32", "oracle_scan_segsum_u32"):
@@ -127,6 +138,48 @@ class OracleLib:
         cnt = self._lib.oracle_select_flagged(_ptr(x), _ptr(flags), x.size, _ptr(out))
         return out[:cnt]
 
+
+    # -- compaction family --------------------------------------------------
+
+    def partition_flagged(self, x: np.ndarray, flags: np.ndarray):
+        """(out, count): selected x in order, then the rejected ones reversed."""
+        x = np.ascontiguousarray(x)
+        flags = np.ascontiguousarray(flags, dtype=np.int32)
+        if x.itemsize != 4 or x.shape != flags.shape:
+            raise ValueError("x must hold 4-byte elements, one flag each")
+        out = np.empty_like(x)
+        cnt = self._lib.oracle_partition_flagged(_ptr(x), _ptr(flags), x.size, _ptr(out))
+        return out, int(cnt)
+
+    def reduce_by_key(self, keys: np.ndarray, vals: np.ndarray):
+        """Runs of equal 32-bit keys: (unique keys, aggregates[, |value| sums]).
+        float32 values give fp64 aggregates and the |value| sums; 32-bit
+        integer values give wrapped sums of the same dtype and no |value| sums."""
+        keys = np.ascontiguousarray(keys)
+        vals = np.ascontiguousarray(vals)
+        if keys.itemsize != 4 or vals.itemsize != 4 or keys.shape != vals.shape:
+            raise ValueError("keys and values are equal-length 4-byte arrays")
+        n = keys.size
+        uk = np.empty(n, dtype=np.uint32)
+        if vals.dtype == np.float32:
+            ag = np.empty(n, dtype=np.float64)
+            ab = np.empty(n, dtype=np.float64)
+            r = self._lib.oracle_reduce_by_key_f32(_ptr(keys), _ptr(vals), n, _ptr(uk), _ptr(ag), _ptr(ab))
+            return uk[:r].view(keys.dtype), ag[:r], ab[:r]
+        ag = np.empty(n, dtype=vals.dtype)
+        r = self._lib.oracle_reduce_by_key_u32(_ptr(keys), _ptr(vals), n, _ptr(uk), _ptr(ag))
+        return uk[:r].view(keys.dtype), ag[:r], None
+
+    def run_length_encode(self, keys: np.ndarray):
+        """Runs of equal 32-bit keys: (unique keys, uint32 lengths)."""
+        keys = np.ascontiguousarray(keys)
+        if keys.itemsize != 4:
+            raise ValueError("keys are 4-byte elements")
+        n = keys.size
+        uk = np.empty(n, dtype=np.uint32)
+        ln = np.empty(n, dtype=np.uint32)
+        r = self._lib.oracle_run_length_encode(_ptr(keys), n, _ptr(uk), _ptr(ln))
+        return uk[:r].view(keys.dtype), ln[:r]
 
     # -- generic operators ---------------------------------------------------
     # Pairs travel as (n, 2) uint32 arrays of bits: column 0 the first
@@ -226,6 +279,18 @@ def scan_f32(x, exclusive=False, want_sabs=True):
 
 def select_flagged(x, flags):
     return _oracle().select_flagged(x, flags)
+
+
+def partition_flagged(x, flags):
+    return _oracle().partition_flagged(x, flags)
+
+
+def reduce_by_key(keys, vals):
+    return _oracle().reduce_by_key(keys, vals)
+
+
+def run_length_encode(keys):
+    return _oracle().run_length_encode(keys)
 
 
 def scan_minmax(x, is_max, exclusive=False):

@@ -42,6 +42,9 @@
  * by numpy's maximum/minimum.accumulate and per-column cumsum, by running the
  * affine recurrence directly from several start values, by brute-force
  * segmented sums and by closed forms (a = 1, b = 0; all heads, no heads).
+ * Partition, reduce-by-key and run-length encoding are pinned by numpy's
+ * boolean masks, itertools.groupby, numpy's add.reduceat and diff over the run
+ * starts, and closed forms (one run, all distinct, keys as bit patterns).
  */
 #include <stddef.h>
 #include <stdint.h>
@@ -301,4 +304,84 @@ int oracle_scan_segsum_i32_f32(const uint32_t* x, size_t n, uint32_t* y_flag, do
         }
     }
     return 0;
+}
+
+/*
+ * The rest of the compaction family the single pass fuses with its scan
+ * (Merrill & Garland, section 4.4 in-place compaction behaviour; section A5:
+ * select-if, partition-if, reduce-by-key, run-length encoding). Plain
+ * sequential definitions.
+ */
+
+/* Partition by flags: the x[i] with a non-zero flag go to out[0 .. count) in
+ * input order, the others to out[count .. n) in reverse input order (the last
+ * rejected element first), which is the layout a single pass can write
+ * without knowing count in advance. Returns count. out must not alias x. */
+size_t oracle_partition_flagged(const uint32_t* x, const int32_t* flags, size_t n, uint32_t* out)
+{
+    size_t sel = 0, rej = 0;
+    for (size_t i = 0; i < n; ++i) {
+        if (flags[i] != 0) {
+            out[sel] = x[i];
+            ++sel;
+        } else {
+            out[n - 1 - rej] = x[i];
+            ++rej;
+        }
+    }
+    return sel;
+}
+
+/* Reduce by key: each maximal run of consecutive equal keys (32-bit patterns)
+ * gives one output: its key in ukeys[r] and the + of its values in aggs[r],
+ * runs in input order. Returns the number of runs. uint32 values wrap modulo
+ * 2^32. */
+size_t oracle_reduce_by_key_u32(const uint32_t* keys, const uint32_t* vals, size_t n, uint32_t* ukeys,
+                                uint32_t* aggs)
+{
+    size_t runs = 0;
+    for (size_t i = 0; i < n; ++i) {
+        if (i == 0 || keys[i] != keys[i - 1]) {
+            ukeys[runs] = keys[i];
+            aggs[runs] = 0u;
+            ++runs;
+        }
+        aggs[runs - 1] += vals[i];
+    }
+    return runs;
+}
+
+/* The same with fp32 values, summed in fp64; abs_sums[r] (may be NULL) is the
+ * sum of |value| over run r, which scales the fp32 tolerance. */
+size_t oracle_reduce_by_key_f32(const uint32_t* keys, const float* vals, size_t n, uint32_t* ukeys, double* aggs,
+                                double* abs_sums)
+{
+    size_t runs = 0;
+    for (size_t i = 0; i < n; ++i) {
+        if (i == 0 || keys[i] != keys[i - 1]) {
+            ukeys[runs] = keys[i];
+            aggs[runs] = 0.0;
+            if (abs_sums != NULL) abs_sums[runs] = 0.0;
+            ++runs;
+        }
+        aggs[runs - 1] += (double)vals[i];
+        if (abs_sums != NULL) abs_sums[runs - 1] += fabs((double)vals[i]);
+    }
+    return runs;
+}
+
+/* Run-length encoding: each maximal run of equal keys gives its key and its
+ * length. Returns the number of runs. */
+size_t oracle_run_length_encode(const uint32_t* keys, size_t n, uint32_t* ukeys, uint32_t* lengths)
+{
+    size_t runs = 0;
+    for (size_t i = 0; i < n; ++i) {
+        if (i == 0 || keys[i] != keys[i - 1]) {
+            ukeys[runs] = keys[i];
+            lengths[runs] = 0u;
+            ++runs;
+        }
+        lengths[runs - 1] += 1u;
+    }
+    return runs;
 }

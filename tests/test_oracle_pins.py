@@ -349,8 +349,58 @@ def _segsum_checks(lib, fail):
         fail("segsum no heads")
 
 
+def _compaction_family_checks(lib, fail):
+    import itertools
+    rng = np.random.default_rng(35)
+    for n in (1, 2, 7, 64, 1000):
+        x = rng.integers(-(2**31), 2**31, size=n, dtype=np.int64).astype(np.int32)
+        f = (rng.random(n) < 0.4).astype(np.int32) * rng.integers(-5, 6, size=n).astype(np.int32)
+        out, cnt = lib.partition_flagged(x, f)
+        # numpy's boolean indexing: selected in order, then rejected reversed
+        if cnt != int(np.count_nonzero(f)) or not np.array_equal(out[:cnt], x[f != 0]) or \
+                not np.array_equal(out[cnt:], x[f == 0][::-1]):
+            fail(f"partition n={n}")
+        # runs of keys drawn from a small alphabet, so that runs have length > 1
+        keys = rng.integers(0, 3, size=n).astype(np.int32)
+        vals = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+        groups = [(k, [int(vals[i]) for i, _ in g]) for k, g in itertools.groupby(enumerate(keys), key=lambda t: t[1])]
+        uk, ag, _ = lib.reduce_by_key(keys, vals)
+        if uk.tolist() != [int(k) for k, _ in groups] or ag.tolist() != [sum(v) & M32 for _, v in groups]:
+            fail(f"reduce by key (groupby) n={n}")
+        starts = np.concatenate([[0], np.flatnonzero(np.diff(keys) != 0) + 1])
+        if not np.array_equal(ag, (np.add.reduceat(vals.astype(np.uint64), starts) & M32).astype(np.uint32)):
+            fail(f"reduce by key (numpy reduceat) n={n}")
+        fv = (rng.integers(-512, 513, size=n) / 32.0).astype(np.float32)
+        ukf, agf, abf = lib.reduce_by_key(keys, fv)
+        want = [math.fsum(float(fv[i]) for i, _ in g) for _, g in itertools.groupby(enumerate(keys), key=lambda t: t[1])]
+        want_abs = [math.fsum(abs(float(fv[i])) for i, _ in g)
+                    for _, g in itertools.groupby(enumerate(keys), key=lambda t: t[1])]
+        if not np.array_equal(ukf, uk) or agf.tolist() != want or abf.tolist() != want_abs:
+            fail(f"reduce by key fp32 n={n}")
+        ur, ln = lib.run_length_encode(keys.view(np.uint32))
+        if ur.tolist() != [int(k) for k, _ in groups] or ln.tolist() != [len(v) for _, v in groups]:
+            fail(f"run-length encode n={n}")
+        if not np.array_equal(ln, np.diff(np.concatenate([starts, [n]]))):
+            fail(f"run-length encode (numpy diff) n={n}")
+    # closed forms: one run, all distinct, and keys compared as bit patterns
+    k1 = np.full(50, 7, dtype=np.uint32)
+    v = np.arange(50, dtype=np.uint32)
+    if lib.reduce_by_key(k1, v)[1].tolist() != [sum(range(50))] or lib.run_length_encode(k1)[1].tolist() != [50]:
+        fail("one run")
+    kd = np.arange(50, dtype=np.uint32)
+    if not np.array_equal(lib.reduce_by_key(kd, v)[1], v) or not np.all(lib.run_length_encode(kd)[1] == 1):
+        fail("all distinct")
+    zf = np.array([0.0, -0.0, -0.0, 0.0], dtype=np.float32).view(np.uint32)
+    if lib.run_length_encode(zf)[1].tolist() != [1, 2, 1]:
+        fail("keys are bit patterns")
+    sel_all, c_all = lib.partition_flagged(v, np.ones(50, np.int32))
+    sel_none, c_none = lib.partition_flagged(v, np.zeros(50, np.int32))
+    if c_all != 50 or not np.array_equal(sel_all, v) or c_none != 0 or not np.array_equal(sel_none, v[::-1]):
+        fail("partition all / none")
+
+
 def _generic_checks(lib, fail):
-    for f in (_minmax_checks, _pair_sum_checks, _affine_checks, _segsum_checks):
+    for f in (_minmax_checks, _pair_sum_checks, _affine_checks, _segsum_checks, _compaction_family_checks):
         try:
             f(lib, fail)
         except (IndexError, ValueError, RuntimeError) as e:   # a broken oracle may produce nonsense shapes
@@ -418,8 +468,9 @@ def test_select_flagged(lib):
     assert np.array_equal(y[:out], x[flags != 0])
 
 
-@pytest.mark.parametrize("checks", [_minmax_checks, _pair_sum_checks, _affine_checks, _segsum_checks],
-                         ids=["minmax", "pair_sum", "affine", "segsum"])
+@pytest.mark.parametrize("checks", [_minmax_checks, _pair_sum_checks, _affine_checks, _segsum_checks,
+                                    _compaction_family_checks],
+                         ids=["minmax", "pair_sum", "affine", "segsum", "compaction_family"])
 def test_generic_operators(lib, checks):
     failures = []
     checks(lib, failures.append)
@@ -500,6 +551,13 @@ MUTANTS = [
     ("segsum flag not accumulated", "F |= f;", "F = f;"),
     ("segsum fp restarts before the head", "            V = v;\n            S = fabs(v);",
      "            V = 0.0;\n            S = 0.0;"),
+    ("partition moves the wrong rejected element", "out[n - 1 - rej] = x[i];", "out[n - 1 - rej] = x[n - 1 - i];"),
+    ("runs start only on increasing keys", "if (i == 0 || keys[i] != keys[i - 1]) {",
+     "if (i == 0 || keys[i] > keys[i - 1]) {"),
+    ("run aggregate keeps only the last value", "aggs[runs - 1] += vals[i];", "aggs[runs - 1] = vals[i];"),
+    ("run |value| sum without abs", "abs_sums[runs - 1] += fabs((double)vals[i]);",
+     "abs_sums[runs - 1] += (double)vals[i];"),
+    ("run length counts one", "lengths[runs - 1] += 1u;", "lengths[runs - 1] = 1u;"),
 ]
 
 
