@@ -38,7 +38,8 @@ EXPORTED_SYMBOLS = (
     "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
-    "dws_scan_profiled", "dws_select_flagged", "dws_scan_op",
+    "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
+    "dws_run_length_encode",
 )
 
 
@@ -97,6 +98,12 @@ def load_library():
     lib.dws_scan_profiled.restype = ci
     lib.dws_scan_op.argtypes = [vp, vp, sz, ci, ci, ci, vp]
     lib.dws_scan_op.restype = ci
+    lib.dws_partition_flagged.argtypes = [vp, vp, vp, sz, ci, vp, vp]
+    lib.dws_partition_flagged.restype = ci
+    lib.dws_reduce_by_key.argtypes = [vp, vp, vp, vp, sz, ci, vp, vp]
+    lib.dws_reduce_by_key.restype = ci
+    lib.dws_run_length_encode.argtypes = [vp, vp, vp, sz, vp, vp]
+    lib.dws_run_length_encode.restype = ci
     lib.dws_select_flagged.argtypes = [vp, vp, vp, sz, ci, vp, vp]
     lib.dws_select_flagged.restype = ci
     lib.dws_selftest_wave.argtypes = [vp, vp, vp, sz, ci, vp]
@@ -298,6 +305,75 @@ def select_flagged(x, flags, out=None, count=None, stream=None):
         _check(select_flagged_ptr(x.data_ptr(), flags.data_ptr(), out.data_ptr(), x.numel(), code,
                                   count.data_ptr(), _stream(x, stream)), "dws_select_flagged")
     return out, count
+
+
+def _count_tensor(x, count):
+    import torch
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=x.device)
+    if count.dtype != torch.int64 or count.numel() < 1 or count.device != x.device:
+        raise ValueError("count must be an int64 tensor on the device of x")
+    return count
+
+
+def _check_like(t, x, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.device != x.device or \
+            t.numel() != x.numel() or t.element_size() != 4:
+        raise ValueError(f"{what} must be a contiguous 4-byte GPU tensor with the size and device of the keys")
+
+
+def partition_flagged(x, flags, out=None, count=None, stream=None):
+    """Partition by flags: out[:count] the selected elements in order,
+    out[count:] the rejected ones in reverse order. Returns (out, count) with
+    count a one-element int64 GPU tensor. out must not overlap x."""
+    import torch
+    code, _ = _prepare(x, x)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_like(out, x, "out")
+    _check_like(flags, x, "flags")
+    count = _count_tensor(x, count)
+    with _device_of(x):
+        _check(load_library().dws_partition_flagged(x.data_ptr(), flags.data_ptr(), out.data_ptr(), x.numel(), code,
+                                                    count.data_ptr(), _stream(x, stream)), "dws_partition_flagged")
+    return out, count
+
+
+def reduce_by_key(keys, values, unique_keys=None, aggregates=None, count=None, stream=None):
+    """Runs of equal keys (32-bit patterns): unique_keys[:r], aggregates[:r]
+    (+ of the values per run), r in the int64 GPU tensor ``count``."""
+    import torch
+    _check_like(keys, keys, "keys")
+    code = _dtype_code(values)
+    _check_like(values, keys, "values")
+    unique_keys = torch.empty_like(keys) if unique_keys is None else unique_keys
+    aggregates = torch.empty_like(values) if aggregates is None else aggregates
+    _check_like(unique_keys, keys, "unique_keys")
+    _check_like(aggregates, keys, "aggregates")
+    count = _count_tensor(keys, count)
+    with _device_of(keys):
+        _check(load_library().dws_reduce_by_key(keys.data_ptr(), values.data_ptr(), unique_keys.data_ptr(),
+                                                aggregates.data_ptr(), keys.numel(), code, count.data_ptr(),
+                                                _stream(keys, stream)), "dws_reduce_by_key")
+    return unique_keys, aggregates, count
+
+
+def run_length_encode(keys, unique_keys=None, lengths=None, count=None, stream=None):
+    """Runs of equal keys: unique_keys[:r], int32 tensor of uint32 lengths[:r],
+    r in the int64 GPU tensor ``count``."""
+    import torch
+    _check_like(keys, keys, "keys")
+    unique_keys = torch.empty_like(keys) if unique_keys is None else unique_keys
+    lengths = torch.empty(keys.numel(), dtype=torch.int32, device=keys.device) if lengths is None else lengths
+    _check_like(unique_keys, keys, "unique_keys")
+    _check_like(lengths, keys, "lengths")
+    count = _count_tensor(keys, count)
+    with _device_of(keys):
+        _check(load_library().dws_run_length_encode(keys.data_ptr(), unique_keys.data_ptr(), lengths.data_ptr(),
+                                                    keys.numel(), count.data_ptr(), _stream(keys, stream)),
+               "dws_run_length_encode")
+    return unique_keys, lengths, count
 
 
 def watchdog_trips() -> int:

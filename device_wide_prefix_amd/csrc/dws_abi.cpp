@@ -634,50 +634,170 @@ dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype 
     }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Compaction and partition by flags (one kernel, see dws_select.hip).
+dws_status select_entry(const void* d_in, const void* d_flags, void* d_out, size_t n, int dtype,
+                        unsigned long long* d_count, bool partition, hipStream_t stream)
+{
+    if (!valid_dtype(dtype)) return DWS_ERR_INVALID_ARG;
+    if (d_count == nullptr) return DWS_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_count) & 7u) != 0) return DWS_ERR_MISALIGNED;
+    if (n > kSelectMaxElems) return DWS_ERR_UNSUPPORTED;
+    if (n > 0) {
+        dws_status s = validate(d_in, d_out, n, dtype);
+        if (s != DWS_OK) return s;
+        s = validate(d_flags, d_flags, n, DWS_INT32);
+        if (s != DWS_OK) return s;
+        const uintptr_t f = reinterpret_cast<uintptr_t>(d_flags), o = reinterpret_cast<uintptr_t>(d_out);
+        const uintptr_t i = reinterpret_cast<uintptr_t>(d_in);
+        const uintptr_t c = reinterpret_cast<uintptr_t>(d_count), bytes = (uintptr_t)n * kElemBytes;
+        // the flags are read by later tiles while earlier ones write: no overlap with the output
+        if (f < o + bytes && o < f + bytes) return DWS_ERR_OVERLAP;
+        // a partition writes the back of the output before later tiles read their input
+        if (partition && i < o + bytes && o < i + bytes) return DWS_ERR_OVERLAP;
+        if ((c < o + bytes && o < c + 8) || (c < f + bytes && f < c + 8)) return DWS_ERR_OVERLAP;
+        if (c < i + bytes && i < c + 8) return DWS_ERR_OVERLAP;
+    }
+    SelectArgs a{};
+    a.in = d_in;
+    a.flags = d_flags;
+    a.out = d_out;
+    a.n = n;
+    a.count = d_count;
+    a.partition = partition;
+    a.aligned = ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out) |
+                  reinterpret_cast<uintptr_t>(d_flags)) & 15u) == 0;
+    const uint64_t tiles = n == 0 ? 0 : ceil_div(n, select_tile_elems(n, a.aligned));
+    a.num_tiles = (uint32_t)tiles;
+    if (tiles <= 1) return from_hip(launch_select(a, stream));
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_desc(ws, tiles);
+    if (s != DWS_OK) return s;
+    s = next_epoch(ws, &a.epoch);
+    if (s != DWS_OK) return s;
+    a.desc = ws->desc;
+    a.counter = ws->counter();
+    a.watchdog = ws->watchdog();
+    return from_hip(launch_select(a, stream));
+}
+
+bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + b_bytes && y < x + a_bytes;
+}
+
+// Reduce-by-key and run-length encoding (mode 0 integer values, 1 fp32
+// values, 2 run lengths without values).
+dws_status rbk_entry(const void* keys, const void* vals, void* ukeys, void* aggs, size_t n, int mode,
+                     unsigned long long* num_runs, hipStream_t stream)
+{
+    if (num_runs == nullptr) return DWS_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(num_runs) & 7u) != 0) return DWS_ERR_MISALIGNED;
+    if (n > kSelectMaxElems) return DWS_ERR_UNSUPPORTED;
+    if (n > 0) {
+        const void* in_arrays[2] = {keys, vals};
+        void* out_arrays[2] = {ukeys, aggs};
+        const int n_in = mode == 2 ? 1 : 2;
+        for (int k = 0; k < n_in; ++k) {
+            const dws_status s = validate_sized(in_arrays[k], in_arrays[k], n, kElemBytes);
+            if (s != DWS_OK) return s;
+        }
+        for (int k = 0; k < 2; ++k) {
+            const dws_status s = validate_sized(out_arrays[k], out_arrays[k], n, kElemBytes);
+            if (s != DWS_OK) return s;
+        }
+        const size_t bytes = n * kElemBytes;
+        // outputs are written while later tiles still read keys around them
+        for (int k = 0; k < n_in; ++k)
+            for (int m = 0; m < 2; ++m)
+                if (overlaps(in_arrays[k], bytes, out_arrays[m], bytes)) return DWS_ERR_OVERLAP;
+        if (overlaps(ukeys, bytes, aggs, bytes)) return DWS_ERR_OVERLAP;
+        for (int m = 0; m < 2; ++m)
+            if (overlaps(num_runs, 8, out_arrays[m], bytes)) return DWS_ERR_OVERLAP;
+        for (int k = 0; k < n_in; ++k)
+            if (overlaps(num_runs, 8, in_arrays[k], bytes)) return DWS_ERR_OVERLAP;
+    }
+    RbkArgs a{};
+    a.keys = keys;
+    a.vals = vals;
+    a.ukeys = ukeys;
+    a.aggs = aggs;
+    a.n = n;
+    a.mode = mode;
+    a.num_runs = num_runs;
+    a.aligned = ((reinterpret_cast<uintptr_t>(keys) | (mode == 2 ? 0u : reinterpret_cast<uintptr_t>(vals))) & 15u) == 0;
+    a.tile_index = (a.aligned && n >= kAutoDrawnMin) ? kTileDrawn : kTileDispatch;
+    const uint64_t tiles = n == 0 ? 0 : ceil_div(n, rbk_tile_elems(n, a.aligned));
+    a.num_tiles = (uint32_t)tiles;
+    if (tiles <= 1) return from_hip(launch_rbk(a, stream));
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_desc(ws, 2 * tiles);
+    if (s != DWS_OK) return s;
+    s = next_epoch(ws, &a.epoch);
+    if (s != DWS_OK) return s;
+    a.desc = ws->desc;
+    a.counter = ws->counter();
+    a.watchdog = ws->watchdog();
+    return from_hip(launch_rbk(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+dws_status dws_reduce_by_key(const void* d_keys, const void* d_values, void* d_unique_keys, void* d_aggregates,
+                             size_t n, dws_dtype value_dtype, unsigned long long* d_num_runs, hipStream_t stream)
+{
+    try {
+        if (!valid_dtype((int)value_dtype)) return DWS_ERR_INVALID_ARG;
+        return rbk_entry(d_keys, d_values, d_unique_keys, d_aggregates, n, value_dtype == DWS_FLOAT32 ? 1 : 0,
+                         d_num_runs, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_run_length_encode(const void* d_keys, void* d_unique_keys, void* d_lengths, size_t n,
+                                 unsigned long long* d_num_runs, hipStream_t stream)
+{
+    try {
+        return rbk_entry(d_keys, nullptr, d_unique_keys, d_lengths, n, 2, d_num_runs, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
 dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out, size_t n, dws_dtype dtype,
                               unsigned long long* d_count, hipStream_t stream)
 {
     try {
-        if (!valid_dtype((int)dtype)) return DWS_ERR_INVALID_ARG;
-        if (d_count == nullptr) return DWS_ERR_INVALID_ARG;
-        if ((reinterpret_cast<uintptr_t>(d_count) & 7u) != 0) return DWS_ERR_MISALIGNED;
-        if (n > kSelectMaxElems) return DWS_ERR_UNSUPPORTED;
-        if (n > 0) {
-            dws_status s = validate(d_in, d_out, n, (int)dtype);
-            if (s != DWS_OK) return s;
-            s = validate(d_flags, d_flags, n, DWS_INT32);
-            if (s != DWS_OK) return s;
-            const uintptr_t f = reinterpret_cast<uintptr_t>(d_flags), o = reinterpret_cast<uintptr_t>(d_out);
-            const uintptr_t c = reinterpret_cast<uintptr_t>(d_count), bytes = (uintptr_t)n * kElemBytes;
-            // the flags are read by later tiles while earlier ones write: no overlap with the output
-            if (f < o + bytes && o < f + bytes) return DWS_ERR_OVERLAP;
-            if ((c < o + bytes && o < c + 8) || (c < f + bytes && f < c + 8)) return DWS_ERR_OVERLAP;
-            const uintptr_t i = reinterpret_cast<uintptr_t>(d_in);
-            if (c < i + bytes && i < c + 8) return DWS_ERR_OVERLAP;
-        }
-        SelectArgs a{};
-        a.in = d_in;
-        a.flags = d_flags;
-        a.out = d_out;
-        a.n = n;
-        a.count = d_count;
-        a.aligned = ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out) |
-                      reinterpret_cast<uintptr_t>(d_flags)) & 15u) == 0;
-        const uint64_t tiles = n == 0 ? 0 : ceil_div(n, select_tile_elems(n, a.aligned));
-        a.num_tiles = (uint32_t)tiles;
-        if (tiles <= 1) return from_hip(launch_select(a, stream));
-        Workspace* ws = nullptr;
-        dws_status s = get_workspace(stream, &ws);
-        if (s != DWS_OK) return s;
-        std::lock_guard<std::mutex> lock(ws->mu);
-        s = ensure_desc(ws, tiles);
-        if (s != DWS_OK) return s;
-        s = next_epoch(ws, &a.epoch);
-        if (s != DWS_OK) return s;
-        a.desc = ws->desc;
-        a.counter = ws->counter();
-        a.watchdog = ws->watchdog();
-        return from_hip(launch_select(a, stream));
+        return select_entry(d_in, d_flags, d_out, n, (int)dtype, d_count, false, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_partition_flagged(const void* d_in, const void* d_flags, void* d_out, size_t n, dws_dtype dtype,
+                                 unsigned long long* d_num_selected, hipStream_t stream)
+{
+    try {
+        return select_entry(d_in, d_flags, d_out, n, (int)dtype, d_num_selected, true, stream);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

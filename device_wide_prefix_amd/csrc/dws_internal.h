@@ -84,6 +84,7 @@ struct SelectArgs {
     unsigned long long* count;
     uint32_t num_tiles;
     uint32_t epoch;
+    bool partition;          // also write the rejected elements, reversed, at the back
 };
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
 constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
@@ -106,6 +107,28 @@ struct DebugArgs {
     uint32_t epoch;
 };
 hipError_t launch_debug(const DebugArgs& a, hipStream_t stream);
+
+// Reduce-by-key / run-length encoding (dws_rbk.hip). mode: 0 integer sums,
+// 1 fp32 sums, 2 run lengths (vals unused).
+struct RbkArgs {
+    const void* keys;
+    const void* vals;
+    void* ukeys;
+    void* aggs;
+    uint64_t n;
+    int mode;
+    bool aligned;            // keys (and vals) 16-byte aligned
+    int tile_index;
+    uint64_t* desc;          // >= 2 * num_tiles slots
+    unsigned long long* counter;
+    unsigned int* watchdog;
+    unsigned long long* num_runs;
+    uint32_t num_tiles;
+    uint32_t epoch;
+};
+constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384-element tiles (512 threads) from here
+uint32_t rbk_tile_elems(uint64_t n, bool aligned);
+hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream);
 
 // Scan under a generic operator (dws_op_kernel.hpp). Kinds name an
 // (operator, element type) pair; pair elements are two 32-bit words.

@@ -1,0 +1,241 @@
+// Reduce-by-key and run-length encoding fused with the single-pass decoupled
+// look-back (Merrill & Garland, section 4.4 compaction behaviour; section A5,
+// reduce-by-key and run-length-encode).
+//
+// Per element i: head(i) = (i == 0 or key[i] != key[i-1]), tail(i) =
+// (i == n-1 or key[i] != key[i+1]). The scan runs over pairs (heads, value)
+// under "count the heads, restart the value sum after the last head" (a
+// segmented sum, not commutative), so after the look-back every element knows
+// its run index heads_incl(i) - 1 and the sum of its run up to i. Heads store
+// their key to unique_keys[run], tails store the run's sum to aggregates[run];
+// the last tile stores the number of runs. Values are 32-bit integers (sums
+// wrap modulo 2^32), fp32, or the constant 1 (run-length encoding: the sum is
+// the run length).
+//
+// The neighbours key[i-1] and key[i+1] come from the registers of the same
+// lane, the adjacent lane (DPP wave shift), the adjacent chunk (readlane) or,
+// at a wave segment's two ends, one extra 4-byte load each. Stores go through
+// per-tile buffer resources ranged to the tile's runs; lanes without a store
+// use an offset past that range, which the hardware drops.
+#include "dws_op_kernel.hpp"
+
+namespace dws {
+
+// (heads so far, running value since the last head); q restarts the value
+// when it holds a head.
+template <bool FLOAT>
+struct OpRunSum {
+    static constexpr int kWords = 2;
+    using V = Val<2>;
+    static __device__ __forceinline__ V identity() { return {{0u, 0u}}; }
+    static __device__ __forceinline__ V combine(V p, V q)
+    {
+        uint32_t sum;
+        if constexpr (FLOAT) sum = f2u(u2f(p.w[1]) + u2f(q.w[1]));
+        else sum = p.w[1] + q.w[1];
+        return {{p.w[0] + q.w[0], q.w[0] != 0u ? q.w[1] : sum}};
+    }
+};
+
+struct RbkParams {
+    const uint32_t* keys;
+    const uint32_t* vals;     // unused for run-length encoding
+    uint32_t* ukeys;
+    uint32_t* aggs;           // sums, or run lengths
+    uint64_t n;
+    uint64_t* desc;
+    unsigned long long* counter;
+    unsigned int* watchdog;
+    unsigned long long* num_runs;
+    uint32_t num_tiles;
+    uint32_t epoch;
+};
+
+constexpr uint32_t kRbkDropped = 0x80000000u;   // past any tile's range: dropped
+constexpr int kDppWaveShl1 = 0x130;              // lane l reads lane l + 1
+
+// Value mode: 0 integer sums, 1 fp32 sums, 2 run lengths.
+template <int BLOCK, int VEC, int CHUNKS, int MODE, int TILE_INDEX>
+__global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
+{
+    static_assert(VEC * CHUNKS <= 64, "one head and one tail bit per element in a 64-bit mask");
+    using Op = OpRunSum<MODE == 1>;
+    using V = Val<2>;
+    constexpr int W = BLOCK / 64;
+    constexpr uint32_t SEG = 64u * VEC * CHUNKS;
+    constexpr uint32_t TILE = W * SEG;
+    __shared__ uint32_t s_draw;
+    __shared__ V s_wave[W];
+    __shared__ V s_prefix;
+
+    const int lane = lane_id();
+    const int wave = (int)uniform(threadIdx.x >> 6);
+    const bool multi = p.num_tiles > 1u;
+    const uint32_t epoch = p.epoch;
+
+    uint32_t tile = 0u;
+    if (multi) {
+        if constexpr (TILE_INDEX == kTileDispatch) {
+            tile = blockIdx.x;
+        } else {
+            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            __syncthreads();
+            tile = uniform(s_draw);
+            if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
+                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
+                return;
+            }
+        }
+    }
+
+    const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
+    const uint32_t vb = valid_bytes(seg_first, SEG, p.n);
+    uint32_t k[CHUNKS][VEC];
+    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.keys + seg_first, vb), lane, k);
+    uint32_t v[CHUNKS][VEC];
+    if constexpr (MODE != 2) load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.vals + seg_first, vb), lane, v);
+    // the keys just outside the wave segment (0-byte ranges where there is none)
+    const bool has_prev = seg_first > 0u && seg_first <= p.n;
+    const bool has_next = seg_first + SEG < p.n;
+    const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
+    const uint32_t next_key = __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(p.keys + (has_next ? seg_first + SEG : 0u), has_next ? 4u : 0u), 0, 0, 0);
+
+    // head and tail bits, scan input
+    uint64_t heads = 0ull, tails = 0ull;
+    V x[CHUNKS][VEC];
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
+                                                                         0xf, true);
+        const uint32_t from_right = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][0], kDppWaveShl1, 0xf,
+                                                                          0xf, true);
+        const uint32_t left_edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : prev_key;
+        const uint32_t right_edge =
+            c < CHUNKS - 1 ? (uint32_t)__builtin_amdgcn_readlane((int)k[(c + 1) % CHUNKS][0], 0) : next_key;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint64_t i = seg_first + (uint64_t)(c * 64 * VEC) + (uint64_t)(lane * VEC + e);
+            const bool valid = i < p.n;
+            const uint32_t prev = e > 0 ? k[c][e - 1] : (lane > 0 ? from_left : left_edge);
+            const uint32_t next = e < VEC - 1 ? k[c][e + 1] : (lane < 63 ? from_right : right_edge);
+            const bool head = valid && (i == 0u || k[c][e] != prev);
+            const bool tail = valid && (i + 1u == p.n || k[c][e] != next);
+            heads |= (uint64_t)head << (c * VEC + e);
+            tails |= (uint64_t)tail << (c * VEC + e);
+            uint32_t val;
+            if constexpr (MODE == 2) val = valid ? 1u : 0u;
+            else val = valid ? v[c][e] : 0u;
+            x[c][e] = {{head ? 1u : 0u, val}};
+        }
+    }
+
+    const V seg_total = scan_segment_op<Op, false, VEC, CHUNKS>(x);
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            asm volatile("" : "+v"(x[c][e].w[0]));
+            asm volatile("" : "+v"(x[c][e].w[1]));
+        }
+
+    if (lane == 0) s_wave[wave] = seg_total;
+    __syncthreads();
+    V wave_pre = Op::identity(), agg = Op::identity();
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        if (w == wave) wave_pre = agg;
+        agg = Op::combine(agg, s_wave[w]);
+    }
+
+    if (wave == 0) {
+        V prefix = Op::identity();
+        if (multi) {
+            if (tile == 0u) {
+                if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
+            } else {
+                if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
+                prefix = lookback_op<Op, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
+                if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+            }
+        }
+        if (lane == 0) s_prefix = prefix;
+    }
+    __syncthreads();
+    const V tile_prefix = s_prefix;
+    const V seed = Op::combine(tile_prefix, wave_pre);
+
+    // runs this tile can write: the one running into it (if any) and its own
+    const uint32_t heads_before = tile_prefix.w[0];
+    const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
+    const uint32_t range = (agg.w[0] + 1u) * 4u;
+    const __amdgpu_buffer_rsrc_t rkeys = make_rsrc(p.ukeys + base_run, range);
+    const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, range);
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const V y = Op::combine(seed, x[c][e]);
+            const uint32_t run_off = (y.w[0] - 1u - base_run) * 4u;
+            const int bit = c * VEC + e;
+            const uint32_t koff = ((heads >> bit) & 1ull) ? run_off : kRbkDropped;
+            const uint32_t aoff = ((tails >> bit) & 1ull) ? run_off : kRbkDropped;
+            __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(y.w[1], raggs, (int)aoff, 0, 0);
+        }
+    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + agg.w[0];
+}
+
+__global__ void __launch_bounds__(64) k_store_runs(unsigned long long* count)
+{
+    if (threadIdx.x == 0) *count = 0ull;
+}
+
+template <int BLOCK, int VEC, int CHUNKS, int MODE>
+static hipError_t launch_rbk_mode(int tile_index, const RbkParams& p, hipStream_t stream)
+{
+    RbkParams arg = p;
+    void* args[] = {&arg};
+    const void* fn = tile_index == kTileDrawn
+                         ? reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDrawn>)
+                         : reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>);
+    return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
+}
+
+template <int BLOCK, int VEC, int CHUNKS>
+static hipError_t launch_rbk_shape(int mode, int tile_index, const RbkParams& p, hipStream_t stream)
+{
+    switch (mode) {
+    case 0: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 0>(tile_index, p, stream);
+    case 1: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 1>(tile_index, p, stream);
+    case 2: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 2>(tile_index, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+uint32_t rbk_tile_elems(uint64_t n, bool aligned)
+{
+    if (!aligned) return 256u * 16u;
+    return n >= kRbkLargeMin ? 512u * 4u * 8u : 256u * 4u * 4u;
+}
+
+hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
+{
+    if (a.n == 0) {
+        unsigned long long* c = a.num_runs;
+        void* args[] = {&c};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&k_store_runs), dim3(1), dim3(64), args, 0, stream);
+    }
+    RbkParams p{static_cast<const uint32_t*>(a.keys), static_cast<const uint32_t*>(a.vals),
+                static_cast<uint32_t*>(a.ukeys),      static_cast<uint32_t*>(a.aggs),
+                a.n,                                  a.desc,
+                a.counter,                            a.watchdog,
+                a.num_runs,                           a.num_tiles,
+                a.epoch};
+    if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, kTileDispatch, p, stream);
+    if (a.n >= kRbkLargeMin) return launch_rbk_shape<512, 4, 8>(a.mode, a.tile_index, p, stream);
+    return launch_rbk_shape<256, 4, 4>(a.mode, kTileDispatch, p, stream);
+}
+
+}  // namespace dws

@@ -19,6 +19,12 @@
 // Writes of tile t land in [prefix_t, prefix_t + count_t), below the end of
 // tile t, and start only after every earlier tile has published (so has read
 // its input): in place is safe.
+//
+// Partition (section A5, partition-if) is the same kernel with one more
+// store: the rejected elements go to the back of the output in reverse input
+// order, element i to out[n - 1 - (number of rejected elements before i)],
+// which needs no total count. Those writes land past the input's unread part,
+// so the partition is never in place.
 #include "dws_device.hpp"
 #include "dws_internal.h"
 
@@ -41,7 +47,7 @@ struct SelectParams {
 // buffer range check drops the store. Offset plus store size stays below 2^32.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
-template <int BLOCK, int VEC, int CHUNKS>
+template <int BLOCK, int VEC, int CHUNKS, bool PARTITION>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
     static_assert(VEC * CHUNKS <= 32, "one selection bit per element in a 32-bit mask");
@@ -123,6 +129,26 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
             const uint32_t off = sel ? (wave_pre + r[c][e]) * 4u : kDroppedOffset;
             __builtin_amdgcn_raw_buffer_store_b32(x[c][e], rout, (int)off, 0, 0);
         }
+    if constexpr (PARTITION) {
+        // rejected elements of the tile: rank rr among them (in-tile index
+        // minus selected before it), stored at base + (rejected - 1 - rr)
+        const uint64_t tile_first = (uint64_t)tile * TILE;
+        const uint64_t left = p.n - tile_first;
+        const uint32_t valid_local = left < TILE ? (uint32_t)left : TILE;
+        const uint32_t rejected = valid_local - count;
+        const uint64_t rejected_before = tile_first - prefix;
+        const __amdgpu_buffer_rsrc_t rrej = make_rsrc(p.out + (p.n - rejected_before - rejected), rejected * 4u);
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t local = (uint32_t)wave * SEG + (uint32_t)(c * 64 * VEC) + (uint32_t)(lane * VEC + e);
+                const bool sel = (selected >> (c * VEC + e)) & 1u;
+                const uint32_t rr = local - (wave_pre + r[c][e]);
+                const uint32_t off = (!sel && local < valid_local) ? (rejected - 1u - rr) * 4u : kDroppedOffset;
+                __builtin_amdgcn_raw_buffer_store_b32(x[c][e], rrej, (int)off, 0, 0);
+            }
+    }
     if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.count = (unsigned long long)prefix + count;
 }
 
@@ -161,12 +187,27 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
                    a.epoch};
     void* args[] = {&p};
     const void* fn = nullptr;
-    if (!a.aligned)
-        fn = reinterpret_cast<const void*>(&k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks>);
-    else if (s.threads == kSelectLarge.threads)
-        fn = reinterpret_cast<const void*>(&k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks>);
-    else
-        fn = reinterpret_cast<const void*>(&k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks>);
+    if (a.partition) {
+        if (!a.aligned)
+            fn = reinterpret_cast<const void*>(
+                &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, true>);
+        else if (s.threads == kSelectLarge.threads)
+            fn = reinterpret_cast<const void*>(
+                &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, true>);
+        else
+            fn = reinterpret_cast<const void*>(
+                &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, true>);
+    } else {
+        if (!a.aligned)
+            fn = reinterpret_cast<const void*>(
+                &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, false>);
+        else if (s.threads == kSelectLarge.threads)
+            fn = reinterpret_cast<const void*>(
+                &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, false>);
+        else
+            fn = reinterpret_cast<const void*>(
+                &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, false>);
+    }
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 

@@ -194,6 +194,45 @@ dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out
                               dws_dtype dtype, unsigned long long* d_count,
                               hipStream_t stream);
 
+/*
+ * Partition by flags (Merrill & Garland, section A5, partition-if), fused with
+ * the single-pass scan like dws_select_flagged: the d_in[i] with a non-zero
+ * 32-bit flag go to d_out[0 .. count) in input order, the others to
+ * d_out[count .. n) in reverse input order (the last rejected element at
+ * d_out[count]), a layout one pass writes without knowing count in advance.
+ * count goes to the DEVICE word *d_num_selected (64-bit, 8-byte aligned).
+ * d_out must not overlap d_in or d_flags (DWS_ERR_OVERLAP): rejected elements
+ * land at the back before later tiles have read it. Other rules as for
+ * dws_select_flagged (n below 2^32, values moved as 32-bit words).
+ */
+dws_status dws_partition_flagged(const void* d_in, const void* d_flags, void* d_out, size_t n,
+                                 dws_dtype dtype, unsigned long long* d_num_selected,
+                                 hipStream_t stream);
+
+/*
+ * Reduce by key (Merrill & Garland, section A5, reduce-by-key), one
+ * single-pass launch: every maximal run of consecutive equal keys (compared
+ * as 32-bit patterns, so +0.0 and -0.0 differ) gives its key in
+ * d_unique_keys[r] and the + of its values in d_aggregates[r], runs in input
+ * order; the number of runs goes to the DEVICE word *d_num_runs (64-bit,
+ * 8-byte aligned). value_dtype DWS_INT32 / DWS_UINT32 sums wrap modulo 2^32,
+ * DWS_FLOAT32 sums in fp32 (rounding order depends on scheduling). Arrays hold
+ * n 4-byte elements (outputs need room for n); outputs must not overlap the
+ * inputs, each other or the count word. n below 2^32. Elements of the outputs
+ * at and past the number of runs are left unchanged.
+ */
+dws_status dws_reduce_by_key(const void* d_keys, const void* d_values, void* d_unique_keys,
+                             void* d_aggregates, size_t n, dws_dtype value_dtype,
+                             unsigned long long* d_num_runs, hipStream_t stream);
+
+/*
+ * Run-length encoding (Merrill & Garland, section A5, run-length-encode):
+ * reduce-by-key with every value 1. d_lengths receives uint32 run lengths.
+ * Same rules as dws_reduce_by_key.
+ */
+dws_status dws_run_length_encode(const void* d_keys, void* d_unique_keys, void* d_lengths, size_t n,
+                                 unsigned long long* d_num_runs, hipStream_t stream);
+
 /* Associative operators of dws_scan_op. The single pass only ever combines
  * contiguous inputs or contiguous partial results, earlier operand first, so
  * an operator need not be commutative (Merrill & Garland, section 4.2). */

@@ -167,6 +167,20 @@ def op_input(kind: str, n: int, seed: int, head_density: float = 0.01) -> np.nda
     return out
 
 
+def run_keys(n: int, mean_run: float, seed: int) -> np.ndarray:
+    """uint32 keys in runs: each element starts a new run with probability
+    1 / mean_run (element 0 always does); run r gets the key r * 2654435761
+    mod 2^32, so adjacent runs differ. mean_run = 1 gives all-distinct keys,
+    mean_run >= n typically one run."""
+    rng = np.random.default_rng(seed)
+    n = int(n)
+    starts = rng.random(n) < (1.0 / mean_run)
+    if n:
+        starts[0] = True
+    run = np.cumsum(starts, dtype=np.uint64) - np.uint64(1)
+    return ((run * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+
+
 def generate(dist: str, n: int, seed: int) -> np.ndarray:
     """Draw ``n`` values of distribution ``dist`` from PCG64(seed)."""
     rng = np.random.default_rng(seed)

@@ -241,3 +241,41 @@ def test_scan_op_binding_checks(lib):
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         dws.scan_op(torch.zeros((4, 2), dtype=torch.int32), dws.OP_AFFINE, dws.PAIR_U32)
+
+
+def test_partition_validation(lib):
+    f = lib.dws_partition_flagged
+    cnt = FAKE + (1 << 24)
+    n = 1000
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, 9, cnt, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, None, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, cnt + 4, None) == dws.ERR_MISALIGNED
+    # never in place: the output must not overlap the input
+    assert f(FAKE, FAKE + 8192, FAKE, n, dws.INT32, cnt, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + 8192, FAKE + 16384, n, dws.INT32, FAKE + 16384 + 8, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + 8192, FAKE + 8192, n, dws.INT32, cnt, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + (1 << 36), FAKE + (2 << 36), 1 << 32, dws.INT32, cnt, None) == dws.ERR_UNSUPPORTED
+
+
+def test_reduce_by_key_and_rle_validation(lib):
+    r = lib.dws_reduce_by_key
+    e = lib.dws_run_length_encode
+    K, V, UK, AG, C = FAKE, FAKE + 8192, FAKE + 16384, FAKE + 24576, FAKE + (1 << 24)
+    n = 1000
+    assert r(K, V, UK, AG, n, 7, C, None) == dws.ERR_INVALID_ARG
+    assert r(K, V, UK, AG, n, dws.INT32, None, None) == dws.ERR_INVALID_ARG
+    assert r(K, V, UK, AG, n, dws.INT32, C + 4, None) == dws.ERR_MISALIGNED
+    assert r(None, V, UK, AG, n, dws.INT32, C, None) == dws.ERR_INVALID_ARG
+    assert r(K, V, UK, None, n, dws.FLOAT32, C, None) == dws.ERR_INVALID_ARG
+    assert r(K + 2, V, UK, AG, n, dws.INT32, C, None) == dws.ERR_MISALIGNED
+    # no output may overlap an input, the other output or the count word
+    assert r(K, V, K, AG, n, dws.INT32, C, None) == dws.ERR_OVERLAP
+    assert r(K, V, UK, V + 400, n, dws.INT32, C, None) == dws.ERR_OVERLAP
+    assert r(K, V, UK, UK + 40, n, dws.INT32, C, None) == dws.ERR_OVERLAP
+    assert r(K, V, UK, AG, n, dws.INT32, UK + 8, None) == dws.ERR_OVERLAP
+    assert r(K, V, UK, AG, n, dws.INT32, K + 8, None) == dws.ERR_OVERLAP
+    assert r(K, V, UK, AG, 1 << 32, dws.INT32, C + (1 << 40), None) == dws.ERR_UNSUPPORTED
+    assert e(K, UK, AG, n, None, None) == dws.ERR_INVALID_ARG
+    assert e(K, K + 3996, AG, n, C, None) == dws.ERR_OVERLAP
+    assert e(K, UK, UK, n, C, None) == dws.ERR_OVERLAP
+    assert e(K + 1, UK, AG, n, C, None) == dws.ERR_MISALIGNED
