@@ -21,7 +21,8 @@ Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained|scan_
 (N = 2^10..2^30, every variant and memcpy, cold and warm caches; stderr),
 --select (stream compaction on the 2^30-12345 flag workload; stderr), --ops
 (generic-operator scans: max, min, {int32, fp32} pair sum, affine maps,
-segmented sum, on 1 GiB inputs; stderr).
+segmented sum, on 1 GiB inputs; stderr), --compaction (select, partition,
+reduce-by-key, run-length encoding on 2^25 items, beside PyTorch; stderr).
 """
 from __future__ import annotations
 
@@ -349,6 +350,96 @@ def run_ops(steps: int, warmup: int):
     return rows
 
 
+COMPACTION_N = 1 << 25   # the 32M-item size the pages measure the compaction family on
+
+
+def run_compaction(steps: int, warmup: int):
+    """Select, partition, reduce-by-key and run-length encoding on 2^25 items,
+    cold caches, each beside the nearest PyTorch equivalent on the same data.
+    GB/s counts the algorithmic bytes: select 8n + 4 count, partition 12n,
+    reduce-by-key 8n + 8 runs, run-length encoding 4n + 8 runs. One COMPACTION
+    line per case on stderr."""
+    import torch
+    import device_wide_prefix_amd as dws
+    n = COMPACTION_N
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    dws.reserve(n)
+    lib = dws.load_library()
+
+    def prepare():
+        flush.sum()
+
+    def emit(name, ms, algo_bytes, torch_ms, ok, extra):
+        row = {"op": name, "n": n, "ms_mean": ms, "gbps": algo_bytes / (ms * 1e-3) / 1e9,
+               "frac_hbm_peak": algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "torch_ms_mean": torch_ms,
+               "speedup_vs_torch": (torch_ms / ms) if torch_ms else None, "property_check": bool(ok), **extra}
+        log("COMPACTION " + json.dumps(row))
+
+    x = torch.from_numpy(wl.generate("i32_full", n, 21)).cuda()
+    flags = torch.from_numpy(wl.generate("flags_half", n, 22)).cuda()
+    mask = flags != 0
+    out = torch.empty_like(x)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for name, fn in (("select_flagged", lib.dws_select_flagged), ("partition_flagged", lib.dws_partition_flagged)):
+        def run(fn=fn):
+            st = fn(x.data_ptr(), flags.data_ptr(), out.data_ptr(), n, dws.INT32, cnt.data_ptr(), stream)
+            if st != dws.OK:
+                raise RuntimeError(f"{name}: {dws.status_string(st)}")
+        ms = float(np.mean(time_steps(run, prepare, steps, warmup)))
+        c = int(cnt.item())
+        ok = c == int(mask.sum().item()) and torch.equal(out[:c], x[mask])
+        if name == "partition_flagged":
+            ok = ok and torch.equal(out[c:], x[~mask].flip(0))
+            t = float(np.mean(time_steps(lambda: torch.cat((x[mask], x[~mask].flip(0))), prepare, steps, warmup)))
+            emit(name, ms, 12 * n, t, ok, {"selected": c, "torch": "cat(x[mask], x[~mask].flip(0))"})
+        else:
+            t = float(np.mean(time_steps(lambda: torch.masked_select(x, mask), prepare, steps, warmup)))
+            emit(name, ms, 8 * n + 4 * c, t, ok, {"selected": c, "torch": "masked_select"})
+    del x, flags, mask, out
+    vals = torch.from_numpy(wl.generate("i32_full", n, 23)).cuda()
+    uk = torch.empty(n, dtype=torch.int32, device="cuda")
+    ag = torch.empty(n, dtype=torch.int32, device="cuda")
+    for mean_run in (1, 16):
+        keys = torch.from_numpy(wl.run_keys(n, mean_run, 24).view(np.int32)).cuda()
+        ref_keys, inverse, counts = torch.unique_consecutive(keys, return_inverse=True, return_counts=True)
+        runs = ref_keys.numel()
+
+        def rbk():
+            st = lib.dws_reduce_by_key(keys.data_ptr(), vals.data_ptr(), uk.data_ptr(), ag.data_ptr(), n,
+                                       dws.INT32, cnt.data_ptr(), stream)
+            if st != dws.OK:
+                raise RuntimeError(dws.status_string(st))
+
+        def rle():
+            st = lib.dws_run_length_encode(keys.data_ptr(), uk.data_ptr(), ag.data_ptr(), n, cnt.data_ptr(), stream)
+            if st != dws.OK:
+                raise RuntimeError(dws.status_string(st))
+
+        def torch_rbk():
+            k, inv = torch.unique_consecutive(keys, return_inverse=True)
+            torch.zeros(k.numel(), dtype=torch.int64, device="cuda").index_add_(0, inv, vals.long())
+
+        ms = float(np.mean(time_steps(rbk, prepare, steps, warmup)))
+        want = torch.zeros(runs, dtype=torch.int64, device="cuda").index_add_(0, inverse, vals.long())
+        want = (want & 0xFFFFFFFF).to(torch.int64)
+        ok = int(cnt.item()) == runs and torch.equal(uk[:runs], ref_keys) and \
+            torch.equal(ag[:runs].to(torch.int64) & 0xFFFFFFFF, want)
+        t = float(np.mean(time_steps(torch_rbk, prepare, steps, warmup)))
+        emit("reduce_by_key", ms, 8 * n + 8 * runs, t, ok,
+             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_"})
+        ms = float(np.mean(time_steps(rle, prepare, steps, warmup)))
+        ok = int(cnt.item()) == runs and torch.equal(uk[:runs], ref_keys) and \
+            torch.equal(ag[:runs].to(torch.int64), counts)
+        t = float(np.mean(time_steps(lambda: torch.unique_consecutive(keys, return_counts=True), prepare, steps,
+                                     warmup)))
+        emit("run_length_encode", ms, 4 * n + 8 * runs, t, ok,
+             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive(return_counts=True)"})
+        del keys, ref_keys, inverse, counts
+    del vals, uk, ag, flush
+    torch.cuda.empty_cache()
+
+
 def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
     """The sequential oracle on the same input, timed on one host core, repeated
     until about budget_s seconds of CPU work (the oracle is one loop: 1 thread)."""
@@ -417,6 +508,9 @@ def main():
                     help="also measure stream compaction on the 2^30-12345 flag workload (stderr)")
     ap.add_argument("--ops", action="store_true",
                     help="also measure the generic-operator scans on 1 GiB inputs (stderr)")
+    ap.add_argument("--compaction", action="store_true",
+                    help="also measure select, partition, reduce-by-key and run-length encoding on 2^25 items "
+                         "(stderr)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -496,6 +590,8 @@ def main():
         run_sweep(max(5, args.steps // 2), 3)
     if args.ops:
         run_ops(args.steps, args.warmup)
+    if args.compaction:
+        run_compaction(args.steps, args.warmup)
     if args.select:
         for in_place in (False, True):
             log("SELECT " + json.dumps(run_select(args.steps, args.warmup, in_place)))
