@@ -56,7 +56,7 @@ def log(*a):
 
 
 # the sources the fp32 single-pass kernel is compiled from
-SINGLE_PASS_SOURCES = ("dws_device.hpp", "dws_internal.h", "dws_protocol.h", "dws_single_pass_kernel.hpp",
+SINGLE_PASS_SOURCES = ("dws_device.hpp", "dws_protocol.h", "dws_single_pass.h", "dws_single_pass_kernel.hpp",
                        "dws_sp_f32.hip")
 
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "dws_protocol.h"
+#include "dws_single_pass.h"
 
 namespace dws {
 
@@ -14,24 +15,6 @@ namespace dws {
 constexpr size_t kCtlBytes = 256;
 constexpr size_t kCtlCounterOffset = 0;
 constexpr size_t kCtlWatchdogOffset = 128;
-
-// Kernel arguments of the single-pass scan.
-struct SinglePassParams {
-    const void* in;
-    void* out;
-    uint64_t n;
-    uint64_t* desc;        // >= num_tiles slots (unused when num_tiles == 1)
-    unsigned long long* counter;
-    unsigned int* watchdog;
-    unsigned long long* stamps;   // kStampsPerTile per tile (instrumented kernels only)
-    uint32_t num_tiles;
-    uint32_t epoch;               // descriptor epoch of this call (1 .. kEpochMax)
-};
-
-// Launch built configuration `cfg` (index into kCfgs) for element type T
-// (uint32_t or float; instantiated in dws_sp_u32.hip / dws_sp_f32.hip).
-template <class T>
-hipError_t launch_single_pass_typed(int cfg, bool exclusive, const SinglePassParams& p, hipStream_t stream);
 
 // Shape index (into kShapes) used for an option value (0 = automatic) and n.
 // Pointers that are not both 16-byte aligned use the scalar-load version of

@@ -24,7 +24,7 @@
 #include <utility>
 
 #include "dws_device.hpp"
-#include "dws_internal.h"
+#include "dws_single_pass.h"
 
 namespace dws {
 
