@@ -7,7 +7,8 @@
 //
 // Per tile (one workgroup, dynamic tile index, same descriptor protocol and
 // workspace as the scan):
-//   1. load the values and the flags of the tile (coalesced, in registers);
+//   1. load the flags, then the values of the tile (coalesced, in registers;
+//      steps 2 and 3 wait for the flags only);
 //   2. exclusive scan of the 0/1 flags in the tile -> each element's rank
 //      among the tile's selected elements, and the tile's selected count;
 //   3. publish {A, count}, look back over predecessors' counts -> the number
@@ -77,8 +78,10 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t seg_valid = valid_bytes(seg_first, SEG, p.n);
     uint32_t x[CHUNKS][VEC], r[CHUNKS][VEC];
-    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    // flags first: the tile's count (its aggregate) needs only the flags, so
+    // it is published and the look-back runs while the values are in flight
     load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
+    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
 
     // selection bits, then ranks (exclusive scan of the 0/1 flags) in place
     uint32_t selected = 0u;
@@ -91,7 +94,6 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
             r[c][e] = bit;
         }
     const uint32_t seg_count = scan_segment_local<uint32_t, true, VEC, CHUNKS>(r);
-    pin_in_registers<uint32_t, VEC, CHUNKS>(x);
     pin_in_registers<uint32_t, VEC, CHUNKS>(r);
 
     if (lane == 0) s_wave[wave] = seg_count;
