@@ -188,6 +188,13 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
             hip.memcpy_d2d(dst.data_ptr(), work.data_ptr(), nbytes, stream)
 
         result["memcpy_times_ms"] = time_steps(memcpy, prepare, steps, warmup)
+        # the vendor library's device-wide scan on the same input, out of
+        # place: torch.cumsum of a 1-D GPU tensor runs hipCUB's inclusive
+        # scan (rocPRIM's look-back scan) on ROCm
+        if w.dtype != "uint32":
+            result["torch_cumsum_times_ms"] = time_steps(lambda: torch.cumsum(work, 0, dtype=work.dtype, out=dst),
+                                                         prepare, steps,
+                                                         warmup)
         del dst
     del pristine, work, out, flush
     torch.cuda.empty_cache()
@@ -486,6 +493,10 @@ def summarize(w, res, variant_name, args):
         mc = float(np.mean(res["memcpy_times_ms"]))
         out["memcpy_ms_mean"] = mc
         out["memcpy_gbps"] = w.algorithmic_bytes / (mc * 1e-3) / 1e9
+    if "torch_cumsum_times_ms" in res:
+        tc = float(np.mean(res["torch_cumsum_times_ms"]))
+        out["torch_cumsum_ms_mean"] = tc
+        out["torch_cumsum_gbps"] = w.algorithmic_bytes / (tc * 1e-3) / 1e9
     return out
 
 
@@ -564,6 +575,11 @@ def main():
         "frac_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
         "memcpy_gbps": round(s["memcpy_gbps"], 2),
         "frac_memcpy": round(achieved / s["memcpy_gbps"], 4),
+        "library_baseline": ({"name": "torch.cumsum (hipCUB / rocPRIM device scan, inclusive, out of place)",
+                              "gbps": round(s["torch_cumsum_gbps"], 2),
+                              "ms_mean": round(s["torch_cumsum_ms_mean"], 5),
+                              "speedup": round(s["torch_cumsum_ms_mean"] / mean_ms, 3)}
+                             if "torch_cumsum_gbps" in s else None),
         "ms_min": round(s["ms_min"], 5),
         "ms_median": round(s["ms_median"], 5),
         "property_check": s["property_check"],
