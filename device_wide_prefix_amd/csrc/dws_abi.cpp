@@ -35,7 +35,7 @@ struct Workspace {
     void* partials = nullptr;     // reduce-then-scan partials (kRtsMaxGroups x 4 B)
     void* stp = nullptr;          // scan-then-propagate tile sums (all levels)
     uint64_t stp_elems = 0;
-    uint32_t epoch = 0;           // descriptor epoch of the last launch (0: none since the clear)
+    uint32_t launches = 0;        // look-back launches issued since the descriptors were cleared
 
     unsigned long long* counter() const
     {
@@ -45,6 +45,7 @@ struct Workspace {
     {
         return reinterpret_cast<unsigned int*>(static_cast<char*>(ctl) + kCtlWatchdogOffset);
     }
+    unsigned int* epoch() const { return reinterpret_cast<unsigned int*>(static_cast<char*>(ctl) + kCtlEpochOffset); }
 };
 
 std::mutex g_mu;
@@ -114,7 +115,7 @@ dws_status get_workspace(hipStream_t stream, Workspace** out)
         (void)hipFree(ws->ctl);
         return from_hip(e);
     }
-    e = launch_workspace_init(nullptr, 0, ws->counter(), ws->watchdog(), stream);
+    e = launch_workspace_init(nullptr, 0, ws->counter(), ws->epoch(), ws->watchdog(), stream);
     if (e != hipSuccess) {
         (void)hipFree(ws->ctl);
         (void)hipFree(ws->partials);
@@ -142,30 +143,34 @@ dws_status ensure_desc(Workspace* ws, uint64_t slots)
     void* p = nullptr;
     hipError_t e = hipMalloc(&p, want * sizeof(uint64_t));
     if (e != hipSuccess) return from_hip(e);
-    // fresh zeroed descriptors (all X for every epoch) and a zero counter
-    e = launch_workspace_init(static_cast<uint64_t*>(p), want, ws->counter(), nullptr, ws->stream);
+    // fresh zeroed descriptors (all X for every epoch), a zero counter, epoch 1
+    e = launch_workspace_init(static_cast<uint64_t*>(p), want, ws->counter(), ws->epoch(), nullptr, ws->stream);
     if (e != hipSuccess) {
         (void)hipFree(p);
         return from_hip(e);
     }
     ws->desc = static_cast<uint64_t*>(p);
     ws->desc_slots = want;
-    ws->epoch = 0;
+    ws->launches = 0;
     return DWS_OK;
 }
 
-// The descriptor epoch of the next launch on the workspace (call with ws->mu
-// held). Every launch gets a new one, so descriptors left by earlier launches
-// read as X; once the epochs are used up, every descriptor is cleared first,
-// so no word of an old launch can carry a reused epoch.
-dws_status next_epoch(Workspace* ws, uint32_t* epoch)
+// Before a look-back launch on the workspace (call with ws->mu held). Every
+// launch reads its descriptor epoch from the workspace's epoch word and
+// advances it, so descriptors left by earlier launches read as X. The epochs
+// wrap after kEpochMax launches: before that, every descriptor is cleared and
+// the word goes back to 1, so no word of an old launch can carry a reused
+// epoch. (Replays of a captured launch advance the word too, without passing
+// here; they count towards the same limit.)
+dws_status before_lookback_launch(Workspace* ws)
 {
-    if (ws->epoch >= kEpochMax) {
-        hipError_t e = launch_workspace_init(ws->desc, ws->desc_slots, ws->counter(), nullptr, ws->stream);
+    if (ws->launches + 1u >= kEpochMax) {
+        hipError_t e = launch_workspace_init(ws->desc, ws->desc_slots, ws->counter(), ws->epoch(), nullptr,
+                                             ws->stream);
         if (e != hipSuccess) return from_hip(e);
-        ws->epoch = 0;
+        ws->launches = 0;
     }
-    *epoch = ++ws->epoch;
+    ++ws->launches;
     return DWS_OK;
 }
 
@@ -223,8 +228,9 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     std::lock_guard<std::mutex> lock(ws->mu);
     s = ensure_desc(ws, num_tiles);
     if (s != DWS_OK) return s;
-    s = next_epoch(ws, &p.epoch);
+    s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
+    p.epoch = ws->epoch();
     p.desc = ws->desc;
     p.counter = ws->counter();
     p.watchdog = ws->watchdog();
@@ -385,8 +391,9 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     std::lock_guard<std::mutex> lock(ws->mu);
     s = ensure_desc(ws, num_tiles * (uint64_t)words);
     if (s != DWS_OK) return s;
-    s = next_epoch(ws, &p.epoch);
+    s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
+    p.epoch = ws->epoch();
     p.desc = ws->desc;
     p.counter = ws->counter();
     p.watchdog = ws->watchdog();
@@ -568,8 +575,9 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
         s = ensure_desc(ws, num_tiles);
         if (s != DWS_OK) return s;
         DebugArgs a{};
-        s = next_epoch(ws, &a.epoch);
+        s = before_lookback_launch(ws);
         if (s != DWS_OK) return s;
+        a.epoch = ws->epoch();
         a.in = d_in;
         a.out = d_out;
         a.n = n;
@@ -679,8 +687,9 @@ dws_status select_entry(const void* d_in, const void* d_flags, void* d_out, size
     std::lock_guard<std::mutex> lock(ws->mu);
     s = ensure_desc(ws, tiles);
     if (s != DWS_OK) return s;
-    s = next_epoch(ws, &a.epoch);
+    s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
+    a.epoch = ws->epoch();
     a.desc = ws->desc;
     a.counter = ws->counter();
     a.watchdog = ws->watchdog();
@@ -743,8 +752,9 @@ dws_status rbk_entry(const void* keys, const void* vals, void* ukeys, void* aggs
     std::lock_guard<std::mutex> lock(ws->mu);
     s = ensure_desc(ws, 2 * tiles);
     if (s != DWS_OK) return s;
-    s = next_epoch(ws, &a.epoch);
+    s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
+    a.epoch = ws->epoch();
     a.desc = ws->desc;
     a.counter = ws->counter();
     a.watchdog = ws->watchdog();

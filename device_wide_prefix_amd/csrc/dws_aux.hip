@@ -181,7 +181,8 @@ struct DebugParams {
     uint64_t* desc;
     unsigned long long* counter;
     unsigned int* watchdog;
-    uint32_t num_tiles, tile_elems, delay_every, delay_phase, delay_ticks, epoch;
+    uint32_t num_tiles, tile_elems, delay_every, delay_phase, delay_ticks;
+    unsigned int* epoch;
 };
 
 template <class T, bool EXCL, int MODE>
@@ -189,7 +190,7 @@ __global__ void __launch_bounds__(64) k_debug(DebugParams p)
 {
     const int lane = lane_id();
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = p.epoch;
+    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
     uint32_t tile = 0u;
     if (multi) {
         uint32_t t = 0u;
@@ -222,9 +223,11 @@ __global__ void __launch_bounds__(64) k_debug(DebugParams p)
             } else {
                 prefix = lookback_chained<T, kOrderRelaxed>(p.desc, tile, epoch, p.watchdog);
             }
-            if (lane == 0)
+            if (lane == 0) {
                 desc_store<kOrderRelaxed>(p.desc + tile,
                                           desc_pack(epoch, kStatusP, Elem<T>::bits(prefix + agg)));
+                if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+            }
         }
     }
     const T y = EXCL ? prefix + wave_shift_up1(incl) : prefix + incl;
@@ -265,23 +268,25 @@ hipError_t launch_debug(const DebugArgs& a, hipStream_t stream)
 // Workspace initialiser.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-    k_workspace_init(uint64_t* desc, uint64_t slots, unsigned long long* counter, unsigned int* watchdog)
+    k_workspace_init(uint64_t* desc, uint64_t slots, unsigned long long* counter, unsigned int* epoch,
+                     unsigned int* watchdog)
 {
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += stride) desc[i] = 0ull;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (counter != nullptr) *counter = kCounterInit;
+        if (epoch != nullptr) *epoch = 1u;
         if (watchdog != nullptr) *watchdog = 0u;
     }
 }
 
-hipError_t launch_workspace_init(uint64_t* desc, uint64_t slots, unsigned long long* counter,
+hipError_t launch_workspace_init(uint64_t* desc, uint64_t slots, unsigned long long* counter, unsigned int* epoch,
                                  unsigned int* watchdog, hipStream_t stream)
 {
     uint64_t blocks64 = (slots + 255u) / 256u;
     if (blocks64 < 1u) blocks64 = 1u;
     if (blocks64 > 1024u) blocks64 = 1024u;
-    void* args[] = {&desc, &slots, &counter, &watchdog};
+    void* args[] = {&desc, &slots, &counter, &epoch, &watchdog};
     return hipLaunchKernel(reinterpret_cast<const void*>(&k_workspace_init), dim3((uint32_t)blocks64), dim3(256),
                            args, 0, stream);
 }

@@ -267,6 +267,24 @@ __device__ __forceinline__ void desc_store(uint64_t* p, uint64_t w)
 
 __device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
+// The launch's descriptor epoch lives in a device word of the workspace, so a
+// launch replayed from a captured graph still gets a new one. A workgroup may
+// read it any time before it publishes: the word only advances after the last
+// tile has published P, and that needs every tile's A or P, so no workgroup
+// of the launch can read it late.
+__device__ __forceinline__ uint32_t load_epoch(const unsigned int* word)
+{
+    return uniform(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Called once per launch, by the owner of the last tile after its P: the next
+// launch on the workspace gets the next epoch (1 again after kEpochMax; the
+// host clears the descriptors before that can matter).
+__device__ __forceinline__ void advance_epoch(unsigned int* word, uint32_t epoch)
+{
+    __hip_atomic_store(word, epoch >= kEpochMax ? 1u : epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Draw the next tile index from the workspace counter with one device-scope
 // atomic (dynamic tile index assignment, PMPP 11.3 notes; "virtual processors"
 // in section 4.4 of the Merrill & Garland notes): the holder of tile t knows

@@ -15,6 +15,7 @@ namespace dws {
 constexpr size_t kCtlBytes = 256;
 constexpr size_t kCtlCounterOffset = 0;
 constexpr size_t kCtlWatchdogOffset = 128;
+constexpr size_t kCtlEpochOffset = 192;
 
 // Shape index (into kShapes) used for an option value (0 = automatic) and n.
 // Pointers that are not both 16-byte aligned use the scalar-load version of
@@ -66,7 +67,7 @@ struct SelectArgs {
     unsigned int* watchdog;
     unsigned long long* count;
     uint32_t num_tiles;
-    uint32_t epoch;
+    unsigned int* epoch;     // the workspace epoch word
     bool partition;          // also write the rejected elements, reversed, at the back
 };
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
@@ -87,7 +88,7 @@ struct DebugArgs {
     unsigned long long* counter;
     unsigned int* watchdog;
     uint32_t num_tiles;
-    uint32_t epoch;
+    unsigned int* epoch;     // the workspace epoch word
 };
 hipError_t launch_debug(const DebugArgs& a, hipStream_t stream);
 
@@ -107,7 +108,7 @@ struct RbkArgs {
     unsigned int* watchdog;
     unsigned long long* num_runs;
     uint32_t num_tiles;
-    uint32_t epoch;
+    unsigned int* epoch;     // the workspace epoch word
 };
 constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384-element tiles (512 threads) from here
 uint32_t rbk_tile_elems(uint64_t n, bool aligned);
@@ -123,7 +124,7 @@ struct OpScanParams {
     unsigned long long* counter;
     unsigned int* watchdog;
     uint32_t num_tiles;
-    uint32_t epoch;
+    unsigned int* epoch;     // the workspace epoch word
 };
 enum OpKind : int {
     kOpMaxI32, kOpMaxU32, kOpMinI32, kOpMinU32,          // one word
@@ -166,10 +167,11 @@ hipError_t launch_op_affine(int kind, bool exclusive, int shape, int tile_index,
 hipError_t launch_op_segsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
                             hipStream_t stream);
 
-// Zero `slots` descriptors and set the counter to kCounterInit and the
-// watchdog to 0 (a kernel, not a memset, so that it may sit in a graph).
+// Zero `slots` descriptors, set the counter to kCounterInit, the epoch word
+// to 1 and the watchdog to 0 (each pointer may be null; a kernel, not a
+// memset, so that it may sit in a graph).
 hipError_t launch_workspace_init(uint64_t* desc, uint64_t slots, unsigned long long* counter,
-                                 unsigned int* watchdog, hipStream_t stream);
+                                 unsigned int* epoch, unsigned int* watchdog, hipStream_t stream);
 
 hipError_t launch_wave_selftest(const void* in, void* incl, void* shift, uint64_t n_waves,
                                 int kind, hipStream_t stream);

@@ -389,7 +389,7 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = p.epoch;
+    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
 
     uint32_t tile = 0u;
     if (multi) {
@@ -444,7 +444,10 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
             } else {
                 if (lane == 0) desc_store_val<W>(p.desc, tile, epoch, kStatusA, agg);
                 prefix = lookback_op<Op, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
-                if (lane == 0) desc_store_val<W>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+                if (lane == 0) {
+                    desc_store_val<W>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+                }
             }
         }
         if (lane == 0) s_prefix = prefix;

@@ -48,7 +48,7 @@ struct RbkParams {
     unsigned int* watchdog;
     unsigned long long* num_runs;
     uint32_t num_tiles;
-    uint32_t epoch;
+    unsigned int* epoch;
 };
 
 constexpr uint32_t kRbkDropped = 0x80000000u;   // past any tile's range: dropped
@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = p.epoch;
+    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
 
     uint32_t tile = 0u;
     if (multi) {
@@ -157,7 +157,10 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
             } else {
                 if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
                 prefix = lookback_op<Op, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
-                if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+                if (lane == 0) {
+                    desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+                }
             }
         }
         if (lane == 0) s_prefix = prefix;

@@ -41,7 +41,7 @@ struct SelectParams {
     unsigned int* watchdog;
     unsigned long long* count;
     uint32_t num_tiles;
-    uint32_t epoch;
+    unsigned int* epoch;
 };
 
 // Byte offset far past any tile's range (at most 4 * 32768 bytes): the
@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = p.epoch;
+    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
 
     uint32_t tile = 0u;
     if (multi) {
@@ -114,7 +114,10 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
                 if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, count));
                 prefix = lookback_decoupled<uint32_t, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch,
                                                                                      p.watchdog);
-                if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusP, prefix + count));
+                if (lane == 0) {
+                    desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusP, prefix + count));
+                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+                }
             }
         }
         if (lane == 0) s_prefix = prefix;

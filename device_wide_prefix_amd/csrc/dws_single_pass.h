@@ -18,7 +18,7 @@ struct SinglePassParams {
     unsigned int* watchdog;
     unsigned long long* stamps;   // kStampsPerTile per tile (instrumented kernels only)
     uint32_t num_tiles;
-    uint32_t epoch;               // descriptor epoch of this call (1 .. kEpochMax)
+    unsigned int* epoch;          // the workspace's epoch word (unused when num_tiles == 1)
 };
 
 // Launch built configuration `cfg` (index into kCfgs) for element type T

@@ -3,8 +3,9 @@
 // Look-back", section 4.1 steps and section 4.4 adaptations), and the chained
 // scan that waits on the immediate predecessor only (section 3.2, Fig 4).
 //
-// One workgroup per tile; the kernel is the whole call (no init launch: the
-// host hands every call a new descriptor epoch):
+// One workgroup per tile; the kernel is the whole call (no init launch: every
+// launch reads a new descriptor epoch from the workspace, and the owner of the
+// last tile advances it):
 //   1. lane 0 draws the tile index from the workspace counter (dynamic tile
 //      index, PMPP 11.3 notes), or the tile is the workgroup index
 //      (TILE_INDEX == kTileDispatch);
@@ -44,7 +45,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = p.epoch;
+    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
 
     uint32_t tile = 0u;
     if (multi) {
@@ -96,9 +97,11 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
-                if (lane == 0)
+                if (lane == 0) {
                     desc_store<ORDER>(p.desc + tile,
                                       desc_pack(epoch, kStatusP, Elem<T>::bits(prefix + agg)));
+                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+                }
             }
         }
         if (lane == 0) s_prefix = prefix;

@@ -587,5 +587,51 @@ def test_select_full_size(gpu):
     assert np.array_equal(got[cnt:], x[cnt:])
 
 
+@pytest.mark.parametrize("n", [(1 << 22) + 7, (1 << 25) + 3], ids=["dispatch_tiles", "drawn_tiles"])
+def test_graph_replays(gpu, n):
+    # a captured call replays with the arguments it was captured with; the
+    # descriptor epoch comes from the workspace, so every replay still sees
+    # only its own descriptors. Eager work (new inputs, an uncaptured scan on
+    # the same stream) runs between replays, and every replay is checked.
+    import torch
+    s = torch.cuda.Stream()
+    x = torch.empty(n, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(x)
+    flags = torch.empty_like(x)
+    sel = torch.empty_like(x)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    pairs = torch.empty((n, 2), dtype=torch.int32, device="cuda")
+    pout = torch.empty_like(pairs)
+    dws.reserve(n, stream=s.cuda_stream)
+    with torch.cuda.stream(s):          # warm-up outside the capture
+        dws.scan_exclusive(x, out)
+        dws.select_flagged(x, flags, out=sel, count=cnt)
+        dws.scan_op(pairs, dws.OP_AFFINE, dws.PAIR_U32, out=pout)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dws.scan_exclusive(x, out)
+        dws.select_flagged(x, flags, out=sel, count=cnt)
+        dws.scan_op(pairs, dws.OP_AFFINE, dws.PAIR_U32, out=pout)
+    for rep in range(4):
+        note(f"graph replay n={n} rep={rep}")
+        data = wl.random_input("int32", n, seed=100 + rep)
+        fl = wl.selection_flags(n, 0.5, seed=200 + rep)
+        pr = wl.op_input("affine_u32", n, seed=300 + rep)
+        x.copy_(torch.from_numpy(data))
+        flags.copy_(torch.from_numpy(fl))
+        pairs.copy_(torch.from_numpy(pr.view(np.int32)))
+        with torch.cuda.stream(s):        # eager launch on the workspace between replays
+            dws.scan_inclusive(flags, torch.empty_like(flags))
+        s.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(data, from_device(out, "int32"), "int32", True, label=f"replay {rep}")
+        want = oracle.select_flagged(data, fl)
+        assert int(cnt.item()) == want.size
+        assert np.array_equal(sel[:want.size].cpu().numpy(), want)
+        assert np.array_equal(pout.cpu().numpy().view(np.uint32), oracle.scan_affine_u32(pr))
+
+
 def test_zz_watchdog_never_tripped(gpu):
     assert dws.watchdog_trips() == 0
