@@ -39,6 +39,14 @@
  * must not be under graph capture; dws_reserve can create it ahead of time)
  * and reused by later calls, which the stream orders; a call that needs more
  * descriptors than the workspace holds synchronises the stream and grows it.
+ *
+ * Graphs: once the workspace of the stream covers n (a first call, or
+ * dws_reserve), calls on that stream allocate nothing and may be captured
+ * into a HIP graph. Replays stay correct: each launch takes its descriptor
+ * epoch from a device word that the launch itself advances. Host-issued calls
+ * clear the descriptors before the 30-bit epoch wraps; replays advance the
+ * epoch without the host seeing them, so about 2^30 replays of a captured
+ * call need a host-issued call (or dws_release_workspaces) in between.
  * Calls on different streams never share a workspace. Host threads may call
  * concurrently. dws_release_workspaces frees every workspace.
  *
