@@ -43,10 +43,11 @@
  * Graphs: once the workspace of the stream covers n (a first call, or
  * dws_reserve), calls on that stream allocate nothing and may be captured
  * into a HIP graph. Replays stay correct: each launch takes its descriptor
- * epoch from a device word that the launch itself advances. Host-issued calls
- * clear the descriptors before the 30-bit epoch wraps; replays advance the
- * epoch without the host seeing them, so about 2^30 replays of a captured
- * call need a host-issued call (or dws_release_workspaces) in between.
+ * epoch from a device word that the launch itself advances. The host clears
+ * the descriptors before its own calls could wrap the 30-bit epoch, but
+ * replays advance it unseen: after about 2^30 launches on one workspace,
+ * replays included, call dws_release_workspaces (and capture again) so that
+ * no epoch is reused.
  * Calls on different streams never share a workspace. Host threads may call
  * concurrently. dws_release_workspaces frees every workspace.
  *
