@@ -587,6 +587,22 @@ def test_select_full_size(gpu):
     assert np.array_equal(got[cnt:], x[cnt:])
 
 
+def test_random_sizes(gpu):
+    # 64 log-uniform sizes from 1 to 2^24 with random dtype, kind, in place
+    # and pointer offset (seeded), through the default entry points
+    rng = np.random.default_rng(2024)
+    for case in range(64):
+        n = int(np.exp(rng.uniform(0.0, np.log(1 << 24))))
+        dtype = DTYPES[int(rng.integers(0, 3))]
+        exclusive = bool(rng.integers(0, 2))
+        in_place = bool(rng.integers(0, 2))
+        offset = int(rng.integers(0, 4)) if rng.random() < 0.25 else 0
+        note(f"random case {case}: n={n} dtype={dtype} excl={exclusive} in_place={in_place} offset={offset}")
+        x = wl.random_input(dtype, n, seed=case)
+        y = _roundtrip(x, dtype, exclusive, in_place=in_place, offset=offset)
+        check(x, y, dtype, exclusive, label=f"random case {case} n={n}")
+
+
 @pytest.mark.parametrize("n", [(1 << 22) + 7, (1 << 25) + 3], ids=["dispatch_tiles", "drawn_tiles"])
 def test_graph_replays(gpu, n):
     # a captured call replays with the arguments it was captured with; the
