@@ -102,7 +102,12 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
     const uint32_t next_key = __builtin_amdgcn_raw_buffer_load_b32(
         make_rsrc(p.keys + (has_next ? seg_first + SEG : 0u), has_next ? 4u : 0u), 0, 0, 0);
 
-    // head and tail bits, scan input
+    // head and tail bits, scan input. Element positions are local to the wave
+    // segment (32-bit); the segment's valid count and whether it holds the
+    // array's first or last element are uniform.
+    const uint32_t seg_elems = vb / 4u;
+    const bool holds_first = seg_first == 0u;
+    const bool holds_last = seg_first + seg_elems == p.n && seg_elems > 0u;
     uint64_t heads = 0ull, tails = 0ull;
     V x[CHUNKS][VEC];
 #pragma unroll
@@ -116,12 +121,12 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
             c < CHUNKS - 1 ? (uint32_t)__builtin_amdgcn_readlane((int)k[(c + 1) % CHUNKS][0], 0) : next_key;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const uint64_t i = seg_first + (uint64_t)(c * 64 * VEC) + (uint64_t)(lane * VEC + e);
-            const bool valid = i < p.n;
+            const uint32_t local = (uint32_t)(c * 64 * VEC) + (uint32_t)(lane * VEC + e);
+            const bool valid = local < seg_elems;
             const uint32_t prev = e > 0 ? k[c][e - 1] : (lane > 0 ? from_left : left_edge);
             const uint32_t next = e < VEC - 1 ? k[c][e + 1] : (lane < 63 ? from_right : right_edge);
-            const bool head = valid && (i == 0u || k[c][e] != prev);
-            const bool tail = valid && (i + 1u == p.n || k[c][e] != next);
+            const bool head = valid && ((holds_first && local == 0u) || k[c][e] != prev);
+            const bool tail = valid && ((holds_last && local + 1u == seg_elems) || k[c][e] != next);
             heads |= (uint64_t)head << (c * VEC + e);
             tails |= (uint64_t)tail << (c * VEC + e);
             uint32_t val;
@@ -169,10 +174,13 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
     const V tile_prefix = s_prefix;
     const V seed = Op::combine(tile_prefix, wave_pre);
 
-    // runs this tile can write: the one running into it (if any) and its own
-    const uint32_t heads_before = tile_prefix.w[0];
+    // runs this tile can write: the one running into it (if any) and its own.
+    // Uniform by construction (read from LDS by every lane); saying so keeps
+    // the buffer resources in SGPRs (no per-store loop).
+    const uint32_t heads_before = uniform(tile_prefix.w[0]);
+    const uint32_t tile_heads = uniform(agg.w[0]);
     const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
-    const uint32_t range = (agg.w[0] + 1u) * 4u;
+    const uint32_t range = (tile_heads + 1u) * 4u;
     const __amdgpu_buffer_rsrc_t rkeys = make_rsrc(p.ukeys + base_run, range);
     const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, range);
 #pragma unroll
@@ -187,7 +195,7 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
             __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(y.w[1], raggs, (int)aoff, 0, 0);
         }
-    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + agg.w[0];
+    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + tile_heads;
 }
 
 __global__ void __launch_bounds__(64) k_store_runs(unsigned long long* count)

@@ -104,6 +104,10 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
         if (w == wave) wave_pre = count;
         count += s_wave[w];
     }
+    // uniform by construction (every lane read the same LDS words); saying so
+    // keeps the buffer resources built from them in SGPRs (no per-store loop)
+    count = uniform(count);
+    wave_pre = uniform(wave_pre);
 
     if (wave == 0) {
         uint32_t prefix = 0u;
