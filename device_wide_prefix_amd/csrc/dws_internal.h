@@ -110,7 +110,7 @@ struct RbkArgs {
     uint32_t num_tiles;
     unsigned int* epoch;     // the workspace epoch word
 };
-constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384-element tiles (512 threads) from here
+constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384-element tiles from here
 uint32_t rbk_tile_elems(uint64_t n, bool aligned);
 hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream);
 

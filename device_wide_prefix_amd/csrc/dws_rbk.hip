@@ -3,14 +3,19 @@
 // reduce-by-key and run-length-encode).
 //
 // Per element i: head(i) = (i == 0 or key[i] != key[i-1]), tail(i) =
-// (i == n-1 or key[i] != key[i+1]). The scan runs over pairs (heads, value)
-// under "count the heads, restart the value sum after the last head" (a
-// segmented sum, not commutative), so after the look-back every element knows
-// its run index heads_incl(i) - 1 and the sum of its run up to i. Heads store
-// their key to unique_keys[run], tails store the run's sum to aggregates[run];
+// (i == n-1 or key[i] != key[i+1]). Both kernels carry the pair (heads, value
+// since the last head) through the look-back, under "count the heads, restart
+// the value sum after the last head" (a segmented sum, not commutative), and
 // the last tile stores the number of runs. Values are 32-bit integers (sums
 // wrap modulo 2^32), fp32, or the constant 1 (run-length encoding: the sum is
 // the run length).
+//
+// k_reduce_by_key (fp32 sums) scans the pairs element by element, so every
+// element knows its run index heads_incl(i) - 1 and the sum of its run up to
+// i; heads store their key to unique_keys[run], tails the run's sum to
+// aggregates[run]. k_run_ends (integer sums, run lengths) needs no segmented
+// scan inside the tile: it counts heads with ballots and takes run sums as
+// differences of one plain prefix sum (described at the kernel).
 //
 // The neighbours key[i-1] and key[i+1] come from the registers of the same
 // lane, the adjacent lane (DPP wave shift), the adjacent chunk (readlane) or,
@@ -53,6 +58,9 @@ struct RbkParams {
 
 constexpr uint32_t kRbkDropped = 0x80000000u;   // past any tile's range: dropped
 constexpr int kDppWaveShl1 = 0x130;              // lane l reads lane l + 1
+// Look-back slots per lane for the run kernels: 128 predecessors per poll,
+// and fewer registers held than with the scan's four.
+constexpr int kRunLookbackSlots = 2;
 
 // Value mode: 0 integer sums, 1 fp32 sums, 2 run lengths.
 template <int BLOCK, int VEC, int CHUNKS, int MODE, int TILE_INDEX>
@@ -198,6 +206,218 @@ __global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
     if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + tile_heads;
 }
 
+// Integer sums and run lengths without a segmented scan. Inside a wave
+// segment every quantity is a plain count or a plain prefix sum:
+//   H(i) heads at or before i (ballots and mbcnt); the run holding i is
+//        H(i) - 1 after the heads before the segment,
+//   S(i) values before i (wrapping +; for run lengths S(i) = i),
+//   B(i) S at the last head at or before i.
+// A run ends where the next one starts, so the head at p also finishes the
+// run before it, whose sum is S(p) - B(p - 1), exact modulo 2^32; when that
+// run started before the segment, B(p - 1) is minus the value carried in.
+// Only the array's last run has no head after it: the segment holding the
+// last element stores its value, which is the segment's aggregate seeded by
+// the prefix. No tail flags are needed. B comes from the lane's own heads,
+// else from the highest lane below with a head in the chunk (one ds_bpermute
+// per chunk), else from earlier chunks. The segment's aggregate for the
+// look-back is (heads, value from its last head on), the pair the segmented
+// scan above uses. fp32 sums stay on the segmented scan: a difference of long
+// prefix sums would lose the short runs' precision.
+// At most 128 VGPRs (four waves per SIMD): two 512-thread workgroups share a
+// CU, so one's loads overlap the other's look-back and stores.
+template <int BLOCK, int VEC, int CHUNKS, int MODE, int TILE_INDEX, int SLOTS = kRunLookbackSlots>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_run_ends(RbkParams p)
+{
+    static_assert(MODE == 0 || MODE == 2, "integer sums or run lengths");
+    using Op = OpRunSum<false>;
+    using V = Val<2>;
+    constexpr int W = BLOCK / 64;
+    constexpr uint32_t CH = 64u * VEC;
+    constexpr uint32_t SEG = CH * CHUNKS;
+    constexpr uint32_t TILE = W * SEG;
+    __shared__ uint32_t s_draw;
+    __shared__ V s_wave[W];
+    __shared__ V s_prefix;
+
+    const int lane = lane_id();
+    const int wave = (int)uniform(threadIdx.x >> 6);
+    const bool multi = p.num_tiles > 1u;
+    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
+
+    uint32_t tile = 0u;
+    if (multi) {
+        if constexpr (TILE_INDEX == kTileDispatch) {
+            tile = blockIdx.x;
+        } else {
+            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            __syncthreads();
+            tile = uniform(s_draw);
+            if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
+                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
+                return;
+            }
+        }
+    }
+
+    const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
+    const uint32_t vb = valid_bytes(seg_first, SEG, p.n);
+    const uint32_t seg_elems = vb / 4u;
+    uint32_t k[CHUNKS][VEC];
+    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.keys + seg_first, vb), lane, k);
+    uint32_t v[CHUNKS][VEC];   // values, then S before each element (integer sums only)
+    if constexpr (MODE == 0) load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.vals + seg_first, vb), lane, v);
+    const bool has_prev = seg_first > 0u && seg_first < p.n;
+    const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
+    const bool holds_last = seg_elems > 0u && seg_first + seg_elems == p.n;
+    // the key compared with the segment's first element: the array's first
+    // element is always a head
+    uint32_t left0 = seg_first == 0u ? ~(uint32_t)__builtin_amdgcn_readlane((int)k[0][0], 0) : prev_key;
+    if (seg_elems < SEG) {
+        // elements past n take the key at n - 1, so they are never heads
+        const uint32_t last_key = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.keys + (p.n - 1u), 4u), 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if ((uint32_t)(c * CH) + (uint32_t)(lane * VEC + e) >= seg_elems) k[c][e] = last_key;
+        if (seg_elems == 0u) left0 = last_key;
+    }
+
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    uint32_t below[CHUNKS];   // heads of the segment before the lane's elements of chunk c
+    uint32_t b_in[CHUNKS];    // B entering the lane's elements of chunk c (used when below[c] > 0)
+    uint32_t h_seg = 0u, s_seg = 0u, b_carry = 0u;   // uniform running totals over the chunks
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
+                                                                         0xf, true);
+        const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
+        const uint32_t first_prev = lane > 0 ? from_left : edge;
+        uint32_t sx[VEC];
+        if constexpr (MODE == 0) {
+            uint32_t acc = 0u;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                sx[e] = acc;
+                acc += v[c][e];
+            }
+            const uint32_t incl = wave_inclusive_scan(acc);
+            const uint32_t base = s_seg + (incl - acc);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                sx[e] += base;
+                v[c][e] = sx[e];
+            }
+            s_seg += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sx[e] = (uint32_t)(c * CH) + (uint32_t)(lane * VEC + e);
+        }
+        uint64_t any = 0ull;
+        uint32_t cnt = 0u, chunk_count = 0u, last = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
+            const bool head = k[c][e] != prev;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(head);
+            any |= m;
+            cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
+            chunk_count += (uint32_t)__builtin_popcountll(m);
+            last = head ? sx[e] : last;
+        }
+        below[c] = cnt + h_seg;
+        h_seg += chunk_count;
+        const uint64_t lower = any & lanes_below;
+        const int src = lower != 0ull ? 63 - __builtin_clzll(lower) : 0;
+        const uint32_t from_lane = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)last);
+        b_in[c] = lower != 0ull ? from_lane : b_carry;
+        if (any != 0ull) b_carry = (uint32_t)__builtin_amdgcn_readlane((int)last, 63 - __builtin_clzll(any));
+        // formed here, chunk by chunk (not sunk, which would hold every ballot)
+        asm volatile("" : "+v"(below[c]));
+        asm volatile("" : "+v"(b_in[c]));
+        if constexpr (MODE == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(v[c][e]));
+        }
+    }
+    if constexpr (MODE == 2) s_seg = seg_elems;
+    const V seg_total = {{h_seg, h_seg > 0u ? s_seg - b_carry : s_seg}};
+
+    if (lane == 0) s_wave[wave] = seg_total;
+    __syncthreads();
+    V wave_pre = Op::identity(), agg = Op::identity();
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        if (w == wave) wave_pre = agg;
+        agg = Op::combine(agg, s_wave[w]);
+    }
+
+    if (wave == 0) {
+        V prefix = Op::identity();
+        if (multi) {
+            if (tile == 0u) {
+                if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
+            } else {
+                if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
+                prefix = lookback_op<Op, SLOTS>(p.desc, tile, epoch, p.watchdog);
+                if (lane == 0) {
+                    desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+                }
+            }
+        }
+        if (lane == 0) s_prefix = prefix;
+    }
+    __syncthreads();
+    const V tile_prefix = s_prefix;
+    const V seed = Op::combine(tile_prefix, wave_pre);
+    const uint32_t seed_heads = uniform(seed.w[0]);
+    const uint32_t seed_value = uniform(seed.w[1]);
+
+    // runs this tile can write: the one running into it (if any) and its own.
+    // Uniform by construction; saying so keeps the buffer resources in SGPRs.
+    const uint32_t heads_before = uniform(tile_prefix.w[0]);
+    const uint32_t tile_heads = uniform(agg.w[0]);
+    const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
+    const uint32_t range = (tile_heads + 1u) * 4u;
+    const __amdgpu_buffer_rsrc_t rkeys = make_rsrc(p.ukeys + base_run, range);
+    const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, range);
+    // byte offset, relative to base_run, of the run before the segment's first head
+    const uint32_t bias = (seed_heads - 1u - base_run) * 4u;
+    uint32_t lane_pos = (uint32_t)lane * VEC;
+    asm volatile("" : "+v"(lane_pos));   // positions formed here, not held through the look-back
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
+                                                                         0xf, true);
+        const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
+        const uint32_t first_prev = lane > 0 ? from_left : edge;
+        uint32_t off = below[c] * 4u + bias;
+        uint32_t b = below[c] > 0u ? b_in[c] : 0u - seed_value;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
+            const bool head = k[c][e] != prev;
+            uint32_t sxe;
+            if constexpr (MODE == 0) sxe = v[c][e];
+            else sxe = (uint32_t)(c * CH + e) + lane_pos;
+            off += head ? 4u : 0u;
+            // a head stores its key at its run and finishes the run before it
+            // (offset - 4; from a dropped offset that is still out of range)
+            const uint32_t koff = head ? off : kRbkDropped;
+            __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(sxe - b, raggs, (int)(koff - 4u), 0, 0);
+            b = head ? sxe : b;
+        }
+    }
+    if (holds_last && lane == 0) {
+        const uint32_t last_off = (seed_heads + h_seg - 1u - base_run) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(Op::combine(seed, seg_total).w[1], raggs, (int)last_off, 0, 0);
+    }
+    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + tile_heads;
+}
+
 __global__ void __launch_bounds__(64) k_store_runs(unsigned long long* count)
 {
     if (threadIdx.x == 0) *count = 0ull;
@@ -208,9 +428,15 @@ static hipError_t launch_rbk_mode(int tile_index, const RbkParams& p, hipStream_
 {
     RbkParams arg = p;
     void* args[] = {&arg};
-    const void* fn = tile_index == kTileDrawn
-                         ? reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDrawn>)
-                         : reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>);
+    const void* fn;
+    if constexpr (MODE == 1)
+        fn = tile_index == kTileDrawn
+                 ? reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDrawn>)
+                 : reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>);
+    else
+        fn = tile_index == kTileDrawn
+                 ? reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, kTileDrawn>)
+                 : reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>);
     return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
 }
 
@@ -228,7 +454,7 @@ static hipError_t launch_rbk_shape(int mode, int tile_index, const RbkParams& p,
 uint32_t rbk_tile_elems(uint64_t n, bool aligned)
 {
     if (!aligned) return 256u * 16u;
-    return n >= kRbkLargeMin ? 512u * 4u * 8u : 256u * 4u * 4u;
+    return n >= kRbkLargeMin ? 16384u : 256u * 4u * 4u;
 }
 
 hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
@@ -245,7 +471,17 @@ hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
                 a.num_runs,                           a.num_tiles,
                 a.epoch};
     if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, kTileDispatch, p, stream);
-    if (a.n >= kRbkLargeMin) return launch_rbk_shape<512, 4, 8>(a.mode, a.tile_index, p, stream);
+    if (a.n >= kRbkLargeMin) {
+        // 16,384-element tiles in each case. The count-and-difference kernels
+        // measured fastest on the workgroup index at 2^25 and 2^28 elements;
+        // fp32 sums (the segmented scan) take the caller's tile index.
+        switch (a.mode) {
+        case 0: return launch_rbk_mode<512, 4, 8, 0>(kTileDispatch, p, stream);
+        case 1: return launch_rbk_mode<512, 4, 8, 1>(a.tile_index, p, stream);
+        case 2: return launch_rbk_mode<256, 4, 16, 2>(kTileDispatch, p, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     return launch_rbk_shape<256, 4, 4>(a.mode, kTileDispatch, p, stream);
 }
 
