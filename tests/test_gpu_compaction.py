@@ -112,6 +112,45 @@ def test_reduce_by_key_and_rle(gpu, value_dtype):
                         int(cnt.item()), vals)
 
 
+def _run_both(keys, vals, name):
+    """Integer reduce-by-key and run-length encoding of the same keys, checked
+    against the oracle."""
+    import torch
+    n = keys.size
+    stream = torch.cuda.current_stream().cuda_stream
+    kd, vd = _dev(keys), _dev(vals)
+    uk, ag, cnt = _empty(n), _empty(n), _count()
+    st = dws.load_library().dws_reduce_by_key(kd.data_ptr(), vd.data_ptr(), uk.data_ptr(), ag.data_ptr(), n,
+                                              dws.UINT32, cnt.data_ptr(), stream)
+    assert st == dws.OK, dws.status_string(st)
+    _check_runs(f"{name} sums", keys, uk.cpu().numpy(), ag.cpu().numpy(), int(cnt.item()), vals)
+    uk, ag, cnt = _empty(n), _empty(n), _count()
+    st = dws.load_library().dws_run_length_encode(kd.data_ptr(), uk.data_ptr(), ag.data_ptr(), n, cnt.data_ptr(),
+                                                  stream)
+    assert st == dws.OK, dws.status_string(st)
+    _check_runs(f"{name} lengths", keys, uk.cpu().numpy(), ag.cpu().numpy(), int(cnt.item()))
+
+
+def test_run_boundaries(gpu):
+    # Where a run's sum comes from: its own segment, the value carried in
+    # through the look-back, or the segment aggregate of the array's last
+    # element. Wave segments hold 2,048 (sums) or 4,096 (run lengths) keys
+    # and tiles 16,384 from 2^22 keys, 4,096-key tiles below.
+    big = (1 << 22) + 4096          # the array ends exactly at a segment's end
+    for n in (5000, big, (1 << 22) + 4097):
+        vals = wl.generate("u32_full", n, n + 7)
+        for key in (0, 0xFFFFFFFF, 12345):
+            note(f"run boundaries: one run of key {key:#x}, n={n}")
+            _run_both(np.full(n, key, dtype=np.uint32), vals, f"one run key={key:#x} n={n}")
+        for length in (2048, 4096, 16384):
+            note(f"run boundaries: runs of exactly {length}, n={n}")
+            keys = (np.arange(n, dtype=np.uint32) // length).astype(np.uint32) * np.uint32(2654435761)
+            _run_both(keys, vals, f"runs of {length} n={n}")
+        note(f"run boundaries: mean run 1 and 50,000, n={n}")
+        for mean_run in (1, 50_000):
+            _run_both(wl.run_keys(n, mean_run, seed=n + mean_run), vals, f"mean run {mean_run} n={n}")
+
+
 def test_reduce_by_key_unaligned_and_special_keys(gpu):
     import torch
     # keys and values one element off 16-byte alignment (scalar-load kernel),
