@@ -71,6 +71,7 @@ struct SelectArgs {
     bool partition;          // also write the rejected elements, reversed, at the back
 };
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
+constexpr uint64_t kSelectHugeMin = (uint64_t)1 << 27;    // 40960-element tiles from here
 constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
 uint32_t select_tile_elems(uint64_t n, bool aligned);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);

@@ -26,6 +26,8 @@
 // order, element i to out[n - 1 - (number of rejected elements before i)],
 // which needs no total count. Those writes land past the input's unread part,
 // so the partition is never in place.
+#include <type_traits>
+
 #include "dws_device.hpp"
 #include "dws_internal.h"
 
@@ -44,14 +46,15 @@ struct SelectParams {
     unsigned int* epoch;
 };
 
-// Byte offset far past any tile's range (at most 4 * 32768 bytes): the
+// Byte offset far past any tile's range (at most 4 * 40960 bytes): the
 // buffer range check drops the store. Offset plus store size stays below 2^32.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
 template <int BLOCK, int VEC, int CHUNKS, bool PARTITION>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
-    static_assert(VEC * CHUNKS <= 32, "one selection bit per element in a 32-bit mask");
+    static_assert(VEC * CHUNKS <= 64, "one selection bit per element in a 64-bit mask");
+    using Mask = typename std::conditional<(VEC * CHUNKS > 32), uint64_t, uint32_t>::type;
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
@@ -84,13 +87,13 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
 
     // selection bits, then ranks (exclusive scan of the 0/1 flags) in place
-    uint32_t selected = 0u;
+    Mask selected = 0u;
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const uint32_t bit = r[c][e] != 0u ? 1u : 0u;
-            selected |= bit << (c * VEC + e);
+            selected |= (Mask)bit << (c * VEC + e);
             r[c][e] = bit;
         }
     const uint32_t seg_count = scan_segment_local<uint32_t, true, VEC, CHUNKS>(r);
@@ -170,17 +173,35 @@ struct SelectShape {
     int threads, vec, chunks;
     constexpr uint32_t elems() const { return (uint32_t)(threads * vec * chunks); }
 };
-constexpr SelectShape kSelectLarge{1024, 4, 8};   // 32768 elements
+// From 2^27 elements 40960-element tiles: 5% faster than 32768 at 2^30 (the
+// look-back and the swap between workgroups are paid over more bytes). Below
+// that, 32768 divides the common power-of-two sizes into whole rounds of the
+// 256 CUs, which measured faster at 2^25.
+constexpr SelectShape kSelectHuge{1024, 4, 10};   // 40960 elements
+constexpr SelectShape kSelectLarge{1024, 4, 8};   // 32768
 constexpr SelectShape kSelectSmall{256, 4, 4};    // 4096
 constexpr SelectShape kSelectScalar{256, 1, 16};  // 4096, pointers not 16-byte aligned
 
 static SelectShape select_shape(uint64_t n, bool aligned)
 {
     if (!aligned) return kSelectScalar;
-    return n >= kSelectLargeMin ? kSelectLarge : kSelectSmall;
+    return n >= kSelectHugeMin ? kSelectHuge : (n >= kSelectLargeMin ? kSelectLarge : kSelectSmall);
 }
 
 uint32_t select_tile_elems(uint64_t n, bool aligned) { return select_shape(n, aligned).elems(); }
+
+template <bool PARTITION>
+static const void* select_kernel(const SelectShape& s)
+{
+    if (s.vec == 1) return reinterpret_cast<const void*>(
+        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION>);
+    if (s.chunks == kSelectHuge.chunks) return reinterpret_cast<const void*>(
+        &k_select<kSelectHuge.threads, kSelectHuge.vec, kSelectHuge.chunks, PARTITION>);
+    if (s.threads == kSelectLarge.threads) return reinterpret_cast<const void*>(
+        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION>);
+    return reinterpret_cast<const void*>(
+        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION>);
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
 {
@@ -195,28 +216,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
                    static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
                    a.epoch};
     void* args[] = {&p};
-    const void* fn = nullptr;
-    if (a.partition) {
-        if (!a.aligned)
-            fn = reinterpret_cast<const void*>(
-                &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, true>);
-        else if (s.threads == kSelectLarge.threads)
-            fn = reinterpret_cast<const void*>(
-                &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, true>);
-        else
-            fn = reinterpret_cast<const void*>(
-                &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, true>);
-    } else {
-        if (!a.aligned)
-            fn = reinterpret_cast<const void*>(
-                &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, false>);
-        else if (s.threads == kSelectLarge.threads)
-            fn = reinterpret_cast<const void*>(
-                &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, false>);
-        else
-            fn = reinterpret_cast<const void*>(
-                &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, false>);
-    }
+    const void* fn = a.partition ? select_kernel<true>(s) : select_kernel<false>(s);
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 
