@@ -361,11 +361,11 @@ COMPACTION_N = 1 << 25   # the 32M-item size the pages measure the compaction fa
 
 
 def run_compaction(steps: int, warmup: int):
-    """Select, partition, reduce-by-key and run-length encoding on 2^25 items,
-    cold caches, each beside the nearest PyTorch equivalent on the same data.
-    GB/s counts the algorithmic bytes: select 8n + 4 count, partition 12n,
-    reduce-by-key 8n + 8 runs, run-length encoding 4n + 8 runs. One COMPACTION
-    line per case on stderr."""
+    """Select, partition, reduce-by-key (int32 and fp32 values) and run-length
+    encoding on 2^25 items, cold caches, each beside the nearest PyTorch
+    equivalent on the same data. GB/s counts the algorithmic bytes: select
+    8n + 4 count, partition 12n, reduce-by-key 8n + 8 runs, run-length encoding
+    4n + 8 runs. One COMPACTION line per case on stderr."""
     import torch
     import device_wide_prefix_amd as dws
     n = COMPACTION_N
@@ -405,6 +405,7 @@ def run_compaction(steps: int, warmup: int):
             emit(name, ms, 8 * n + 4 * c, t, ok, {"selected": c, "torch": "masked_select"})
     del x, flags, mask, out
     vals = torch.from_numpy(wl.generate("i32_full", n, 23)).cuda()
+    fvals = torch.from_numpy(wl.generate("f32_pm1", n, 25)).cuda()
     uk = torch.empty(n, dtype=torch.int32, device="cuda")
     ag = torch.empty(n, dtype=torch.int32, device="cuda")
     for mean_run in (1, 16):
@@ -435,6 +436,28 @@ def run_compaction(steps: int, warmup: int):
         t = float(np.mean(time_steps(torch_rbk, prepare, steps, warmup)))
         emit("reduce_by_key", ms, 8 * n + 8 * runs, t, ok,
              {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_"})
+
+        def rbk_f32():
+            st = lib.dws_reduce_by_key(keys.data_ptr(), fvals.data_ptr(), uk.data_ptr(), ag.data_ptr(), n,
+                                       dws.FLOAT32, cnt.data_ptr(), stream)
+            if st != dws.OK:
+                raise RuntimeError(dws.status_string(st))
+
+        def torch_rbk_f32():
+            k, inv = torch.unique_consecutive(keys, return_inverse=True)
+            torch.zeros(k.numel(), dtype=torch.float32, device="cuda").index_add_(0, inv, fvals)
+
+        ms = float(np.mean(time_steps(rbk_f32, prepare, steps, warmup)))
+        # fp32 sums within 1e-4 * (sum of |value| over the run) + 1e-6 of the fp64 sums
+        want = torch.zeros(runs, dtype=torch.float64, device="cuda").index_add_(0, inverse, fvals.double())
+        scale = torch.zeros(runs, dtype=torch.float64, device="cuda").index_add_(0, inverse, fvals.double().abs())
+        got = ag[:runs].view(torch.float32).double()
+        ok = int(cnt.item()) == runs and torch.equal(uk[:runs], ref_keys) and \
+            bool(((got - want).abs() <= 1e-4 * scale + 1e-6).all())
+        t = float(np.mean(time_steps(torch_rbk_f32, prepare, steps, warmup)))
+        emit("reduce_by_key_f32", ms, 8 * n + 8 * runs, t, ok,
+             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_ (fp32)"})
+        del want, scale, got
         ms = float(np.mean(time_steps(rle, prepare, steps, warmup)))
         ok = int(cnt.item()) == runs and torch.equal(uk[:runs], ref_keys) and \
             torch.equal(ag[:runs].to(torch.int64), counts)
@@ -443,7 +466,7 @@ def run_compaction(steps: int, warmup: int):
         emit("run_length_encode", ms, 4 * n + 8 * runs, t, ok,
              {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive(return_counts=True)"})
         del keys, ref_keys, inverse, counts
-    del vals, uk, ag, flush
+    del vals, fvals, uk, ag, flush
     torch.cuda.empty_cache()
 
 

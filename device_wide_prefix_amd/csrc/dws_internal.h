@@ -103,7 +103,6 @@ struct RbkArgs {
     uint64_t n;
     int mode;
     bool aligned;            // keys (and vals) 16-byte aligned
-    int tile_index;
     uint64_t* desc;          // >= 2 * num_tiles slots
     unsigned long long* counter;
     unsigned int* watchdog;

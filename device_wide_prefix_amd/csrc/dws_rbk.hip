@@ -2,26 +2,21 @@
 // look-back (Merrill & Garland, section 4.4 compaction behaviour; section A5,
 // reduce-by-key and run-length-encode).
 //
-// Per element i: head(i) = (i == 0 or key[i] != key[i-1]), tail(i) =
-// (i == n-1 or key[i] != key[i+1]). Both kernels carry the pair (heads, value
-// since the last head) through the look-back, under "count the heads, restart
-// the value sum after the last head" (a segmented sum, not commutative), and
-// the last tile stores the number of runs. Values are 32-bit integers (sums
-// wrap modulo 2^32), fp32, or the constant 1 (run-length encoding: the sum is
-// the run length).
+// Per element i: head(i) = (i == 0 or key[i] != key[i-1]). A run ends where
+// the next one starts, so the head at p stores its key to unique_keys[run]
+// and also finishes the run before it in aggregates[run - 1]; only the array's
+// last run has no head after it and is stored from its segment's aggregate.
+// The look-back carries the pair (heads, value since the last head) under
+// "count the heads, restart the value sum after the last head" (a segmented
+// sum, not commutative); the last tile stores the number of runs. Values are
+// 32-bit integers (sums wrap modulo 2^32), fp32, or the constant 1 (run-length
+// encoding: the sum is the run length).
 //
-// k_reduce_by_key (fp32 sums) scans the pairs element by element, so every
-// element knows its run index heads_incl(i) - 1 and the sum of its run up to
-// i; heads store their key to unique_keys[run], tails the run's sum to
-// aggregates[run]. k_run_ends (integer sums, run lengths) needs no segmented
-// scan inside the tile: it counts heads with ballots and takes run sums as
-// differences of one plain prefix sum (described at the kernel).
-//
-// The neighbours key[i-1] and key[i+1] come from the registers of the same
-// lane, the adjacent lane (DPP wave shift), the adjacent chunk (readlane) or,
-// at a wave segment's two ends, one extra 4-byte load each. Stores go through
-// per-tile buffer resources ranged to the tile's runs; lanes without a store
-// use an offset past that range, which the hardware drops.
+// The neighbour key[i-1] comes from the same lane, the adjacent lane (DPP
+// wave shift), the previous chunk (readlane) or, at a wave segment's start,
+// one extra 4-byte load. Stores go through per-tile buffer resources ranged
+// to the tile's runs; lanes without a store use an offset past that range,
+// which the hardware drops.
 #include "dws_op_kernel.hpp"
 
 namespace dws {
@@ -57,179 +52,58 @@ struct RbkParams {
 };
 
 constexpr uint32_t kRbkDropped = 0x80000000u;   // past any tile's range: dropped
-constexpr int kDppWaveShl1 = 0x130;              // lane l reads lane l + 1
 // Look-back slots per lane for the run kernels: 128 predecessors per poll,
 // and fewer registers held than with the scan's four.
 constexpr int kRunLookbackSlots = 2;
 
-// Value mode: 0 integer sums, 1 fp32 sums, 2 run lengths.
-template <int BLOCK, int VEC, int CHUNKS, int MODE, int TILE_INDEX>
-__global__ void __launch_bounds__(BLOCK) k_reduce_by_key(RbkParams p)
+// Inclusive fp32 + scan over the 64 lanes in lane order, restarted at the
+// lanes set in `starts`: lane l sums lanes s..l, where s is the highest lane
+// <= l in starts (lane 0 when there is none). It is the plain scan's row-shift
+// and row-broadcast doubling with each step taken only when its source lane
+// is not before s; a step not taken adds -0.0, the exact identity.
+__device__ __forceinline__ float wave_segmented_scan_f32(float v, uint64_t starts, int lane)
 {
-    static_assert(VEC * CHUNKS <= 64, "one head and one tail bit per element in a 64-bit mask");
-    using Op = OpRunSum<MODE == 1>;
-    using V = Val<2>;
-    constexpr int W = BLOCK / 64;
-    constexpr uint32_t SEG = 64u * VEC * CHUNKS;
-    constexpr uint32_t TILE = W * SEG;
-    __shared__ uint32_t s_draw;
-    __shared__ V s_wave[W];
-    __shared__ V s_prefix;
-
-    const int lane = lane_id();
-    const int wave = (int)uniform(threadIdx.x >> 6);
-    const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
-
-    uint32_t tile = 0u;
-    if (multi) {
-        if constexpr (TILE_INDEX == kTileDispatch) {
-            tile = blockIdx.x;
-        } else {
-            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
-            __syncthreads();
-            tile = uniform(s_draw);
-            if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
-                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
-                return;
-            }
-        }
-    }
-
-    const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
-    const uint32_t vb = valid_bytes(seg_first, SEG, p.n);
-    uint32_t k[CHUNKS][VEC];
-    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.keys + seg_first, vb), lane, k);
-    uint32_t v[CHUNKS][VEC];
-    if constexpr (MODE != 2) load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.vals + seg_first, vb), lane, v);
-    // the keys just outside the wave segment (0-byte ranges where there is none)
-    const bool has_prev = seg_first > 0u && seg_first <= p.n;
-    const bool has_next = seg_first + SEG < p.n;
-    const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
-        make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
-    const uint32_t next_key = __builtin_amdgcn_raw_buffer_load_b32(
-        make_rsrc(p.keys + (has_next ? seg_first + SEG : 0u), has_next ? 4u : 0u), 0, 0, 0);
-
-    // head and tail bits, scan input. Element positions are local to the wave
-    // segment (32-bit); the segment's valid count and whether it holds the
-    // array's first or last element are uniform.
-    const uint32_t seg_elems = vb / 4u;
-    const bool holds_first = seg_first == 0u;
-    const bool holds_last = seg_first + seg_elems == p.n && seg_elems > 0u;
-    uint64_t heads = 0ull, tails = 0ull;
-    V x[CHUNKS][VEC];
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
-                                                                         0xf, true);
-        const uint32_t from_right = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][0], kDppWaveShl1, 0xf,
-                                                                          0xf, true);
-        const uint32_t left_edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : prev_key;
-        const uint32_t right_edge =
-            c < CHUNKS - 1 ? (uint32_t)__builtin_amdgcn_readlane((int)k[(c + 1) % CHUNKS][0], 0) : next_key;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t local = (uint32_t)(c * 64 * VEC) + (uint32_t)(lane * VEC + e);
-            const bool valid = local < seg_elems;
-            const uint32_t prev = e > 0 ? k[c][e - 1] : (lane > 0 ? from_left : left_edge);
-            const uint32_t next = e < VEC - 1 ? k[c][e + 1] : (lane < 63 ? from_right : right_edge);
-            const bool head = valid && ((holds_first && local == 0u) || k[c][e] != prev);
-            const bool tail = valid && ((holds_last && local + 1u == seg_elems) || k[c][e] != next);
-            heads |= (uint64_t)head << (c * VEC + e);
-            tails |= (uint64_t)tail << (c * VEC + e);
-            uint32_t val;
-            if constexpr (MODE == 2) val = valid ? 1u : 0u;
-            else val = valid ? v[c][e] : 0u;
-            x[c][e] = {{head ? 1u : 0u, val}};
-        }
-    }
-
-    const V seg_total = scan_segment_op<Op, false, VEC, CHUNKS>(x);
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            asm volatile("" : "+v"(x[c][e].w[0]));
-            asm volatile("" : "+v"(x[c][e].w[1]));
-        }
-
-    if (lane == 0) s_wave[wave] = seg_total;
-    __syncthreads();
-    V wave_pre = Op::identity(), agg = Op::identity();
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-        if (w == wave) wave_pre = agg;
-        agg = Op::combine(agg, s_wave[w]);
-    }
-
-    if (wave == 0) {
-        V prefix = Op::identity();
-        if (multi) {
-            if (tile == 0u) {
-                if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
-            } else {
-                if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
-                if (lane == 0) {
-                    desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
-                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
-                }
-            }
-        }
-        if (lane == 0) s_prefix = prefix;
-    }
-    __syncthreads();
-    const V tile_prefix = s_prefix;
-    const V seed = Op::combine(tile_prefix, wave_pre);
-
-    // runs this tile can write: the one running into it (if any) and its own.
-    // Uniform by construction (read from LDS by every lane); saying so keeps
-    // the buffer resources in SGPRs (no per-store loop).
-    const uint32_t heads_before = uniform(tile_prefix.w[0]);
-    const uint32_t tile_heads = uniform(agg.w[0]);
-    const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
-    const uint32_t range = (tile_heads + 1u) * 4u;
-    const __amdgpu_buffer_rsrc_t rkeys = make_rsrc(p.ukeys + base_run, range);
-    const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, range);
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const V y = Op::combine(seed, x[c][e]);
-            const uint32_t run_off = (y.w[0] - 1u - base_run) * 4u;
-            const int bit = c * VEC + e;
-            const uint32_t koff = ((heads >> bit) & 1ull) ? run_off : kRbkDropped;
-            const uint32_t aoff = ((tails >> bit) & 1ull) ? run_off : kRbkDropped;
-            __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(y.w[1], raggs, (int)aoff, 0, 0);
-        }
-    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + tile_heads;
+    const uint64_t upto = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+    const int dist = upto != 0ull ? lane - (63 - __builtin_clzll(upto)) : lane;
+    const int pos = lane & 15;
+    float t;
+    t = dpp_read<kDppRowShr1, 0xf, true>(v);
+    v = v + (dist >= 1 ? t : -0.0f);
+    t = dpp_read<kDppRowShr2, 0xf, true>(v);
+    v = v + (dist >= 2 ? t : -0.0f);
+    t = dpp_read<kDppRowShr4, 0xf, true>(v);
+    v = v + (dist >= 4 ? t : -0.0f);
+    t = dpp_read<kDppRowShr8, 0xf, true>(v);
+    v = v + (dist >= 8 ? t : -0.0f);
+    t = dpp_read<kDppRowBcast15, 0xa, false>(v);   // rows 1 and 3 take lane 15 of the row before
+    v = v + (dist > pos ? t : -0.0f);
+    t = dpp_read<kDppRowBcast31, 0xc, false>(v);   // rows 2 and 3 take lane 31
+    v = v + (dist >= lane - 31 ? t : -0.0f);
+    return v;
 }
 
-// Integer sums and run lengths without a segmented scan. Inside a wave
-// segment every quantity is a plain count or a plain prefix sum:
+// Inside a wave segment no (heads, value) pairs are scanned:
 //   H(i) heads at or before i (ballots and mbcnt); the run holding i is
-//        H(i) - 1 after the heads before the segment,
+//        H(i) - 1 after the heads before the segment.
+// Integer sums and run lengths use one plain prefix sum,
 //   S(i) values before i (wrapping +; for run lengths S(i) = i),
-//   B(i) S at the last head at or before i.
-// A run ends where the next one starts, so the head at p also finishes the
-// run before it, whose sum is S(p) - B(p - 1), exact modulo 2^32; when that
-// run started before the segment, B(p - 1) is minus the value carried in.
-// Only the array's last run has no head after it: the segment holding the
-// last element stores its value, which is the segment's aggregate seeded by
-// the prefix. No tail flags are needed. B comes from the lane's own heads,
-// else from the highest lane below with a head in the chunk (one ds_bpermute
-// per chunk), else from earlier chunks. The segment's aggregate for the
-// look-back is (heads, value from its last head on), the pair the segmented
-// scan above uses. fp32 sums stay on the segmented scan: a difference of long
-// prefix sums would lose the short runs' precision.
+//   B(i) S at the last head at or before i,
+// and the run finished by the head at p sums to S(p) - B(p - 1), exact modulo
+// 2^32 (when that run started before the segment, B(p - 1) is minus the value
+// carried in). B comes from the lane's own heads, else from the highest lane
+// below with a head in the chunk (one ds_bpermute per chunk), else from earlier
+// chunks. fp32 sums would lose short runs' precision in such a difference, so
+// each element instead holds its run's fp32 sum since the last head: summed in
+// the lane, then across the lanes by a segmented wave scan restarted at lanes
+// that hold a head, with the sum carried in from earlier chunks. The segment's
+// aggregate for the look-back is (heads, value from its last head on).
 // At most 128 VGPRs (four waves per SIMD): two 512-thread workgroups share a
 // CU, so one's loads overlap the other's look-back and stores.
 template <int BLOCK, int VEC, int CHUNKS, int MODE, int TILE_INDEX, int SLOTS = kRunLookbackSlots>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_run_ends(RbkParams p)
 {
-    static_assert(MODE == 0 || MODE == 2, "integer sums or run lengths");
-    using Op = OpRunSum<false>;
+    static_assert(MODE >= 0 && MODE <= 2, "integer sums, fp32 sums or run lengths");
+    using Op = OpRunSum<MODE == 1>;
     using V = Val<2>;
     constexpr int W = BLOCK / 64;
     constexpr uint32_t CH = 64u * VEC;
@@ -264,8 +138,9 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const uint32_t seg_elems = vb / 4u;
     uint32_t k[CHUNKS][VEC];
     load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.keys + seg_first, vb), lane, k);
-    uint32_t v[CHUNKS][VEC];   // values, then S before each element (integer sums only)
-    if constexpr (MODE == 0) load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.vals + seg_first, vb), lane, v);
+    uint32_t v[CHUNKS][VEC];   // values, then S before each element (integer sums) or the fp32 sum
+                               // since the last head up to the element (fp32 sums)
+    if constexpr (MODE != 2) load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.vals + seg_first, vb), lane, v);
     const bool has_prev = seg_first > 0u && seg_first < p.n;
     const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
         make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
@@ -288,6 +163,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     uint32_t below[CHUNKS];   // heads of the segment before the lane's elements of chunk c
     uint32_t b_in[CHUNKS];    // B entering the lane's elements of chunk c (used when below[c] > 0)
     uint32_t h_seg = 0u, s_seg = 0u, b_carry = 0u;   // uniform running totals over the chunks
+    float f_carry = -0.0f;                            // fp32: the sum since the last head so far
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
         const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
@@ -310,39 +186,69 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                 v[c][e] = sx[e];
             }
             s_seg += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-        } else {
+        } else if constexpr (MODE == 2) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) sx[e] = (uint32_t)(c * CH) + (uint32_t)(lane * VEC + e);
         }
         uint64_t any = 0ull;
         uint32_t cnt = 0u, chunk_count = 0u, last = 0u;
+        bool head[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
-            const bool head = k[c][e] != prev;
-            const uint64_t m = __builtin_amdgcn_ballot_w64(head);
+            head[e] = k[c][e] != prev;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(head[e]);
             any |= m;
             cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
             chunk_count += (uint32_t)__builtin_popcountll(m);
-            last = head ? sx[e] : last;
+            if constexpr (MODE != 1) last = head[e] ? sx[e] : last;
         }
         below[c] = cnt + h_seg;
         h_seg += chunk_count;
-        const uint64_t lower = any & lanes_below;
-        const int src = lower != 0ull ? 63 - __builtin_clzll(lower) : 0;
-        const uint32_t from_lane = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)last);
-        b_in[c] = lower != 0ull ? from_lane : b_carry;
-        if (any != 0ull) b_carry = (uint32_t)__builtin_amdgcn_readlane((int)last, 63 - __builtin_clzll(any));
+        if constexpr (MODE == 1) {
+            // fp32: the sum since the last head, in the lane, then across the
+            // lanes restarted at those holding a head; the value carried in
+            // from earlier chunks enters lane 0's elements before its first head
+            float g[VEC];
+            bool seen[VEC];
+            float acc = -0.0f;
+            bool any_head = false;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float x = u2f(v[c][e]);
+                acc = head[e] ? x : acc + x;
+                g[e] = acc;
+                any_head = any_head || head[e];
+                seen[e] = any_head;
+            }
+            const float lane_total = (lane == 0 && !any_head) ? f_carry + acc : acc;
+            const float incl = wave_segmented_scan_f32(lane_total, any, lane);
+            // the shift runs with every lane active (a DPP read of an inactive
+            // lane returns 0), then lane 0 takes the carry instead
+            const float from_lower = wave_shift_up1(incl);
+            const float into = lane == 0 ? f_carry : from_lower;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[c][e] = f2u(seen[e] ? g[e] : into + g[e]);
+            f_carry = u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(incl), 63));
+        } else {
+            const uint64_t lower = any & lanes_below;
+            const int src = lower != 0ull ? 63 - __builtin_clzll(lower) : 0;
+            const uint32_t from_lane = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)last);
+            b_in[c] = lower != 0ull ? from_lane : b_carry;
+            if (any != 0ull) b_carry = (uint32_t)__builtin_amdgcn_readlane((int)last, 63 - __builtin_clzll(any));
+        }
         // formed here, chunk by chunk (not sunk, which would hold every ballot)
         asm volatile("" : "+v"(below[c]));
-        asm volatile("" : "+v"(b_in[c]));
-        if constexpr (MODE == 0) {
+        if constexpr (MODE != 1) asm volatile("" : "+v"(b_in[c]));
+        if constexpr (MODE != 2) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(v[c][e]));
         }
     }
     if constexpr (MODE == 2) s_seg = seg_elems;
-    const V seg_total = {{h_seg, h_seg > 0u ? s_seg - b_carry : s_seg}};
+    V seg_total;
+    if constexpr (MODE == 1) seg_total = {{h_seg, f2u(f_carry)}};
+    else seg_total = {{h_seg, h_seg > 0u ? s_seg - b_carry : s_seg}};
 
     if (lane == 0) s_wave[wave] = seg_total;
     __syncthreads();
@@ -394,21 +300,47 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
         const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
         const uint32_t first_prev = lane > 0 ? from_left : edge;
         uint32_t off = below[c] * 4u + bias;
-        uint32_t b = below[c] > 0u ? b_in[c] : 0u - seed_value;
+        if constexpr (MODE == 1) {
+            // the run before a head ends at the element before it, whose sum
+            // since its own last head is in v (from the lane before, or the
+            // chunk before; nothing precedes the segment's first element)
+            const uint32_t g_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[c][VEC - 1], kDppWaveShr1, 0xf,
+                                                                          0xf, true);
+            const uint32_t g_edge =
+                c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v[c > 0 ? c - 1 : 0][VEC - 1], 63) : 0x80000000u;
+            const uint32_t g_first = lane > 0 ? g_left : g_edge;
+            const float seed_f = u2f(seed_value);
+            uint32_t heads_before_elem = below[c];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
-            const bool head = k[c][e] != prev;
-            uint32_t sxe;
-            if constexpr (MODE == 0) sxe = v[c][e];
-            else sxe = (uint32_t)(c * CH + e) + lane_pos;
-            off += head ? 4u : 0u;
-            // a head stores its key at its run and finishes the run before it
-            // (offset - 4; from a dropped offset that is still out of range)
-            const uint32_t koff = head ? off : kRbkDropped;
-            __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(sxe - b, raggs, (int)(koff - 4u), 0, 0);
-            b = head ? sxe : b;
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
+                const bool head = k[c][e] != prev;
+                const float g_prev = u2f(e > 0 ? v[c][e - 1] : g_first);
+                // a run that started before the segment adds the value carried in
+                const float run_sum = heads_before_elem > 0u ? g_prev : seed_f + g_prev;
+                heads_before_elem += head ? 1u : 0u;
+                off += head ? 4u : 0u;
+                const uint32_t koff = head ? off : kRbkDropped;
+                __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(f2u(run_sum), raggs, (int)(koff - 4u), 0, 0);
+            }
+        } else {
+            uint32_t b = below[c] > 0u ? b_in[c] : 0u - seed_value;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
+                const bool head = k[c][e] != prev;
+                uint32_t sxe;
+                if constexpr (MODE == 0) sxe = v[c][e];
+                else sxe = (uint32_t)(c * CH + e) + lane_pos;
+                off += head ? 4u : 0u;
+                // a head stores its key at its run and finishes the run before
+                // it (offset - 4; from a dropped offset that is still out of range)
+                const uint32_t koff = head ? off : kRbkDropped;
+                __builtin_amdgcn_raw_buffer_store_b32(k[c][e], rkeys, (int)koff, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(sxe - b, raggs, (int)(koff - 4u), 0, 0);
+                b = head ? sxe : b;
+            }
         }
     }
     if (holds_last && lane == 0) {
@@ -423,30 +355,24 @@ __global__ void __launch_bounds__(64) k_store_runs(unsigned long long* count)
     if (threadIdx.x == 0) *count = 0ull;
 }
 
+// Every shape and mode takes the workgroup index as the tile index (measured
+// faster than a drawn index at 2^25 and 2^28 elements for all three modes).
 template <int BLOCK, int VEC, int CHUNKS, int MODE>
-static hipError_t launch_rbk_mode(int tile_index, const RbkParams& p, hipStream_t stream)
+static hipError_t launch_rbk_mode(const RbkParams& p, hipStream_t stream)
 {
     RbkParams arg = p;
     void* args[] = {&arg};
-    const void* fn;
-    if constexpr (MODE == 1)
-        fn = tile_index == kTileDrawn
-                 ? reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDrawn>)
-                 : reinterpret_cast<const void*>(&k_reduce_by_key<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>);
-    else
-        fn = tile_index == kTileDrawn
-                 ? reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, kTileDrawn>)
-                 : reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>);
-    return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>),
+                           dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
 }
 
 template <int BLOCK, int VEC, int CHUNKS>
-static hipError_t launch_rbk_shape(int mode, int tile_index, const RbkParams& p, hipStream_t stream)
+static hipError_t launch_rbk_shape(int mode, const RbkParams& p, hipStream_t stream)
 {
     switch (mode) {
-    case 0: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 0>(tile_index, p, stream);
-    case 1: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 1>(tile_index, p, stream);
-    case 2: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 2>(tile_index, p, stream);
+    case 0: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 0>(p, stream);
+    case 1: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 1>(p, stream);
+    case 2: return launch_rbk_mode<BLOCK, VEC, CHUNKS, 2>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -470,19 +396,18 @@ hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
                 a.counter,                            a.watchdog,
                 a.num_runs,                           a.num_tiles,
                 a.epoch};
-    if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, kTileDispatch, p, stream);
+    if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, p, stream);
     if (a.n >= kRbkLargeMin) {
-        // 16,384-element tiles in each case. The count-and-difference kernels
-        // measured fastest on the workgroup index at 2^25 and 2^28 elements;
-        // fp32 sums (the segmented scan) take the caller's tile index.
+        // 16,384-element tiles in each case: 512 x 4 x 8 for sums, 256 x 4 x 16
+        // for run lengths (more, smaller workgroups per CU: fewer registers)
         switch (a.mode) {
-        case 0: return launch_rbk_mode<512, 4, 8, 0>(kTileDispatch, p, stream);
-        case 1: return launch_rbk_mode<512, 4, 8, 1>(a.tile_index, p, stream);
-        case 2: return launch_rbk_mode<256, 4, 16, 2>(kTileDispatch, p, stream);
+        case 0: return launch_rbk_mode<512, 4, 8, 0>(p, stream);
+        case 1: return launch_rbk_mode<512, 4, 8, 1>(p, stream);
+        case 2: return launch_rbk_mode<256, 4, 16, 2>(p, stream);
         default: return hipErrorInvalidValue;
         }
     }
-    return launch_rbk_shape<256, 4, 4>(a.mode, kTileDispatch, p, stream);
+    return launch_rbk_shape<256, 4, 4>(a.mode, p, stream);
 }
 
 }  // namespace dws
