@@ -742,7 +742,7 @@ dws_status rbk_entry(const void* keys, const void* vals, void* ukeys, void* aggs
     a.mode = mode;
     a.num_runs = num_runs;
     a.aligned = ((reinterpret_cast<uintptr_t>(keys) | (mode == 2 ? 0u : reinterpret_cast<uintptr_t>(vals))) & 15u) == 0;
-    const uint64_t tiles = n == 0 ? 0 : ceil_div(n, rbk_tile_elems(n, a.aligned));
+    const uint64_t tiles = n == 0 ? 0 : ceil_div(n, rbk_tile_elems(n, a.aligned, mode));
     a.num_tiles = (uint32_t)tiles;
     if (tiles <= 1) return from_hip(launch_rbk(a, stream));
     Workspace* ws = nullptr;

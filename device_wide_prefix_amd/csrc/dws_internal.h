@@ -110,8 +110,8 @@ struct RbkArgs {
     uint32_t num_tiles;
     unsigned int* epoch;     // the workspace epoch word
 };
-constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384-element tiles from here
-uint32_t rbk_tile_elems(uint64_t n, bool aligned);
+constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384 (32768 for run lengths) from here
+uint32_t rbk_tile_elems(uint64_t n, bool aligned, int mode);
 hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream);
 
 // Scan under a generic operator (dws_op_kernel.hpp). Kinds name an

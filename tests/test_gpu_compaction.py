@@ -77,8 +77,9 @@ def _check_runs(name, keys, got_keys, got_aggs, got_count, vals=None):
     assert np.all(got_keys[r:] == SENTINEL) and np.all(got_aggs[r:] == SENTINEL), f"{name}: wrote past the runs"
 
 
-# around the small (4096) and large (16384, from 2^22) tiles and the drawn
-# tile index (2^25); runs from length 1 to longer than a tile
+# around the small (4096) and large (16384 or 32768, from 2^22) tiles, a
+# ragged last tile with empty wave segments, and 2^25 + 5; runs from length
+# 1 to longer than a tile
 RBK_SIZES = [1, 2, 3, 4095, 4096, 4097, 3 * 4096 + 7, 100_003, (1 << 22) - 1, (1 << 22) + 16384 + 3,
              (1 << 25) + 5]
 MEAN_RUNS = [1, 3, 200, 50_000]
@@ -134,15 +135,15 @@ def _run_both(keys, vals, name):
 def test_run_boundaries(gpu):
     # Where a run's sum comes from: its own segment, the value carried in
     # through the look-back, or the segment aggregate of the array's last
-    # element. Wave segments hold 2,048 (sums) or 4,096 (run lengths) keys
-    # and tiles 16,384 from 2^22 keys, 4,096-key tiles below.
+    # element. From 2^22 keys wave segments hold 2,048 (sums) or 4,096 (run
+    # lengths) keys and tiles 16,384 or 32,768; 4,096-key tiles below.
     big = (1 << 22) + 4096          # the array ends exactly at a segment's end
     for n in (5000, big, (1 << 22) + 4097):
         vals = wl.generate("u32_full", n, n + 7)
         for key in (0, 0xFFFFFFFF, 12345):
             note(f"run boundaries: one run of key {key:#x}, n={n}")
             _run_both(np.full(n, key, dtype=np.uint32), vals, f"one run key={key:#x} n={n}")
-        for length in (2048, 4096, 16384):
+        for length in (2048, 4096, 16384, 32768):
             note(f"run boundaries: runs of exactly {length}, n={n}")
             keys = (np.arange(n, dtype=np.uint32) // length).astype(np.uint32) * np.uint32(2654435761)
             _run_both(keys, vals, f"runs of {length} n={n}")
