@@ -755,7 +755,6 @@ dws_status rbk_entry(const void* keys, const void* vals, void* ukeys, void* aggs
     if (s != DWS_OK) return s;
     a.epoch = ws->epoch();
     a.desc = ws->desc;
-    a.counter = ws->counter();
     a.watchdog = ws->watchdog();
     return from_hip(launch_rbk(a, stream));
 }

@@ -104,7 +104,6 @@ struct RbkArgs {
     int mode;
     bool aligned;            // keys (and vals) 16-byte aligned
     uint64_t* desc;          // >= 2 * num_tiles slots
-    unsigned long long* counter;
     unsigned int* watchdog;
     unsigned long long* num_runs;
     uint32_t num_tiles;

@@ -44,7 +44,6 @@ struct RbkParams {
     uint32_t* aggs;           // sums, or run lengths
     uint64_t n;
     uint64_t* desc;
-    unsigned long long* counter;
     unsigned int* watchdog;
     unsigned long long* num_runs;
     uint32_t num_tiles;
@@ -98,8 +97,11 @@ __device__ __forceinline__ float wave_segmented_scan_f32(float v, uint64_t start
 // that hold a head, with the sum carried in from earlier chunks. The segment's
 // aggregate for the look-back is (heads, value from its last head on).
 // At most 128 VGPRs (four waves per SIMD): two 512-thread workgroups share a
-// CU, so one's loads overlap the other's look-back and stores.
-template <int BLOCK, int VEC, int CHUNKS, int MODE, int TILE_INDEX, int SLOTS = kRunLookbackSlots>
+// CU, so one's loads overlap the other's look-back and stores. The tile index
+// is the workgroup index (measured faster than a drawn index at 2^25 and 2^28
+// elements in every mode): it relies on the GPU starting each XCD's
+// workgroups in index order, and the watchdog bounds every wait.
+template <int BLOCK, int VEC, int CHUNKS, int MODE, int SLOTS = kRunLookbackSlots>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_run_ends(RbkParams p)
 {
     static_assert(MODE >= 0 && MODE <= 2, "integer sums, fp32 sums or run lengths");
@@ -109,7 +111,6 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr uint32_t CH = 64u * VEC;
     constexpr uint32_t SEG = CH * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
-    __shared__ uint32_t s_draw;
     __shared__ V s_wave[W];
     __shared__ V s_prefix;
 
@@ -117,21 +118,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
     const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
-
-    uint32_t tile = 0u;
-    if (multi) {
-        if constexpr (TILE_INDEX == kTileDispatch) {
-            tile = blockIdx.x;
-        } else {
-            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
-            __syncthreads();
-            tile = uniform(s_draw);
-            if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
-                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
-                return;
-            }
-        }
-    }
+    const uint32_t tile = multi ? (uint32_t)blockIdx.x : 0u;
 
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t vb = valid_bytes(seg_first, SEG, p.n);
@@ -362,14 +349,12 @@ __global__ void __launch_bounds__(64) k_store_runs(unsigned long long* count)
     if (threadIdx.x == 0) *count = 0ull;
 }
 
-// Every shape and mode takes the workgroup index as the tile index (measured
-// faster than a drawn index at 2^25 and 2^28 elements for all three modes).
 template <int BLOCK, int VEC, int CHUNKS, int MODE>
 static hipError_t launch_rbk_mode(const RbkParams& p, hipStream_t stream)
 {
     RbkParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, kTileDispatch>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE>),
                            dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
 }
 
@@ -401,9 +386,8 @@ hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
     RbkParams p{static_cast<const uint32_t*>(a.keys), static_cast<const uint32_t*>(a.vals),
                 static_cast<uint32_t*>(a.ukeys),      static_cast<uint32_t*>(a.aggs),
                 a.n,                                  a.desc,
-                a.counter,                            a.watchdog,
-                a.num_runs,                           a.num_tiles,
-                a.epoch};
+                a.watchdog,                           a.num_runs,
+                a.num_tiles,                          a.epoch};
     if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, p, stream);
     if (a.n >= kRbkLargeMin) {
         // sums: 16,384-element tiles (512 x 4 x 8); run lengths hold no values
