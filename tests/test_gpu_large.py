@@ -51,3 +51,77 @@ def test_all_ones_past_32_bits(gpu, n, exclusive):
         del x
         torch.cuda.empty_cache()
     assert dws.watchdog_trips() == 0
+
+
+# The compaction family takes n below 2^32 (counts travel in 32-bit descriptor
+# values): 2^32 - 1 is its largest input.
+COMPACTION_MAX = (1 << 32) - 1
+
+
+def _fill(t, n: int, fn):
+    """t[i] = fn(i) (an int64 tensor expression of the indices), slice by slice."""
+    import torch
+    for s in range(0, n, SLICE):
+        e = min(n, s + SLICE)
+        t[s:e] = fn(torch.arange(s, e, dtype=torch.int64, device=t.device)).to(t.dtype)
+
+
+def test_select_at_the_count_limit(gpu):
+    # x[i] = i mod 2^32, selected where i mod 3 != 0; the j-th selected index
+    # is 3 (j // 2) + j % 2 + 1
+    import torch
+    n = COMPACTION_MAX
+    _need(12 * n)
+    note(f"select n={n} (i mod 3 != 0)")
+    x = torch.empty(n, dtype=torch.int32, device="cuda")
+    flags = torch.empty(n, dtype=torch.int32, device="cuda")
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    try:
+        _fill(x, n, lambda i: (i & 0xFFFFFFFF) - ((i & 0x80000000) << 1))
+        _fill(flags, n, lambda i: (i % 3 != 0).to(torch.int64))
+        _, cnt = dws.select_flagged(x, flags, out=out)
+        torch.cuda.synchronize()
+        count = int(cnt.item())
+        assert count == n - (n + 2) // 3
+        for s in range(0, count, SLICE):
+            e = min(count, s + SLICE)
+            j = torch.arange(s, e, dtype=torch.int64, device="cuda")
+            want = (3 * (j // 2) + j % 2 + 1) & 0xFFFFFFFF
+            got = out[s:e].to(torch.int64) & 0xFFFFFFFF
+            assert torch.equal(got, want), f"select mismatch in [{s}, {e})"
+    finally:
+        del x, flags, out
+        torch.cuda.empty_cache()
+
+
+def test_runs_at_the_count_limit(gpu):
+    # keys[i] = i // 7: runs of 7 and a last one of 3; reduce-by-key of
+    # all-ones values gives the same lengths as run-length encoding
+    import torch
+    n = COMPACTION_MAX
+    _need(16 * n)
+    runs = (n + 6) // 7
+    keys = torch.empty(n, dtype=torch.int32, device="cuda")
+    try:
+        _fill(keys, n, lambda i: i // 7)
+        ones = torch.ones(n, dtype=torch.int32, device="cuda")
+        for kind in ("rle", "sums"):
+            note(f"{kind} n={n} (runs of 7)")
+            if kind == "rle":
+                uk, ag, cnt = dws.run_length_encode(keys)
+            else:
+                uk, ag, cnt = dws.reduce_by_key(keys, ones)
+            torch.cuda.synchronize()
+            assert int(cnt.item()) == runs
+            for s in range(0, runs, SLICE):
+                e = min(runs, s + SLICE)
+                r = torch.arange(s, e, dtype=torch.int64, device="cuda")
+                assert torch.equal(uk[s:e].to(torch.int64), r), f"{kind}: keys in [{s}, {e})"
+                want = torch.where(r == runs - 1, n - 7 * (runs - 1), 7)
+                assert torch.equal(ag[s:e].to(torch.int64), want), f"{kind}: lengths in [{s}, {e})"
+            del uk, ag, cnt
+        del ones
+    finally:
+        del keys
+        torch.cuda.empty_cache()
+    assert dws.watchdog_trips() == 0
