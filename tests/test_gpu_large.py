@@ -125,3 +125,51 @@ def test_runs_at_the_count_limit(gpu):
         del keys
         torch.cuda.empty_cache()
     assert dws.watchdog_trips() == 0
+
+
+def test_operators_past_32_bits(gpu):
+    # dws_scan_op past 2^32 elements, in place, against closed forms:
+    # max of x[i] = i mod 2^32 (uint32) climbs to 2^32 - 1 and stays there after
+    # the wrap; the componentwise sum of all-ones uint32 pairs is (i + 1, i + 1)
+    # mod 2^32, inclusive
+    import torch
+    n = (1 << 32) + 12345
+    stream = torch.cuda.current_stream().cuda_stream
+    _need(8 * n)
+    x = torch.empty(n, dtype=torch.int32, device="cuda")
+    try:
+        _fill(x, n, lambda i: (i & 0xFFFFFFFF) - ((i & 0x80000000) << 1))
+        for exclusive in (False, True):
+            note(f"uint32 max scan n={n} exclusive={exclusive}, in place")
+            if exclusive:
+                _fill(x, n, lambda i: (i & 0xFFFFFFFF) - ((i & 0x80000000) << 1))
+            st = dws.scan_op_ptr(x.data_ptr(), x.data_ptr(), n, dws.UINT32, dws.OP_MAX, exclusive, stream)
+            assert st == dws.OK, dws.status_string(st)
+            torch.cuda.synchronize()
+            for s in range(0, n, SLICE):
+                e = min(n, s + SLICE)
+                i = torch.arange(s, e, dtype=torch.int64, device="cuda")
+                last = i - 1 if exclusive else i                 # the last index the max covers
+                want = torch.clamp(last, 0, 0xFFFFFFFF)          # exclusive y[0] is the identity 0
+                got = x[s:e].to(torch.int64) & 0xFFFFFFFF
+                assert torch.equal(got, want), f"max exclusive={exclusive}: mismatch in [{s}, {e})"
+    finally:
+        del x
+        torch.cuda.empty_cache()
+    _need(8 * n)
+    pairs = torch.ones((n, 2), dtype=torch.int32, device="cuda")
+    try:
+        note(f"uint32 pair sum n={n} pairs, in place")
+        st = dws.scan_op_ptr(pairs.data_ptr(), pairs.data_ptr(), n, dws.PAIR_U32, dws.OP_SUM, False, stream)
+        assert st == dws.OK, dws.status_string(st)
+        torch.cuda.synchronize()
+        for s in range(0, n, SLICE):
+            e = min(n, s + SLICE)
+            want = torch.arange(s + 1, e + 1, dtype=torch.int64, device="cuda") & 0xFFFFFFFF
+            for w in range(2):
+                got = pairs[s:e, w].to(torch.int64) & 0xFFFFFFFF
+                assert torch.equal(got, want), f"pair sum word {w}: mismatch in [{s}, {e})"
+    finally:
+        del pairs
+        torch.cuda.empty_cache()
+    assert dws.watchdog_trips() == 0
