@@ -470,6 +470,19 @@ def run_compaction(steps: int, warmup: int):
     torch.cuda.empty_cache()
 
 
+def device_info():
+    """Name, compute units, memory clock and bus width as the runtime reports
+    them, and the bandwidth those imply, beside the published 8 TB/s used as
+    the roofline peak. HBM3E moves 4 bits per pin per reported memory clock
+    (8 Gb/s per pin at 2 GHz), so the implied figure is 4 x clock x width."""
+    import torch
+    import device_wide_prefix_amd as dws
+    m = dws.device_memory_info()
+    implied = 4.0 * m["memory_clock_khz"] * 1e3 * m["memory_bus_width_bits"] / 8 / 1e9
+    return {"name": torch.cuda.get_device_properties(0).name, "arch": torch.cuda.get_device_properties(0).gcnArchName,
+            **m, "implied_peak_gbps": round(implied, 1), "roofline_peak_gbps": HBM_PEAK_GBPS}
+
+
 def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
     """The sequential oracle on the same input, timed on one host core, repeated
     until about budget_s seconds of CPU work (the oracle is one loop: 1 thread)."""
@@ -610,6 +623,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "lookback_stall_share": s.get("lookback_stall_share"),
         "tile_phase_mean_us": s.get("phase_mean_us"),
+        "device": device_info(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

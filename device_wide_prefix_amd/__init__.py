@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
-    "dws_run_length_encode",
+    "dws_run_length_encode", "dws_device_memory_info",
 )
 
 
@@ -91,6 +91,8 @@ def load_library():
     lib.dws_release_workspaces.restype = ci
     lib.dws_watchdog_trips.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
     lib.dws_watchdog_trips.restype = ci
+    lib.dws_device_memory_info.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
+    lib.dws_device_memory_info.restype = ci
     lib.dws_scan_debug.argtypes = [vp, vp, sz, ci, ci, ci, cu, cu, cu, cu,
                                    ctypes.POINTER(ctypes.c_ulonglong), vp]
     lib.dws_scan_debug.restype = ci
@@ -374,6 +376,15 @@ def run_length_encode(keys, unique_keys=None, lengths=None, count=None, stream=N
                                                     keys.numel(), count.data_ptr(), _stream(keys, stream)),
                "dws_run_length_encode")
     return unique_keys, lengths, count
+
+
+def device_memory_info() -> dict:
+    """Memory clock (kHz), memory bus width (bits) and compute units of the
+    current device, as the HIP runtime reports them."""
+    clk, width, cus = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(load_library().dws_device_memory_info(ctypes.byref(clk), ctypes.byref(width), ctypes.byref(cus)),
+           "dws_device_memory_info")
+    return {"memory_clock_khz": clk.value, "memory_bus_width_bits": width.value, "compute_units": cus.value}
 
 
 def watchdog_trips() -> int:

@@ -530,6 +530,18 @@ dws_status dws_release_workspaces(void)
     }
 }
 
+dws_status dws_device_memory_info(int* memory_clock_khz, int* memory_bus_width_bits, int* compute_units)
+{
+    if (memory_clock_khz == nullptr || memory_bus_width_bits == nullptr || compute_units == nullptr)
+        return DWS_ERR_INVALID_ARG;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(memory_clock_khz, hipDeviceAttributeMemoryClockRate, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(memory_bus_width_bits, hipDeviceAttributeMemoryBusWidth, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(compute_units, hipDeviceAttributeMultiprocessorCount, dev);
+    return e == hipSuccess ? DWS_OK : from_hip(e);
+}
+
 dws_status dws_watchdog_trips(unsigned long long* trips)
 {
     if (trips == nullptr) return DWS_ERR_INVALID_ARG;

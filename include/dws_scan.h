@@ -324,6 +324,14 @@ dws_status dws_release_workspaces(void);
 dws_status dws_watchdog_trips(unsigned long long* trips);
 
 /*
+ * Memory clock (kHz), memory bus width (bits) and compute-unit count of the
+ * current device, as the HIP runtime reports them, for stating the HBM
+ * roofline beside measurements. Every pointer must be non-null
+ * (DWS_ERR_INVALID_ARG); a failing runtime query returns DWS_ERR_HIP.
+ */
+dws_status dws_device_memory_info(int* memory_clock_khz, int* memory_bus_width_bits, int* compute_units);
+
+/*
  * Protocol inspection kernel: the same descriptor protocol and look-back as
  * the single-pass scan, but with one wavefront per tile and a run-time tile
  * size of 1..64 elements, so that small inputs exercise many tiles and

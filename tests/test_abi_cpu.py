@@ -148,6 +148,7 @@ def test_debug_and_selftest_validation(lib):
     assert s(None, FAKE, FAKE, 1, dws.INT32, None) == dws.ERR_INVALID_ARG
     assert s(FAKE, FAKE, FAKE, 1, 5, None) == dws.ERR_INVALID_ARG
     assert lib.dws_watchdog_trips(None) == dws.ERR_INVALID_ARG
+    assert lib.dws_device_memory_info(None, None, None) == dws.ERR_INVALID_ARG
     assert lib.dws_reserve((1 << 35) + 1, None) == dws.ERR_UNSUPPORTED
 
 
