@@ -229,7 +229,10 @@ def run_sweep(steps: int, warmup: int):
     return rows
 
 
-def run_select(steps: int, warmup: int, in_place: bool):
+ORACLE_SAMPLE = 1 << 26   # elements of a large input the oracle is timed on
+
+
+def run_select(steps: int, warmup: int, in_place: bool, with_oracle: bool = True):
     """Stream compaction: C5's 0/1 flags (Bernoulli 0.5, seed 4) select from
     uniform int32 values (seed 5). Algorithmic bytes = read values and flags
     (8 n) + write the selected values (4 count). Also times torch.masked_select
@@ -238,8 +241,10 @@ def run_select(steps: int, warmup: int, in_place: bool):
     import device_wide_prefix_amd as dws
     w = wl.WORKLOADS["C5"]
     n = w.n
-    flags = torch.from_numpy(wl.generate_workload(w)).to("cuda")
-    vals = torch.from_numpy(wl.generate("i32_full", n, wl.SELECT_VALUE_SEED)).to("cuda")
+    flags_h = wl.generate_workload(w)
+    vals_h = wl.generate("i32_full", n, wl.SELECT_VALUE_SEED)
+    flags = torch.from_numpy(flags_h).to("cuda")
+    vals = torch.from_numpy(vals_h).to("cuda")
     work = torch.empty_like(vals)
     out = work if in_place else torch.empty_like(vals)
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
@@ -274,7 +279,14 @@ def run_select(steps: int, warmup: int, in_place: bool):
     tt = time_steps(torch_select, prepare, max(3, steps // 2), 2)
     row["torch_masked_select_ms_mean"] = float(np.mean(tt))
     row["speedup_vs_torch_masked_select"] = float(np.mean(tt)) / mean
-    del flags, vals, work, out, flush, mask
+    if with_oracle:
+        import oracle
+        m = min(n, ORACLE_SAMPLE)
+        fs, vs = flags_h[:m], vals_h[:m]
+        sel = int(np.count_nonzero(fs))
+        row["cpu_baseline"] = oracle_rate(lambda: oracle.select_flagged(vs, fs), 8 * m + 4 * sel,
+                                        f"first {m} values and flags of the same input")
+    del flags, vals, work, out, flush, mask, flags_h, vals_h
     torch.cuda.empty_cache()
     return row
 
@@ -288,6 +300,18 @@ OP_CASES = {
     "segsum_i32_f32": (0x4, 3, "segsum_i32_f32", 8),
 }
 OP_BYTES = 1 << 31
+
+
+def _op_oracle():
+    """Operator name -> the oracle's inclusive scan for it (CPU baseline only)."""
+    import oracle
+    return {
+        "max_i32": lambda x: oracle.scan_minmax(x, True),
+        "min_u32": lambda x: oracle.scan_minmax(x, False),
+        "sum_pair_i32_f32": lambda x: oracle.scan_pair_sum_i32_f32(x),
+        "affine_u32": lambda x: oracle.scan_affine_u32(x),
+        "segsum_i32_f32": lambda x: oracle.scan_segsum_i32_f32(x),
+    }
 
 
 def op_property_check(name: str, x: np.ndarray, y: np.ndarray) -> bool:
@@ -315,7 +339,7 @@ def op_property_check(name: str, x: np.ndarray, y: np.ndarray) -> bool:
     return False
 
 
-def run_ops(steps: int, warmup: int):
+def run_ops(steps: int, warmup: int, with_oracle: bool = True):
     """Generic-operator scans of 1 GiB of input (2^28 32-bit or 2^27 pair
     elements), out of place, cold caches; GB/s counts 2 x the input bytes,
     like the + scan, against a same-size memcpy. One OPS line per operator."""
@@ -325,6 +349,7 @@ def run_ops(steps: int, warmup: int):
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     hip = Hip()
+    OP_ORACLE = _op_oracle() if with_oracle else {}
     for name, (op, dtype, kind, esize) in OP_CASES.items():
         n = (OP_BYTES // 2) // esize
         x = wl.op_input(kind, n, seed=11)
@@ -350,6 +375,11 @@ def run_ops(steps: int, warmup: int):
                "gbps": 2 * n * esize / (mean * 1e-3) / 1e9, "memcpy_gbps": 2 * n * esize / (mcm * 1e-3) / 1e9,
                "frac_memcpy": mcm / mean, "frac_hbm_peak": 2 * n * esize / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                "property_check": ok}
+        if with_oracle:
+            m = min(n, ORACLE_SAMPLE // 4)
+            xs = np.ascontiguousarray(x[:m])
+            row["cpu_baseline"] = oracle_rate(lambda: OP_ORACLE[name](xs), 2 * m * esize,
+                                              f"first {m} elements of the same input")
         log("OPS " + json.dumps(row))
         rows.append(row)
         del xd, out
@@ -360,7 +390,7 @@ def run_ops(steps: int, warmup: int):
 COMPACTION_N = 1 << 25   # the 32M-item size the pages measure the compaction family on
 
 
-def run_compaction(steps: int, warmup: int):
+def run_compaction(steps: int, warmup: int, with_oracle: bool = True):
     """Select, partition, reduce-by-key (int32 and fp32 values) and run-length
     encoding on 2^25 items, cold caches, each beside the nearest PyTorch
     equivalent on the same data. GB/s counts the algorithmic bytes: select
@@ -377,14 +407,20 @@ def run_compaction(steps: int, warmup: int):
     def prepare():
         flush.sum()
 
-    def emit(name, ms, algo_bytes, torch_ms, ok, extra):
+    def emit(name, ms, algo_bytes, torch_ms, ok, extra, oracle_call=None):
         row = {"op": name, "n": n, "ms_mean": ms, "gbps": algo_bytes / (ms * 1e-3) / 1e9,
                "frac_hbm_peak": algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "torch_ms_mean": torch_ms,
                "speedup_vs_torch": (torch_ms / ms) if torch_ms else None, "property_check": bool(ok), **extra}
+        if with_oracle and oracle_call is not None:
+            row["cpu_baseline"] = oracle_rate(oracle_call, algo_bytes, "the same input, whole")
         log("COMPACTION " + json.dumps(row))
 
-    x = torch.from_numpy(wl.generate("i32_full", n, 21)).cuda()
-    flags = torch.from_numpy(wl.generate("flags_half", n, 22)).cuda()
+    if with_oracle:
+        import oracle
+    x_h = wl.generate("i32_full", n, 21)
+    flags_h = wl.generate("flags_half", n, 22)
+    x = torch.from_numpy(x_h).cuda()
+    flags = torch.from_numpy(flags_h).cuda()
     mask = flags != 0
     out = torch.empty_like(x)
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
@@ -399,17 +435,22 @@ def run_compaction(steps: int, warmup: int):
         if name == "partition_flagged":
             ok = ok and torch.equal(out[c:], x[~mask].flip(0))
             t = float(np.mean(time_steps(lambda: torch.cat((x[mask], x[~mask].flip(0))), prepare, steps, warmup)))
-            emit(name, ms, 12 * n, t, ok, {"selected": c, "torch": "cat(x[mask], x[~mask].flip(0))"})
+            emit(name, ms, 12 * n, t, ok, {"selected": c, "torch": "cat(x[mask], x[~mask].flip(0))"},
+                 (lambda: oracle.partition_flagged(x_h, flags_h)) if with_oracle else None)
         else:
             t = float(np.mean(time_steps(lambda: torch.masked_select(x, mask), prepare, steps, warmup)))
-            emit(name, ms, 8 * n + 4 * c, t, ok, {"selected": c, "torch": "masked_select"})
-    del x, flags, mask, out
-    vals = torch.from_numpy(wl.generate("i32_full", n, 23)).cuda()
-    fvals = torch.from_numpy(wl.generate("f32_pm1", n, 25)).cuda()
+            emit(name, ms, 8 * n + 4 * c, t, ok, {"selected": c, "torch": "masked_select"},
+                 (lambda: oracle.select_flagged(x_h, flags_h)) if with_oracle else None)
+    del x, flags, mask, out, x_h, flags_h
+    vals_h = wl.generate("i32_full", n, 23)
+    fvals_h = wl.generate("f32_pm1", n, 25)
+    vals = torch.from_numpy(vals_h).cuda()
+    fvals = torch.from_numpy(fvals_h).cuda()
     uk = torch.empty(n, dtype=torch.int32, device="cuda")
     ag = torch.empty(n, dtype=torch.int32, device="cuda")
     for mean_run in (1, 16):
-        keys = torch.from_numpy(wl.run_keys(n, mean_run, 24).view(np.int32)).cuda()
+        keys_h = wl.run_keys(n, mean_run, 24)
+        keys = torch.from_numpy(keys_h.view(np.int32)).cuda()
         ref_keys, inverse, counts = torch.unique_consecutive(keys, return_inverse=True, return_counts=True)
         runs = ref_keys.numel()
 
@@ -435,7 +476,8 @@ def run_compaction(steps: int, warmup: int):
             torch.equal(ag[:runs].to(torch.int64) & 0xFFFFFFFF, want)
         t = float(np.mean(time_steps(torch_rbk, prepare, steps, warmup)))
         emit("reduce_by_key", ms, 8 * n + 8 * runs, t, ok,
-             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_"})
+             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_"},
+             (lambda: oracle.reduce_by_key(keys_h, vals_h)) if with_oracle else None)
 
         def rbk_f32():
             st = lib.dws_reduce_by_key(keys.data_ptr(), fvals.data_ptr(), uk.data_ptr(), ag.data_ptr(), n,
@@ -456,7 +498,8 @@ def run_compaction(steps: int, warmup: int):
             bool(((got - want).abs() <= 1e-4 * scale + 1e-6).all())
         t = float(np.mean(time_steps(torch_rbk_f32, prepare, steps, warmup)))
         emit("reduce_by_key_f32", ms, 8 * n + 8 * runs, t, ok,
-             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_ (fp32)"})
+             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive + index_add_ (fp32)"},
+             (lambda: oracle.reduce_by_key(keys_h, fvals_h)) if with_oracle else None)
         del want, scale, got
         ms = float(np.mean(time_steps(rle, prepare, steps, warmup)))
         ok = int(cnt.item()) == runs and torch.equal(uk[:runs], ref_keys) and \
@@ -464,9 +507,10 @@ def run_compaction(steps: int, warmup: int):
         t = float(np.mean(time_steps(lambda: torch.unique_consecutive(keys, return_counts=True), prepare, steps,
                                      warmup)))
         emit("run_length_encode", ms, 4 * n + 8 * runs, t, ok,
-             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive(return_counts=True)"})
-        del keys, ref_keys, inverse, counts
-    del vals, fvals, uk, ag, flush
+             {"mean_run": mean_run, "runs": runs, "torch": "unique_consecutive(return_counts=True)"},
+             (lambda: oracle.run_length_encode(keys_h)) if with_oracle else None)
+        del keys, ref_keys, inverse, counts, keys_h
+    del vals, fvals, uk, ag, flush, vals_h, fvals_h
     torch.cuda.empty_cache()
 
 
@@ -502,6 +546,24 @@ def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
     return {"value": round(w.algorithmic_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full {w.name} input (N={w.n}), {len(reps)} repetitions, median "
                       f"{med * 1e3:.1f} ms; host has {os.cpu_count()} logical CPUs"}
+
+
+def oracle_rate(call, algo_bytes: int, sample: str, budget_s: float = 2.0):
+    """The oracle's rate on one bounded sample: call() repeated until about
+    budget_s seconds of CPU work (at least once), median time, the same
+    algorithmic-bytes convention as the GPU row it stands beside. The oracle
+    is one sequential loop, so one host core."""
+    reps = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        call()
+        reps.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(reps) >= 20:
+            break
+    med = float(np.median(reps))
+    return {"gbps": round(algo_bytes / med / 1e9, 3), "ms": round(med * 1e3, 2), "cores": 1, "kind": "oracle",
+            "repetitions": len(reps), "sample": sample}
 
 
 def traffic_for_current_kernel():
@@ -641,13 +703,14 @@ def main():
 
     if args.sweep:
         run_sweep(max(5, args.steps // 2), 3)
+    timed_oracle = not args.no_cpu_baseline
     if args.ops:
-        run_ops(args.steps, args.warmup)
+        run_ops(args.steps, args.warmup, timed_oracle)
     if args.compaction:
-        run_compaction(args.steps, args.warmup)
+        run_compaction(args.steps, args.warmup, timed_oracle)
     if args.select:
         for in_place in (False, True):
-            log("SELECT " + json.dumps(run_select(args.steps, args.warmup, in_place)))
+            log("SELECT " + json.dumps(run_select(args.steps, args.warmup, in_place, timed_oracle and not in_place)))
 
     print(json.dumps(line), flush=True)
 
