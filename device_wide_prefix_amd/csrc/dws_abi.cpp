@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstring>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -60,6 +61,20 @@ dws_status from_hip(hipError_t e)
 }
 
 bool valid_dtype(int d) { return d == DWS_INT32 || d == DWS_UINT32 || d == DWS_FLOAT32; }
+
+// The value a C caller passed in an enum parameter, read from its bytes. A C
+// caller may pass any int there; in C++ reading an enum object whose value is
+// outside the enum's range is undefined, so the ABI never reads these
+// parameters as enums, only as the int they hold.
+// Taken by reference: copying the parameter by value would be such a read.
+template <class E>
+int enum_arg(const E& e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums travel as int");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
 
 // All checks on the data pointers that need no HIP call, for elements of
 // `esize` bytes. n == 0 is accepted with any pointers.
@@ -408,11 +423,12 @@ dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                        hipStream_t stream)
 {
     try {
-        if ((int)dtype < DWS_INT32 || (int)dtype > DWS_PAIR_U32) return DWS_ERR_INVALID_ARG;
-        if ((int)op < DWS_OP_SUM || (int)op > DWS_OP_SEGMENTED_SUM) return DWS_ERR_INVALID_ARG;
-        if (op == DWS_OP_SUM && valid_dtype((int)dtype))
-            return scan_entry(d_in, d_out, n, (int)dtype, exclusive, nullptr, stream);
-        const int kind = op_kind((int)dtype, (int)op);
+        const int dt = enum_arg(dtype), o = enum_arg(op);
+        if (dt < DWS_INT32 || dt > DWS_PAIR_U32) return DWS_ERR_INVALID_ARG;
+        if (o < DWS_OP_SUM || o > DWS_OP_SEGMENTED_SUM) return DWS_ERR_INVALID_ARG;
+        if (o == DWS_OP_SUM && valid_dtype(dt))
+            return scan_entry(d_in, d_out, n, dt, exclusive, nullptr, stream);
+        const int kind = op_kind(dt, o);
         if (kind < 0) return DWS_ERR_UNSUPPORTED;
         const dws_status s = validate_sized(d_in, d_out, n, 4u * (size_t)op_kind_words(kind));
         if (s != DWS_OK || n == 0) return s;
@@ -426,23 +442,23 @@ dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
 
 dws_status scan_inclusive(const void* d_in, void* d_out, size_t n, dws_dtype dtype, hipStream_t stream)
 {
-    return scan_entry(d_in, d_out, n, (int)dtype, 0, nullptr, stream);
+    return scan_entry(d_in, d_out, n, enum_arg(dtype), 0, nullptr, stream);
 }
 
 dws_status scan_exclusive(const void* d_in, void* d_out, size_t n, dws_dtype dtype, hipStream_t stream)
 {
-    return scan_entry(d_in, d_out, n, (int)dtype, 1, nullptr, stream);
+    return scan_entry(d_in, d_out, n, enum_arg(dtype), 1, nullptr, stream);
 }
 
 dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive,
                        const dws_options* opt, hipStream_t stream)
 {
-    return scan_entry(d_in, d_out, n, (int)dtype, exclusive, opt, stream);
+    return scan_entry(d_in, d_out, n, enum_arg(dtype), exclusive, opt, stream);
 }
 
 const char* dws_status_string(dws_status status)
 {
-    switch (status) {
+    switch (enum_arg(status)) {
     case DWS_OK: return "ok";
     case DWS_ERR_INVALID_ARG: return "invalid argument";
     case DWS_ERR_UNSUPPORTED: return "unsupported size or option combination";
@@ -576,7 +592,7 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
         if (tile_elems == 0 || tile_elems > kDebugMaxTile) return DWS_ERR_INVALID_ARG;
         if (delay_ticks > kMaxDebugDelayTicks) return DWS_ERR_INVALID_ARG;
         if (delay_every != 0 && delay_phase >= delay_every) return DWS_ERR_INVALID_ARG;
-        dws_status s = validate(d_in, d_out, n, (int)dtype);
+        dws_status s = validate(d_in, d_out, n, enum_arg(dtype));
         if (s != DWS_OK || n == 0) return s;
         const uint64_t num_tiles = ceil_div(n, tile_elems);
         if (num_tiles > 0x7fffffffull || num_tiles * 64ull > kMaxGridThreads) return DWS_ERR_UNSUPPORTED;
@@ -593,7 +609,7 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
         a.in = d_in;
         a.out = d_out;
         a.n = n;
-        a.kind = kind_of((int)dtype);
+        a.kind = kind_of(enum_arg(dtype));
         a.exclusive = exclusive != 0;
         a.mode = variant == DWS_VARIANT_CHAINED ? kModeChained : kModeDecoupled;
         a.tile_elems = tile_elems;
@@ -629,7 +645,7 @@ dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype 
                              hipStream_t stream)
 {
     try {
-        if (!valid_dtype((int)dtype)) return DWS_ERR_INVALID_ARG;
+        if (!valid_dtype(enum_arg(dtype))) return DWS_ERR_INVALID_ARG;
         if (n == 0) {
             if (num_tiles != nullptr) *num_tiles = 0;
             return DWS_OK;
@@ -642,11 +658,11 @@ dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype 
         if (d_stamps == nullptr) return DWS_OK;   // size query
         if (stamps_capacity < tiles * kStampsPerTile) return DWS_ERR_INVALID_ARG;
         if ((reinterpret_cast<uintptr_t>(d_stamps) & 7u) != 0) return DWS_ERR_MISALIGNED;
-        dws_status s = validate(d_in, d_out, n, (int)dtype);
+        dws_status s = validate(d_in, d_out, n, enum_arg(dtype));
         if (s != DWS_OK) return s;
         if (!aligned16(d_in, d_out)) return DWS_ERR_UNSUPPORTED;
         dws_options o{};
-        return run_single_pass(d_in, d_out, n, (int)dtype, exclusive != 0, kModeDecoupled, o, stream, d_stamps);
+        return run_single_pass(d_in, d_out, n, enum_arg(dtype), exclusive != 0, kModeDecoupled, o, stream, d_stamps);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {
@@ -779,8 +795,9 @@ dws_status dws_reduce_by_key(const void* d_keys, const void* d_values, void* d_u
                              size_t n, dws_dtype value_dtype, unsigned long long* d_num_runs, hipStream_t stream)
 {
     try {
-        if (!valid_dtype((int)value_dtype)) return DWS_ERR_INVALID_ARG;
-        return rbk_entry(d_keys, d_values, d_unique_keys, d_aggregates, n, value_dtype == DWS_FLOAT32 ? 1 : 0,
+        const int vt = enum_arg(value_dtype);
+        if (!valid_dtype(vt)) return DWS_ERR_INVALID_ARG;
+        return rbk_entry(d_keys, d_values, d_unique_keys, d_aggregates, n, vt == DWS_FLOAT32 ? 1 : 0,
                          d_num_runs, stream);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
@@ -805,7 +822,7 @@ dws_status dws_select_flagged(const void* d_in, const void* d_flags, void* d_out
                               unsigned long long* d_count, hipStream_t stream)
 {
     try {
-        return select_entry(d_in, d_flags, d_out, n, (int)dtype, d_count, false, stream);
+        return select_entry(d_in, d_flags, d_out, n, enum_arg(dtype), d_count, false, stream);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {
@@ -817,7 +834,7 @@ dws_status dws_partition_flagged(const void* d_in, const void* d_flags, void* d_
                                  unsigned long long* d_num_selected, hipStream_t stream)
 {
     try {
-        return select_entry(d_in, d_flags, d_out, n, (int)dtype, d_num_selected, true, stream);
+        return select_entry(d_in, d_flags, d_out, n, enum_arg(dtype), d_num_selected, true, stream);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {
@@ -828,11 +845,11 @@ dws_status dws_partition_flagged(const void* d_in, const void* d_flags, void* d_
 dws_status dws_selftest_wave(const void* d_in, void* d_incl, void* d_shift, size_t n_waves, dws_dtype dtype,
                              hipStream_t stream)
 {
-    if (!valid_dtype((int)dtype)) return DWS_ERR_INVALID_ARG;
+    if (!valid_dtype(enum_arg(dtype))) return DWS_ERR_INVALID_ARG;
     if (n_waves == 0) return DWS_OK;
     if (d_in == nullptr || d_incl == nullptr || d_shift == nullptr) return DWS_ERR_INVALID_ARG;
     if (n_waves > 0xffffffffull / 64ull) return DWS_ERR_UNSUPPORTED;
-    return from_hip(launch_wave_selftest(d_in, d_incl, d_shift, n_waves, kind_of((int)dtype), stream));
+    return from_hip(launch_wave_selftest(d_in, d_incl, d_shift, n_waves, kind_of(enum_arg(dtype)), stream));
 }
 
 }  // extern "C"
