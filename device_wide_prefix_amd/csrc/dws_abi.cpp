@@ -63,10 +63,10 @@ dws_status from_hip(hipError_t e)
 bool valid_dtype(int d) { return d == DWS_INT32 || d == DWS_UINT32 || d == DWS_FLOAT32; }
 
 // The value a C caller passed in an enum parameter, read from its bytes. A C
-// caller may pass any int there; in C++ reading an enum object whose value is
-// outside the enum's range is undefined, so the ABI never reads these
-// parameters as enums, only as the int they hold.
-// Taken by reference: copying the parameter by value would be such a read.
+// caller may pass any int there, and in C++ reading an enum object whose value
+// is outside the enum's range is undefined, so the ABI reads these parameters
+// only as the int they hold. The parameter is taken by reference: copying it
+// by value would itself be such a read.
 template <class E>
 int enum_arg(const E& e)
 {
