@@ -320,15 +320,21 @@ __device__ __forceinline__ uint32_t draw_tile(unsigned long long* counter, uint3
 // of latency L covers W predecessors, P can advance by at most W tiles per L.
 // Tiles arriving faster than W / L fall further and further behind the last
 // P and need ever more polls; W = 64 K keeps W / L above the tile rate.
+//
+// Back-off: a blocked window is polled again after a short sleep; with
+// long_backoff (uniform) every poll after that first re-poll waits
+// 127 x 64 clocks, which keeps the descriptor traffic down when many tiles
+// wait at once.
 template <class T, int ORDER, int K>
 __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t epoch,
-                               unsigned int* watchdog)
+                               unsigned int* watchdog, bool long_backoff = false)
 {
     const int lane = lane_id();
     const uint64_t lane_bit = 1ull << lane;
     T prefix = T(0);
     int64_t hi = (int64_t)tile - 1;
     const uint64_t t0 = realtime();
+    bool repolled = false;
     for (;;) {
         uint64_t d[K];
 #pragma unroll
@@ -374,7 +380,9 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
             if (lane == 0) atomicAdd(watchdog, 1u);
             return prefix;
         }
-        __builtin_amdgcn_s_sleep(1);
+        if (long_backoff && repolled) __builtin_amdgcn_s_sleep(127);
+        else __builtin_amdgcn_s_sleep(1);
+        repolled = true;
     }
 }
 

@@ -44,6 +44,7 @@ struct SelectParams {
     unsigned long long* count;
     uint32_t num_tiles;
     unsigned int* epoch;
+    uint32_t long_backoff;   // 1: long back-off between blocked look-back polls
 };
 
 // Byte offset far past any tile's range (at most 4 * 40960 bytes): the
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
             } else {
                 if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, count));
                 prefix = lookback_decoupled<uint32_t, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch,
-                                                                                     p.watchdog);
+                                                                                     p.watchdog, p.long_backoff != 0u);
                 if (lane == 0) {
                     desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusP, prefix + count));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
@@ -214,7 +215,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     const SelectShape s = select_shape(a.n, a.aligned);
     SelectParams p{static_cast<const uint32_t*>(a.in), static_cast<const uint32_t*>(a.flags),
                    static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
-                   a.epoch};
+                   a.epoch, a.n >= kLongBackoffMin ? 1u : 0u};
     void* args[] = {&p};
     const void* fn = a.partition ? select_kernel<true>(s) : select_kernel<false>(s);
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);

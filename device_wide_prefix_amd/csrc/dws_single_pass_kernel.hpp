@@ -93,7 +93,8 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)
                         desc_store<ORDER>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
-                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
+                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog,
+                                                                          p.long_backoff != 0u);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
