@@ -400,6 +400,7 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     p.out = out;
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
+    p.long_backoff = n >= kLongBackoffMin ? 1u : 0u;
     if (num_tiles == 1) return from_hip(launch_op_kind(kind, excl, shape, tile_index, p, stream));
     Workspace* ws = nullptr;
     dws_status s = get_workspace(stream, &ws);

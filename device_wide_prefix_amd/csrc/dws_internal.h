@@ -124,6 +124,7 @@ struct OpScanParams {
     unsigned int* watchdog;
     uint32_t num_tiles;
     unsigned int* epoch;     // the workspace epoch word
+    uint32_t long_backoff;   // 1: long back-off between blocked look-back polls
 };
 enum OpKind : int {
     kOpMaxI32, kOpMaxU32, kOpMinI32, kOpMinU32,          // one word

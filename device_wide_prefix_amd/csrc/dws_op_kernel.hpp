@@ -298,9 +298,11 @@ __device__ __forceinline__ void desc_store_val(uint64_t* desc, uint32_t tile, ui
 // including the nearest P) are combined in tile order, earliest first, and the
 // window goes in front of what nearer windows gave. Returns the exclusive
 // prefix of `tile` (uniform); a wait beyond kWatchdogTicks counts a trip and
-// returns what it has.
+// returns what it has. Back-off as in the + kernel's look-back: with
+// long_backoff, every poll after the first re-poll waits 127 x 64 clocks.
 template <class Op, int K>
-__device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint32_t epoch, unsigned int* watchdog)
+__device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint32_t epoch, unsigned int* watchdog,
+                                      bool long_backoff = false)
 {
     using V = typename Op::V;
     constexpr int W = Op::kWords;
@@ -309,6 +311,7 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
     V prefix = Op::identity();
     int64_t hi = (int64_t)tile - 1;
     const uint64_t t0 = realtime();
+    bool repolled = false;
     for (;;) {
         V d[K];
         uint64_t has_p[K], has_x[K];
@@ -363,7 +366,9 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
             if (lane == 0) atomicAdd(watchdog, 1u);
             return prefix;
         }
-        __builtin_amdgcn_s_sleep(1);
+        if (long_backoff && repolled) __builtin_amdgcn_s_sleep(127);
+        else __builtin_amdgcn_s_sleep(1);
+        repolled = true;
     }
 }
 
@@ -443,7 +448,7 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
                 if (lane == 0) desc_store_val<W>(p.desc, 0u, epoch, kStatusP, agg);
             } else {
                 if (lane == 0) desc_store_val<W>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
+                prefix = lookback_op<Op, kLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.long_backoff != 0u);
                 if (lane == 0) {
                     desc_store_val<W>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);

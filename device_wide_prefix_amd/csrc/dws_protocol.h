@@ -86,8 +86,13 @@ constexpr uint64_t kAutoMediumMin = (uint64_t)1 << 20;  // 16384 (512 threads)
 constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 25;   // drawn tile index from here
 // From here a look-back that is still blocked after its first re-poll backs
 // off for 127 x 64 clocks before each further poll (the first re-poll still
-// comes at once). Fewer descriptor polls while many tiles wait measured 2 to
-// 3.5% faster at 2^26 to 2^28 elements on MI355X; at 2^25 it was no better.
+// comes at once); every look-back kernel (scan, select, generic operators,
+// run kernels) takes it from the element count. Fewer descriptor polls while
+// many tiles wait measured on MI355X: the + scan 2 to 3.5% faster at 2^26 to
+// 2^28 and no better at 2^25; the run kernels 4 to 8.5% faster with all keys
+// distinct at 2^26 and 2^28, between 0.6% faster and 3.5% slower at mean run
+// 16 and 2^26, 1 to 4% faster at 2^28, but 4 to 5.5% slower at 2^25 and mean
+// run 16.
 constexpr uint64_t kLongBackoffMin = (uint64_t)1 << 26;
 
 constexpr int auto_shape(uint64_t n)

@@ -48,6 +48,7 @@ struct RbkParams {
     unsigned long long* num_runs;
     uint32_t num_tiles;
     unsigned int* epoch;
+    uint32_t long_backoff;    // 1: long back-off between blocked look-back polls
 };
 
 constexpr uint32_t kRbkDropped = 0x80000000u;   // past any tile's range: dropped
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                 if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
             } else {
                 if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, SLOTS>(p.desc, tile, epoch, p.watchdog);
+                prefix = lookback_op<Op, SLOTS>(p.desc, tile, epoch, p.watchdog, p.long_backoff != 0u);
                 if (lane == 0) {
                     desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
@@ -387,7 +388,8 @@ hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
                 static_cast<uint32_t*>(a.ukeys),      static_cast<uint32_t*>(a.aggs),
                 a.n,                                  a.desc,
                 a.watchdog,                           a.num_runs,
-                a.num_tiles,                          a.epoch};
+                a.num_tiles,                          a.epoch,
+                a.n >= kLongBackoffMin ? 1u : 0u};
     if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, p, stream);
     if (a.n >= kRbkLargeMin) {
         // sums: 16,384-element tiles (512 x 4 x 8); run lengths hold no values
