@@ -623,8 +623,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the scan runs on a "
-              "single device; see the sharding note in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported. The scan runs on a single "
+              "device; across GPUs each would scan its shard seeded by an exchange of the shard totals, "
+              "which is not built here.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -16,7 +16,7 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def gpu():
     """The GPU tests need a device; fail loudly rather than skip when none is
-    visible, so a broken GPU machine never passes as green."""
+    visible, so a machine whose GPU is missing never passes as green."""
     import torch
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible to torch (HIP); the gpu-marked tests need one")
