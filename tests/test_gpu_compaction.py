@@ -78,10 +78,10 @@ def _check_runs(name, keys, got_keys, got_aggs, got_count, vals=None):
 
 
 # around the small (4096) and large (16384 or 32768, from 2^22) tiles, a
-# ragged last tile with empty wave segments, and 2^25 + 5; runs from length
-# 1 to longer than a tile
+# ragged last tile with empty wave segments, 2^25 + 5, and 2^26 + 5 where the
+# look-back's long back-off is on; runs from length 1 to longer than a tile
 RBK_SIZES = [1, 2, 3, 4095, 4096, 4097, 3 * 4096 + 7, 100_003, (1 << 22) - 1, (1 << 22) + 16384 + 3,
-             (1 << 25) + 5]
+             (1 << 25) + 5, (1 << 26) + 5]
 MEAN_RUNS = [1, 3, 200, 50_000]
 
 
