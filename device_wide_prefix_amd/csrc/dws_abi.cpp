@@ -108,6 +108,16 @@ bool aligned16(const void* in, const void* out)
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 // Workspace of (current device, stream), created on first use.
+// True while `stream` is being captured into a graph. Nothing may be allocated
+// or synchronised then, so a call that would have to create or grow a
+// workspace returns DWS_ERR_UNSUPPORTED before making any such call (and the
+// capture stays valid); dws_reserve ahead of the capture avoids it.
+bool stream_capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 dws_status get_workspace(hipStream_t stream, Workspace** out)
 {
     int dev = 0;
@@ -120,6 +130,7 @@ dws_status get_workspace(hipStream_t stream, Workspace** out)
         *out = it->second.get();
         return DWS_OK;
     }
+    if (stream_capturing(stream)) return DWS_ERR_UNSUPPORTED;
     auto ws = std::make_unique<Workspace>();
     ws->device = dev;
     ws->stream = stream;
@@ -147,6 +158,7 @@ dws_status get_workspace(hipStream_t stream, Workspace** out)
 dws_status ensure_desc(Workspace* ws, uint64_t slots)
 {
     if (slots <= ws->desc_slots) return DWS_OK;
+    if (stream_capturing(ws->stream)) return DWS_ERR_UNSUPPORTED;
     uint64_t want = std::max<uint64_t>({slots, ws->desc_slots * 2, kMinDescSlots});
     if (ws->desc != nullptr) {
         hipError_t e = hipStreamSynchronize(ws->stream);
@@ -284,6 +296,7 @@ dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hi
 dws_status ensure_stp(Workspace* ws, uint64_t elems)
 {
     if (elems <= ws->stp_elems) return DWS_OK;
+    if (stream_capturing(ws->stream)) return DWS_ERR_UNSUPPORTED;
     const uint64_t want = std::max<uint64_t>({elems, ws->stp_elems * 2, 1024});
     if (ws->stp != nullptr) {
         hipError_t e = hipStreamSynchronize(ws->stream);

@@ -42,7 +42,9 @@
  *
  * Graphs: once the workspace of the stream covers n (a first call, or
  * dws_reserve), calls on that stream allocate nothing and may be captured
- * into a HIP graph. Replays stay correct: each launch takes its descriptor
+ * into a HIP graph. A call captured before that, which would have to create
+ * or grow the workspace, returns DWS_ERR_UNSUPPORTED without allocating,
+ * synchronising or enqueuing anything, so the capture stays valid. Replays stay correct: each launch takes its descriptor
  * epoch from a device word that the launch itself advances. The host clears
  * the descriptors before its own calls could wrap the 30-bit epoch, but
  * replays advance it unseen: after about 2^30 launches on one workspace,

@@ -662,5 +662,50 @@ def test_graph_replays(gpu, n):
         assert np.array_equal(pout.cpu().numpy().view(np.uint32), oracle.scan_affine_u32(pr))
 
 
+def test_capture_without_workspace_is_refused(gpu):
+    # a call captured on a stream whose workspace does not exist yet, or lacks
+    # the scan-then-propagate scratch, is refused before it allocates or
+    # synchronises anything, so the capture itself stays valid; the same
+    # stream then works eagerly
+    import torch
+    n = (1 << 20) + 3
+    s = torch.cuda.Stream()
+    data = wl.random_input("int32", n, seed=41)
+    x = torch.from_numpy(data).cuda()
+    out = torch.empty_like(x)
+    torch.cuda.synchronize()
+    note("capture on a stream with no workspace")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        with pytest.raises(dws.ScanError) as err:
+            dws.scan_exclusive(x, out)
+    assert err.value.status == dws.ERR_UNSUPPORTED
+    del g
+    # a workspace reserved for a small n holds 1,024 scan-then-propagate tile
+    # sums; 2^23 + 5 elements need more, so capturing that call must grow it
+    s2 = torch.cuda.Stream()
+    dws.reserve(4097, stream=s2.cuda_stream)
+    n2 = (1 << 23) + 5
+    data2 = wl.random_input("int32", n2, seed=43)
+    x2 = torch.from_numpy(data2).cuda()
+    out2 = torch.empty_like(x2)
+    torch.cuda.synchronize()
+    note("capture that would grow the scan-then-propagate scratch")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s2):
+        with pytest.raises(dws.ScanError) as err:
+            dws.scan_ex(x2, out2, exclusive=True, variant=dws.SCAN_THEN_PROPAGATE)
+    assert err.value.status == dws.ERR_UNSUPPORTED
+    del g
+    note("eager calls on the same streams after the refused captures")
+    with torch.cuda.stream(s):
+        dws.scan_exclusive(x, out)
+    with torch.cuda.stream(s2):
+        dws.scan_ex(x2, out2, exclusive=True, variant=dws.SCAN_THEN_PROPAGATE)
+    torch.cuda.synchronize()
+    check(data, from_device(out, "int32"), "int32", True, label="after refused capture")
+    check(data2, from_device(out2, "int32"), "int32", True, label="scan-then-propagate after refused capture")
+
+
 def test_zz_watchdog_never_tripped(gpu):
     assert dws.watchdog_trips() == 0
