@@ -527,6 +527,18 @@ def device_info():
             **m, "implied_peak_gbps": round(implied, 1), "roofline_peak_gbps": HBM_PEAK_GBPS}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it, or "unknown"."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
     """The sequential oracle on the same input, timed on one host core, repeated
     until about budget_s seconds of CPU work (the oracle is one loop: 1 thread)."""
@@ -545,7 +557,7 @@ def cpu_baseline(w: wl.Workload, x: np.ndarray, budget_s: float = 10.0):
     med = float(np.median(reps))
     return {"value": round(w.algorithmic_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full {w.name} input (N={w.n}), {len(reps)} repetitions, median "
-                      f"{med * 1e3:.1f} ms; host has {os.cpu_count()} logical CPUs"}
+                      f"{med * 1e3:.1f} ms; host has {os.cpu_count()} logical CPUs ({cpu_model()})"}
 
 
 def oracle_rate(call, algo_bytes: int, sample: str, budget_s: float = 2.0):
