@@ -72,6 +72,7 @@ struct SelectArgs {
 };
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
 constexpr uint64_t kSelectHugeMin = (uint64_t)1 << 27;    // 40960-element tiles from here
+constexpr uint64_t kSelectDrawnMin = (uint64_t)1 << 25;   // drawn tile index from here (below: workgroup index)
 constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
 uint32_t select_tile_elems(uint64_t n, bool aligned);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);

@@ -5,7 +5,8 @@
 // writes, so the output may overwrite the input) and section A5 (select-if
 // fused with the scan, no extra pass).
 //
-// Per tile (one workgroup, dynamic tile index, same descriptor protocol and
+// Per tile (one workgroup; tile index drawn from the workspace counter from
+// 2^25 elements, the workgroup index below; same descriptor protocol and
 // workspace as the scan):
 //   1. load the flags, then the values of the tile (coalesced, in registers;
 //      steps 2 and 3 wait for the flags only);
@@ -51,7 +52,7 @@ struct SelectParams {
 // buffer range check drops the store. Offset plus store size stays below 2^32.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
-template <int BLOCK, int VEC, int CHUNKS, bool PARTITION>
+template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
     static_assert(VEC * CHUNKS <= 64, "one selection bit per element in a 64-bit mask");
@@ -70,12 +71,16 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 
     uint32_t tile = 0u;
     if (multi) {
-        if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
-        __syncthreads();
-        tile = uniform(s_draw);
-        if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
-            if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
-            return;
+        if constexpr (TILE_INDEX == kTileDispatch) {
+            tile = blockIdx.x;
+        } else {
+            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            __syncthreads();
+            tile = uniform(s_draw);
+            if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
+                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
+                return;
+            }
         }
     }
 
@@ -191,17 +196,17 @@ static SelectShape select_shape(uint64_t n, bool aligned)
 
 uint32_t select_tile_elems(uint64_t n, bool aligned) { return select_shape(n, aligned).elems(); }
 
-template <bool PARTITION>
+template <bool PARTITION, int TI>
 static const void* select_kernel(const SelectShape& s)
 {
     if (s.vec == 1) return reinterpret_cast<const void*>(
-        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION>);
+        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION, TI>);
     if (s.chunks == kSelectHuge.chunks) return reinterpret_cast<const void*>(
-        &k_select<kSelectHuge.threads, kSelectHuge.vec, kSelectHuge.chunks, PARTITION>);
+        &k_select<kSelectHuge.threads, kSelectHuge.vec, kSelectHuge.chunks, PARTITION, TI>);
     if (s.threads == kSelectLarge.threads) return reinterpret_cast<const void*>(
-        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION>);
+        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION, TI>);
     return reinterpret_cast<const void*>(
-        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION>);
+        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION, TI>);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
@@ -217,7 +222,12 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
                    static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
                    a.epoch, a.n >= kLongBackoffMin ? 1u : 0u};
     void* args[] = {&p};
-    const void* fn = a.partition ? select_kernel<true>(s) : select_kernel<false>(s);
+    // the workgroup index as the tile index below kSelectDrawnMin, as for the
+    // scan: no atomic on the critical path while there are few tiles per CU;
+    // the watchdog still bounds every wait
+    const bool drawn = a.n >= kSelectDrawnMin;
+    const void* fn = a.partition ? (drawn ? select_kernel<true, kTileDrawn>(s) : select_kernel<true, kTileDispatch>(s))
+                                 : (drawn ? select_kernel<false, kTileDrawn>(s) : select_kernel<false, kTileDispatch>(s));
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 
