@@ -16,7 +16,7 @@ library launches on. The call is a single kernel launch, so the event time is
 the kernel's launch duration.
 
 Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained|scan_then_propagate,
---order relaxed|acq_rel, --tile-shape K, --nontemporal, --no-cpu-baseline,
+--order relaxed|acq_rel, --tile-shape K, --nontemporal auto|on|off, --no-cpu-baseline,
 --all (extra JSON lines for every workload and variant on stderr), --sweep
 (N = 2^10..2^30, every variant and memcpy, cold and warm caches; stderr),
 --select (stream compaction on the 2^30-12345 flag workload; stderr), --ops
@@ -49,6 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_c4.json")
 VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2, "scan_then_propagate": 3}
 ORDERS = {"relaxed": 0, "acq_rel": 1}
 TILE_INDEX = {"auto": 0, "drawn": 1, "dispatch": 2}
+NONTEMPORAL = {"auto": 0, "on": 1, "off": 2}
 
 
 def log(*a):
@@ -107,7 +108,7 @@ def time_steps(fn, prepare, steps: int, warmup: int):
     return times
 
 
-def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool, steps: int, warmup: int,
+def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: int, steps: int, warmup: int,
                  with_memcpy: bool, x_host=None, instrument: bool = True, flush_caches: bool = True,
                  tile_index: int = 0):
     import torch
@@ -124,7 +125,7 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: bool,
     stream = torch.cuda.current_stream().cuda_stream
     dws.reserve(w.n)
     opt = dws.DwsOptions(variant, order, shape, int(nt), tile_index)
-    default = variant == 0 and order == 0 and shape == 0 and not nt and tile_index == 0
+    default = variant == 0 and order == 0 and shape == 0 and nt == 0 and tile_index == 0
     entry = dws.scan_exclusive_ptr if w.exclusive else dws.scan_inclusive_ptr
 
     def prepare():
@@ -219,7 +220,7 @@ def run_sweep(steps: int, warmup: int):
         x = x_all[:n]
         for cold in (True, False):
             for vname, v in VARIANTS.items():
-                r = run_workload(w, v, 0, 0, False, steps, warmup, with_memcpy=(v == 0), x_host=x,
+                r = run_workload(w, v, 0, 0, 0, steps, warmup, with_memcpy=(v == 0), x_host=x,
                                  instrument=False, flush_caches=cold)
                 row = summarize(w, r, vname, None)
                 row["cache"] = "cold" if cold else "warm"
@@ -619,7 +620,8 @@ def main():
     ap.add_argument("--variant", default="single_pass", choices=sorted(VARIANTS))
     ap.add_argument("--order", default="relaxed", choices=sorted(ORDERS))
     ap.add_argument("--tile-shape", type=int, default=0)
-    ap.add_argument("--nontemporal", action="store_true")
+    ap.add_argument("--nontemporal", default="auto", choices=sorted(NONTEMPORAL),
+                    help="non-temporal loads: the library's choice (on from 2^28 elements), on or off")
     ap.add_argument("--tile-index", default="auto", choices=sorted(TILE_INDEX))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also measure every workload and variant (stderr)")
@@ -652,7 +654,7 @@ def main():
     log(f"generating {w.description}")
     x = wl.generate_workload(w)
     variant = VARIANTS[args.variant]
-    res = run_workload(w, variant, ORDERS[args.order], args.tile_shape, args.nontemporal, args.steps,
+    res = run_workload(w, variant, ORDERS[args.order], args.tile_shape, NONTEMPORAL[args.nontemporal], args.steps,
                        args.warmup, with_memcpy=True, x_host=x, tile_index=TILE_INDEX[args.tile_index])
     s = summarize(w, res, args.variant, args)
     log(json.dumps(s))
@@ -662,7 +664,7 @@ def main():
     mean_ms = s["ms_mean"]
     achieved = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
     traffic = traffic_for_current_kernel() if (variant == 0 and args.workload == "C4" and args.order == "relaxed"
-                                               and args.tile_shape == 0 and not args.nontemporal
+                                               and args.tile_shape == 0 and args.nontemporal == "auto"
                                                and args.tile_index == "auto") else None
     line = {
         "metric": METRIC,
@@ -680,7 +682,7 @@ def main():
         "config": {"workload": w.description, "n": w.n, "element": w.dtype,
                    "scan": "exclusive" if w.exclusive else "inclusive", "in_place": w.in_place,
                    "seed": w.seed, "variant": args.variant, "memory_order": args.order,
-                   "tile_shape": args.tile_shape, "nontemporal": bool(args.nontemporal),
+                   "tile_shape": args.tile_shape, "nontemporal": args.nontemporal,
                    "tile_index": args.tile_index,
                    "parallelism": "single GPU"},
         "frac_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
@@ -710,7 +712,7 @@ def main():
             wk = wl.WORKLOADS[name]
             xk = wl.generate_workload(wk)
             for vname, v in VARIANTS.items():
-                r = run_workload(wk, v, 0, 0, False, max(5, args.steps // 2), 3, with_memcpy=(v == 0), x_host=xk)
+                r = run_workload(wk, v, 0, 0, 0, max(5, args.steps // 2), 3, with_memcpy=(v == 0), x_host=xk)
                 log("ALL " + json.dumps(summarize(wk, r, vname, args)))
             del xk
 

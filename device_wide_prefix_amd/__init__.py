@@ -7,7 +7,7 @@ fallback; if the library is not built, importing the binding's functions raises.
     scan_inclusive(x, out=None)            -> out
     scan_exclusive(x, out=None)            -> out      (out may be x: in place)
     scan_ex(x, out=None, exclusive=False, variant=..., memory_order=...,
-            tile_shape=0, nontemporal=False) -> out
+            tile_shape=0, nontemporal=None) -> out
     scan_debug(x, out, tile_elems, ...)    -> descriptor words (numpy uint64)
     watchdog_trips()                       -> int
     selftest_wave(x)                       -> (incl, shift)
@@ -33,6 +33,8 @@ SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED, SCAN_THEN_PROPAGATE = 0, 1, 2, 3
 ORDER_RELAXED, ORDER_ACQ_REL = 0, 1
 # dws_tile_index
 TILE_AUTO, TILE_DRAWN, TILE_DISPATCH = 0, 1, 2
+# dws_options.nontemporal
+NT_AUTO, NT_ON, NT_OFF = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
@@ -193,11 +195,13 @@ def scan_exclusive(x, out=None, stream=None):
 
 
 def scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=ORDER_RELAXED,
-            tile_shape=0, nontemporal=False, tile_index=TILE_AUTO, stream=None):
+            tile_shape=0, nontemporal=None, tile_index=TILE_AUTO, stream=None):
     """Scan with explicit options (variant, descriptor memory order, tile shape,
-    non-temporal memory access, tile index source); returns ``out``."""
+    non-temporal loads: None for the library's choice, True or False to force
+    them on or off; tile index source); returns ``out``."""
     code, out = _prepare(x, out)
-    opt = DwsOptions(int(variant), int(memory_order), int(tile_shape), int(bool(nontemporal)), int(tile_index))
+    nt = NT_AUTO if nontemporal is None else (NT_ON if nontemporal else NT_OFF)
+    opt = DwsOptions(int(variant), int(memory_order), int(tile_shape), nt, int(tile_index))
     with _device_of(x):
         _check(scan_ex_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, opt,
                            _stream(x, stream)), "dws_scan_ex")

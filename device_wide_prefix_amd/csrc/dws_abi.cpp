@@ -219,8 +219,16 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
                            const dws_options& o, hipStream_t stream, unsigned long long* stamps = nullptr)
 {
     const bool aligned = aligned16(in, out);
-    // non-temporal access is a hint, built for aligned pointers only
-    const bool nt = o.nontemporal != 0 && aligned;
+    // non-temporal loads are a hint, built for aligned pointers only: 1 asks
+    // for them, 2 never uses them, 0 leaves it to the library, which uses them
+    // from kNtLoadMin elements on the automatic drawn relaxed single pass
+    bool nt = false;
+    if (o.nontemporal == 1) {
+        nt = aligned;
+    } else if (o.nontemporal == 0) {
+        nt = aligned && n >= kNtLoadMin && o.tile_shape == 0 && mode == kModeDecoupled &&
+             o.memory_order == DWS_ORDER_RELAXED && o.tile_index != DWS_TILE_DISPATCH;
+    }
     const int shape = resolve_shape(o.tile_shape, n, aligned);
     if (shape < 0) return DWS_ERR_INVALID_ARG;
     // automatic: the workgroup index below kAutoDrawnMin elements where that
@@ -342,7 +350,7 @@ dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclus
         if (o.memory_order != DWS_ORDER_RELAXED && o.memory_order != DWS_ORDER_ACQ_REL)
             return DWS_ERR_INVALID_ARG;
         if (o.tile_shape < 0 || o.tile_shape > kNumShapes) return DWS_ERR_INVALID_ARG;
-        if (o.nontemporal != 0 && o.nontemporal != 1) return DWS_ERR_INVALID_ARG;
+        if (o.nontemporal < 0 || o.nontemporal > 2) return DWS_ERR_INVALID_ARG;
         if (o.tile_index < DWS_TILE_AUTO || o.tile_index > DWS_TILE_DISPATCH) return DWS_ERR_INVALID_ARG;
         if (o.tile_index != DWS_TILE_AUTO && o.variant != DWS_VARIANT_SINGLE_PASS && o.variant != DWS_VARIANT_CHAINED)
             return DWS_ERR_UNSUPPORTED;
@@ -351,12 +359,12 @@ dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclus
         const bool excl = exclusive != 0;
         switch (o.variant) {
         case DWS_VARIANT_REDUCE_THEN_SCAN:
-            if (o.tile_shape != 0 || o.nontemporal != 0) return DWS_ERR_UNSUPPORTED;
+            if (o.tile_shape != 0 || o.nontemporal == 1) return DWS_ERR_UNSUPPORTED;
             return run_rts(in, out, n, dtype, excl, stream);
         case DWS_VARIANT_CHAINED:
             return run_single_pass(in, out, n, dtype, excl, kModeChained, o, stream);
         case DWS_VARIANT_SCAN_THEN_PROPAGATE:
-            if (o.tile_shape != 0 || o.nontemporal != 0) return DWS_ERR_UNSUPPORTED;
+            if (o.tile_shape != 0 || o.nontemporal == 1) return DWS_ERR_UNSUPPORTED;
             return run_stp(in, out, n, dtype, excl, stream);
         default:
             return run_single_pass(in, out, n, dtype, excl, kModeDecoupled, o, stream);

@@ -11,7 +11,8 @@
 //      (TILE_INDEX == kTileDispatch);
 //   2. every wave loads its segment of the tile with coalesced vector loads,
 //      CHUNKS x VEC elements per lane kept in registers (thread coarsening,
-//      PMPP 11.2 notes);
+//      PMPP 11.2 notes); with NT the loads are non-temporal (the input is read
+//      once), the stores never are;
 //   3. lane-serial totals -> wave64 DPP scans -> the wave totals go through
 //      LDS, giving each wave its prefix inside the tile and the tile aggregate;
 //   4. wave 0 publishes {A, aggregate} (tile 0: {P, aggregate}), looks back
@@ -112,7 +113,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     const T seed = s_prefix + wave_pre;
 
     add_seed<T, VEC, CHUNKS>(x, seed);
-    store_segment<T, VEC, CHUNKS, NT>(make_rsrc(static_cast<T*>(p.out) + seg_first, seg_valid), lane, x);
+    store_segment<T, VEC, CHUNKS, false>(make_rsrc(static_cast<T*>(p.out) + seg_first, seg_valid), lane, x);
     if constexpr (INSTR) {
         stamp[4] = realtime();
         if (threadIdx.x == 0) {

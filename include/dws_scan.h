@@ -164,7 +164,11 @@ typedef struct dws_options {
                            else 4096);
                            1 .. dws_num_tile_shapes()-1 force one shape of
                            the single-pass kernel, for sweeps */
-    int nontemporal;    /* 1 = non-temporal (streaming) loads and stores */
+    int nontemporal;    /* non-temporal (streaming) loads of the input:
+                           0 = the library's choice (on from 2^28
+                           elements for the automatic single pass),
+                           1 = on, 2 = off; stores are never
+                           non-temporal */
     int tile_index;     /* dws_tile_index; default DWS_TILE_AUTO */
 } dws_options;
 
@@ -174,12 +178,12 @@ typedef struct dws_options {
  * DWS_ERR_INVALID_ARG. Built combinations (others give DWS_ERR_UNSUPPORTED):
  *   single pass: every tile_shape with relaxed order; the automatically
  *                chosen shapes also with release/acquire and with
- *                nontemporal (relaxed);
+ *                nontemporal 1 (relaxed);
  *   chained:     the automatically chosen shapes, either order;
- *   reduce-then-scan, scan-then-propagate: tile_shape 0, nontemporal 0,
- *                tile_index 0 (memory_order ignored);
+ *   reduce-then-scan, scan-then-propagate: tile_shape 0, nontemporal 0
+ *                or 2, tile_index 0 (memory_order ignored);
  *   DWS_TILE_DISPATCH: single pass with relaxed order, every tile_shape,
- *                nontemporal 0.
+ *                nontemporal 0 or 2.
  * Pointers that are not both 16-byte aligned use scalar loads; a forced
  * shape without a scalar-load kernel then falls back to the automatic one,
  * and nontemporal is ignored.

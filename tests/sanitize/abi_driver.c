@@ -80,7 +80,7 @@ static void scans(void)
 
     dws_options o;
     const int bad_opts[][5] = {{4, 0, 0, 0, 0}, {-1, 0, 0, 0, 0}, {0, 2, 0, 0, 0}, {0, 0, -1, 0, 0},
-                               {0, 0, 0, 2, 0}, {0, 0, 0, 0, 3}, {0, 0, 0, 0, -1}};
+                               {0, 0, 0, 3, 0}, {0, 0, 0, -1, 0}, {0, 0, 0, 0, 3}, {0, 0, 0, 0, -1}};
     for (size_t k = 0; k < sizeof(bad_opts) / sizeof(bad_opts[0]); ++k) {
         o.variant = bad_opts[k][0];
         o.memory_order = bad_opts[k][1];

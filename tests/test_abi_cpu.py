@@ -108,7 +108,8 @@ def test_option_validation(lib):
     assert call(order=2) == dws.ERR_INVALID_ARG
     assert call(shape=dws.num_tile_shapes()) == dws.ERR_INVALID_ARG
     assert call(shape=-1) == dws.ERR_INVALID_ARG
-    assert call(nt=2) == dws.ERR_INVALID_ARG
+    assert call(nt=3) == dws.ERR_INVALID_ARG
+    assert call(nt=-1) == dws.ERR_INVALID_ARG
     # combinations that are not built
     # forced shapes 2 (256 x 32) and 4 (1024 x 16) are built for the relaxed
     # single pass only
@@ -119,6 +120,9 @@ def test_option_validation(lib):
     assert call(variant=dws.REDUCE_THEN_SCAN, nt=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.SCAN_THEN_PROPAGATE, shape=1) == dws.ERR_UNSUPPORTED
     assert call(variant=dws.SCAN_THEN_PROPAGATE, nt=1) == dws.ERR_UNSUPPORTED
+    # nontemporal 0 (the library's choice) and 2 (off) are valid everywhere;
+    # with an unbuilt combination they still fail before any HIP call
+    assert call(variant=dws.REDUCE_THEN_SCAN, nt=2, shape=1) == dws.ERR_UNSUPPORTED
     # tile index source: 0..2; dispatch order is built for the relaxed single
     # pass without non-temporal access
     assert call(tile_index=3) == dws.ERR_INVALID_ARG

@@ -209,9 +209,9 @@ def test_epochs_across_launch_kinds(gpu):
             check(x, from_device(out, "int32"), "int32", rep % 2 == 1, label=f"{kind} rep {rep}")
 
 
-@pytest.mark.parametrize("opts", [dict(order=dws.ORDER_ACQ_REL), dict(nt=1),
+@pytest.mark.parametrize("opts", [dict(order=dws.ORDER_ACQ_REL), dict(nt=1), dict(nt=2),
                                   dict(variant=dws.CHAINED, order=dws.ORDER_ACQ_REL)],
-                         ids=["acq_rel", "nontemporal", "chained_acq_rel"])
+                         ids=["acq_rel", "nontemporal", "nontemporal_off", "chained_acq_rel"])
 def test_order_and_nontemporal(gpu, opts):
     for dtype in DTYPES:
         for exclusive in (False, True):
@@ -445,6 +445,22 @@ def test_profiled_scan(gpu, n):
             assert st.shape == (dws.profiled_num_tiles(n), 5)
             assert np.all(st > 0), "every tile writes its stamps"
             assert np.all(np.diff(st, axis=1) >= 0), "phases are in order within a tile"
+
+
+def test_profiled_scan_nontemporal(gpu):
+    # from 2^28 elements the automatic choice loads with non-temporal loads;
+    # the instrumented kernel the benchmark's phase stamps come from is that one
+    import torch
+    n = (1 << 28) + 5
+    note(f"profiled fp32 exclusive n={n} (non-temporal loads)")
+    x = wl.random_input("float32", n, seed=29)
+    _, xd = to_device(x)
+    out, stamps = dws.scan_profiled(xd, exclusive=True)
+    torch.cuda.synchronize()
+    check_chunked(x, from_device(out, "float32"), "float32", True, label="profiled non-temporal")
+    st = stamps.cpu().numpy()
+    assert st.shape == (dws.profiled_num_tiles(n), 5)
+    assert np.all(st > 0) and np.all(np.diff(st, axis=1) >= 0)
 
 
 # ---------------------------------------------------------------------------
