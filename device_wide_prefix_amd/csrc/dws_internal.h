@@ -159,13 +159,13 @@ constexpr uint32_t op_tile_threads(int shape)
 }
 // Only the large shape is built with a drawn tile index (used from
 // kAutoDrawnMin elements); the others take the workgroup index.
-hipError_t launch_op_minmax(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+hipError_t launch_op_minmax(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
                             hipStream_t stream);
-hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
                              hipStream_t stream);
-hipError_t launch_op_affine(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+hipError_t launch_op_affine(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
                             hipStream_t stream);
-hipError_t launch_op_segsum(int kind, bool exclusive, int shape, int tile_index, const OpScanParams& p,
+hipError_t launch_op_segsum(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
                             hipStream_t stream);
 
 // Zero `slots` descriptors, set the counter to kCounterInit, the epoch word

@@ -198,23 +198,24 @@ __device__ __forceinline__ typename Op::V wave_reduce_reversed_op(typename Op::V
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int LOADW, int CHUNKS>
+template <int LOADW, int CHUNKS, bool NT>
 __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, int lane, uint32_t (&raw)[CHUNKS][LOADW])
 {
+    constexpr int aux = NT ? kBufferNonTemporal : 0;
     const int voff = lane * LOADW * 4;
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
         const int soff = c * 64 * LOADW * 4;
         if constexpr (LOADW == 4) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, aux);
 #pragma unroll
             for (int k = 0; k < 4; ++k) raw[c][k] = v[k];
         } else if constexpr (LOADW == 2) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, aux);
             raw[c][0] = v[0];
             raw[c][1] = v[1];
         } else {
-            raw[c][0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+            raw[c][0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, aux);
         }
     }
 }
@@ -381,7 +382,7 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
 // The kernel. LOADW words per lane per chunk load (4: dwordx4), E = LOADW / W
 // elements per lane per chunk.
 // ---------------------------------------------------------------------------
-template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, int TILE_INDEX>
+template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, int TILE_INDEX, bool NT = false>
 __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
 {
     using V = typename Op::V;
@@ -419,7 +420,7 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t vb = valid_bytes_sized(seg_first, SEG, p.n, ESIZE);
     uint32_t raw[CHUNKS][LOADW];
-    load_words<LOADW, CHUNKS>(make_rsrc(static_cast<const char*>(p.in) + seg_first * ESIZE, vb), lane, raw);
+    load_words<LOADW, CHUNKS, NT>(make_rsrc(static_cast<const char*>(p.in) + seg_first * ESIZE, vb), lane, raw);
 
     V x[CHUNKS][E];
 #pragma unroll
@@ -480,35 +481,39 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
 // Shapes and launch. Shapes are (threads, words per load, loads per lane);
 // the unaligned shape loads one element per access.
 // ---------------------------------------------------------------------------
-template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, int TILE_INDEX>
+template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, int TILE_INDEX, bool NT = false>
 static hipError_t launch_op_shape(const OpScanParams& p, hipStream_t stream)
 {
     OpScanParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_scan_op<Op, EXCL, BLOCK, LOADW, CHUNKS, TILE_INDEX>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_scan_op<Op, EXCL, BLOCK, LOADW, CHUNKS, TILE_INDEX, NT>),
                            dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
 }
 
 template <class Op, bool EXCL>
-static hipError_t launch_op_excl(int shape, int tile_index, const OpScanParams& p, hipStream_t stream)
+static hipError_t launch_op_excl(int shape, int tile_index, bool nt, const OpScanParams& p, hipStream_t stream)
 {
     constexpr int W = Op::kWords;
     switch (shape) {
     case kOpShapeSmall: return launch_op_shape<Op, EXCL, 256, 4, 4, kTileDispatch>(p, stream);
     case kOpShapeMedium: return launch_op_shape<Op, EXCL, 512, 4, 8, kTileDispatch>(p, stream);
     case kOpShapeLarge:
-        return tile_index == kTileDrawn ? launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn>(p, stream)
-                                        : launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDispatch>(p, stream);
+        // non-temporal loads are built for the drawn large shape only (the
+        // caller asks for them from 1 GiB of input)
+        if (tile_index == kTileDrawn)
+            return nt ? launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn, true>(p, stream)
+                      : launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn>(p, stream);
+        return launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDispatch>(p, stream);
     case kOpShapeUnaligned: return launch_op_shape<Op, EXCL, 256, W, 16, kTileDispatch>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <class Op>
-hipError_t launch_op_typed(bool exclusive, int shape, int tile_index, const OpScanParams& p, hipStream_t stream)
+hipError_t launch_op_typed(bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p, hipStream_t stream)
 {
-    return exclusive ? launch_op_excl<Op, true>(shape, tile_index, p, stream)
-                     : launch_op_excl<Op, false>(shape, tile_index, p, stream);
+    return exclusive ? launch_op_excl<Op, true>(shape, tile_index, nt, p, stream)
+                     : launch_op_excl<Op, false>(shape, tile_index, nt, p, stream);
 }
 
 }  // namespace dws

@@ -52,7 +52,7 @@ struct SelectParams {
 // buffer range check drops the store. Offset plus store size stays below 2^32.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
-template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX>
+template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX, bool NT = false>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
     static_assert(VEC * CHUNKS <= 64, "one selection bit per element in a 64-bit mask");
@@ -89,8 +89,8 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     uint32_t x[CHUNKS][VEC], r[CHUNKS][VEC];
     // flags first: the tile's count (its aggregate) needs only the flags, so
     // it is published and the look-back runs while the values are in flight
-    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
-    load_segment<uint32_t, VEC, CHUNKS, false>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
+    load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
 
     // selection bits, then ranks (exclusive scan of the 0/1 flags) in place
     Mask selected = 0u;
@@ -228,6 +228,14 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     const bool drawn = a.n >= kSelectDrawnMin;
     const void* fn = a.partition ? (drawn ? select_kernel<true, kTileDrawn>(s) : select_kernel<true, kTileDispatch>(s))
                                  : (drawn ? select_kernel<false, kTileDrawn>(s) : select_kernel<false, kTileDispatch>(s));
+    // from kNtLoadMin elements the values and flags are loaded non-temporally
+    // (each is read once): measured 3% faster at 2^30 - 12,345 elements. That
+    // size always runs the aligned huge shape with a drawn tile index.
+    if (a.n >= kNtLoadMin && s.chunks == kSelectHuge.chunks && s.vec == kSelectHuge.vec && drawn)
+        fn = a.partition ? reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
+                                                                   kSelectHuge.chunks, true, kTileDrawn, true>)
+                         : reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
+                                                                   kSelectHuge.chunks, false, kTileDrawn, true>);
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 
