@@ -111,6 +111,7 @@ struct RbkArgs {
     unsigned int* epoch;     // the workspace epoch word
 };
 constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384 (32768 for run lengths) from here
+constexpr uint64_t kRbkNtMin = (uint64_t)1 << 25;      // non-temporal key and value loads from here
 uint32_t rbk_tile_elems(uint64_t n, bool aligned, int mode);
 hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream);
 
