@@ -228,14 +228,22 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     const bool drawn = a.n >= kSelectDrawnMin;
     const void* fn = a.partition ? (drawn ? select_kernel<true, kTileDrawn>(s) : select_kernel<true, kTileDispatch>(s))
                                  : (drawn ? select_kernel<false, kTileDrawn>(s) : select_kernel<false, kTileDispatch>(s));
-    // from kNtLoadMin elements the values and flags are loaded non-temporally
-    // (each is read once): measured 3% faster at 2^30 - 12,345 elements. That
-    // size always runs the aligned huge shape with a drawn tile index.
-    if (a.n >= kNtLoadMin && s.chunks == kSelectHuge.chunks && s.vec == kSelectHuge.vec && drawn)
-        fn = a.partition ? reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
-                                                                   kSelectHuge.chunks, true, kTileDrawn, true>)
-                         : reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
-                                                                   kSelectHuge.chunks, false, kTileDrawn, true>);
+    // with a drawn tile index (from 2^25 elements) the values and flags are
+    // loaded non-temporally, each being read once: measured 0.5 to 2% faster
+    // at 2^25, 3 to 5.6% at 2^26 and 2^27, 3% at 2^30 - 12,345. Those sizes run
+    // the large or huge shape when the pointers are aligned.
+    if (drawn && s.vec == 4) {
+        if (s.chunks == kSelectHuge.chunks)
+            fn = a.partition ? reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
+                                                                       kSelectHuge.chunks, true, kTileDrawn, true>)
+                             : reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
+                                                                       kSelectHuge.chunks, false, kTileDrawn, true>);
+        else if (s.threads == kSelectLarge.threads && s.chunks == kSelectLarge.chunks)
+            fn = a.partition ? reinterpret_cast<const void*>(&k_select<kSelectLarge.threads, kSelectLarge.vec,
+                                                                       kSelectLarge.chunks, true, kTileDrawn, true>)
+                             : reinterpret_cast<const void*>(&k_select<kSelectLarge.threads, kSelectLarge.vec,
+                                                                       kSelectLarge.chunks, false, kTileDrawn, true>);
+    }
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 
