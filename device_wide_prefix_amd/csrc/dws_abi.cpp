@@ -413,9 +413,10 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     const bool aligned = aligned16(in, out);
     const int shape = op_auto_shape(n, aligned);
     const int tile_index = (shape == kOpShapeLarge && n >= kAutoDrawnMin) ? kTileDrawn : kTileDispatch;
-    // non-temporal loads from 1 GiB of input (kNtLoadMin 4-byte words), as for
-    // the + scan: measured 2.3 to 5.1% faster on 1 GiB inputs
-    const bool nt = tile_index == kTileDrawn && (uint64_t)n * (uint64_t)words >= kNtLoadMin;
+    // non-temporal loads with the drawn tile index (from 2^25 elements, the
+    // large shape): each input word is read once. Measured 2 to 3% faster on
+    // 128 and 256 MB inputs, 4.6 to 5.1% on 512 MB and 1 GiB.
+    const bool nt = tile_index == kTileDrawn;
     const uint64_t num_tiles = ceil_div(n, op_tile_elems(words, shape));
     if (num_tiles > 0xffffffffull || num_tiles * op_tile_threads(shape) > kMaxGridThreads)
         return DWS_ERR_UNSUPPORTED;

@@ -498,8 +498,8 @@ static hipError_t launch_op_excl(int shape, int tile_index, bool nt, const OpSca
     case kOpShapeSmall: return launch_op_shape<Op, EXCL, 256, 4, 4, kTileDispatch>(p, stream);
     case kOpShapeMedium: return launch_op_shape<Op, EXCL, 512, 4, 8, kTileDispatch>(p, stream);
     case kOpShapeLarge:
-        // non-temporal loads are built for the drawn large shape only (the
-        // caller asks for them from 1 GiB of input)
+        // non-temporal loads are built for the drawn large shape only, which
+        // the caller uses from 2^25 elements
         if (tile_index == kTileDrawn)
             return nt ? launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn, true>(p, stream)
                       : launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn>(p, stream);

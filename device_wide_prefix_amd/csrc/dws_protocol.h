@@ -99,9 +99,9 @@ constexpr uint64_t kLongBackoffMin = (uint64_t)1 << 26;
 // 65,536-element drawn kernel, alternating builds on two GPU machines: 3.4 to
 // 3.9% faster at 2^28 elements, 3.0 to 3.2% at 2^29, 3.3% at 2^30; at 2^27
 // no better, at 2^25 and 2^26 3.5% slower. Non-temporal stores, alone or with
-// the loads, were slower at every size measured. The generic operators use
-// the same input size (1 GiB): 2.3 to 5.1% faster. Select, partition and the
-// run kernels measured faster from 2^25 elements and use their own limit.
+// the loads, were slower at every size measured. The generic operators,
+// select, partition and the run kernels measured faster from 2^25 elements and
+// load non-temporally from there (with their drawn or large-tile kernels).
 constexpr uint64_t kNtLoadMin = (uint64_t)1 << 28;
 
 constexpr int auto_shape(uint64_t n)
