@@ -221,12 +221,14 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     const bool aligned = aligned16(in, out);
     // non-temporal loads are a hint, built for aligned pointers only: 1 asks
     // for them, 2 never uses them, 0 leaves it to the library, which uses them
-    // from kNtLoadMin elements on the automatic drawn relaxed single pass
+    // on the automatic drawn relaxed single pass from kNtLoadMin elements, or
+    // from kNtLoadOutOfPlaceMin when the output is another buffer
     bool nt = false;
     if (o.nontemporal == 1) {
         nt = aligned;
     } else if (o.nontemporal == 0) {
-        nt = aligned && n >= kNtLoadMin && o.tile_shape == 0 && mode == kModeDecoupled &&
+        const uint64_t nt_min = in == out ? kNtLoadMin : kNtLoadOutOfPlaceMin;
+        nt = aligned && n >= nt_min && o.tile_shape == 0 && mode == kModeDecoupled &&
              o.memory_order == DWS_ORDER_RELAXED && o.tile_index != DWS_TILE_DISPATCH;
     }
     const int shape = resolve_shape(o.tile_shape, n, aligned);

@@ -103,6 +103,11 @@ constexpr uint64_t kLongBackoffMin = (uint64_t)1 << 26;
 // select, partition and the run kernels measured faster from 2^25 elements and
 // load non-temporally from there (with their drawn or large-tile kernels).
 constexpr uint64_t kNtLoadMin = (uint64_t)1 << 28;
+// Out of place (d_out != d_in) the + scan's non-temporal loads pay from here:
+// 3.6% faster at 2^26, 2.9% at 2^27, 2.0% at 2^28; at 2^25 no better. In
+// place they were slower below 2^27, where an ordinary load can leave the
+// line cached for the store to the same address.
+constexpr uint64_t kNtLoadOutOfPlaceMin = (uint64_t)1 << 26;
 
 constexpr int auto_shape(uint64_t n)
 {

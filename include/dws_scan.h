@@ -165,8 +165,9 @@ typedef struct dws_options {
                            1 .. dws_num_tile_shapes()-1 force one shape of
                            the single-pass kernel, for sweeps */
     int nontemporal;    /* non-temporal (streaming) loads of the input:
-                           0 = the library's choice (on from 2^28
-                           elements for the automatic single pass),
+                           0 = the library's choice (for the automatic
+                           single pass: on from 2^28 elements in place,
+                           from 2^26 out of place),
                            1 = on, 2 = off; stores are never
                            non-temporal */
     int tile_index;     /* dws_tile_index; default DWS_TILE_AUTO */
