@@ -61,15 +61,39 @@ SINGLE_PASS_SOURCES = ("dws_device.hpp", "dws_protocol.h", "dws_single_pass.h", 
                        "dws_sp_f32.hip")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments and with every whitespace run reduced
+    to one space: what the compiler sees, as far as a fingerprint needs."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] in "\"'":
+            j = i + 1
+            while j < n and src[j] != src[i]:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha(names=SINGLE_PASS_SOURCES) -> str:
-    """Hash of the sources a kernel is built from, to tell whether stored
-    counters still apply to it."""
+    """Hash of the code (comments and layout left out) of the sources a kernel
+    is built from, to tell whether stored counters still apply to it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "device_wide_prefix_amd", "csrc")
     for name in sorted(names):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

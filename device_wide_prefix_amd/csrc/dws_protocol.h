@@ -96,7 +96,7 @@ constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 25;   // drawn tile index from
 constexpr uint64_t kLongBackoffMin = (uint64_t)1 << 26;
 // From here the automatic choice loads the input with non-temporal loads (each
 // element is read once); stores stay ordinary. Measured on MI355X with the
-// 65,536-element drawn kernel, alternating builds on two GPU machines: 3.4 to
+// 65,536-element drawn kernel, alternating builds on two MI355X GPUs: 3.4 to
 // 3.9% faster at 2^28 elements, 3.0 to 3.2% at 2^29, 3.3% at 2^30; at 2^27
 // no better, at 2^25 and 2^26 3.5% slower. Non-temporal stores, alone or with
 // the loads, were slower at every size measured. The generic operators,
