@@ -52,6 +52,13 @@
  * no epoch is reused.
  * Calls on different streams never share a workspace. Host threads may call
  * concurrently. dws_release_workspaces frees every workspace.
+ * Workspaces are keyed by the stream handle and outlive the stream: destroying
+ * a stream frees nothing, and a stream created later may receive the same
+ * handle and then reuses that workspace. So synchronise a stream that has
+ * called the library before destroying it (a call still running on it would
+ * otherwise share its descriptors and tile counter with the new stream's
+ * calls), and call dws_release_workspaces to free the workspaces of streams
+ * that are gone.
  *
  * Errors: argument checks run before any HIP call and enqueue nothing. No C++
  * exception crosses this interface.
@@ -317,7 +324,9 @@ unsigned dws_tile_threads(int tile_shape, size_t n, int aligned);
  */
 dws_status dws_reserve(size_t n, hipStream_t stream);
 
-/* Synchronise the device and free every workspace the library holds. */
+/* Synchronise every device that holds a workspace and free every workspace
+ * the library holds. Not to be called while another host thread is inside a
+ * call of this library: that call may still be using a workspace. */
 dws_status dws_release_workspaces(void);
 
 /* ---- diagnostics (tests and benchmarks) --------------------------------- */
