@@ -15,7 +15,8 @@ buffer; a step is one scan call bracketed by HIP events on the stream the
 library launches on. The call is a single kernel launch, so the event time is
 the kernel's launch duration.
 
-Options: --workload C1..C5, --variant single_pass|reduce_then_scan|chained|scan_then_propagate,
+Options: --workload NAME (a key of scan_workloads.WORKLOADS),
+         --variant single_pass|reduce_then_scan|chained|scan_then_propagate,
 --order relaxed|acq_rel, --tile-shape K, --nontemporal auto|on|off, --no-cpu-baseline,
 --all (extra JSON lines for every workload and variant on stderr), --sweep
 (N = 2^10..2^30, every variant and memcpy, cold and warm caches; stderr),
@@ -45,7 +46,7 @@ import scan_workloads as wl  # noqa: E402
 METRIC = "scan GB/s (2n·sizeof(T)/time) at N=2^28 fp32; % of HBM peak & of D2D memcpy"
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_c4.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_f32_2p28.json")
 VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2, "scan_then_propagate": 3}
 ORDERS = {"relaxed": 0, "acq_rel": 1}
 TILE_INDEX = {"auto": 0, "drawn": 1, "dispatch": 2}
@@ -234,7 +235,7 @@ def run_sweep(steps: int, warmup: int):
     2^30, every variant, against a same-size device-to-device memcpy; cold
     (caches flushed before each step) and warm (no flush). Inputs are prefixes
     of one seeded draw. One JSON line per (N, variant, cache state) on stderr."""
-    w_big = wl.WORKLOADS["C4"]
+    w_big = wl.WORKLOADS["f32_2p28_excl_inplace"]
     x_all = wl.generate(w_big.dist, 1 << max(SWEEP_EXPONENTS), w_big.seed)
     rows = []
     for k in SWEEP_EXPONENTS:
@@ -258,13 +259,13 @@ ORACLE_SAMPLE = 1 << 26   # elements of a large input the oracle is timed on
 
 
 def run_select(steps: int, warmup: int, in_place: bool, with_oracle: bool = True):
-    """Stream compaction: C5's 0/1 flags (Bernoulli 0.5, seed 4) select from
+    """Stream compaction: the 2^30 - 12345 0/1 flags (Bernoulli 0.5, seed 4) select from
     uniform int32 values (seed 5). Algorithmic bytes = read values and flags
     (8 n) + write the selected values (4 count). Also times torch.masked_select
     on the same data (its output size needs a host synchronisation)."""
     import torch
     import device_wide_prefix_amd as dws
-    w = wl.WORKLOADS["C5"]
+    w = wl.WORKLOADS["flags_2p30m12345_excl"]
     n = w.n
     flags_h = wl.generate_workload(w)
     vals_h = wl.generate("i32_full", n, wl.SELECT_VALUE_SEED)
@@ -640,7 +641,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C4", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--workload", default="f32_2p28_excl_inplace", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--variant", default="single_pass", choices=sorted(VARIANTS))
     ap.add_argument("--order", default="relaxed", choices=sorted(ORDERS))
     ap.add_argument("--tile-shape", type=int, default=0)
@@ -687,7 +688,7 @@ def main():
 
     mean_ms = s["ms_mean"]
     achieved = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
-    traffic = traffic_for_current_kernel() if (variant == 0 and args.workload == "C4" and args.order == "relaxed"
+    traffic = traffic_for_current_kernel() if (variant == 0 and args.workload == "f32_2p28_excl_inplace" and args.order == "relaxed"
                                                and args.tile_shape == 0 and args.nontemporal == "auto"
                                                and args.tile_index == "auto") else None
     line = {
@@ -732,7 +733,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(w, x)
 
     if args.all:
-        for name in ("C1", "C2", "C3", "C4", "C5"):
+        for name in ("i32_4096_incl", "f32_2p20_incl", "u32_2p26_incl", "f32_2p28_excl_inplace", "flags_2p30m12345_excl"):
             wk = wl.WORKLOADS[name]
             xk = wl.generate_workload(wk)
             for vname, v in VARIANTS.items():

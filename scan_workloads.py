@@ -12,13 +12,13 @@ consume the same array.
 
 Workloads (sizes, dtypes, distributions and scan kinds of the measured
 configurations):
-  C1  N = 4096          int32   uniform integers 0..9        inclusive, seed 0
-  C2  N = 2^20          float32 uniform [-1, 1)              inclusive, seed 1
-  C3  N = 2^26          uint32  uniform over [0, 2^32)       inclusive, seed 2
-  C4  N = 2^28          float32 uniform [0, 1), in place     exclusive, seed 3
-  C5  N = 2^30 - 12345  int32   Bernoulli(0.5) 0/1 flags     exclusive, seed 4
+  i32_4096_incl                 N = 4096          int32   uniform integers 0..9        inclusive, seed 0
+  f32_2p20_incl                 N = 2^20          float32 uniform [-1, 1)              inclusive, seed 1
+  u32_2p26_incl                 N = 2^26          uint32  uniform over [0, 2^32)       inclusive, seed 2
+  f32_2p28_excl_inplace         N = 2^28          float32 uniform [0, 1), in place     exclusive, seed 3
+  flags_2p30m12345_excl N = 2^30 - 12345  int32   Bernoulli(0.5) 0/1 flags     exclusive, seed 4
 
-Stream compaction (select by flags) reuses C5's flags as the selection and
+Stream compaction (select by flags) reuses the 0/1 flags workload's flags as the selection and
 draws the values to move as uniform int32 with seed 5 (SELECT_VALUE_SEED).
 """
 from __future__ import annotations
@@ -50,16 +50,21 @@ class Workload:
 
 
 WORKLOADS = {
-    "C1": Workload("C1", 4096, "int32", "int_0_9", 0, False, False,
-                   "inclusive + scan, N=4096 int32 uniform integers 0..9, seed 0"),
-    "C2": Workload("C2", 1 << 20, "float32", "f32_pm1", 1, False, False,
-                   "inclusive + scan, N=2^20 fp32 uniform [-1,1), seed 1"),
-    "C3": Workload("C3", 1 << 26, "uint32", "u32_full", 2, False, False,
-                   "inclusive + scan mod 2^32, N=2^26 uint32 uniform over [0,2^32), seed 2"),
-    "C4": Workload("C4", 1 << 28, "float32", "f32_01", 3, True, True,
-                   "exclusive + scan in place, N=2^28 fp32 uniform [0,1), seed 3"),
-    "C5": Workload("C5", (1 << 30) - 12345, "int32", "flags_half", 4, True, False,
-                   "exclusive + scan, N=2^30-12345 int32 0/1 flags Bernoulli(0.5), seed 4"),
+    "i32_4096_incl": Workload(
+        "i32_4096_incl", 4096, "int32", "int_0_9", 0, False, False,
+        "inclusive + scan, N=4096 int32 uniform integers 0..9, seed 0"),
+    "f32_2p20_incl": Workload(
+        "f32_2p20_incl", 1 << 20, "float32", "f32_pm1", 1, False, False,
+        "inclusive + scan, N=2^20 fp32 uniform [-1,1), seed 1"),
+    "u32_2p26_incl": Workload(
+        "u32_2p26_incl", 1 << 26, "uint32", "u32_full", 2, False, False,
+        "inclusive + scan mod 2^32, N=2^26 uint32 uniform over [0,2^32), seed 2"),
+    "f32_2p28_excl_inplace": Workload(
+        "f32_2p28_excl_inplace", 1 << 28, "float32", "f32_01", 3, True, True,
+        "exclusive + scan in place, N=2^28 fp32 uniform [0,1), seed 3"),
+    "flags_2p30m12345_excl": Workload(
+        "flags_2p30m12345_excl", (1 << 30) - 12345, "int32", "flags_half", 4, True, False,
+        "exclusive + scan, N=2^30-12345 int32 0/1 flags Bernoulli(0.5), seed 4"),
 }
 
 

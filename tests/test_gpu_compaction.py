@@ -175,10 +175,10 @@ def test_reduce_by_key_unaligned_and_special_keys(gpu):
 
 
 def test_binding_full_size(gpu):
-    # the C5 flags partition 2^30 - 12345 uniform int32 values; reduce-by-key
+    # the 2^30 - 12345 0/1 flags partition 2^30 - 12345 uniform int32 values; reduce-by-key
     # over 2^27 keys in runs of mean length 32 with fp32 values
     import torch
-    w = wl.WORKLOADS["C5"]
+    w = wl.WORKLOADS["flags_2p30m12345_excl"]
     note(f"partition full size n={w.n}")
     flags = wl.generate_workload(w)
     x = wl.generate("i32_full", w.n, seed=wl.SELECT_VALUE_SEED)

@@ -407,7 +407,7 @@ def test_errors_enqueue_nothing(gpu):
 # the five workloads at full size, in the launch configuration the benchmark
 # times (default options through scan_inclusive / scan_exclusive)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["i32_4096_incl", "f32_2p20_incl", "u32_2p26_incl", "f32_2p28_excl_inplace", "flags_2p30m12345_excl"])
 def test_workload_full_size(gpu, name):
     import torch
     w = wl.WORKLOADS[name]
@@ -424,7 +424,7 @@ def test_workload_full_size(gpu, name):
     del store, xd, out
     worst = check_chunked(x, y, w.dtype, w.exclusive, label=name)
     note(f"workload {name}: parity ok, max fp32 tolerance ratio {worst:.3g}")
-    if name == "C5":
+    if name == "flags_2p30m12345_excl":
         # stream-compaction offsets: the exclusive scan of 0/1 flags ends at
         # popcount - last flag
         assert int(y[-1]) + int(x[-1]) == int(x.sum(dtype=np.int64))
@@ -602,8 +602,8 @@ def test_select_repeated_and_streams(gpu):
 
 
 def test_select_full_size(gpu):
-    # C5's flags select from uniform int32 values, in place
-    w = wl.WORKLOADS["C5"]
+    # the 2^30 - 12345 0/1 flags select from uniform int32 values, in place
+    w = wl.WORKLOADS["flags_2p30m12345_excl"]
     note(f"select full size n={w.n}")
     flags = wl.generate_workload(w)
     x = wl.generate("i32_full", w.n, seed=wl.SELECT_VALUE_SEED)

@@ -458,7 +458,7 @@ def test_select_flagged(lib):
     failures = []
     _select_checks(lib, failures.append)
     assert failures == []
-    # numpy's boolean indexing as an independent routine, on a C5-like input
+    # numpy's boolean indexing as an independent routine, on an input like the 2^30 - 12345 flags workload
     x = np.arange(1 << 20, dtype=np.uint32)
     flags = wl.generate("flags_half", 1 << 20, 4)
     assert np.array_equal(lib.select_flagged(x, flags), x[flags != 0])
@@ -487,7 +487,7 @@ def test_empty_and_in_place(lib):
     assert np.array_equal(x, want)
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+@pytest.mark.parametrize("name", ["i32_4096_incl", "f32_2p20_incl", "u32_2p26_incl"])
 def test_numpy_cumsum_on_workloads(lib, name):
     w = wl.WORKLOADS[name]
     x = wl.generate_workload(w)
