@@ -250,7 +250,7 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
     p.stamps = stamps;
-    p.long_backoff = n >= kLongBackoffMin ? 1u : 0u;
+    p.long_backoff = n >= kLongerBackoffMin ? 2u : (n >= kLongBackoffMin ? 1u : 0u);
     const bool f32 = kind_of(dtype) == kKindF32;
     auto launch = [&]() {
         return f32 ? launch_single_pass_typed<float>(cfg, excl, p, stream)

@@ -321,13 +321,13 @@ __device__ __forceinline__ uint32_t draw_tile(unsigned long long* counter, uint3
 // Tiles arriving faster than W / L fall further and further behind the last
 // P and need ever more polls; W = 64 K keeps W / L above the tile rate.
 //
-// Back-off: a blocked window is polled again after a short sleep; with
-// long_backoff (uniform) every poll after that first re-poll waits
-// 127 x 64 clocks, which keeps the descriptor traffic down when many tiles
-// wait at once.
+// Back-off: a blocked window is polled again after a short sleep. With
+// backoff 1 (uniform) every poll after that first re-poll waits 127 x 64
+// clocks, with backoff 2 190 x 64; fewer polls while many tiles wait leave the
+// memory system to the loads of the tiles being waited on.
 template <class T, int ORDER, int K>
 __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t epoch,
-                               unsigned int* watchdog, bool long_backoff = false)
+                               unsigned int* watchdog, uint32_t backoff = 0u)
 {
     const int lane = lane_id();
     const uint64_t lane_bit = 1ull << lane;
@@ -380,8 +380,12 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
             if (lane == 0) atomicAdd(watchdog, 1u);
             return prefix;
         }
-        if (long_backoff && repolled) __builtin_amdgcn_s_sleep(127);
-        else __builtin_amdgcn_s_sleep(1);
+        if (backoff != 0u && repolled) {
+            __builtin_amdgcn_s_sleep(127);
+            if (backoff > 1u) __builtin_amdgcn_s_sleep(63);
+        } else {
+            __builtin_amdgcn_s_sleep(1);
+        }
         repolled = true;
     }
 }

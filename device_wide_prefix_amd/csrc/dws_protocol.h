@@ -94,6 +94,12 @@ constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 25;   // drawn tile index from
 // 16 and 2^26, 1 to 4% faster at 2^28, but 4 to 5.5% slower at 2^25 and mean
 // run 16.
 constexpr uint64_t kLongBackoffMin = (uint64_t)1 << 26;
+// From here the + scan's blocked polls wait 190 x 64 clocks instead of 127 x
+// 64. Measured with non-temporal loads, six rounds each: 1.3 to 1.5% faster
+// at 2^28 to 2^30 in place; at 2^26 out of place 1.4% slower, at 2^27 equal.
+// A shorter sleep (24, 48 or 80 units) was slower at every size, 381 units
+// 2 to 11% slower.
+constexpr uint64_t kLongerBackoffMin = (uint64_t)1 << 28;
 // From here the automatic choice loads the input with non-temporal loads (each
 // element is read once); stores stay ordinary. Measured on MI355X with the
 // 65,536-element drawn kernel, alternating builds on two MI355X GPUs: 3.4 to

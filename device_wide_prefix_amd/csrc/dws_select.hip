@@ -126,7 +126,7 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
             } else {
                 if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, count));
                 prefix = lookback_decoupled<uint32_t, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch,
-                                                                                     p.watchdog, p.long_backoff != 0u);
+                                                                                     p.watchdog, p.long_backoff);
                 if (lane == 0) {
                     desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusP, prefix + count));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);

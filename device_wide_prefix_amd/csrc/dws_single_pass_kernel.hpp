@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
                     if (lane == 0)
                         desc_store<ORDER>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
                     prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog,
-                                                                          p.long_backoff != 0u);
+                                                                          p.long_backoff);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
