@@ -220,7 +220,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     const SelectShape s = select_shape(a.n, a.aligned);
     SelectParams p{static_cast<const uint32_t*>(a.in), static_cast<const uint32_t*>(a.flags),
                    static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
-                   a.epoch, a.n >= kLongBackoffMin ? 1u : 0u};
+                   a.epoch,
+                   a.n >= kLongerBackoffMin ? 2u : (a.n >= kLongBackoffMin ? 1u : 0u)};
     void* args[] = {&p};
     // the workgroup index as the tile index below kSelectDrawnMin, as for the
     // scan: no atomic on the critical path while there are few tiles per CU;
