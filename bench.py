@@ -162,7 +162,7 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: int, 
         if default:
             st = entry(work.data_ptr(), out.data_ptr(), w.n, code, stream)
         else:
-            st = dws.scan_ex_ptr(work.data_ptr(), out.data_ptr(), w.n, code, w.exclusive, opt, stream)
+            st = dws.scan_opts_ptr(work.data_ptr(), out.data_ptr(), w.n, code, w.exclusive, opt, stream)
         if st != dws.OK:
             raise RuntimeError(f"scan failed: {dws.status_string(st)}")
 

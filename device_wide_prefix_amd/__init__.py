@@ -6,8 +6,9 @@ fallback; if the library is not built, importing the binding's functions raises.
 
     scan_inclusive(x, out=None)            -> out
     scan_exclusive(x, out=None)            -> out      (out may be x: in place)
-    scan_ex(x, out=None, exclusive=False, variant=..., memory_order=...,
-            tile_shape=0, nontemporal=None) -> out
+    scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS) -> out
+    scan_opts(x, out=None, exclusive=False, variant=..., memory_order=...,
+              tile_shape=0, nontemporal=None, tile_index=...) -> out
     scan_debug(x, out, tile_elems, ...)    -> descriptor words (numpy uint64)
     watchdog_trips()                       -> int
     selftest_wave(x)                       -> (incl, shift)
@@ -22,7 +23,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libdws_scan.so")
 
 # dws_status
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_MISALIGNED, ERR_HIP, ERR_OOM = range(7)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OVERLAP, ERR_HIP, ERR_OOM, ERR_MISALIGNED = range(7)
 # dws_dtype
 INT32, UINT32, FLOAT32, PAIR_I32_F32, PAIR_U32 = 0, 1, 2, 3, 4
 # dws_op
@@ -37,7 +38,7 @@ TILE_AUTO, TILE_DRAWN, TILE_DISPATCH = 0, 1, 2
 NT_AUTO, NT_ON, NT_OFF = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
-    "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string", "dws_version",
+    "scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_scan_opts", "dws_status_string", "dws_version",
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
@@ -78,8 +79,10 @@ def load_library():
         f = getattr(lib, name)
         f.argtypes = [vp, vp, sz, ci, vp]
         f.restype = ci
-    lib.dws_scan_ex.argtypes = [vp, vp, sz, ci, ci, ctypes.POINTER(DwsOptions), vp]
+    lib.dws_scan_ex.argtypes = [vp, vp, sz, ci, ci, ci, vp]
     lib.dws_scan_ex.restype = ci
+    lib.dws_scan_opts.argtypes = [vp, vp, sz, ci, ci, ctypes.POINTER(DwsOptions), vp]
+    lib.dws_scan_opts.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -135,10 +138,15 @@ def scan_exclusive_ptr(d_in: int, d_out: int, n: int, dtype: int, stream: int = 
     return load_library().scan_exclusive(d_in, d_out, n, dtype, stream)
 
 
-def scan_ex_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,
-                options: DwsOptions | None, stream: int = 0) -> int:
+def scan_ex_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool, variant: int,
+                stream: int = 0) -> int:
+    return load_library().dws_scan_ex(d_in, d_out, n, dtype, int(bool(exclusive)), int(variant), stream)
+
+
+def scan_opts_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,
+                  options: DwsOptions | None, stream: int = 0) -> int:
     opt = ctypes.byref(options) if options is not None else None
-    return load_library().dws_scan_ex(d_in, d_out, n, dtype, int(bool(exclusive)), opt, stream)
+    return load_library().dws_scan_opts(d_in, d_out, n, dtype, int(bool(exclusive)), opt, stream)
 
 
 # ---- torch-tensor entry points --------------------------------------------
@@ -194,8 +202,17 @@ def scan_exclusive(x, out=None, stream=None):
     return out
 
 
-def scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=ORDER_RELAXED,
-            tile_shape=0, nontemporal=None, tile_index=TILE_AUTO, stream=None):
+def scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS, stream=None):
+    """Scan by the global strategy ``variant`` (dws_variant); returns ``out``."""
+    code, out = _prepare(x, out)
+    with _device_of(x):
+        _check(scan_ex_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, variant,
+                           _stream(x, stream)), "dws_scan_ex")
+    return out
+
+
+def scan_opts(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=ORDER_RELAXED,
+              tile_shape=0, nontemporal=None, tile_index=TILE_AUTO, stream=None):
     """Scan with explicit options (variant, descriptor memory order, tile shape,
     non-temporal loads: None for the library's choice, True or False to force
     them on or off; tile index source); returns ``out``."""
@@ -203,8 +220,8 @@ def scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=ORDE
     nt = NT_AUTO if nontemporal is None else (NT_ON if nontemporal else NT_OFF)
     opt = DwsOptions(int(variant), int(memory_order), int(tile_shape), nt, int(tile_index))
     with _device_of(x):
-        _check(scan_ex_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, opt,
-                           _stream(x, stream)), "dws_scan_ex")
+        _check(scan_opts_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, opt,
+                             _stream(x, stream)), "dws_scan_opts")
     return out
 
 

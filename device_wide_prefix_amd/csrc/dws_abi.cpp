@@ -37,6 +37,7 @@ struct Workspace {
     void* stp = nullptr;          // scan-then-propagate tile sums (all levels)
     uint64_t stp_elems = 0;
     uint32_t launches = 0;        // look-back launches issued since the descriptors were cleared
+    unsigned int trips_seen = 0;  // watchdog count when dws_watchdog_trips last cleared the state
 
     unsigned long long* counter() const
     {
@@ -215,8 +216,19 @@ int cu_count()
     return cus;
 }
 
-dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
-                           const dws_options& o, hipStream_t stream, unsigned long long* stamps = nullptr)
+}  // namespace
+
+namespace dws {
+
+dws_status status_from_hip(hipError_t e) { return from_hip(e); }
+
+dws_status validate_scan_args(const void* in, const void* out, size_t n, int dtype)
+{
+    return validate(in, out, n, dtype);
+}
+
+dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
+                            const dws_options& o, unsigned long long* stamps, SinglePassPlan* plan)
 {
     const bool aligned = aligned16(in, out);
     // non-temporal loads are a hint, built for aligned pointers only: 1 asks
@@ -251,28 +263,48 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     p.num_tiles = (uint32_t)num_tiles;
     p.stamps = stamps;
     p.long_backoff = n >= kLongerBackoffMin ? 2u : (n >= kLongBackoffMin ? 1u : 0u);
-    const bool f32 = kind_of(dtype) == kKindF32;
-    auto launch = [&]() {
-        return f32 ? launch_single_pass_typed<float>(cfg, excl, p, stream)
-                   : launch_single_pass_typed<uint32_t>(cfg, excl, p, stream);
-    };
-    if (num_tiles == 1) {
-        // one tile: no predecessors, no descriptors, no counter
-        return from_hip(launch());
+    plan->cfg = cfg;
+    plan->f32 = kind_of(dtype) == kKindF32;
+    plan->exclusive = excl;
+    plan->params = p;
+    return DWS_OK;
+}
+
+hipError_t launch_single_pass_plan(const SinglePassPlan& plan, const LookbackState* state, hipStream_t stream)
+{
+    SinglePassParams p = plan.params;
+    if (state != nullptr) {
+        p.desc = state->desc;
+        p.counter = state->counter;
+        p.watchdog = state->watchdog;
+        p.epoch = state->epoch;
     }
+    return plan.f32 ? launch_single_pass_typed<float>(plan.cfg, plan.exclusive, p, stream)
+                    : launch_single_pass_typed<uint32_t>(plan.cfg, plan.exclusive, p, stream);
+}
+
+}  // namespace dws
+
+namespace {
+
+dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
+                           const dws_options& o, hipStream_t stream, unsigned long long* stamps = nullptr)
+{
+    SinglePassPlan plan{};
+    dws_status s = plan_single_pass(in, out, n, dtype, excl, mode, o, stamps, &plan);
+    if (s != DWS_OK) return s;
+    // one tile: no predecessors, no descriptors, no counter
+    if (plan.params.num_tiles == 1) return from_hip(launch_single_pass_plan(plan, nullptr, stream));
     Workspace* ws = nullptr;
-    dws_status s = get_workspace(stream, &ws);
+    s = get_workspace(stream, &ws);
     if (s != DWS_OK) return s;
     std::lock_guard<std::mutex> lock(ws->mu);
-    s = ensure_desc(ws, num_tiles);
+    s = ensure_desc(ws, plan.params.num_tiles);
     if (s != DWS_OK) return s;
     s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
-    p.epoch = ws->epoch();
-    p.desc = ws->desc;
-    p.counter = ws->counter();
-    p.watchdog = ws->watchdog();
-    return from_hip(launch());
+    const LookbackState st{ws->desc, ws->desc_slots, ws->counter(), ws->watchdog(), ws->epoch()};
+    return from_hip(launch_single_pass_plan(plan, &st, stream));
 }
 
 dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hipStream_t stream)
@@ -479,8 +511,16 @@ dws_status scan_exclusive(const void* d_in, void* d_out, size_t n, dws_dtype dty
     return scan_entry(d_in, d_out, n, enum_arg(dtype), 1, nullptr, stream);
 }
 
-dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive,
-                       const dws_options* opt, hipStream_t stream)
+dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive, int variant,
+                       hipStream_t stream)
+{
+    dws_options o{};
+    o.variant = variant;
+    return scan_entry(d_in, d_out, n, enum_arg(dtype), exclusive, &o, stream);
+}
+
+dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive,
+                         const dws_options* opt, hipStream_t stream)
 {
     return scan_entry(d_in, d_out, n, enum_arg(dtype), exclusive, opt, stream);
 }
@@ -600,10 +640,24 @@ dws_status dws_watchdog_trips(unsigned long long* trips)
         std::lock_guard<std::mutex> lock(g_mu);
         for (auto& kv : g_workspaces) {
             if (kv.first.first != dev) continue;
+            Workspace* ws = kv.second.get();
             unsigned int v = 0;
-            e = hipMemcpy(&v, kv.second->watchdog(), sizeof(v), hipMemcpyDeviceToHost);
+            e = hipMemcpy(&v, ws->watchdog(), sizeof(v), hipMemcpyDeviceToHost);
             if (e != hipSuccess) return from_hip(e);
             total += v;
+            if (v != ws->trips_seen) {
+                // a wait that timed out may have left a late workgroup's
+                // descriptor under a later launch's epoch: start the look-back
+                // state afresh (the count itself is kept). The workspace's
+                // stream may be gone by now, so the clearing kernel runs on
+                // the null stream of the (synchronised) device.
+                std::lock_guard<std::mutex> wlock(ws->mu);
+                e = launch_workspace_init(ws->desc, ws->desc_slots, ws->counter(), ws->epoch(), nullptr, nullptr);
+                if (e == hipSuccess) e = hipDeviceSynchronize();
+                if (e != hipSuccess) return from_hip(e);
+                ws->launches = 0;
+                ws->trips_seen = v;
+            }
         }
         *trips = total;
         return DWS_OK;

@@ -6,9 +6,37 @@
 #include <stdint.h>
 
 #include "dws_protocol.h"
+#include "dws_scan.h"
 #include "dws_single_pass.h"
 
 namespace dws {
+
+// Look-back state a launch with more than one tile needs: descriptors, tile
+// counter, watchdog word and epoch word (a workspace).
+struct LookbackState {
+    uint64_t* desc;
+    uint64_t desc_slots;
+    unsigned long long* counter;
+    unsigned int* watchdog;
+    unsigned int* epoch;
+};
+
+// The single-pass kernel and arguments a validated scan call runs with
+// (dws_abi.cpp). params.desc, counter, watchdog and epoch are left empty;
+// launch_single_pass_plan takes them from `state` (null for one tile, which
+// touches none of them).
+struct SinglePassPlan {
+    int cfg;                  // index into kCfgs
+    bool f32;
+    bool exclusive;
+    SinglePassParams params;
+};
+dws_status status_from_hip(hipError_t e);
+dws_status validate_scan_args(const void* in, const void* out, size_t n, int dtype);
+dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
+                            const dws_options& o, unsigned long long* stamps, SinglePassPlan* plan);
+hipError_t launch_single_pass_plan(const SinglePassPlan& plan, const LookbackState* state, hipStream_t stream);
+
 
 // Workspace control block layout (one 256-byte allocation per workspace):
 // the tile counter and the watchdog counter sit on separate cache lines.

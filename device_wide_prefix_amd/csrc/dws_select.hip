@@ -1,15 +1,14 @@
 // Fused stream compaction (select by flags) on the single-pass decoupled
 // look-back: Merrill & Garland, section 4.4 (in-place compaction behaviour:
-// scatter offsets come from a prefix sum of 0/1 flags, and the look-back's
-// signalling guarantees every predecessor has read its input before a tile
-// writes, so the output may overwrite the input) and section A5 (select-if
-// fused with the scan, no extra pass).
+// scatter offsets come from a prefix sum of 0/1 flags; the look-back's
+// signalling can guarantee that every predecessor has read its input before a
+// tile writes, so the output may overwrite the input) and section A5
+// (select-if fused with the scan, no extra pass).
 //
 // Per tile (one workgroup; tile index drawn from the workspace counter from
 // 2^25 elements, the workgroup index below; same descriptor protocol and
 // workspace as the scan):
-//   1. load the flags, then the values of the tile (coalesced, in registers;
-//      steps 2 and 3 wait for the flags only);
+//   1. load the flags, then the values of the tile (coalesced, in registers);
 //   2. exclusive scan of the 0/1 flags in the tile -> each element's rank
 //      among the tile's selected elements, and the tile's selected count;
 //   3. publish {A, count}, look back over predecessors' counts -> the number
@@ -18,9 +17,22 @@
 //      through a buffer resource based at out + prefix whose range is the
 //      tile's count; unselected elements get an offset past that range, which
 //      the hardware drops, so the scatter needs no branch.
-// Writes of tile t land in [prefix_t, prefix_t + count_t), below the end of
-// tile t, and start only after every earlier tile has published (so has read
-// its input): in place is safe.
+//
+// In place (ALIAS: out == in). Writes of tile t land in [prefix_t, prefix_t +
+// count_t), which lies below the end of tile t and may reach into the input of
+// any earlier tile. They are issued only after tile t knows its prefix, which
+// needs an A or P of every earlier tile (a P is published only after its own
+// tile's look-back, so by induction every earlier tile has published). What
+// makes that safe is the order inside each tile: every wave consumes its value
+// registers before the barrier that precedes the tile's A, which makes the
+// compiler wait until every value load has returned its data (s_waitcnt
+// vmcnt). So when any tile can see this tile's A, its whole input is already
+// in registers, and no later store can change what it read. That wait is the
+// load-ordering half of a release; the other half (writing back earlier
+// stores) has nothing to order, since a tile stores only after its look-back.
+// Out of place (ALIAS false) no tile writes another's input, and steps 2 and 3
+// wait for the flags only, so the look-back runs while the values are still in
+// flight.
 //
 // Partition (section A5, partition-if) is the same kernel with one more
 // store: the rejected elements go to the back of the output in reverse input
@@ -52,9 +64,10 @@ struct SelectParams {
 // buffer range check drops the store. Offset plus store size stays below 2^32.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
-template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX, bool NT = false>
+template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX, bool NT = false, bool ALIAS = false>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
+    static_assert(!(PARTITION && ALIAS), "a partition is never in place");
     static_assert(VEC * CHUNKS <= 64, "one selection bit per element in a 64-bit mask");
     using Mask = typename std::conditional<(VEC * CHUNKS > 32), uint64_t, uint32_t>::type;
     constexpr int W = BLOCK / 64;
@@ -88,7 +101,8 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     const uint32_t seg_valid = valid_bytes(seg_first, SEG, p.n);
     uint32_t x[CHUNKS][VEC], r[CHUNKS][VEC];
     // flags first: the tile's count (its aggregate) needs only the flags, so
-    // it is published and the look-back runs while the values are in flight
+    // out of place it is published and the look-back runs while the values
+    // are in flight
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
 
@@ -104,6 +118,10 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
         }
     const uint32_t seg_count = scan_segment_local<uint32_t, true, VEC, CHUNKS>(r);
     pin_in_registers<uint32_t, VEC, CHUNKS>(r);
+    // in place: the values must be in registers before this tile can publish
+    // (the use below waits for every value load of the wave; the barrier then
+    // covers every wave of the tile)
+    if constexpr (ALIAS) pin_in_registers<uint32_t, VEC, CHUNKS>(x);
 
     if (lane == 0) s_wave[wave] = seg_count;
     __syncthreads();
@@ -196,17 +214,17 @@ static SelectShape select_shape(uint64_t n, bool aligned)
 
 uint32_t select_tile_elems(uint64_t n, bool aligned) { return select_shape(n, aligned).elems(); }
 
-template <bool PARTITION, int TI>
+template <bool PARTITION, int TI, bool NT = false, bool ALIAS = false>
 static const void* select_kernel(const SelectShape& s)
 {
     if (s.vec == 1) return reinterpret_cast<const void*>(
-        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION, TI>);
+        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION, TI, false, ALIAS>);
     if (s.chunks == kSelectHuge.chunks) return reinterpret_cast<const void*>(
-        &k_select<kSelectHuge.threads, kSelectHuge.vec, kSelectHuge.chunks, PARTITION, TI>);
+        &k_select<kSelectHuge.threads, kSelectHuge.vec, kSelectHuge.chunks, PARTITION, TI, NT, ALIAS>);
     if (s.threads == kSelectLarge.threads) return reinterpret_cast<const void*>(
-        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION, TI>);
+        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION, TI, NT, ALIAS>);
     return reinterpret_cast<const void*>(
-        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION, TI>);
+        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION, TI, false, ALIAS>);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
@@ -225,26 +243,23 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     void* args[] = {&p};
     // the workgroup index as the tile index below kSelectDrawnMin, as for the
     // scan: no atomic on the critical path while there are few tiles per CU;
-    // the watchdog still bounds every wait
-    const bool drawn = a.n >= kSelectDrawnMin;
-    const void* fn = a.partition ? (drawn ? select_kernel<true, kTileDrawn>(s) : select_kernel<true, kTileDispatch>(s))
-                                 : (drawn ? select_kernel<false, kTileDrawn>(s) : select_kernel<false, kTileDispatch>(s));
-    // with a drawn tile index (from 2^25 elements) the values and flags are
+    // the watchdog still bounds every wait.
+    // With a drawn tile index (from 2^25 elements) the values and flags are
     // loaded non-temporally, each being read once: measured 0.5 to 2% faster
     // at 2^25, 3 to 5.6% at 2^26 and 2^27, 3% at 2^30 - 12,345. Those sizes run
-    // the large or huge shape when the pointers are aligned.
-    if (drawn && s.vec == 4) {
-        if (s.chunks == kSelectHuge.chunks)
-            fn = a.partition ? reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
-                                                                       kSelectHuge.chunks, true, kTileDrawn, true>)
-                             : reinterpret_cast<const void*>(&k_select<kSelectHuge.threads, kSelectHuge.vec,
-                                                                       kSelectHuge.chunks, false, kTileDrawn, true>);
-        else if (s.threads == kSelectLarge.threads && s.chunks == kSelectLarge.chunks)
-            fn = a.partition ? reinterpret_cast<const void*>(&k_select<kSelectLarge.threads, kSelectLarge.vec,
-                                                                       kSelectLarge.chunks, true, kTileDrawn, true>)
-                             : reinterpret_cast<const void*>(&k_select<kSelectLarge.threads, kSelectLarge.vec,
-                                                                       kSelectLarge.chunks, false, kTileDrawn, true>);
-    }
+    // the large or huge shape when the pointers are aligned (the small and
+    // scalar shapes have no non-temporal build).
+    // In place (select only) the kernel waits for its values before it
+    // publishes, which is what makes writing over the input safe.
+    const bool drawn = a.n >= kSelectDrawnMin;
+    const bool alias = !a.partition && a.out == a.in;
+    const void* fn;
+    if (a.partition)
+        fn = drawn ? select_kernel<true, kTileDrawn, true>(s) : select_kernel<true, kTileDispatch>(s);
+    else if (alias)
+        fn = drawn ? select_kernel<false, kTileDrawn, true, true>(s) : select_kernel<false, kTileDispatch, false, true>(s);
+    else
+        fn = drawn ? select_kernel<false, kTileDrawn, true>(s) : select_kernel<false, kTileDispatch>(s);
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 

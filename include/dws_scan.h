@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DWS_VERSION 2
+#define DWS_VERSION 3
 
 typedef enum dws_status {
     DWS_OK = 0,
@@ -81,9 +81,9 @@ typedef enum dws_status {
     DWS_ERR_UNSUPPORTED = 2,   /* n above a limit, or an option, operator or
                                   type combination that is not built */
     DWS_ERR_OVERLAP = 3,       /* d_in and d_out overlap without being equal */
-    DWS_ERR_MISALIGNED = 4,    /* a pointer is not aligned to the element size */
-    DWS_ERR_HIP = 5,           /* a HIP runtime call failed */
-    DWS_ERR_OOM = 6            /* workspace allocation failed */
+    DWS_ERR_HIP = 4,           /* a HIP runtime call failed */
+    DWS_ERR_OOM = 5,           /* workspace allocation failed */
+    DWS_ERR_MISALIGNED = 6     /* a pointer is not aligned to the element size */
 } dws_status;
 
 typedef enum dws_dtype {
@@ -117,7 +117,7 @@ dws_status scan_inclusive(const void* d_in, void* d_out, size_t n,
 dws_status scan_exclusive(const void* d_in, void* d_out, size_t n,
                           dws_dtype dtype, hipStream_t stream);
 
-/* Global strategy selected by dws_options.variant. */
+/* Global strategy: the variant argument of dws_scan_ex, or dws_options.variant. */
 typedef enum dws_variant {
     /* one pass, decoupled look-back: ~2n traffic (Merrill & Garland, 4.1) */
     DWS_VARIANT_SINGLE_PASS = 0,
@@ -181,9 +181,20 @@ typedef struct dws_options {
 } dws_options;
 
 /*
- * Scan with explicit options. opt == NULL (or a zeroed struct) means all
- * defaults; exclusive != 0 selects the exclusive scan. Unknown values give
- * DWS_ERR_INVALID_ARG. Built combinations (others give DWS_ERR_UNSUPPORTED):
+ * Scan by a chosen global strategy: exclusive != 0 selects the exclusive scan,
+ * variant is a dws_variant (DWS_VARIANT_SINGLE_PASS is exactly scan_inclusive
+ * / scan_exclusive; the others are the comparison strategies). Every other
+ * choice is the library's automatic one. An unknown variant gives
+ * DWS_ERR_INVALID_ARG. Same contract as scan_inclusive.
+ */
+dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                       int exclusive, int variant, hipStream_t stream);
+
+/*
+ * Scan with explicit options, for measurements and sweeps. opt == NULL (or a
+ * zeroed struct) means all defaults; exclusive != 0 selects the exclusive
+ * scan. Unknown values give DWS_ERR_INVALID_ARG. Built combinations (others
+ * give DWS_ERR_UNSUPPORTED):
  *   single pass: every tile_shape with relaxed order; the automatically
  *                chosen shapes also with release/acquire and with
  *                nontemporal 1 (relaxed);
@@ -196,8 +207,8 @@ typedef struct dws_options {
  * shape without a scalar-load kernel then falls back to the automatic one,
  * and nontemporal is ignored.
  */
-dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
-                       int exclusive, const dws_options* opt, hipStream_t stream);
+dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                         int exclusive, const dws_options* opt, hipStream_t stream);
 
 /*
  * Stream compaction (select by flags), fused with the single-pass scan
@@ -333,9 +344,21 @@ dws_status dws_release_workspaces(void);
 
 /*
  * Number of look-back waits on the current device that exceeded the safety
- * limit (about two seconds) since the library was loaded. A correct run keeps
- * it at 0; when it trips, the waiting tile proceeds with an incomplete prefix
- * rather than hang, so that run's output is wrong. Synchronous.
+ * limit (about two seconds) since the library was loaded, over every
+ * workspace. A correct run keeps it at 0.
+ *
+ * A trip means WRONG OUTPUT that no status reports: the calls are
+ * asynchronous and have already returned DWS_OK when a wait times out. Rather
+ * than hang the GPU, the waiting tile goes on with an incomplete prefix, so
+ * the output of the call it belongs to (a scan, compaction, partition,
+ * reduce-by-key, run-length encoding or operator scan) is wrong from that
+ * tile on. Check this count after results that matter.
+ *
+ * Synchronous: it synchronises the current device first. When the count of a
+ * workspace has grown since the last check, this call
+ * also clears that look-back state, so that no descriptor left behind by the
+ * timed-out call can reach a later one; call it after a trip before relying on
+ * further results. The count itself is never reset.
  */
 dws_status dws_watchdog_trips(unsigned long long* trips);
 

@@ -56,7 +56,7 @@ def run(x_dev, out_dev, n: int, dtype: str, exclusive: bool, variant=0, order=0,
         st = f(x_dev.data_ptr(), out_dev.data_ptr(), n, CODE[dtype], stream)
     else:
         opt = dws.DwsOptions(variant, order, shape, nt, tile_index)
-        st = dws.scan_ex_ptr(x_dev.data_ptr(), out_dev.data_ptr(), n, CODE[dtype], exclusive, opt, stream)
+        st = dws.scan_opts_ptr(x_dev.data_ptr(), out_dev.data_ptr(), n, CODE[dtype], exclusive, opt, stream)
     assert st == dws.OK, f"scan returned {st}: {dws.status_string(st)}"
 
 

@@ -87,20 +87,25 @@ static void scans(void)
         o.tile_shape = bad_opts[k][2];
         o.nontemporal = bad_opts[k][3];
         o.tile_index = bad_opts[k][4];
-        CHECK(dws_scan_ex(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, &o, NULL), DWS_ERR_INVALID_ARG);
-        CHECK(dws_scan_ex(NULL, NULL, 0, DWS_INT32, 0, &o, NULL), DWS_ERR_INVALID_ARG);
+        CHECK(dws_scan_opts(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, &o, NULL), DWS_ERR_INVALID_ARG);
+        CHECK(dws_scan_opts(NULL, NULL, 0, DWS_INT32, 0, &o, NULL), DWS_ERR_INVALID_ARG);
     }
     o.variant = 0;
     o.memory_order = 0;
     o.tile_shape = dws_num_tile_shapes();
     o.nontemporal = 0;
     o.tile_index = 0;
-    CHECK(dws_scan_ex(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, &o, NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_opts(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, &o, NULL), DWS_ERR_INVALID_ARG);
     o.tile_shape = 0;
     o.variant = DWS_VARIANT_CHAINED;
     o.tile_index = DWS_TILE_DISPATCH;
-    CHECK(dws_scan_ex(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, &o, NULL), DWS_ERR_UNSUPPORTED);
-    CHECK(dws_scan_ex(NULL, NULL, 0, DWS_INT32, 0, NULL, NULL), DWS_OK);
+    CHECK(dws_scan_opts(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, &o, NULL), DWS_ERR_UNSUPPORTED);
+    CHECK(dws_scan_opts(NULL, NULL, 0, DWS_INT32, 0, NULL, NULL), DWS_OK);
+    /* the variant as a plain int */
+    CHECK(dws_scan_ex(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, 4, NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_ex(at(FAKE), at(FAKE + (1 << 20)), 1 << 16, DWS_FLOAT32, 1, -1, NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_ex(NULL, NULL, 0, DWS_INT32, 0, DWS_VARIANT_CHAINED, NULL), DWS_OK);
+    CHECK(dws_scan_ex(at(FAKE), at(FAKE + 4), 10, DWS_INT32, 0, DWS_VARIANT_REDUCE_THEN_SCAN, NULL), DWS_ERR_OVERLAP);
 }
 
 static void compaction(void)

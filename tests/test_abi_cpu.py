@@ -29,11 +29,58 @@ def lib():
     return dws.load_library()
 
 
+def _prototype(text: str, name: str) -> str:
+    """The declaration of `name` in the header, comments dropped and
+    whitespace collapsed: 'ret name(type a, type b)'."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"^([A-Za-z_][\w \t\*]*?\b" + name + r"\s*\([^;]*\))\s*;", text, flags=re.M)
+    assert m, f"{name} not declared"
+    return " ".join(m.group(1).replace("(", " ( ").replace(")", " ) ").replace(",", " , ").replace("*", " * ").split())
+
+
+def _enum_values(text: str, enum: str) -> dict:
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"typedef enum " + enum + r"\s*\{(.*?)\}", text, flags=re.S)
+    assert m, enum
+    return {k: int(v) for k, v in re.findall(r"(\w+)\s*=\s*(-?\d+)", m.group(1))}
+
+
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("scan_inclusive", "scan_exclusive", "dws_scan_ex", "dws_status_string"):
         assert required in names
     assert set(names) == set(dws.EXPORTED_SYMBOLS)
+
+
+def test_header_pins_the_boundary_signatures():
+    """The four calls of the boundary with the argument lists, enum values and
+    status numbering they are specified with; later additions (MISALIGNED,
+    the pair types) are appended after them."""
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    want = {
+        "scan_inclusive": "dws_status scan_inclusive ( const void * d_in , void * d_out , size_t n , "
+                          "dws_dtype dtype , hipStream_t stream )",
+        "scan_exclusive": "dws_status scan_exclusive ( const void * d_in , void * d_out , size_t n , "
+                          "dws_dtype dtype , hipStream_t stream )",
+        "dws_scan_ex": "dws_status dws_scan_ex ( const void * d_in , void * d_out , size_t n , dws_dtype dtype , "
+                       "int exclusive , int variant , hipStream_t stream )",
+        "dws_status_string": "const char * dws_status_string ( dws_status status )",
+    }
+    for name, proto in want.items():
+        assert _prototype(text, name) == proto
+    st = _enum_values(text, "dws_status")
+    assert [st[k] for k in ("DWS_OK", "DWS_ERR_INVALID_ARG", "DWS_ERR_UNSUPPORTED", "DWS_ERR_OVERLAP",
+                            "DWS_ERR_HIP", "DWS_ERR_OOM")] == [0, 1, 2, 3, 4, 5]
+    assert st["DWS_ERR_MISALIGNED"] == 6
+    dt = _enum_values(text, "dws_dtype")
+    assert [dt[k] for k in ("DWS_INT32", "DWS_UINT32", "DWS_FLOAT32")] == [0, 1, 2]
+    var = _enum_values(text, "dws_variant")
+    assert [var[k] for k in ("DWS_VARIANT_SINGLE_PASS", "DWS_VARIANT_REDUCE_THEN_SCAN",
+                             "DWS_VARIANT_CHAINED")] == [0, 1, 2]
+    # the binding's constants are the header's
+    assert (dws.OK, dws.ERR_INVALID_ARG, dws.ERR_UNSUPPORTED, dws.ERR_OVERLAP, dws.ERR_HIP, dws.ERR_OOM,
+            dws.ERR_MISALIGNED) == (0, 1, 2, 3, 4, 5, 6)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -42,7 +89,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dws_version() == 2
+    assert lib.dws_version() == 3
     for code in range(7):
         s = dws.status_string(code)
         assert isinstance(s, str) and s
@@ -102,7 +149,7 @@ def test_option_validation(lib):
     def call(**kw):
         o = dws.DwsOptions(kw.get("variant", 0), kw.get("order", 0), kw.get("shape", 0), kw.get("nt", 0),
                            kw.get("tile_index", 0))
-        return lib.dws_scan_ex(FAKE, FAKE + (1 << 20), 1 << 16, dws.FLOAT32, 1, ctypes.byref(o), None)
+        return lib.dws_scan_opts(FAKE, FAKE + (1 << 20), 1 << 16, dws.FLOAT32, 1, ctypes.byref(o), None)
     assert call(variant=4) == dws.ERR_INVALID_ARG
     assert call(variant=-1) == dws.ERR_INVALID_ARG
     assert call(order=2) == dws.ERR_INVALID_ARG
@@ -134,8 +181,22 @@ def test_option_validation(lib):
     assert call(tile_index=dws.TILE_DISPATCH, nt=1) == dws.ERR_UNSUPPORTED
     # options are validated before the arguments: n == 0 with bad options
     o = dws.DwsOptions(9, 0, 0, 0)
-    assert lib.dws_scan_ex(None, None, 0, dws.INT32, 0, ctypes.byref(o), None) == dws.ERR_INVALID_ARG
-    assert lib.dws_scan_ex(None, None, 0, dws.INT32, 0, None, None) == dws.OK
+    assert lib.dws_scan_opts(None, None, 0, dws.INT32, 0, ctypes.byref(o), None) == dws.ERR_INVALID_ARG
+    assert lib.dws_scan_opts(None, None, 0, dws.INT32, 0, None, None) == dws.OK
+
+
+def test_variant_validation(lib):
+    """dws_scan_ex takes the variant as a plain int: unknown values are
+    rejected before any HIP call, known ones pass to argument validation."""
+    f = lib.dws_scan_ex
+    for bad in (4, -1, 1 << 20):
+        assert f(FAKE, FAKE + (1 << 20), 1 << 16, dws.FLOAT32, 1, bad, None) == dws.ERR_INVALID_ARG
+        assert f(None, None, 0, dws.INT32, 0, bad, None) == dws.ERR_INVALID_ARG
+    for v in (dws.SINGLE_PASS, dws.REDUCE_THEN_SCAN, dws.CHAINED, dws.SCAN_THEN_PROPAGATE):
+        assert f(None, None, 0, dws.INT32, 0, v, None) == dws.OK
+        assert f(FAKE, FAKE + 4, 10, dws.INT32, 0, v, None) == dws.ERR_OVERLAP
+        assert f(FAKE + 2, FAKE + 4096, 10, dws.UINT32, 1, v, None) == dws.ERR_MISALIGNED
+        assert f(FAKE, FAKE + 4096, 10, 9, 1, v, None) == dws.ERR_INVALID_ARG
 
 
 def test_debug_and_selftest_validation(lib):
