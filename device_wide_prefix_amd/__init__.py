@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
-    "dws_run_length_encode", "dws_device_memory_info",
+    "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc",
 )
 
 
@@ -83,6 +83,8 @@ def load_library():
     lib.dws_scan_ex.restype = ci
     lib.dws_scan_opts.argtypes = [vp, vp, sz, ci, ci, ctypes.POINTER(DwsOptions), vp]
     lib.dws_scan_opts.restype = ci
+    lib.dws_scan_noalloc.argtypes = [vp, vp, sz, ci, ci, vp]
+    lib.dws_scan_noalloc.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -141,6 +143,10 @@ def scan_exclusive_ptr(d_in: int, d_out: int, n: int, dtype: int, stream: int = 
 def scan_ex_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool, variant: int,
                 stream: int = 0) -> int:
     return load_library().dws_scan_ex(d_in, d_out, n, dtype, int(bool(exclusive)), int(variant), stream)
+
+
+def scan_noalloc_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool, stream: int = 0) -> int:
+    return load_library().dws_scan_noalloc(d_in, d_out, n, dtype, int(bool(exclusive)), stream)
 
 
 def scan_opts_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,

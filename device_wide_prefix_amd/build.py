@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 SOURCES = ["dws_sp_u32.hip", "dws_sp_f32.hip", "dws_aux.hip", "dws_stp.hip", "dws_select.hip",
            "dws_op_minmax.hip", "dws_op_pairsum.hip", "dws_op_affine.hip", "dws_op_segsum.hip", "dws_rbk.hip",
-           "dws_single_pass_host.cpp", "dws_abi.cpp"]
+           "dws_static.hip", "dws_single_pass_host.cpp", "dws_abi.cpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

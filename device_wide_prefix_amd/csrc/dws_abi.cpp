@@ -659,6 +659,11 @@ dws_status dws_watchdog_trips(unsigned long long* trips)
                 ws->trips_seen = v;
             }
         }
+        // the fixed array of dws_scan_noalloc, once set up on this device
+        unsigned int v = 0;
+        e = static_check_trips(dev, &v);
+        if (e != hipSuccess) return from_hip(e);
+        total += v;
         *trips = total;
         return DWS_OK;
     } catch (...) {

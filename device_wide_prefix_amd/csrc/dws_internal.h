@@ -12,7 +12,8 @@
 namespace dws {
 
 // Look-back state a launch with more than one tile needs: descriptors, tile
-// counter, watchdog word and epoch word (a workspace).
+// counter, watchdog word and epoch word (a workspace, or the fixed device
+// array of dws_scan_noalloc).
 struct LookbackState {
     uint64_t* desc;
     uint64_t desc_slots;
@@ -37,6 +38,11 @@ dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool
                             const dws_options& o, unsigned long long* stamps, SinglePassPlan* plan);
 hipError_t launch_single_pass_plan(const SinglePassPlan& plan, const LookbackState* state, hipStream_t stream);
 
+// Watchdog count of the no-allocation entry point's array on `device` (0
+// before that device's first multi-tile call), read after the caller has
+// synchronised the device. When it has grown since the last check, the array's
+// look-back state is cleared (the count is kept). dws_static.hip.
+hipError_t static_check_trips(int device, unsigned int* trips);
 
 // Workspace control block layout (one 256-byte allocation per workspace):
 // the tile counter and the watchdog counter sit on separate cache lines.

@@ -210,6 +210,41 @@ dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
 dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                          int exclusive, const dws_options* opt, hipStream_t stream);
 
+/* Descriptor slots in the fixed device array of dws_scan_noalloc: one per
+ * tile, so n may be up to 2^33 elements when both pointers are 16-byte
+ * aligned (65,536-element tiles) and up to 2^31 otherwise (16,384). */
+#define DWS_NOALLOC_MAX_TILES 131072
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * scan as scan_inclusive (exclusive == 0) or scan_exclusive (exclusive != 0),
+ * with the same kernels, arguments, validation and results, but the call
+ * allocates nothing. The look-back state the scans otherwise keep in a
+ * per-stream workspace (a 256-byte control block and one 8-byte descriptor
+ * per tile) lives in a fixed array of the library in device memory, 256 B +
+ * DWS_NOALLOC_MAX_TILES x 8 B (1 MiB) per GPU, held until the process ends.
+ *
+ * Limit: a call whose tile count would exceed DWS_NOALLOC_MAX_TILES returns
+ * DWS_ERR_UNSUPPORTED before any HIP call (see DWS_NOALLOC_MAX_TILES for the
+ * element counts).
+ *
+ * Set-up: the first call on a device with more than one tile (n above 4,096
+ * elements) finds the array's address on that device and clears it with a
+ * kernel on `stream`. That first call must not be under graph capture: there
+ * it returns DWS_ERR_UNSUPPORTED without enqueuing anything. Later calls,
+ * captured or not, need nothing more.
+ *
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ * last call's contents. Calls that overlap in time on one GPU (on different
+ * streams, or from host threads with nothing ordering them) race on it and
+ * give wrong results; calls in order on one stream are safe. Asynchronous on
+ * `stream`, like scan_inclusive; look-back timeouts count in
+ * dws_watchdog_trips like those of the other calls.
+ */
+dws_status dws_scan_noalloc(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                            int exclusive, hipStream_t stream);
+
 /*
  * Stream compaction (select by flags), fused with the single-pass scan
  * (Merrill & Garland, section 4.4, in-place compaction; section A5): copies,
@@ -345,7 +380,7 @@ dws_status dws_release_workspaces(void);
 /*
  * Number of look-back waits on the current device that exceeded the safety
  * limit (about two seconds) since the library was loaded, over every
- * workspace. A correct run keeps it at 0.
+ * workspace and the array of dws_scan_noalloc. A correct run keeps it at 0.
  *
  * A trip means WRONG OUTPUT that no status reports: the calls are
  * asynchronous and have already returned DWS_OK when a wait times out. Rather
@@ -355,7 +390,7 @@ dws_status dws_release_workspaces(void);
  * tile on. Check this count after results that matter.
  *
  * Synchronous: it synchronises the current device first. When the count of a
- * workspace has grown since the last check, this call
+ * workspace (or of the fixed array) has grown since the last check, this call
  * also clears that look-back state, so that no descriptor left behind by the
  * timed-out call can reach a later one; call it after a trip before relying on
  * further results. The count itself is never reset.

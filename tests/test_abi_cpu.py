@@ -345,3 +345,23 @@ def test_reduce_by_key_and_rle_validation(lib):
     assert e(K, K + 3996, AG, n, C, None) == dws.ERR_OVERLAP
     assert e(K, UK, UK, n, C, None) == dws.ERR_OVERLAP
     assert e(K + 1, UK, AG, n, C, None) == dws.ERR_MISALIGNED
+
+
+def test_noalloc_validation_and_limit(lib):
+    """dws_scan_noalloc: the scans' argument checks, and the size limit of its
+    fixed array, all before any HIP call."""
+    f = lib.dws_scan_noalloc
+    assert f(None, None, 0, dws.INT32, 0, None) == dws.OK
+    assert f(None, FAKE, 10, dws.INT32, 1, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, 7, 0, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE + 2, FAKE + 4096, 10, dws.UINT32, 0, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, FAKE + 4, 10, dws.INT32, 0, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + (1 << 40), (1 << 35) + 1, dws.INT32, 0, None) == dws.ERR_UNSUPPORTED
+    # one descriptor per tile, DWS_NOALLOC_MAX_TILES of them: 65,536-element
+    # tiles with 16-byte aligned pointers, 16,384 otherwise
+    max_tiles = 131072
+    big = FAKE + (1 << 36)
+    assert dws.tile_elems(0, max_tiles * 65536, True) == 65536
+    assert f(FAKE, big, max_tiles * 65536 + 1, dws.FLOAT32, 1, None) == dws.ERR_UNSUPPORTED
+    assert dws.tile_elems(0, max_tiles * 16384, False) == 16384
+    assert f(FAKE + 4, big, max_tiles * 16384 + 1, dws.FLOAT32, 1, None) == dws.ERR_UNSUPPORTED
