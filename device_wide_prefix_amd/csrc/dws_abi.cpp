@@ -22,7 +22,7 @@ namespace {
 using namespace dws;
 
 constexpr size_t kElemBytes = 4;
-constexpr uint64_t kMinDescSlots = 1u << 16;
+constexpr uint64_t kMinDescSlots = (uint64_t)8192 * kDescStride;   // descriptors for 8,192 tiles
 constexpr unsigned kMaxDebugDelayTicks = 50000000u;  // 0.5 s of the 100 MHz clock
 constexpr uint64_t kMaxGridThreads = (1ull << 32) - 1ull;
 
@@ -262,7 +262,7 @@ dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
     p.stamps = stamps;
-    p.long_backoff = n >= kLongerBackoffMin ? 2u : (n >= kLongBackoffMin ? 1u : 0u);
+    p.backoff = scan_backoff(n);
     plan->cfg = cfg;
     plan->f32 = kind_of(dtype) == kKindF32;
     plan->exclusive = excl;
@@ -299,7 +299,7 @@ dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool 
     s = get_workspace(stream, &ws);
     if (s != DWS_OK) return s;
     std::lock_guard<std::mutex> lock(ws->mu);
-    s = ensure_desc(ws, plan.params.num_tiles);
+    s = ensure_desc(ws, (uint64_t)plan.params.num_tiles * kDescStride);
     if (s != DWS_OK) return s;
     s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
@@ -446,7 +446,7 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     const int words = op_kind_words(kind);
     const bool aligned = aligned16(in, out);
     const int shape = op_auto_shape(n, aligned);
-    const int tile_index = (shape == kOpShapeLarge && n >= kAutoDrawnMin) ? kTileDrawn : kTileDispatch;
+    const int tile_index = (shape == kOpShapeLarge && n >= kOpDrawnMin) ? kTileDrawn : kTileDispatch;
     // non-temporal loads with the drawn tile index (from 2^25 elements, the
     // large shape): each input word is read once. Measured 2 to 3% faster on
     // 128 and 256 MB inputs, 4.6 to 5.1% on 512 MB and 1 GiB.
@@ -459,13 +459,13 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     p.out = out;
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
-    p.long_backoff = n >= kLongBackoffMin ? 1u : 0u;
+    p.backoff = op_backoff(n);
     if (num_tiles == 1) return from_hip(launch_op_kind(kind, excl, shape, tile_index, false, p, stream));
     Workspace* ws = nullptr;
     dws_status s = get_workspace(stream, &ws);
     if (s != DWS_OK) return s;
     std::lock_guard<std::mutex> lock(ws->mu);
-    s = ensure_desc(ws, num_tiles * (uint64_t)words);
+    s = ensure_desc(ws, num_tiles * kDescStride);
     if (s != DWS_OK) return s;
     s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
@@ -570,16 +570,17 @@ dws_status dws_reserve(size_t n, hipStream_t stream)
         Workspace* ws = nullptr;
         dws_status s = get_workspace(stream, &ws);
         if (s != DWS_OK) return s;
-        // the most descriptor slots any scan of n elements uses: the smallest
-        // single-pass tile, or the generic kernels' tiles times their words
+        // the most tiles any scan, compaction or generic-operator scan of n
+        // elements uses (the smallest tile of each, 4,096 elements for all
+        // but the pair types), kDescStride descriptor words each
         const uint64_t m = std::max<uint64_t>(n, 1);
-        uint64_t slots = 0;
-        for (int i = 0; i < kNumShapes; ++i) slots = std::max(slots, ceil_div(m, (uint64_t)kShapes[i].elems()));
+        uint64_t tiles = 0;
+        for (int i = 0; i < kNumShapes; ++i) tiles = std::max(tiles, ceil_div(m, (uint64_t)kShapes[i].elems()));
         for (int w = 1; w <= 2; ++w)
             for (int shape = kOpShapeSmall; shape <= kOpShapeUnaligned; ++shape)
-                slots = std::max(slots, ceil_div(m, op_tile_elems(w, shape)) * (uint64_t)w);
+                tiles = std::max(tiles, ceil_div(m, op_tile_elems(w, shape)));
         std::lock_guard<std::mutex> lock(ws->mu);
-        s = ensure_desc(ws, slots);
+        s = ensure_desc(ws, tiles * kDescStride);
         if (s != DWS_OK) return s;
         const uint64_t stp = stp_scratch_elems(m);
         return stp == 0 ? DWS_OK : ensure_stp(ws, stp);
@@ -688,7 +689,7 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
         s = get_workspace(stream, &ws);
         if (s != DWS_OK) return s;
         std::lock_guard<std::mutex> lock(ws->mu);
-        s = ensure_desc(ws, num_tiles);
+        s = ensure_desc(ws, num_tiles * kDescStride);
         if (s != DWS_OK) return s;
         DebugArgs a{};
         s = before_lookback_launch(ws);
@@ -714,7 +715,9 @@ dws_status dws_scan_debug(const void* d_in, void* d_out, size_t n, dws_dtype dty
             hipError_t e = hipStreamSynchronize(stream);
             if (e != hipSuccess) return from_hip(e);
             if (num_tiles > 1) {
-                e = hipMemcpy(h_desc, ws->desc, num_tiles * sizeof(uint64_t), hipMemcpyDeviceToHost);
+                // every kDescStride-th word of the array: the tiles' descriptors
+                e = hipMemcpy2D(h_desc, sizeof(uint64_t), ws->desc, kDescStride * sizeof(uint64_t),
+                                sizeof(uint64_t), num_tiles, hipMemcpyDeviceToHost);
                 if (e != hipSuccess) return from_hip(e);
             } else {
                 h_desc[0] = 0;   // a single tile publishes nothing
@@ -801,7 +804,7 @@ dws_status select_entry(const void* d_in, const void* d_flags, void* d_out, size
     dws_status s = get_workspace(stream, &ws);
     if (s != DWS_OK) return s;
     std::lock_guard<std::mutex> lock(ws->mu);
-    s = ensure_desc(ws, tiles);
+    s = ensure_desc(ws, tiles * kDescStride);
     if (s != DWS_OK) return s;
     s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;
@@ -865,7 +868,7 @@ dws_status rbk_entry(const void* keys, const void* vals, void* ukeys, void* aggs
     dws_status s = get_workspace(stream, &ws);
     if (s != DWS_OK) return s;
     std::lock_guard<std::mutex> lock(ws->mu);
-    s = ensure_desc(ws, 2 * tiles);
+    s = ensure_desc(ws, tiles * kDescStride);
     if (s != DWS_OK) return s;
     s = before_lookback_launch(ws);
     if (s != DWS_OK) return s;

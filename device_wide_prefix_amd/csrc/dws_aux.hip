@@ -214,17 +214,17 @@ __global__ void __launch_bounds__(64) k_debug(DebugParams p)
     T prefix = T(0);
     if (multi) {
         if (tile == 0u) {
-            if (lane == 0) desc_store<kOrderRelaxed>(p.desc, desc_pack(epoch, kStatusP, Elem<T>::bits(agg)));
+            if (lane == 0) desc_store<kOrderRelaxed>(desc_at(p.desc, 0u), desc_pack(epoch, kStatusP, Elem<T>::bits(agg)));
         } else {
             if constexpr (MODE == kModeDecoupled) {
                 if (lane == 0)
-                    desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
+                    desc_store<kOrderRelaxed>(desc_at(p.desc, tile), desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
                 prefix = lookback_decoupled<T, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch, p.watchdog);
             } else {
                 prefix = lookback_chained<T, kOrderRelaxed>(p.desc, tile, epoch, p.watchdog);
             }
             if (lane == 0) {
-                desc_store<kOrderRelaxed>(p.desc + tile,
+                desc_store<kOrderRelaxed>(desc_at(p.desc, tile),
                                           desc_pack(epoch, kStatusP, Elem<T>::bits(prefix + agg)));
                 if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
             }

@@ -247,6 +247,29 @@ __device__ __forceinline__ uint32_t desc_status(uint64_t d, uint32_t epoch)
     return ((hi >> kDescStatusBits) == epoch) ? (hi & kDescStatusMask) : kStatusX;
 }
 
+// Address of tile t's descriptor (its first word) in the descriptor array.
+__device__ __forceinline__ uint64_t* desc_at(uint64_t* desc, uint64_t t) { return desc + t * kDescStride; }
+__device__ __forceinline__ const uint64_t* desc_at(const uint64_t* desc, uint64_t t)
+{
+    return desc + t * kDescStride;
+}
+
+// Pause before re-polling a blocked look-back window. The first re-poll comes
+// at once (`first`); after that, level kPauseShort keeps a short pause and the
+// other levels sleep 64, 127 or 190 x 64 clocks: fewer polls while many tiles
+// wait leave the memory system to the loads of the tiles being waited on.
+__device__ __forceinline__ void lookback_pause(uint32_t level, bool first)
+{
+    if (first || level == kPauseShort) {
+        __builtin_amdgcn_s_sleep(1);
+    } else if (level == kPause64) {
+        __builtin_amdgcn_s_sleep(64);
+    } else {
+        __builtin_amdgcn_s_sleep(127);
+        if (level == kPause190) __builtin_amdgcn_s_sleep(63);
+    }
+}
+
 template <int ORDER>
 __device__ __forceinline__ uint64_t desc_load(const uint64_t* p)
 {
@@ -275,6 +298,14 @@ __device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memre
 __device__ __forceinline__ uint32_t load_epoch(const unsigned int* word)
 {
     return uniform(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// The same read, left in a VGPR: take uniform() of it where it is used, so
+// the read stays in flight with whatever is issued after it (the tile draw,
+// or the tile's own loads) instead of costing a round trip of its own first.
+__device__ __forceinline__ uint32_t load_epoch_async(const unsigned int* word)
+{
+    return __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Called once per launch, by the owner of the last tile after its P: the next
@@ -316,15 +347,12 @@ __device__ __forceinline__ uint32_t draw_tile(unsigned long long* counter, uint3
 // *watchdog and returns the incomplete prefix instead of hanging. Call with the
 // whole wave active.
 //
-// Why K > 1: a tile publishes P only after its own look-back, so if one poll
-// of latency L covers W predecessors, P can advance by at most W tiles per L.
-// Tiles arriving faster than W / L fall further and further behind the last
-// P and need ever more polls; W = 64 K keeps W / L above the tile rate.
+// The width: a tile publishes P only after its own look-back, so if one poll
+// of latency L covers W = 64 K predecessors, P can advance by at most W tiles
+// per L; W must keep W / L above the rate at which tiles arrive.
 //
-// Back-off: a blocked window is polled again after a short sleep. With
-// backoff 1 (uniform) every poll after that first re-poll waits 127 x 64
-// clocks, with backoff 2 190 x 64; fewer polls while many tiles wait leave the
-// memory system to the loads of the tiles being waited on.
+// Back-off: a blocked window is polled again at once, then after the pause
+// of level `backoff` (lookback_pause) before every further poll.
 template <class T, int ORDER, int K>
 __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t epoch,
                                unsigned int* watchdog, uint32_t backoff = 0u)
@@ -340,7 +368,7 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int64_t idx = hi - (int64_t)(j * 64 + lane);
-            d[j] = (idx >= 0) ? desc_load<ORDER>(desc + idx) : desc_pack(epoch, kStatusP, 0u);
+            d[j] = (idx >= 0) ? desc_load<ORDER>(desc_at(desc, (uint64_t)idx)) : desc_pack(epoch, kStatusP, 0u);
         }
         uint64_t has_p[K], has_x[K];
 #pragma unroll
@@ -380,12 +408,7 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
             if (lane == 0) atomicAdd(watchdog, 1u);
             return prefix;
         }
-        if (backoff != 0u && repolled) {
-            __builtin_amdgcn_s_sleep(127);
-            if (backoff > 1u) __builtin_amdgcn_s_sleep(63);
-        } else {
-            __builtin_amdgcn_s_sleep(1);
-        }
+        lookback_pause(backoff, !repolled);
         repolled = true;
     }
 }
@@ -400,7 +423,7 @@ __device__ T lookback_chained(const uint64_t* desc, uint32_t tile, uint32_t epoc
     if (lane_id() == 0) {
         const uint64_t t0 = realtime();
         for (;;) {
-            const uint64_t d = desc_load<ORDER>(desc + (tile - 1u));
+            const uint64_t d = desc_load<ORDER>(desc_at(desc, tile - 1u));
             if (desc_status(d, epoch) == kStatusP) {
                 bits = (uint32_t)d;
                 break;

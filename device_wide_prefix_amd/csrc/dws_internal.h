@@ -108,6 +108,8 @@ constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles
 constexpr uint64_t kSelectHugeMin = (uint64_t)1 << 27;    // 40960-element tiles from here
 constexpr uint64_t kSelectDrawnMin = (uint64_t)1 << 25;   // drawn tile index from here (below: workgroup index)
 constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
+// pause level between blocked look-back polls of the compaction kernels
+constexpr uint32_t select_backoff(uint64_t n) { return n >= ((uint64_t)1 << 25) ? kPause64 : kPauseShort; }
 uint32_t select_tile_elems(uint64_t n, bool aligned);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
@@ -146,6 +148,8 @@ struct RbkArgs {
 };
 constexpr uint64_t kRbkLargeMin = (uint64_t)1 << 22;   // 16384 (32768 for run lengths) from here
 constexpr uint64_t kRbkNtMin = (uint64_t)1 << 25;      // non-temporal key and value loads from here
+// pause level between blocked look-back polls of the run kernels
+constexpr uint32_t rbk_backoff(uint64_t n) { return n >= ((uint64_t)1 << 25) ? kPause64 : kPauseShort; }
 uint32_t rbk_tile_elems(uint64_t n, bool aligned, int mode);
 hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream);
 
@@ -160,7 +164,7 @@ struct OpScanParams {
     unsigned int* watchdog;
     uint32_t num_tiles;
     unsigned int* epoch;     // the workspace epoch word
-    uint32_t long_backoff;   // 1: long back-off between blocked look-back polls
+    uint32_t backoff;        // pause level between blocked look-back polls (kPause*)
 };
 enum OpKind : int {
     kOpMaxI32, kOpMaxU32, kOpMinI32, kOpMinU32,          // one word
@@ -175,6 +179,9 @@ constexpr int kOpShapeMedium = 1;
 constexpr int kOpShapeLarge = 2;
 constexpr int kOpShapeUnaligned = 3;
 constexpr uint64_t kOpMediumMin = (uint64_t)1 << 20;
+constexpr uint64_t kOpDrawnMin = (uint64_t)1 << 25;    // drawn tile index (large shape) from here
+// pause level between blocked look-back polls of the generic-operator kernels
+constexpr uint32_t op_backoff(uint64_t n) { return n >= ((uint64_t)1 << 25) ? kPause64 : kPauseShort; }
 constexpr uint64_t kOpLargeMin = (uint64_t)1 << 24;
 constexpr int op_auto_shape(uint64_t n, bool aligned)
 {

@@ -283,7 +283,8 @@ __device__ __forceinline__ typename Op::V scan_segment_op(typename Op::V (&x)[CH
 }
 
 // ---------------------------------------------------------------------------
-// Descriptors of W words per tile (words tile W .. tile W + W - 1).
+// Descriptors of W words per tile (words desc_at(tile) .. + W - 1; W is at
+// most 2, within the tile's kDescStride words).
 // ---------------------------------------------------------------------------
 template <int W>
 __device__ __forceinline__ void desc_store_val(uint64_t* desc, uint32_t tile, uint32_t epoch, uint32_t status,
@@ -291,24 +292,23 @@ __device__ __forceinline__ void desc_store_val(uint64_t* desc, uint32_t tile, ui
 {
 #pragma unroll
     for (int k = 0; k < W; ++k)
-        desc_store<kOrderRelaxed>(desc + (uint64_t)tile * W + k, desc_pack(epoch, status, v.w[k]));
+        desc_store<kOrderRelaxed>(desc_at(desc, tile) + k, desc_pack(epoch, status, v.w[k]));
 }
 
-// Look-back slots per lane of the generic-operator kernels: four, 256
-// predecessors per poll. On 1 GiB inputs one or two slots were no faster
-// (up to 1.3% slower for the pair operators).
-constexpr int kOpLookbackSlots = 4;
+// Look-back slots per lane of the generic-operator kernels: one, 64
+// predecessors per poll, as for the + scan with spread descriptors.
+constexpr int kOpLookbackSlots = 1;
 
 // Decoupled look-back under Op (section 4.4, parallelized look-back, K slots
 // per lane as in the + kernel): the window's needed descriptors (back to and
 // including the nearest P) are combined in tile order, earliest first, and the
 // window goes in front of what nearer windows gave. Returns the exclusive
 // prefix of `tile` (uniform); a wait beyond kWatchdogTicks counts a trip and
-// returns what it has. Back-off as in the + kernel's look-back: with
-// long_backoff, every poll after the first re-poll waits 127 x 64 clocks.
+// returns what it has. Back-off as in the + kernel's look-back: the pause of
+// level `backoff` (lookback_pause) before every poll after the first re-poll.
 template <class Op, int K>
 __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint32_t epoch, unsigned int* watchdog,
-                                      bool long_backoff = false)
+                                      uint32_t backoff = kPauseShort)
 {
     using V = typename Op::V;
     constexpr int W = Op::kWords;
@@ -329,7 +329,7 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
             if (idx >= 0) {
                 uint64_t wd[W];
 #pragma unroll
-                for (int k = 0; k < W; ++k) wd[k] = desc_load<kOrderRelaxed>(desc + (uint64_t)idx * W + k);
+                for (int k = 0; k < W; ++k) wd[k] = desc_load<kOrderRelaxed>(desc_at(desc, (uint64_t)idx) + k);
                 st = desc_status(wd[0], epoch);
 #pragma unroll
                 for (int k = 1; k < W; ++k)
@@ -372,8 +372,7 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
             if (lane == 0) atomicAdd(watchdog, 1u);
             return prefix;
         }
-        if (long_backoff && repolled) __builtin_amdgcn_s_sleep(127);
-        else __builtin_amdgcn_s_sleep(1);
+        lookback_pause(backoff, !repolled);
         repolled = true;
     }
 }
@@ -393,23 +392,30 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     constexpr uint32_t SEG = 64u * E * CHUNKS;
     constexpr uint32_t TILE = WAVES * SEG;
     constexpr uint32_t ESIZE = 4u * W;
-    __shared__ uint32_t s_draw;
+    __shared__ uint32_t s_draw, s_epoch;
     __shared__ V s_wave[WAVES];
     __shared__ V s_prefix;
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
+    // the descriptor epoch is read with the draw, or after the tile loads,
+    // so that it never costs a round trip of its own (needed only to publish)
+    uint32_t epoch_v = 0u;
 
     uint32_t tile = 0u;
     if (multi) {
         if constexpr (TILE_INDEX == kTileDispatch) {
             tile = blockIdx.x;
         } else {
-            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            if (threadIdx.x == 0) {
+                const uint32_t e = load_epoch_async(p.epoch);
+                s_draw = draw_tile(p.counter, p.num_tiles);
+                s_epoch = e;
+            }
             __syncthreads();
             tile = uniform(s_draw);
+            epoch_v = s_epoch;
             if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
                 if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
                 return;
@@ -421,6 +427,8 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     const uint32_t vb = valid_bytes_sized(seg_first, SEG, p.n, ESIZE);
     uint32_t raw[CHUNKS][LOADW];
     load_words<LOADW, CHUNKS, NT>(make_rsrc(static_cast<const char*>(p.in) + seg_first * ESIZE, vb), lane, raw);
+    if constexpr (TILE_INDEX == kTileDispatch)
+        if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
 
     V x[CHUNKS][E];
 #pragma unroll
@@ -450,11 +458,12 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     if (wave == 0) {
         V prefix = Op::identity();
         if (multi) {
+            const uint32_t epoch = uniform(epoch_v);
             if (tile == 0u) {
                 if (lane == 0) desc_store_val<W>(p.desc, 0u, epoch, kStatusP, agg);
             } else {
                 if (lane == 0) desc_store_val<W>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, kOpLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.long_backoff != 0u);
+                prefix = lookback_op<Op, kOpLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.backoff);
                 if (lane == 0) {
                     desc_store_val<W>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);

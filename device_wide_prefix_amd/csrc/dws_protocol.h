@@ -20,6 +20,19 @@ constexpr uint32_t kDescStatusBits = 2u;
 constexpr uint32_t kDescStatusMask = 3u;
 constexpr uint32_t kEpochMax = (1u << 30) - 1u;  // epochs run 1 .. kEpochMax
 
+// Descriptor spacing: the descriptor of tile t (the first of its words, for
+// the two-word descriptors of the pair operators) is word t * kDescStride of
+// the descriptor array, so consecutive tiles' descriptors sit 64 bytes apart.
+// Packed 8 bytes apart, the few cache lines of the most recent tiles' words
+// take every look-back poll and every publication on the GPU at once; spread
+// out, the same traffic goes to many lines. Measured on MI355X (+ scan, fp32,
+// exclusive in place, one look-back slot): 342 us at 2^28 against 359-362 us
+// packed (the best packed schedule), 5-10% faster at 2^20 to 2^23, 2-3% at
+// 2^24, 4-6% at 2^25 to 2^27 and 3% at 2^30. 128- and 256-byte spacing measured
+// the same as 64; 4 KiB apart (a poll then touches 64 distinct pages) was
+// slower.
+constexpr uint32_t kDescStride = 8;
+
 // Tile counter word: draws made in the current call (the last draw of a call
 // puts it back to 0).
 constexpr uint64_t kCounterInit = 0ull;
@@ -75,45 +88,42 @@ constexpr int kNumShapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
 // Automatic shape and tile index source, from a sweep of every shape with
 // both sources at n = 2^16 .. 2^28 on MI355X (fp32, exclusive, in place,
 // caches flushed): the best tile grows with n as long as every CU still gets
-// tiles. Below 2^25 elements (at most a few hundred tiles) the workgroup
-// index is the better tile index: no atomic on the critical path. From 2^25
-// the drawn index wins by 2-11%: many workgroups run one after another on
-// each CU, and a drawn index follows the order in which they really start,
-// so a tile rarely waits on a predecessor that started after it.
+// tiles. Below 2^27 elements (at most 2,048 tiles) the workgroup index is the
+// better tile index: no atomic on the critical path (with spread descriptors:
+// 1.5-2% faster than drawn at 2^25, 2-3% at 2^26). From 2^27 the drawn index
+// wins (3% at 2^27, 2-11% at 2^28 and up): many workgroups run one after
+// another on each CU, and a drawn index follows the order in which they
+// really start, so a tile rarely waits on a predecessor that started after it.
 constexpr uint64_t kAutoHugeMin = (uint64_t)1 << 24;    // 65536-element tiles
 constexpr uint64_t kAutoLargeMin = (uint64_t)1 << 23;   // 32768
 constexpr uint64_t kAutoMediumMin = (uint64_t)1 << 20;  // 16384 (512 threads)
-constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 25;   // drawn tile index from here
-// From here a look-back that is still blocked after its first re-poll backs
-// off for 127 x 64 clocks before each further poll (the first re-poll still
-// comes at once); every look-back kernel (scan, select, generic operators,
-// run kernels) takes it from the element count. Fewer descriptor polls while
-// many tiles wait measured on MI355X: the + scan 2 to 3.5% faster at 2^26 to
-// 2^28 and no better at 2^25; the run kernels 4 to 8.5% faster with all keys
-// distinct at 2^26 and 2^28, between 0.6% faster and 3.5% slower at mean run
-// 16 and 2^26, 1 to 4% faster at 2^28, but 4 to 5.5% slower at 2^25 and mean
-// run 16.
-constexpr uint64_t kLongBackoffMin = (uint64_t)1 << 26;
-// From here the + scan's blocked polls wait 190 x 64 clocks instead of 127 x
-// 64. Measured with non-temporal loads, six rounds each: 1.3 to 1.5% faster
-// at 2^28 to 2^30 in place; at 2^26 out of place 1.4% slower, at 2^27 equal.
-// A shorter sleep (24, 48 or 80 units) was slower at every size, 381 units
-// 2 to 11% slower. Compaction on 2^30 - 12345 flags: 1.5% faster with it.
-constexpr uint64_t kLongerBackoffMin = (uint64_t)1 << 28;
+constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 27;   // drawn tile index from here
+// Back-off levels of a look-back that is still blocked after its first,
+// immediate re-poll (lookback_pause): 0 a short pause (s_sleep 1), then 64,
+// 127 or 190 units of 64 clocks before every further poll.
+constexpr uint32_t kPauseShort = 0u;
+constexpr uint32_t kPause64 = 1u;
+constexpr uint32_t kPause127 = 2u;
+constexpr uint32_t kPause190 = 3u;
+// The + scan backs off from here: 64 units, the best of 16 / 32 / 64 / 127 at
+// 2^25 to 2^30 with spread descriptors (127 equal from 2^27). Below 2^25 (the
+// workgroup-index sizes) any sleep was slower than the short pause.
+constexpr uint64_t kScanBackoffMin = (uint64_t)1 << 25;
+
+constexpr uint32_t scan_backoff(uint64_t n) { return n >= kScanBackoffMin ? kPause64 : kPauseShort; }
 // From here the automatic choice loads the input with non-temporal loads (each
 // element is read once); stores stay ordinary. Measured on MI355X with the
 // 65,536-element drawn kernel, alternating builds on two MI355X GPUs: 3.4 to
-// 3.9% faster at 2^28 elements, 3.0 to 3.2% at 2^29, 3.3% at 2^30; at 2^27
-// no better, at 2^25 and 2^26 3.5% slower. Non-temporal stores, alone or with
-// the loads, were slower at every size measured. The generic operators,
-// select, partition and the run kernels measured faster from 2^25 elements and
-// load non-temporally from there (with their drawn or large-tile kernels).
-constexpr uint64_t kNtLoadMin = (uint64_t)1 << 28;
-// Out of place (d_out != d_in) the + scan's non-temporal loads pay from here:
-// 3.6% faster at 2^26, 2.9% at 2^27, 2.0% at 2^28; at 2^25 no better. In
-// place they were slower below 2^27, where an ordinary load can leave the
-// line cached for the store to the same address.
-constexpr uint64_t kNtLoadOutOfPlaceMin = (uint64_t)1 << 26;
+// 3.9% faster at 2^28 elements, 3.0 to 3.2% at 2^29, 3.3% at 2^30; with spread
+// descriptors 0.7% faster at 2^27 in place and 5% out of place. Below 2^27 the
+// workgroup-index kernel (built without them) is faster still. Non-temporal
+// stores, alone or with the loads, were slower at every size measured. The
+// generic operators, select, partition and the run kernels measured faster
+// from 2^25 elements and load non-temporally from there (with their drawn or
+// large-tile kernels).
+constexpr uint64_t kNtLoadMin = (uint64_t)1 << 27;
+// The same threshold when the output is another buffer.
+constexpr uint64_t kNtLoadOutOfPlaceMin = (uint64_t)1 << 27;
 
 constexpr int auto_shape(uint64_t n)
 {
@@ -129,11 +139,12 @@ constexpr TileShape scalar_shape(const TileShape& s)
     return TileShape{s.threads, 1, s.vec * s.chunks < 16 ? s.vec * s.chunks : 16};
 }
 
-// Look-back width: descriptors per lane per poll (64 * K per poll). P can
-// advance by at most 64 K tiles per poll latency (~0.8 us measured); with
-// fewer slots the walk back to the last P grows (measured: K = 4 beats K = 1
-// by 6% at 32K-element tiles and by 1% at 64K).
-constexpr int kLookbackSlots = 4;
+// Look-back width: descriptors per lane per poll (64 * K per poll). With
+// spread descriptors one slot is enough: P advances by up to 64 tiles per poll
+// latency, and each poll costs half the lines of two slots. Measured at 2^25 to
+// 2^30 elements: K = 1 equal to or up to 2% faster than K = 2, 1-5% faster than
+// K = 4. (With packed descriptors K = 4 had been the best.)
+constexpr int kLookbackSlots = 1;
 
 // Built single-pass kernel configurations. Shape index into kShapes; vec 1
 // means the scalar-load version of that shape.

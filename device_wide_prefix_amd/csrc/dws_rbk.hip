@@ -48,7 +48,7 @@ struct RbkParams {
     unsigned long long* num_runs;
     uint32_t num_tiles;
     unsigned int* epoch;
-    uint32_t long_backoff;    // 1: long back-off between blocked look-back polls
+    uint32_t backoff;         // pause level between blocked look-back polls (kPause*)
 };
 
 constexpr uint32_t kRbkDropped = 0x80000000u;   // past any tile's range: dropped
@@ -121,7 +121,6 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
     const uint32_t tile = multi ? (uint32_t)blockIdx.x : 0u;
 
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
@@ -132,6 +131,8 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     uint32_t v[CHUNKS][VEC];   // values, then S before each element (integer sums) or the fp32 sum
                                // since the last head up to the element (fp32 sums)
     if constexpr (MODE != 2) load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.vals + seg_first, vb), lane, v);
+    // the descriptor epoch, read after the tile loads (needed only to publish)
+    const uint32_t epoch_v = (multi && wave == 0) ? load_epoch_async(p.epoch) : 0u;
     const bool has_prev = seg_first > 0u && seg_first < p.n;
     const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
         make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
@@ -258,11 +259,12 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     if (wave == 0) {
         V prefix = Op::identity();
         if (multi) {
+            const uint32_t epoch = uniform(epoch_v);
             if (tile == 0u) {
                 if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
             } else {
                 if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, SLOTS>(p.desc, tile, epoch, p.watchdog, p.long_backoff != 0u);
+                prefix = lookback_op<Op, SLOTS>(p.desc, tile, epoch, p.watchdog, p.backoff);
                 if (lane == 0) {
                     desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
@@ -392,7 +394,7 @@ hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
                 a.n,                                  a.desc,
                 a.watchdog,                           a.num_runs,
                 a.num_tiles,                          a.epoch,
-                a.n >= kLongBackoffMin ? 1u : 0u};
+                rbk_backoff(a.n)};
     if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, p, stream);
     if (a.n >= kRbkLargeMin) {
         // sums: 16,384-element tiles (512 x 4 x 8); run lengths hold no values

@@ -57,7 +57,7 @@ struct SelectParams {
     unsigned long long* count;
     uint32_t num_tiles;
     unsigned int* epoch;
-    uint32_t long_backoff;   // 1: long back-off between blocked look-back polls
+    uint32_t backoff;        // pause level between blocked look-back polls (kPause*)
 };
 
 // Byte offset far past any tile's range (at most 4 * 40960 bytes): the
@@ -73,23 +73,30 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
-    __shared__ uint32_t s_draw;
+    __shared__ uint32_t s_draw, s_epoch;
     __shared__ uint32_t s_wave[W];
     __shared__ uint32_t s_prefix;
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
+    // the descriptor epoch is read with the draw, or after the tile loads,
+    // so that it never costs a round trip of its own (needed only to publish)
+    uint32_t epoch_v = 0u;
 
     uint32_t tile = 0u;
     if (multi) {
         if constexpr (TILE_INDEX == kTileDispatch) {
             tile = blockIdx.x;
         } else {
-            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            if (threadIdx.x == 0) {
+                const uint32_t e = load_epoch_async(p.epoch);
+                s_draw = draw_tile(p.counter, p.num_tiles);
+                s_epoch = e;
+            }
             __syncthreads();
             tile = uniform(s_draw);
+            epoch_v = s_epoch;
             if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
                 if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
                 return;
@@ -105,6 +112,8 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     // are in flight
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    if constexpr (TILE_INDEX == kTileDispatch)
+        if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
 
     // selection bits, then ranks (exclusive scan of the 0/1 flags) in place
     Mask selected = 0u;
@@ -139,14 +148,15 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     if (wave == 0) {
         uint32_t prefix = 0u;
         if (multi) {
+            const uint32_t epoch = uniform(epoch_v);
             if (tile == 0u) {
-                if (lane == 0) desc_store<kOrderRelaxed>(p.desc, desc_pack(epoch, kStatusP, count));
+                if (lane == 0) desc_store<kOrderRelaxed>(desc_at(p.desc, 0u), desc_pack(epoch, kStatusP, count));
             } else {
-                if (lane == 0) desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusA, count));
+                if (lane == 0) desc_store<kOrderRelaxed>(desc_at(p.desc, tile), desc_pack(epoch, kStatusA, count));
                 prefix = lookback_decoupled<uint32_t, kOrderRelaxed, kLookbackSlots>(p.desc, tile, epoch,
-                                                                                     p.watchdog, p.long_backoff);
+                                                                                     p.watchdog, p.backoff);
                 if (lane == 0) {
-                    desc_store<kOrderRelaxed>(p.desc + tile, desc_pack(epoch, kStatusP, prefix + count));
+                    desc_store<kOrderRelaxed>(desc_at(p.desc, tile), desc_pack(epoch, kStatusP, prefix + count));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
                 }
             }
@@ -239,7 +249,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     SelectParams p{static_cast<const uint32_t*>(a.in), static_cast<const uint32_t*>(a.flags),
                    static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
                    a.epoch,
-                   a.n >= kLongerBackoffMin ? 2u : (a.n >= kLongBackoffMin ? 1u : 0u)};
+                   select_backoff(a.n)};
     void* args[] = {&p};
     // the workgroup index as the tile index below kSelectDrawnMin, as for the
     // scan: no atomic on the critical path while there are few tiles per CU;

@@ -19,7 +19,7 @@ struct SinglePassParams {
     unsigned long long* stamps;   // kStampsPerTile per tile (instrumented kernels only)
     uint32_t num_tiles;
     unsigned int* epoch;          // the workspace's epoch word (unused when num_tiles == 1)
-    uint32_t long_backoff;        // 0: short re-polls; 1, 2: longer back-off between blocked polls
+    uint32_t backoff;             // pause level between blocked look-back polls (kPause*)
 };
 
 // Launch built configuration `cfg` (index into kCfgs) for element type T

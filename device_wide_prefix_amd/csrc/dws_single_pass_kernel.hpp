@@ -39,23 +39,32 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
-    __shared__ uint32_t s_draw;
+    __shared__ uint32_t s_draw, s_epoch;
     __shared__ T s_wave[W];
     __shared__ T s_prefix;
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    const uint32_t epoch = multi ? load_epoch(p.epoch) : 0u;
+    // the launch's descriptor epoch: read with the draw (drawn index), or in
+    // wave 0 after the tile loads (workgroup index); it is only needed to
+    // publish, and any time before that is early enough
+    uint32_t epoch_v = 0u;
 
     uint32_t tile = 0u;
     if (multi) {
         if constexpr (TILE_INDEX == kTileDispatch) {
             tile = blockIdx.x;
         } else {
-            if (threadIdx.x == 0) s_draw = draw_tile(p.counter, p.num_tiles);
+            if (threadIdx.x == 0) {
+                // both reads in flight together: one round trip, not two
+                const uint32_t e = load_epoch_async(p.epoch);
+                s_draw = draw_tile(p.counter, p.num_tiles);
+                s_epoch = e;
+            }
             __syncthreads();
             tile = uniform(s_draw);
+            epoch_v = s_epoch;
             // a counter that was not put back to 0 would hand out indices past
             // the grid; never touch memory with them (counts as a watchdog trip)
             if (tile >= p.num_tiles) {
@@ -71,6 +80,8 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
 
     T x[CHUNKS][VEC];
     load_segment<T, VEC, CHUNKS, NT>(make_rsrc(static_cast<const T*>(p.in) + seg_first, seg_valid), lane, x);
+    if constexpr (TILE_INDEX == kTileDispatch)
+        if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
 
     const T seg_total = scan_segment_local<T, EXCL, VEC, CHUNKS>(x);
     pin_in_registers<T, VEC, CHUNKS>(x);
@@ -88,19 +99,20 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     if (wave == 0) {
         T prefix = T(0);
         if (multi) {
+            const uint32_t epoch = uniform(epoch_v);
             if (tile == 0u) {
-                if (lane == 0) desc_store<ORDER>(p.desc, desc_pack(epoch, kStatusP, Elem<T>::bits(agg)));
+                if (lane == 0) desc_store<ORDER>(desc_at(p.desc, 0u), desc_pack(epoch, kStatusP, Elem<T>::bits(agg)));
             } else {
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)
-                        desc_store<ORDER>(p.desc + tile, desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
+                        desc_store<ORDER>(desc_at(p.desc, tile), desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
                     prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog,
-                                                                          p.long_backoff);
+                                                                          p.backoff);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
                 if (lane == 0) {
-                    desc_store<ORDER>(p.desc + tile,
+                    desc_store<ORDER>(desc_at(p.desc, tile),
                                       desc_pack(epoch, kStatusP, Elem<T>::bits(prefix + agg)));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
                 }

@@ -30,9 +30,11 @@ namespace {
 using namespace dws;
 
 constexpr uint64_t kCtlWords = kCtlBytes / sizeof(uint64_t);
-constexpr uint64_t kScratchWords = kCtlWords + (uint64_t)DWS_NOALLOC_MAX_TILES;
+constexpr uint64_t kDescWords = (uint64_t)DWS_NOALLOC_MAX_TILES * kDescStride;
+constexpr uint64_t kScratchWords = kCtlWords + kDescWords;
 
-// Control block (kCtlBytes), then DWS_NOALLOC_MAX_TILES descriptors.
+// Control block (kCtlBytes), then the descriptors of DWS_NOALLOC_MAX_TILES
+// tiles, kDescStride words each.
 static __device__ __align__(256) uint64_t scratch[kScratchWords];
 
 struct DeviceScratch {
@@ -48,7 +50,7 @@ LookbackState state_of(const DeviceScratch& d)
 {
     LookbackState s{};
     s.desc = reinterpret_cast<uint64_t*>(d.base + kCtlBytes);
-    s.desc_slots = DWS_NOALLOC_MAX_TILES;
+    s.desc_slots = kDescWords;
     s.counter = reinterpret_cast<unsigned long long*>(d.base + kCtlCounterOffset);
     s.watchdog = reinterpret_cast<unsigned int*>(d.base + kCtlWatchdogOffset);
     s.epoch = reinterpret_cast<unsigned int*>(d.base + kCtlEpochOffset);

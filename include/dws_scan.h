@@ -148,7 +148,7 @@ typedef enum dws_memory_order {
 
 /* Where a tile's index comes from in the single-pass and chained kernels. */
 typedef enum dws_tile_index {
-    /* the library's choice: DWS_TILE_DISPATCH below 2^25 elements for the
+    /* the library's choice: DWS_TILE_DISPATCH below 2^27 elements for the
      * relaxed single pass without non-temporal access, else DWS_TILE_DRAWN */
     DWS_TILE_AUTO = 0,
     /* one atomic add on a device-wide counter per workgroup, in the order the
@@ -210,10 +210,10 @@ dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
 dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                          int exclusive, const dws_options* opt, hipStream_t stream);
 
-/* Descriptor slots in the fixed device array of dws_scan_noalloc: one per
- * tile, so n may be up to 2^33 elements when both pointers are 16-byte
- * aligned (65,536-element tiles) and up to 2^31 otherwise (16,384). */
-#define DWS_NOALLOC_MAX_TILES 131072
+/* Tiles the fixed device array of dws_scan_noalloc has descriptors for (64
+ * bytes each), so n may be up to 2^32 elements when both pointers are 16-byte
+ * aligned (65,536-element tiles) and up to 2^30 otherwise (16,384). */
+#define DWS_NOALLOC_MAX_TILES 65536
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph
@@ -221,9 +221,10 @@ dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtyp
  * scan as scan_inclusive (exclusive == 0) or scan_exclusive (exclusive != 0),
  * with the same kernels, arguments, validation and results, but the call
  * allocates nothing. The look-back state the scans otherwise keep in a
- * per-stream workspace (a 256-byte control block and one 8-byte descriptor
- * per tile) lives in a fixed array of the library in device memory, 256 B +
- * DWS_NOALLOC_MAX_TILES x 8 B (1 MiB) per GPU, held until the process ends.
+ * per-stream workspace (a 256-byte control block and one 64-byte descriptor
+ * slot per tile) lives in a fixed array of the library in device memory,
+ * 256 B + DWS_NOALLOC_MAX_TILES x 64 B (4 MiB) per GPU, held until the
+ * process ends.
  *
  * Limit: a call whose tile count would exceed DWS_NOALLOC_MAX_TILES returns
  * DWS_ERR_UNSUPPORTED before any HIP call (see DWS_NOALLOC_MAX_TILES for the

@@ -359,7 +359,7 @@ def test_noalloc_validation_and_limit(lib):
     assert f(FAKE, FAKE + (1 << 40), (1 << 35) + 1, dws.INT32, 0, None) == dws.ERR_UNSUPPORTED
     # one descriptor per tile, DWS_NOALLOC_MAX_TILES of them: 65,536-element
     # tiles with 16-byte aligned pointers, 16,384 otherwise
-    max_tiles = 131072
+    max_tiles = 65536
     big = FAKE + (1 << 36)
     assert dws.tile_elems(0, max_tiles * 65536, True) == 65536
     assert f(FAKE, big, max_tiles * 65536 + 1, dws.FLOAT32, 1, None) == dws.ERR_UNSUPPORTED

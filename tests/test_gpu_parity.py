@@ -65,15 +65,16 @@ def test_wave_primitives_lane_layout(gpu, dtype):
 # sizes around tile and wave boundaries, all dtypes, both kinds
 # ---------------------------------------------------------------------------
 # sizes around wave and tile boundaries of every automatic tile size (4096
-# below 2^20, 16384 from 2^20, 32768 from 2^23, 65536 from 2^24) and around
-# the switch from workgroup-index tiles to drawn tiles at 2^25
+# below 2^20, 16384 from 2^20, 32768 from 2^23, 65536 from 2^24), around the
+# back-off switch at 2^25 and the switch from workgroup-index tiles to drawn
+# tiles with non-temporal loads at 2^27
 M, L, H = 16384, 32768, 65536
 EDGE_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, TILE - 1, TILE, TILE + 1,
               2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 255 * TILE + 3,
               (1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 20) + M - 1, 150 * M + 7, (1 << 22) + 1,
               (1 << 23) - 1, 1 << 23, (1 << 23) + 1, (1 << 23) + L + 1, 301 * L - 5,
               (1 << 24) - 1, 1 << 24, (1 << 24) + 1, (1 << 24) + H + 3, 301 * H - 7,
-              (1 << 25) - 1, (1 << 25) + 1]
+              (1 << 25) - 1, (1 << 25) + 1, (1 << 27) - 1, (1 << 27) + 1]
 
 
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
@@ -632,7 +633,7 @@ def test_random_sizes(gpu):
         check(x, y, dtype, exclusive, label=f"random case {case} n={n}")
 
 
-@pytest.mark.parametrize("n", [(1 << 22) + 7, (1 << 25) + 3], ids=["dispatch_tiles", "drawn_tiles"])
+@pytest.mark.parametrize("n", [(1 << 22) + 7, (1 << 27) + 3], ids=["dispatch_tiles", "drawn_tiles"])
 def test_graph_replays(gpu, n):
     # a captured call replays with the arguments it was captured with; the
     # descriptor epoch comes from the workspace, so every replay still sees
