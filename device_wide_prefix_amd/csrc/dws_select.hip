@@ -60,10 +60,6 @@ struct SelectParams {
     uint32_t backoff;        // pause level between blocked look-back polls (kPause*)
 };
 
-// Byte offset far past any tile's range (at most 4 * 40960 bytes): the
-// buffer range check drops the store. Offset plus store size stays below 2^32.
-constexpr uint32_t kDroppedOffset = 0x80000000u;
-
 template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX, bool NT = false, bool ALIAS = false>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
@@ -73,9 +69,14 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     constexpr int W = BLOCK / 64;
     constexpr uint32_t SEG = 64u * VEC * CHUNKS;
     constexpr uint32_t TILE = W * SEG;
+    constexpr uint32_t CH = 64u * VEC;
     __shared__ uint32_t s_draw, s_epoch;
     __shared__ uint32_t s_wave[W];
     __shared__ uint32_t s_prefix;
+    // per wave: one chunk's selected elements by rank (and, for a partition,
+    // its rejected elements, reversed), then one slot per lane that the other
+    // elements write to
+    __shared__ uint32_t s_stage[W][PARTITION ? 2 : 1][CH + 64];
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
@@ -166,34 +167,70 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     __syncthreads();
     const uint32_t prefix = uniform(s_prefix);
 
-    const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.out + prefix, count * 4u);
+    // Stores, chunk by chunk. The selected elements of one chunk of a wave
+    // (64 x VEC elements) have consecutive ranks, so they fill one contiguous
+    // range of the output: each writes itself into the wave's LDS stage at its
+    // rank within the chunk, and the wave stores the range with
+    // lane-contiguous dword stores, one instruction per 64 elements. The
+    // partition's rejected elements of the chunk fill one contiguous range at
+    // the back in reverse order, staged reversed the same way.
+    const uint64_t tile_first = (uint64_t)tile * TILE;
+    const uint64_t left = p.n - tile_first;
+    const uint32_t valid_local = left < TILE ? (uint32_t)left : TILE;
+    const uint64_t rejected_before = tile_first - prefix;
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c)
+    for (int c = 0; c < CHUNKS; ++c) {
+        const uint32_t sel_before = uniform(r[c][0]);   // lane 0: selected in the segment before chunk c
+        const uint32_t chunk_local = (uint32_t)wave * SEG + (uint32_t)c * CH;
+        uint32_t csel = 0u;
+        bool sel[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const bool sel = (selected >> (c * VEC + e)) & 1u;
-            const uint32_t off = sel ? (wave_pre + r[c][e]) * 4u : kDroppedOffset;
-            __builtin_amdgcn_raw_buffer_store_b32(x[c][e], rout, (int)off, 0, 0);
+            sel[e] = (selected >> (c * VEC + e)) & 1u;
+            csel += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(sel[e]));
         }
-    if constexpr (PARTITION) {
-        // rejected elements of the tile: rank rr among them (in-tile index
-        // minus selected before it), stored at base + (rejected - 1 - rr)
-        const uint64_t tile_first = (uint64_t)tile * TILE;
-        const uint64_t left = p.n - tile_first;
-        const uint32_t valid_local = left < TILE ? (uint32_t)left : TILE;
-        const uint32_t rejected = valid_local - count;
-        const uint64_t rejected_before = tile_first - prefix;
-        const __amdgpu_buffer_rsrc_t rrej = make_rsrc(p.out + (p.n - rejected_before - rejected), rejected * 4u);
+        csel = uniform(csel);
+        const uint32_t valid_c = valid_local > chunk_local ? (valid_local - chunk_local < CH ? valid_local - chunk_local
+                                                                                          : CH)
+                                                           : 0u;
+        const uint32_t crej = valid_c - csel;
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint32_t local = (uint32_t)wave * SEG + (uint32_t)(c * 64 * VEC) + (uint32_t)(lane * VEC + e);
-                const bool sel = (selected >> (c * VEC + e)) & 1u;
-                const uint32_t rr = local - (wave_pre + r[c][e]);
-                const uint32_t off = (!sel && local < valid_local) ? (rejected - 1u - rr) * 4u : kDroppedOffset;
-                __builtin_amdgcn_raw_buffer_store_b32(x[c][e], rrej, (int)off, 0, 0);
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t in_chunk = (uint32_t)(lane * VEC + e);
+            const uint32_t rank = r[c][e] - sel_before;   // selected before it in the chunk
+            s_stage[wave][0][sel[e] ? rank : CH + (uint32_t)lane] = x[c][e];
+            if constexpr (PARTITION) {
+                const uint32_t j = in_chunk - rank;         // rejected before it in the chunk
+                const bool rej = !sel[e] && in_chunk < valid_c;
+                s_stage[wave][1][rej ? crej - 1u - j : CH + (uint32_t)lane] = x[c][e];
             }
+        }
+        // the wave's LDS accesses run in order: the reads below see every
+        // lane's writes above (and the next chunk's writes follow the reads)
+        __builtin_amdgcn_wave_barrier();
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.out + ((uint64_t)prefix + wave_pre + sel_before), csel * 4u);
+#pragma unroll
+        for (int q = 0; q < (int)(CH / 64u); ++q) {
+            if (csel > (uint32_t)(64 * q)) {
+                const uint32_t i = (uint32_t)(64 * q + lane);
+                __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][0][i], rs, (int)(i * 4u), 0, 0);
+            }
+        }
+        if constexpr (PARTITION) {
+            // tile rejected ranks rr0 .. rr0 + crej - 1 land at the back in
+            // reverse: element index n - rejected_before - 1 - rr, so the
+            // chunk's block starts at n - rejected_before - rr0 - crej
+            const uint32_t rr0 = chunk_local - (wave_pre + sel_before);
+            const __amdgpu_buffer_rsrc_t rj = make_rsrc(p.out + (p.n - rejected_before - rr0 - crej), crej * 4u);
+#pragma unroll
+            for (int q = 0; q < (int)(CH / 64u); ++q) {
+                if (crej > (uint32_t)(64 * q)) {
+                    const uint32_t i = (uint32_t)(64 * q + lane);
+                    __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][1][i], rj, (int)(i * 4u), 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
     }
     if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.count = (unsigned long long)prefix + count;
 }
