@@ -295,9 +295,10 @@ __device__ __forceinline__ void desc_store_val(uint64_t* desc, uint32_t tile, ui
         desc_store<kOrderRelaxed>(desc_at(desc, tile) + k, desc_pack(epoch, status, v.w[k]));
 }
 
-// Look-back slots per lane of the generic-operator kernels: one, 64
-// predecessors per poll, as for the + scan with spread descriptors.
-constexpr int kOpLookbackSlots = 1;
+// Look-back slots per lane of the generic-operator kernels: two, 128
+// predecessors per poll. On 1 GiB inputs, against one slot: pair operators 0.1
+// to 2% faster, max/min within 1%; four slots were no better.
+constexpr int kOpLookbackSlots = 2;
 
 // Decoupled look-back under Op (section 4.4, parallelized look-back, K slots
 // per lane as in the + kernel): the window's needed descriptors (back to and
