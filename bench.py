@@ -46,6 +46,8 @@ import scan_workloads as wl  # noqa: E402
 METRIC = "scan GB/s (2n·sizeof(T)/time) at N=2^28 fp32; % of HBM peak & of D2D memcpy"
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30
+# shader clocks of the spin kernel that precedes every timed call (~100 us)
+SPIN_CYCLES = 250_000
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_f32_2p28.json")
 VARIANTS = {"single_pass": 0, "reduce_then_scan": 1, "chained": 2, "scan_then_propagate": 3}
 ORDERS = {"relaxed": 0, "acq_rel": 1}
@@ -115,12 +117,19 @@ class Hip:
 
 def time_steps(fn, prepare, steps: int, warmup: int):
     """Run warmup + steps; each step: prepare() untimed, then fn() between two
-    events on the current stream. Returns per-step milliseconds."""
+    events on the current stream. Returns per-step milliseconds.
+
+    Between prepare() and the first event the stream runs a short spin kernel
+    (about 100 us, no memory traffic), so the GPU is still busy while the host
+    records the event and issues fn(): the events then time the GPU's work on
+    fn() from the moment the GPU is free, not the interpreter's latency in
+    issuing it. Every timed callable (scans, memcpy, library comparisons) is
+    timed this way."""
     import torch
     times = []
     for i in range(warmup + steps):
         prepare()
-        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
