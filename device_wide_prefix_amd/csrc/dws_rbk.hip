@@ -9,20 +9,19 @@
 // The look-back carries the pair (heads, value since the last head) under
 // "count the heads, restart the value sum after the last head" (a segmented
 // sum, not commutative); the last tile stores the number of runs. Values are
-// 32-bit integers (sums wrap modulo 2^32), fp32, or the constant 1 (run-length
-// encoding: the sum is the run length).
+// 32-bit integers (sums wrap modulo 2^32) or fp32 (k_run_ends), or the
+// constant 1 (k_rle: the sum is the run length).
 //
 // The neighbour key[i-1] comes from the same lane, the adjacent lane (DPP
 // wave shift), the previous chunk (readlane) or, at a wave segment's start,
-// one extra 4-byte load. The heads of one chunk of a wave (256 elements)
+// one extra 4-byte load. The heads of one chunk of a wave (64 x VEC elements)
 // hold consecutive runs, so their outputs are two contiguous ranges: each
-// head writes its key and the finished run before it into a per-wave LDS
-// stage at its rank among the chunk's heads, and the wave then stores the
-// ranges with lane-contiguous dword stores, one instruction per 64 heads and
-// array. Storing from the elements' own lanes instead (lanes 16 bytes apart,
-// one instruction per element and array, mostly dropped) measured 1.35 to
-// 1.55x slower with all keys distinct at 2^25 and 3 to 7% slower at mean run
-// 16.
+// head writes into a per-wave LDS stage at its rank among the chunk's heads,
+// and the wave then stores the ranges with lane-contiguous dword stores, one
+// instruction per 64 heads and array. Storing from the elements' own lanes
+// instead (lanes 16 bytes apart, one instruction per element and array,
+// mostly dropped) measured 1.35 to 1.55x slower with all keys distinct at
+// 2^25 and 3 to 7% slower at mean run 16.
 #include "dws_op_kernel.hpp"
 
 namespace dws {
@@ -93,8 +92,8 @@ __device__ __forceinline__ float wave_segmented_scan_f32(float v, uint64_t start
 // Inside a wave segment no (heads, value) pairs are scanned:
 //   H(i) heads at or before i (ballots and mbcnt); the run holding i is
 //        H(i) - 1 after the heads before the segment.
-// Integer sums and run lengths use one plain prefix sum,
-//   S(i) values before i (wrapping +; for run lengths S(i) = i),
+// Integer sums use one plain prefix sum,
+//   S(i) values before i (wrapping +),
 //   B(i) S at the last head at or before i,
 // and the run finished by the head at p sums to S(p) - B(p - 1), exact modulo
 // 2^32 (when that run started before the segment, B(p - 1) is minus the value
@@ -113,7 +112,7 @@ __device__ __forceinline__ float wave_segmented_scan_f32(float v, uint64_t start
 template <int BLOCK, int VEC, int CHUNKS, int MODE, bool NT = false, int SLOTS = kRunLookbackSlots>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_run_ends(RbkParams p)
 {
-    static_assert(MODE >= 0 && MODE <= 2, "integer sums, fp32 sums or run lengths");
+    static_assert(MODE == 0 || MODE == 1, "integer or fp32 sums (run lengths: k_rle)");
     using Op = OpRunSum<MODE == 1>;
     using V = Val<2>;
     constexpr int W = BLOCK / 64;
@@ -138,7 +137,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.keys + seg_first, vb), lane, k);
     uint32_t v[CHUNKS][VEC];   // values, then S before each element (integer sums) or the fp32 sum
                                // since the last head up to the element (fp32 sums)
-    if constexpr (MODE != 2) load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.vals + seg_first, vb), lane, v);
+    load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.vals + seg_first, vb), lane, v);
     // the descriptor epoch, read after the tile loads (needed only to publish)
     const uint32_t epoch_v = (multi && wave == 0) ? load_epoch_async(p.epoch) : 0u;
     const bool has_prev = seg_first > 0u && seg_first < p.n;
@@ -162,10 +161,6 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const uint64_t lanes_below = (1ull << lane) - 1ull;
     uint32_t below[CHUNKS];   // heads of the segment before the lane's elements of chunk c
     uint32_t b_in[CHUNKS];    // B entering the lane's elements of chunk c (used when below[c] > 0)
-    // Run lengths: both are below SEG <= 2^16, so one register holds the pair
-    // (below << 16 | B), which keeps 64 keys per lane within 128 VGPRs.
-    constexpr bool kPack = MODE == 2;
-    static_assert(!kPack || SEG <= 65536u, "head counts and positions in 16 bits");
     uint32_t h_seg = 0u, s_seg = 0u, b_carry = 0u;   // uniform running totals over the chunks
     float f_carry = -0.0f;                            // fp32: the sum since the last head so far
 #pragma unroll
@@ -190,9 +185,6 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                 v[c][e] = sx[e];
             }
             s_seg += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-        } else if constexpr (MODE == 2) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sx[e] = (uint32_t)(c * CH) + (uint32_t)(lane * VEC + e);
         }
         uint64_t any = 0ull;
         uint32_t cnt = 0u, chunk_count = 0u, last = 0u;
@@ -205,7 +197,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
             any |= m;
             cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
             chunk_count += (uint32_t)__builtin_popcountll(m);
-            if constexpr (MODE != 1) last = head[e] ? sx[e] : last;
+            if constexpr (MODE == 0) last = head[e] ? sx[e] : last;
         }
         below[c] = cnt + h_seg;
         h_seg += chunk_count;
@@ -239,18 +231,14 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
             const int src = lower != 0ull ? 63 - __builtin_clzll(lower) : 0;
             const uint32_t from_lane = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)last);
             b_in[c] = lower != 0ull ? from_lane : b_carry;
-            if constexpr (kPack) below[c] = below[c] << 16 | b_in[c];
             if (any != 0ull) b_carry = (uint32_t)__builtin_amdgcn_readlane((int)last, 63 - __builtin_clzll(any));
         }
         // formed here, chunk by chunk (not sunk, which would hold every ballot)
         asm volatile("" : "+v"(below[c]));
         if constexpr (MODE == 0) asm volatile("" : "+v"(b_in[c]));
-        if constexpr (MODE != 2) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(v[c][e]));
-        }
+        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(v[c][e]));
     }
-    if constexpr (MODE == 2) s_seg = seg_elems;
     V seg_total;
     if constexpr (MODE == 1) seg_total = {{h_seg, f2u(f_carry)}};
     else seg_total = {{h_seg, h_seg > 0u ? s_seg - b_carry : s_seg}};
@@ -293,8 +281,6 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const uint32_t tile_heads = uniform(agg.w[0]);
     const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
     const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, (tile_heads + 1u) * 4u);
-    uint32_t lane_pos = (uint32_t)lane * VEC;
-    asm volatile("" : "+v"(lane_pos));   // positions formed here, not held through the look-back
     uint32_t run0 = seed_heads;          // run of the chunk's first head (uniform)
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
@@ -302,7 +288,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                                                                          0xf, true);
         const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
         const uint32_t first_prev = lane > 0 ? from_left : edge;
-        const uint32_t heads_below = kPack ? below[c] >> 16 : below[c];
+        const uint32_t heads_below = below[c];
         // each element: is it a head, and the value of the run it finishes
         // (the run before it)
         bool hd[VEC];
@@ -328,15 +314,12 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                 heads_before_elem += hd[e] ? 1u : 0u;
             }
         } else {
-            const uint32_t b_entering = kPack ? below[c] & 0xffffu : b_in[c];
-            uint32_t b = heads_below > 0u ? b_entering : 0u - seed_value;
+            uint32_t b = heads_below > 0u ? b_in[c] : 0u - seed_value;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
                 hd[e] = k[c][e] != prev;
-                uint32_t sxe;
-                if constexpr (MODE == 0) sxe = v[c][e];
-                else sxe = (uint32_t)(c * CH + e) + lane_pos;
+                const uint32_t sxe = v[c][e];
                 fin[e] = sxe - b;
                 b = hd[e] ? sxe : b;
             }
@@ -386,6 +369,231 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + tile_heads;
 }
 
+// Run-length encoding (the value of every element is 1, so a run's value is
+// its length). The run a head finishes has the length pos(head) - pos(head
+// before), and no per-element prefix is needed:
+//   first pass (before the look-back): the segment's head count and its last
+//     head, whose distance to the segment's end is the value carried on;
+//   second pass (after it), chunk by chunk: each head's rank among the
+//     chunk's heads (mbcnt over the ballots), its key and its position staged
+//     in LDS at that rank, then one lane per head reads them back and stores
+//     its key and the length of the run it finishes (its position minus the
+//     next lower lane's, or minus the previous chunk's last head).
+// The first head of a segment finishes a run that started seed value
+// elements before the segment (the value carried in). Against k_run_ends with
+// the constant 1 as the value (per-element positions, run ends, ranks and a
+// per-chunk ds_bpermute, 1,653 VALU instructions per wave) this has 761, and
+// measured 10 to 16% faster at mean run 16 (2^25 and 2^28 keys) and 1 to 2%
+// with all keys distinct. The heads are found again after the look-back
+// instead of keeping 64 ballot masks per wave in scalar registers.
+template <int BLOCK, int VEC, int CHUNKS, bool NT = false>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_rle(RbkParams p)
+{
+    using Op = OpRunSum<false>;
+    using V = Val<2>;
+    constexpr int W = BLOCK / 64;
+    constexpr uint32_t CH = 64u * VEC;
+    constexpr uint32_t SEG = CH * CHUNKS;
+    constexpr uint32_t TILE = W * SEG;
+    __shared__ V s_wave[W];
+    __shared__ V s_prefix;
+    __shared__ uint32_t s_stage[W][2][CH];   // per wave: keys, then positions, of one chunk's heads by rank
+
+    const int lane = lane_id();
+    const int wave = (int)uniform(threadIdx.x >> 6);
+    const bool multi = p.num_tiles > 1u;
+    const uint32_t tile = multi ? (uint32_t)blockIdx.x : 0u;
+    const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
+    const uint32_t vb = valid_bytes(seg_first, SEG, p.n);
+    const uint32_t seg_elems = vb / 4u;
+    uint32_t k[CHUNKS][VEC];
+    load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.keys + seg_first, vb), lane, k);
+    const uint32_t epoch_v = (multi && wave == 0) ? load_epoch_async(p.epoch) : 0u;
+    const bool has_prev = seg_first > 0u && seg_first < p.n;
+    const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
+    const bool holds_last = seg_elems > 0u && seg_first + seg_elems == p.n;
+    // the key compared with the segment's first element: the array's first
+    // element is always a head
+    uint32_t left0 = seg_first == 0u ? ~(uint32_t)__builtin_amdgcn_readlane((int)k[0][0], 0) : prev_key;
+    if (seg_elems < SEG) {
+        // elements past n take the key at n - 1, so they are never heads
+        const uint32_t last_key = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.keys + (p.n - 1u), 4u), 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if ((uint32_t)(c * CH) + (uint32_t)(lane * VEC + e) >= seg_elems) k[c][e] = last_key;
+        if (seg_elems == 0u) left0 = last_key;
+    }
+
+    // first pass: the key before each lane's first element of every chunk
+    // (kept for the second pass) and the segment's head count
+    uint32_t fprev[CHUNKS];
+    uint32_t h_seg = 0u;
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
+                                                                         0xf, true);
+        const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
+        fprev[c] = lane > 0 ? from_left : edge;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            h_seg += (uint32_t)__builtin_popcountll(
+                __builtin_amdgcn_ballot_w64(k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c])));
+        asm volatile("" : "+v"(fprev[c]));
+    }
+    h_seg = uniform(h_seg);
+    // the segment's last head: in the last chunk that has one, searched from
+    // the end (at mean runs above a few elements, the last chunk). Its
+    // compares are made again (the opaque copies below) rather than keeping
+    // the first pass's masks in scalar registers.
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+    uint32_t last_pos = 0u;
+    bool found = h_seg == 0u;
+#pragma unroll
+    for (int c = CHUNKS - 1; c >= 0; --c) {
+        if (!found) {
+            uint64_t m[VEC];
+            uint64_t any = 0ull;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                m[e] = __builtin_amdgcn_ballot_w64(k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]));
+                any |= m[e];
+            }
+            if (any != 0ull) {
+                const int top = 63 - __builtin_clzll(any);
+                uint32_t em = 0u;
+                bool got = false;
+#pragma unroll
+                for (int e = VEC - 1; e > 0; --e) {
+                    if (!got && ((m[e] >> top) & 1ull)) {
+                        em = (uint32_t)e;
+                        got = true;
+                    }
+                }
+                last_pos = (uint32_t)(c * CH) + (uint32_t)top * VEC + em;
+                found = true;
+            }
+        }
+    }
+    const V seg_total = {{h_seg, h_seg > 0u ? seg_elems - uniform(last_pos) : seg_elems}};
+
+    if (lane == 0) s_wave[wave] = seg_total;
+    __syncthreads();
+    V wave_pre = Op::identity(), agg = Op::identity();
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        if (w == wave) wave_pre = agg;
+        agg = Op::combine(agg, s_wave[w]);
+    }
+    if (wave == 0) {
+        V prefix = Op::identity();
+        if (multi) {
+            const uint32_t epoch = uniform(epoch_v);
+            if (tile == 0u) {
+                if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
+            } else {
+                if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
+                prefix = lookback_op<Op, kRunLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.backoff);
+                if (lane == 0) {
+                    desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
+                    if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
+                }
+            }
+        }
+        if (lane == 0) s_prefix = prefix;
+    }
+    __syncthreads();
+    const V tile_prefix = s_prefix;
+    const V seed = Op::combine(tile_prefix, wave_pre);
+    const uint32_t seed_heads = uniform(seed.w[0]);
+    const uint32_t seed_value = uniform(seed.w[1]);
+    const uint32_t heads_before = uniform(tile_prefix.w[0]);
+    const uint32_t tile_heads = uniform(agg.w[0]);
+
+    // second pass
+    uint32_t pos_lane = (uint32_t)lane * VEC;
+    asm volatile("" : "+v"(pos_lane));   // formed here, not held through the look-back
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+    uint32_t run0 = seed_heads;          // run of the chunk's first head (uniform)
+    uint32_t before = 0u - seed_value;   // position of the head before the chunk's first head
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        bool hd[VEC];
+        uint64_t m[VEC];
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+            m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+            cnt += (uint32_t)__builtin_popcountll(m[e]);
+        }
+        cnt = uniform(cnt);
+        // rank among the chunk's heads: heads in lower lanes, then the lane's own
+        uint32_t r = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (hd[e]) {
+                s_stage[wave][0][r] = k[c][e];
+                s_stage[wave][1][r] = pos_lane + (uint32_t)e;
+                ++r;
+            }
+        }
+        // the wave's LDS accesses run in order: the reads below see every
+        // lane's writes above (and the next chunk's writes follow the reads)
+        __builtin_amdgcn_wave_barrier();
+        if (cnt > 0u) {
+            // head q of the chunk is run run0 + q: its key goes to
+            // unique_keys[run0 + q], and it finishes run run0 + q - 1 (the
+            // array's first head finishes none, so its lane stores no length)
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
+            const bool first_of_array = run0 == 0u;
+            const uint32_t abase = uniform(first_of_array ? 0u : run0 - 1u);
+            const uint32_t arange = uniform(first_of_array ? cnt * 4u - 4u : cnt * 4u);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) {
+                if (cnt > (uint32_t)(64 * q)) {
+                    const uint32_t i = (uint32_t)(64 * q + lane);
+                    const uint32_t key = s_stage[wave][0][i];
+                    const uint32_t pos = s_stage[wave][1][i] + (uint32_t)(c * CH);
+                    const uint32_t left = wave_shift_up1(pos);
+                    const uint32_t len = pos - (lane == 0 ? before : left);
+                    __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
+                    if (!first_of_array || i > 0u)
+                        __builtin_amdgcn_raw_buffer_store_b32(len, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0,
+                                                              0);
+                    // the last head of this group of 64 is the next group's
+                    // (or the next chunk's) head before
+                    const uint32_t in_group = cnt - (uint32_t)(64 * q);
+                    before = (uint32_t)__builtin_amdgcn_readlane((int)pos, in_group >= 64u ? 63 : (int)in_group - 1);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        run0 += cnt;
+    }
+    if (holds_last && lane == 0) {
+        // the array's last run has no head after it: its length is the value
+        // carried to the end of the array
+        const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
+        const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, (tile_heads + 1u) * 4u);
+        const uint32_t last_off = (seed_heads + h_seg - 1u - base_run) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(Op::combine(seed, seg_total).w[1], raggs, (int)last_off, 0, 0);
+    }
+    if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.num_runs = (unsigned long long)heads_before + tile_heads;
+}
+
 __global__ void __launch_bounds__(64) k_store_runs(unsigned long long* count)
 {
     if (threadIdx.x == 0) *count = 0ull;
@@ -396,8 +604,10 @@ static hipError_t launch_rbk_mode(const RbkParams& p, hipStream_t stream)
 {
     RbkParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, NT>),
-                           dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
+    const void* fn;
+    if constexpr (MODE == 2) fn = reinterpret_cast<const void*>(&k_rle<BLOCK, VEC, CHUNKS, NT>);
+    else fn = reinterpret_cast<const void*>(&k_run_ends<BLOCK, VEC, CHUNKS, MODE, NT>);
+    return hipLaunchKernel(fn, dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
 }
 
 template <int BLOCK, int VEC, int CHUNKS>
@@ -433,9 +643,11 @@ hipError_t launch_rbk(const RbkArgs& a, hipStream_t stream)
                 rbk_backoff(a.n)};
     if (!a.aligned) return launch_rbk_shape<256, 1, 16>(a.mode, p, stream);
     if (a.n >= kRbkLargeMin) {
-        // sums: 16,384-element tiles (512 x 4 x 8); run lengths hold no values
-        // and pack their per-chunk state, so 32,768 (512 x 4 x 16) fit the
-        // same registers, which measured 5 to 11% faster at 2^25 and 2^28
+        // sums: 16,384-element tiles (512 x 4 x 8); run lengths hold no values,
+        // so 32,768 (512 x 4 x 16) fit the same registers (measured 5 to 11%
+        // faster at 2^25 and 2^28). For k_rle at 2^25 keys and mean run 16,
+        // 512 x 4 x 16 was 6% faster than 1024 x 4 x 16 and 3% faster than
+        // 256 x 4 x 16; with all keys distinct 1024 x 4 x 16 was 4% faster.
         // from kRbkNtMin keys the keys and values are loaded non-temporally
         // (each is read once): 1.6 to 3.4% faster with all keys distinct and
         // up to 1.3% at mean run 16, at 2^25, 2^26 and 2^28 keys
