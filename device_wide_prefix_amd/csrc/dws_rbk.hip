@@ -89,30 +89,38 @@ __device__ __forceinline__ float wave_segmented_scan_f32(float v, uint64_t start
     return v;
 }
 
-// Inside a wave segment no (heads, value) pairs are scanned:
-//   H(i) heads at or before i (ballots and mbcnt); the run holding i is
-//        H(i) - 1 after the heads before the segment.
-// Integer sums use one plain prefix sum,
-//   S(i) values before i (wrapping +),
-//   B(i) S at the last head at or before i,
-// and the run finished by the head at p sums to S(p) - B(p - 1), exact modulo
-// 2^32 (when that run started before the segment, B(p - 1) is minus the value
-// carried in). B comes from the lane's own heads, else from the highest lane
-// below with a head in the chunk (one ds_bpermute per chunk), else from earlier
-// chunks. fp32 sums would lose short runs' precision in such a difference, so
-// each element instead holds its run's fp32 sum since the last head: summed in
-// the lane, then across the lanes by a segmented wave scan restarted at lanes
-// that hold a head, with the sum carried in from earlier chunks. The segment's
-// aggregate for the look-back is (heads, value from its last head on).
-// At most 128 VGPRs (four waves per SIMD): two 512-thread workgroups share a
-// CU, so one's loads overlap the other's look-back and stores. The tile index
-// is the workgroup index (measured faster than a drawn index at 2^25 and 2^28
-// elements in every mode): it relies on the GPU starting each XCD's
-// workgroups in index order, and the watchdog bounds every wait.
-template <int BLOCK, int VEC, int CHUNKS, int MODE, bool NT = false, int SLOTS = kRunLookbackSlots>
+// Inside a wave segment no (heads, value) pairs are scanned. Heads are
+// counted with ballots before the look-back; after it, chunk by chunk, each
+// head stages its key and a value in LDS at its rank among the chunk's heads
+// (mbcnt over the ballots), and one lane per head stores the key and the run
+// it finishes:
+//   integer sums: S(i), the segment's values before i (wrapping +), is formed
+//     before the look-back; the run finished by the head at p sums to
+//     S(p) - S(previous head), exact modulo 2^32, where the previous head is
+//     the next lower lane's staged one, or the previous chunk's last, or, for
+//     the segment's first head, at S = minus the value carried in;
+//   fp32 sums: differences of long fp32 prefix sums would lose short runs'
+//     precision, so each element instead holds its run's fp32 sum since the
+//     last head: summed in the lane, then across the lanes by a segmented
+//     wave scan restarted at lanes that hold a head, with the sum carried in
+//     from earlier chunks. A head stages the sum of the element before it;
+//     the segment's first head adds the value carried in.
+// The segment's aggregate for the look-back is (heads, value from its last
+// head on). Against the former kernel (per-lane run starts formed before the
+// look-back with a ds_bpermute per chunk) this measured 2 to 3% faster at
+// mean run 16 (2^25 and 2^28 keys) and equal with all keys distinct. The
+// heads are found again after the look-back, and the last head's S by a
+// search from the segment's end, rather than keeping ballot masks in scalar
+// registers. At most 128 VGPRs (four waves per SIMD): two 512-thread
+// workgroups share a CU, so one's loads overlap the other's look-back and
+// stores. The tile index is the workgroup index (measured faster than a drawn
+// index at 2^25 and 2^28 elements in every mode): it relies on the GPU
+// starting each XCD's workgroups in index order, and the watchdog bounds
+// every wait.
+template <int BLOCK, int VEC, int CHUNKS, int MODE, bool NT = false>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_run_ends(RbkParams p)
 {
-    static_assert(MODE == 0 || MODE == 1, "integer or fp32 sums (run lengths: k_rle)");
+    static_assert(MODE == 0 || MODE == 1, "integer or fp32 sums");
     using Op = OpRunSum<MODE == 1>;
     using V = Val<2>;
     constexpr int W = BLOCK / 64;
@@ -121,34 +129,26 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr uint32_t TILE = W * SEG;
     __shared__ V s_wave[W];
     __shared__ V s_prefix;
-    // per wave: the keys and the finished runs of one chunk's heads by rank,
-    // then one slot per lane that the chunk's other elements write to
-    __shared__ uint32_t s_stage[W][2][CH + 64];
+    __shared__ uint32_t s_stage[W][2][CH];   // per wave: keys, then values, of one chunk's heads by rank
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
     const uint32_t tile = multi ? (uint32_t)blockIdx.x : 0u;
-
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t vb = valid_bytes(seg_first, SEG, p.n);
     const uint32_t seg_elems = vb / 4u;
     uint32_t k[CHUNKS][VEC];
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.keys + seg_first, vb), lane, k);
-    uint32_t v[CHUNKS][VEC];   // values, then S before each element (integer sums) or the fp32 sum
-                               // since the last head up to the element (fp32 sums)
+    uint32_t v[CHUNKS][VEC];
     load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.vals + seg_first, vb), lane, v);
-    // the descriptor epoch, read after the tile loads (needed only to publish)
     const uint32_t epoch_v = (multi && wave == 0) ? load_epoch_async(p.epoch) : 0u;
     const bool has_prev = seg_first > 0u && seg_first < p.n;
     const uint32_t prev_key = __builtin_amdgcn_raw_buffer_load_b32(
         make_rsrc(p.keys + (has_prev ? seg_first - 1u : 0u), has_prev ? 4u : 0u), 0, 0, 0);
     const bool holds_last = seg_elems > 0u && seg_first + seg_elems == p.n;
-    // the key compared with the segment's first element: the array's first
-    // element is always a head
     uint32_t left0 = seg_first == 0u ? ~(uint32_t)__builtin_amdgcn_readlane((int)k[0][0], 0) : prev_key;
     if (seg_elems < SEG) {
-        // elements past n take the key at n - 1, so they are never heads
         const uint32_t last_key = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.keys + (p.n - 1u), 4u), 0, 0, 0);
 #pragma unroll
         for (int c = 0; c < CHUNKS; ++c)
@@ -158,19 +158,26 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
         if (seg_elems == 0u) left0 = last_key;
     }
 
-    const uint64_t lanes_below = (1ull << lane) - 1ull;
-    uint32_t below[CHUNKS];   // heads of the segment before the lane's elements of chunk c
-    uint32_t b_in[CHUNKS];    // B entering the lane's elements of chunk c (used when below[c] > 0)
-    uint32_t h_seg = 0u, s_seg = 0u, b_carry = 0u;   // uniform running totals over the chunks
-    float f_carry = -0.0f;                            // fp32: the sum since the last head so far
+    uint32_t fprev[CHUNKS];
+    uint32_t h_seg = 0u, s_seg = 0u;
+    float f_carry = -0.0f;
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
         const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
                                                                          0xf, true);
         const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
-        const uint32_t first_prev = lane > 0 ? from_left : edge;
-        uint32_t sx[VEC];
+        fprev[c] = lane > 0 ? from_left : edge;
+        bool head[VEC];
+        uint64_t any = 0ull;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            head[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(head[e]);
+            any |= m;
+            h_seg += (uint32_t)__builtin_popcountll(m);
+        }
         if constexpr (MODE == 0) {
+            uint32_t sx[VEC];
             uint32_t acc = 0u;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -180,31 +187,9 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
             const uint32_t incl = wave_inclusive_scan(acc);
             const uint32_t base = s_seg + (incl - acc);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                sx[e] += base;
-                v[c][e] = sx[e];
-            }
+            for (int e = 0; e < VEC; ++e) v[c][e] = sx[e] + base;
             s_seg += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-        }
-        uint64_t any = 0ull;
-        uint32_t cnt = 0u, chunk_count = 0u, last = 0u;
-        bool head[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
-            head[e] = k[c][e] != prev;
-            const uint64_t m = __builtin_amdgcn_ballot_w64(head[e]);
-            any |= m;
-            cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, cnt));
-            chunk_count += (uint32_t)__builtin_popcountll(m);
-            if constexpr (MODE == 0) last = head[e] ? sx[e] : last;
-        }
-        below[c] = cnt + h_seg;
-        h_seg += chunk_count;
-        if constexpr (MODE == 1) {
-            // fp32: the sum since the last head, in the lane, then across the
-            // lanes restarted at those holding a head; the value carried in
-            // from earlier chunks enters lane 0's elements before its first head
+        } else {
             float g[VEC];
             bool seen[VEC];
             float acc = -0.0f;
@@ -219,29 +204,54 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
             }
             const float lane_total = (lane == 0 && !any_head) ? f_carry + acc : acc;
             const float incl = wave_segmented_scan_f32(lane_total, any, lane);
-            // the shift runs with every lane active (a DPP read of an inactive
-            // lane returns 0), then lane 0 takes the carry instead
             const float from_lower = wave_shift_up1(incl);
             const float into = lane == 0 ? f_carry : from_lower;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[c][e] = f2u(seen[e] ? g[e] : into + g[e]);
             f_carry = u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(incl), 63));
-        } else {
-            const uint64_t lower = any & lanes_below;
-            const int src = lower != 0ull ? 63 - __builtin_clzll(lower) : 0;
-            const uint32_t from_lane = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)last);
-            b_in[c] = lower != 0ull ? from_lane : b_carry;
-            if (any != 0ull) b_carry = (uint32_t)__builtin_amdgcn_readlane((int)last, 63 - __builtin_clzll(any));
         }
-        // formed here, chunk by chunk (not sunk, which would hold every ballot)
-        asm volatile("" : "+v"(below[c]));
-        if constexpr (MODE == 0) asm volatile("" : "+v"(b_in[c]));
+        asm volatile("" : "+v"(fprev[c]));
 #pragma unroll
         for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(v[c][e]));
     }
+    h_seg = uniform(h_seg);
     V seg_total;
-    if constexpr (MODE == 1) seg_total = {{h_seg, f2u(f_carry)}};
-    else seg_total = {{h_seg, h_seg > 0u ? s_seg - b_carry : s_seg}};
+    if constexpr (MODE == 1) {
+        seg_total = {{h_seg, f2u(f_carry)}};
+    } else {
+        // S at the segment's last head, from the last chunk that has one
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+        uint32_t b_last = 0u;
+        bool found = h_seg == 0u;
+#pragma unroll
+        for (int c = CHUNKS - 1; c >= 0; --c) {
+            if (!found) {
+                uint64_t m[VEC];
+                uint64_t any = 0ull;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    m[e] = __builtin_amdgcn_ballot_w64(k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]));
+                    any |= m[e];
+                }
+                if (any != 0ull) {
+                    const int top = 63 - __builtin_clzll(any);
+                    bool got = false;
+#pragma unroll
+                    for (int e = VEC - 1; e >= 0; --e) {
+                        if (!got && ((m[e] >> top) & 1ull)) {
+                            b_last = (uint32_t)__builtin_amdgcn_readlane((int)v[c][e], top);
+                            got = true;
+                        }
+                    }
+                    found = true;
+                }
+            }
+        }
+        seg_total = {{h_seg, h_seg > 0u ? s_seg - uniform(b_last) : s_seg}};
+    }
 
     if (lane == 0) s_wave[wave] = seg_total;
     __syncthreads();
@@ -251,7 +261,6 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
         if (w == wave) wave_pre = agg;
         agg = Op::combine(agg, s_wave[w]);
     }
-
     if (wave == 0) {
         V prefix = Op::identity();
         if (multi) {
@@ -260,7 +269,7 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                 if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
             } else {
                 if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, SLOTS>(p.desc, tile, epoch, p.watchdog, p.backoff);
+                prefix = lookback_op<Op, kRunLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.backoff);
                 if (lane == 0) {
                     desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
@@ -274,95 +283,86 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const V seed = Op::combine(tile_prefix, wave_pre);
     const uint32_t seed_heads = uniform(seed.w[0]);
     const uint32_t seed_value = uniform(seed.w[1]);
-
-    // runs this tile can write: the one running into it (if any) and its own.
-    // Uniform by construction; saying so keeps the buffer resources in SGPRs.
     const uint32_t heads_before = uniform(tile_prefix.w[0]);
     const uint32_t tile_heads = uniform(agg.w[0]);
-    const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
-    const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, (tile_heads + 1u) * 4u);
-    uint32_t run0 = seed_heads;          // run of the chunk's first head (uniform)
+
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+    uint32_t run0 = seed_heads;
+    uint32_t before = 0u - seed_value;   // integer sums: S at the head before the chunk's first head
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
-        const uint32_t from_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k[c][VEC - 1], kDppWaveShr1, 0xf,
-                                                                         0xf, true);
-        const uint32_t edge = c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)k[c - 1][VEC - 1], 63) : left0;
-        const uint32_t first_prev = lane > 0 ? from_left : edge;
-        const uint32_t heads_below = below[c];
-        // each element: is it a head, and the value of the run it finishes
-        // (the run before it)
         bool hd[VEC];
-        uint32_t fin[VEC];
+        uint64_t m[VEC];
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+            m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+            cnt += (uint32_t)__builtin_popcountll(m[e]);
+        }
+        cnt = uniform(cnt);
+        uint32_t r = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+        uint32_t g_first = 0u;
         if constexpr (MODE == 1) {
-            // the run before a head ends at the element before it, whose sum
-            // since its own last head is in v (from the lane before, or the
-            // chunk before; nothing precedes the segment's first element)
             const uint32_t g_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[c][VEC - 1], kDppWaveShr1, 0xf,
                                                                           0xf, true);
             const uint32_t g_edge =
                 c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v[c > 0 ? c - 1 : 0][VEC - 1], 63) : 0x80000000u;
-            const uint32_t g_first = lane > 0 ? g_left : g_edge;
-            const float seed_f = u2f(seed_value);
-            uint32_t heads_before_elem = heads_below;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
-                hd[e] = k[c][e] != prev;
-                const float g_prev = u2f(e > 0 ? v[c][e - 1] : g_first);
-                // a run that started before the segment adds the value carried in
-                fin[e] = f2u(heads_before_elem > 0u ? g_prev : seed_f + g_prev);
-                heads_before_elem += hd[e] ? 1u : 0u;
-            }
-        } else {
-            uint32_t b = heads_below > 0u ? b_in[c] : 0u - seed_value;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint32_t prev = e > 0 ? k[c][e - 1] : first_prev;
-                hd[e] = k[c][e] != prev;
-                const uint32_t sxe = v[c][e];
-                fin[e] = sxe - b;
-                b = hd[e] ? sxe : b;
-            }
+            g_first = lane > 0 ? g_left : g_edge;
         }
-        // rank among the chunk's heads: heads in lower lanes, then the lane's own
-        uint32_t rank = 0u, cnt = 0u;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const uint64_t m = __builtin_amdgcn_ballot_w64(hd[e]);
-            rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, rank));
-            cnt += (uint32_t)__builtin_popcountll(m);
+            if (hd[e]) {
+                s_stage[wave][0][r] = k[c][e];
+                if constexpr (MODE == 0) s_stage[wave][1][r] = v[c][e];
+                else s_stage[wave][1][r] = e > 0 ? v[c][e - 1] : g_first;
+                ++r;
+            }
         }
-        cnt = uniform(cnt);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t slot = hd[e] ? rank : CH + (uint32_t)lane;
-            s_stage[wave][0][slot] = k[c][e];
-            s_stage[wave][1][slot] = fin[e];
-            rank += hd[e] ? 1u : 0u;
-        }
-        // the wave's LDS accesses run in order: the reads below see every
-        // lane's writes above (and the next chunk's writes follow the reads)
         __builtin_amdgcn_wave_barrier();
-        // the chunk's heads hold runs run0 .. run0 + cnt - 1; head q stores its
-        // key at unique_keys[run0 + q] and finishes run run0 + q - 1 (none
-        // before the array's first head)
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
-        const bool first_of_array = run0 == 0u;
-        const __amdgpu_buffer_rsrc_t ra = first_of_array ? make_rsrc(p.aggs, cnt > 0u ? cnt * 4u - 4u : 0u)
-                                                         : make_rsrc(p.aggs + (run0 - 1u), cnt * 4u);
-        const uint32_t skip = first_of_array ? 1u : 0u;
+        if (cnt > 0u) {
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
+            const bool first_of_array = run0 == 0u;
+            const bool first_of_seg = run0 == seed_heads;
+            const uint32_t abase = uniform(first_of_array ? 0u : run0 - 1u);
+            const uint32_t arange = uniform(first_of_array ? cnt * 4u - 4u : cnt * 4u);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
 #pragma unroll
-        for (int q = 0; q < (int)(CH / 64u); ++q) {
-            if (cnt > (uint32_t)(64 * q)) {
-                const uint32_t i = (uint32_t)(64 * q + lane);
-                __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][0][i], rk, (int)(i * 4u), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][1][i + skip], ra, (int)(i * 4u), 0, 0);
+            for (int q = 0; q < VEC; ++q) {
+                if (cnt > (uint32_t)(64 * q)) {
+                    const uint32_t i = (uint32_t)(64 * q + lane);
+                    const uint32_t key = s_stage[wave][0][i];
+                    const uint32_t val = s_stage[wave][1][i];
+                    uint32_t fin;
+                    if constexpr (MODE == 0) {
+                        const uint32_t left = wave_shift_up1(val);
+                        fin = val - (lane == 0 ? before : left);
+                        const uint32_t in_group = cnt - (uint32_t)(64 * q);
+                        before = (uint32_t)__builtin_amdgcn_readlane((int)val, in_group >= 64u ? 63 : (int)in_group - 1);
+                    } else {
+                        // the segment's first head finishes a run that started
+                        // before the segment: it adds the value carried in
+                        fin = (first_of_seg && i == 0u) ? f2u(u2f(seed_value) + u2f(val)) : val;
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
+                    if (!first_of_array || i > 0u)
+                        __builtin_amdgcn_raw_buffer_store_b32(fin, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0,
+                                                              0);
+                }
             }
         }
         __builtin_amdgcn_wave_barrier();
         run0 += cnt;
     }
     if (holds_last && lane == 0) {
+        const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
+        const __amdgpu_buffer_rsrc_t raggs = make_rsrc(p.aggs + base_run, (tile_heads + 1u) * 4u);
         const uint32_t last_off = (seed_heads + h_seg - 1u - base_run) * 4u;
         __builtin_amdgcn_raw_buffer_store_b32(Op::combine(seed, seg_total).w[1], raggs, (int)last_off, 0, 0);
     }
@@ -380,12 +380,13 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 //     its key and the length of the run it finishes (its position minus the
 //     next lower lane's, or minus the previous chunk's last head).
 // The first head of a segment finishes a run that started seed value
-// elements before the segment (the value carried in). Against k_run_ends with
-// the constant 1 as the value (per-element positions, run ends, ranks and a
-// per-chunk ds_bpermute, 1,653 VALU instructions per wave) this has 761, and
-// measured 10 to 16% faster at mean run 16 (2^25 and 2^28 keys) and 1 to 2%
-// with all keys distinct. The heads are found again after the look-back
-// instead of keeping 64 ballot masks per wave in scalar registers.
+// elements before the segment (the value carried in). Against the former
+// shared kernel with the constant 1 as the value (per-element positions, run
+// starts and ranks formed before the look-back, a ds_bpermute per chunk: 1,653
+// VALU instructions per wave) this has 761, and measured 10 to 16% faster at
+// mean run 16 (2^25 and 2^28 keys) and 1 to 2% with all keys distinct. The
+// heads are found again after the look-back instead of keeping 64 ballot
+// masks per wave in scalar registers.
 template <int BLOCK, int VEC, int CHUNKS, bool NT = false>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) k_rle(RbkParams p)
 {
