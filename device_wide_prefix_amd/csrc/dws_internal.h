@@ -105,7 +105,6 @@ struct SelectArgs {
     bool partition;          // also write the rejected elements, reversed, at the back
 };
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
-constexpr uint64_t kSelectHugeMin = (uint64_t)1 << 27;    // 40960-element tiles from here
 constexpr uint64_t kSelectDrawnMin = (uint64_t)1 << 25;   // drawn tile index from here (below: workgroup index)
 constexpr uint64_t kSelectMaxElems = 0xffffffffull;       // counts travel in 32-bit descriptors
 // pause level between blocked look-back polls of the compaction kernels: the

@@ -244,11 +244,11 @@ struct SelectShape {
     int threads, vec, chunks;
     constexpr uint32_t elems() const { return (uint32_t)(threads * vec * chunks); }
 };
-// From 2^27 elements 40960-element tiles: 5% faster than 32768 at 2^30 (the
-// look-back and the swap between workgroups are paid over more bytes). Below
-// that, 32768 divides the common power-of-two sizes into whole rounds of the
-// 256 CUs, which measured faster at 2^25.
-constexpr SelectShape kSelectHuge{1024, 4, 10};   // 40960 elements
+// 32768-element tiles from kSelectLargeMin: with descriptors 64 bytes apart
+// and the short pause between polls they measured 2.6 to 5% faster than
+// 40960-element tiles (1024 x 4 x 10) at 2^27, 2^28 and 2^30 - 12,345
+// elements, and 5 to 7% faster at 2^26 (the larger tile had been 5% faster at
+// 2^30 with packed descriptors and a long back-off).
 constexpr SelectShape kSelectLarge{1024, 4, 8};   // 32768
 constexpr SelectShape kSelectSmall{256, 4, 4};    // 4096
 constexpr SelectShape kSelectScalar{256, 1, 16};  // 4096, pointers not 16-byte aligned
@@ -256,7 +256,7 @@ constexpr SelectShape kSelectScalar{256, 1, 16};  // 4096, pointers not 16-byte 
 static SelectShape select_shape(uint64_t n, bool aligned)
 {
     if (!aligned) return kSelectScalar;
-    return n >= kSelectHugeMin ? kSelectHuge : (n >= kSelectLargeMin ? kSelectLarge : kSelectSmall);
+    return n >= kSelectLargeMin ? kSelectLarge : kSelectSmall;
 }
 
 uint32_t select_tile_elems(uint64_t n, bool aligned) { return select_shape(n, aligned).elems(); }
@@ -266,8 +266,6 @@ static const void* select_kernel(const SelectShape& s)
 {
     if (s.vec == 1) return reinterpret_cast<const void*>(
         &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION, TI, false, ALIAS>);
-    if (s.chunks == kSelectHuge.chunks) return reinterpret_cast<const void*>(
-        &k_select<kSelectHuge.threads, kSelectHuge.vec, kSelectHuge.chunks, PARTITION, TI, NT, ALIAS>);
     if (s.threads == kSelectLarge.threads) return reinterpret_cast<const void*>(
         &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION, TI, NT, ALIAS>);
     return reinterpret_cast<const void*>(
@@ -294,8 +292,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     // With a drawn tile index (from 2^25 elements) the values and flags are
     // loaded non-temporally, each being read once: measured 0.5 to 2% faster
     // at 2^25, 3 to 5.6% at 2^26 and 2^27, 3% at 2^30 - 12,345. Those sizes run
-    // the large or huge shape when the pointers are aligned (the small and
-    // scalar shapes have no non-temporal build).
+    // the large shape when the pointers are aligned (the small and scalar
+    // shapes have no non-temporal build).
     // In place (select only) the kernel waits for its values before it
     // publishes, which is what makes writing over the input safe.
     const bool drawn = a.n >= kSelectDrawnMin;

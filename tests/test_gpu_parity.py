@@ -468,7 +468,6 @@ def test_profiled_scan_nontemporal(gpu):
 # stream compaction (select by flags) fused with the single-pass scan
 # ---------------------------------------------------------------------------
 SEL_TILE_LARGE = 32768    # from 2^22 elements
-SEL_TILE_HUGE = 40960     # from 2^27 elements
 SELECT_SIZES = [0, 1, 2, 63, 64, 65, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, 1_000_003,
                 (1 << 22) - 1, 1 << 22, (1 << 22) + 1, (1 << 22) + SEL_TILE_LARGE + 5, 129 * SEL_TILE_LARGE - 3]
 DENSITIES = [0.0, 0.01, 0.5, 0.99, 1.0]
@@ -516,10 +515,11 @@ def test_select_sizes_and_densities(gpu, density, in_place):
         _check_select(x, flags, got, cnt, in_place, f"n={n} d={density}")
 
 
-def test_select_huge_tiles(gpu):
-    # the 40960-element tiles (from 2^27): either side of the threshold, a
-    # ragged last tile, in and out of place
-    for n in ((1 << 27) - 1, (1 << 27) + SEL_TILE_HUGE + 5):
+def test_select_drawn_tiles(gpu):
+    # the drawn tile index with non-temporal loads (from 2^25): either side of
+    # the threshold, and a size past 2^27 with a ragged last tile, in and out
+    # of place
+    for n in ((1 << 25) - 1, (1 << 25) + SEL_TILE_LARGE + 5, (1 << 27) + SEL_TILE_LARGE + 5):
         x = wl.generate("i32_full", n, seed=n + 1)
         flags = wl.selection_flags(n, 0.5, seed=n + 2, any_nonzero=True)
         for in_place in (False, True):
