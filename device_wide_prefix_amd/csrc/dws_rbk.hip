@@ -63,6 +63,17 @@ struct RbkParams {
 // slots do not fit: with four, the kernels spill registers to scratch memory.
 constexpr int kRunLookbackSlots = 1;
 
+// A wave segment of the large shapes (2,048 elements or more) with at most
+// this many heads stages all of them in LDS right after publishing its
+// aggregate, while wave 0 waits in the look-back (wave 0 itself after it), so
+// that only the stores are left once the prefix is known. Segments with more
+// heads, and the small shapes, stage chunk by chunk after the look-back. With
+// 1,024 (8 KiB per wave) it measured 11% faster at mean run 16 for run-length
+// encoding (2^22, 2^25 and 2^28 keys) and equal with all keys distinct or at
+// mean run 3 (which take the chunk path); 512 measured the same at mean run
+// 16.
+constexpr uint32_t kRunPreHeads = 1024u;
+
 // Inclusive fp32 + scan over the 64 lanes in lane order, restarted at the
 // lanes set in `starts`: lane l sums lanes s..l, where s is the highest lane
 // <= l in starts (lane 0 when there is none). It is the plain scan's row-shift
@@ -129,9 +140,12 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr uint32_t TILE = W * SEG;
     __shared__ V s_wave[W];
     __shared__ V s_prefix;
-    // per wave: keys, then values, of one chunk's heads by rank, then one
-    // spare slot per lane that the chunk's other elements write to
-    __shared__ uint32_t s_stage[W][2][CH + 64];
+    // per wave: keys, then values, of the segment's heads (or of one
+    // chunk's) by rank, then one spare slot per lane that the other elements
+    // write to
+    constexpr uint32_t PRE = SEG < 2048u ? 0u : (SEG < kRunPreHeads ? SEG : kRunPreHeads);
+    constexpr uint32_t SLOTS = PRE > CH ? PRE : CH;
+    __shared__ uint32_t s_stage[W][2][SLOTS + 64];
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
@@ -280,6 +294,47 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
         }
         if (lane == 0) s_prefix = prefix;
     }
+    // a segment with few heads stages all of them now (key and value at the
+    // head's rank in the segment)
+    const bool pre = PRE > 0u && (SEG <= PRE || h_seg <= PRE);
+    if (pre) {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+        uint32_t base = 0u;   // heads of the segment before chunk c (uniform)
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            bool hd[VEC];
+            uint64_t m[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+                m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+            }
+            uint32_t r = base;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+            uint32_t g_first = 0u;
+            if constexpr (MODE == 1) {
+                const uint32_t g_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[c][VEC - 1], kDppWaveShr1,
+                                                                              0xf, 0xf, true);
+                const uint32_t g_edge =
+                    c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v[c > 0 ? c - 1 : 0][VEC - 1], 63) : 0x80000000u;
+                g_first = lane > 0 ? g_left : g_edge;
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t slot = hd[e] ? r : SLOTS + (uint32_t)lane;
+                s_stage[wave][0][slot] = k[c][e];
+                if constexpr (MODE == 0) s_stage[wave][1][slot] = v[c][e];
+                else s_stage[wave][1][slot] = e > 0 ? v[c][e - 1] : g_first;
+                r += hd[e] ? 1u : 0u;
+            }
+            base = uniform((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+        }
+    }
     __syncthreads();
     const V tile_prefix = s_prefix;
     const V seed = Op::combine(tile_prefix, wave_pre);
@@ -288,78 +343,109 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const uint32_t heads_before = uniform(tile_prefix.w[0]);
     const uint32_t tile_heads = uniform(agg.w[0]);
 
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
-    uint32_t run0 = seed_heads;
-    uint32_t before = 0u - seed_value;   // integer sums: S at the head before the chunk's first head
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        bool hd[VEC];
-        uint64_t m[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
-            m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+    if (pre) {
+        // head i of the segment is run seed_heads + i and finishes run
+        // seed_heads + i - 1 (the array's first head finishes none)
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + seed_heads, h_seg * 4u);
+        const bool first_of_array = seed_heads == 0u;
+        const uint32_t abase = uniform(first_of_array ? 0u : seed_heads - 1u);
+        const uint32_t arange = uniform(first_of_array ? (h_seg > 0u ? h_seg * 4u - 4u : 0u) : h_seg * 4u);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+        uint32_t before = 0u - seed_value;   // integer sums: S at the head before this group's first
+        for (uint32_t g = 0u; g < h_seg; g += 64u) {
+            const uint32_t i = g + (uint32_t)lane;
+            const uint32_t key = s_stage[wave][0][i];
+            const uint32_t val = s_stage[wave][1][i];
+            uint32_t fin;
+            if constexpr (MODE == 0) {
+                const uint32_t left = wave_shift_up1(val);
+                fin = val - (lane == 0 ? before : left);
+                before = (uint32_t)__builtin_amdgcn_readlane((int)val, 63);
+            } else {
+                // the segment's first head finishes a run that started before
+                // the segment: it adds the value carried in
+                fin = i == 0u ? f2u(u2f(seed_value) + u2f(val)) : val;
+            }
+            __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
+            if (!first_of_array || i > 0u)
+                __builtin_amdgcn_raw_buffer_store_b32(fin, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0, 0);
         }
-        // rank among the chunk's heads (as in k_rle: every element writes,
-        // the others to their lane's spare slot)
-        uint32_t r = 0u;
+    } else {
+        // the chunk path
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
-        uint32_t g_first = 0u;
-        if constexpr (MODE == 1) {
-            const uint32_t g_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[c][VEC - 1], kDppWaveShr1, 0xf,
-                                                                          0xf, true);
-            const uint32_t g_edge =
-                c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v[c > 0 ? c - 1 : 0][VEC - 1], 63) : 0x80000000u;
-            g_first = lane > 0 ? g_left : g_edge;
-        }
+        for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t slot = hd[e] ? r : CH + (uint32_t)lane;
-            s_stage[wave][0][slot] = k[c][e];
-            if constexpr (MODE == 0) s_stage[wave][1][slot] = v[c][e];
-            else s_stage[wave][1][slot] = e > 0 ? v[c][e - 1] : g_first;
-            r += hd[e] ? 1u : 0u;
-        }
-        const uint32_t cnt = uniform((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
-        __builtin_amdgcn_wave_barrier();
-        if (cnt > 0u) {
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
-            const bool first_of_array = run0 == 0u;
-            const bool first_of_seg = run0 == seed_heads;
-            const uint32_t abase = uniform(first_of_array ? 0u : run0 - 1u);
-            const uint32_t arange = uniform(first_of_array ? cnt * 4u - 4u : cnt * 4u);
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+        uint32_t run0 = seed_heads;
+        uint32_t before = 0u - seed_value;   // integer sums: S at the head before the chunk's first head
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) {
-                if (cnt > (uint32_t)(64 * q)) {
-                    const uint32_t i = (uint32_t)(64 * q + lane);
-                    const uint32_t key = s_stage[wave][0][i];
-                    const uint32_t val = s_stage[wave][1][i];
-                    uint32_t fin;
-                    if constexpr (MODE == 0) {
-                        const uint32_t left = wave_shift_up1(val);
-                        fin = val - (lane == 0 ? before : left);
-                        const uint32_t in_group = cnt - (uint32_t)(64 * q);
-                        before = (uint32_t)__builtin_amdgcn_readlane((int)val, in_group >= 64u ? 63 : (int)in_group - 1);
-                    } else {
-                        // the segment's first head finishes a run that started
-                        // before the segment: it adds the value carried in
-                        fin = (first_of_seg && i == 0u) ? f2u(u2f(seed_value) + u2f(val)) : val;
+        for (int c = 0; c < CHUNKS; ++c) {
+            bool hd[VEC];
+            uint64_t m[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+                m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+            }
+            // rank among the chunk's heads (as in k_rle: every element writes,
+            // the others to their lane's spare slot)
+            uint32_t r = 0u;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+            uint32_t g_first = 0u;
+            if constexpr (MODE == 1) {
+                const uint32_t g_left = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[c][VEC - 1], kDppWaveShr1, 0xf,
+                                                                              0xf, true);
+                const uint32_t g_edge =
+                    c > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v[c > 0 ? c - 1 : 0][VEC - 1], 63) : 0x80000000u;
+                g_first = lane > 0 ? g_left : g_edge;
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t slot = hd[e] ? r : CH + (uint32_t)lane;
+                s_stage[wave][0][slot] = k[c][e];
+                if constexpr (MODE == 0) s_stage[wave][1][slot] = v[c][e];
+                else s_stage[wave][1][slot] = e > 0 ? v[c][e - 1] : g_first;
+                r += hd[e] ? 1u : 0u;
+            }
+            const uint32_t cnt = uniform((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+            __builtin_amdgcn_wave_barrier();
+            if (cnt > 0u) {
+                const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
+                const bool first_of_array = run0 == 0u;
+                const bool first_of_seg = run0 == seed_heads;
+                const uint32_t abase = uniform(first_of_array ? 0u : run0 - 1u);
+                const uint32_t arange = uniform(first_of_array ? cnt * 4u - 4u : cnt * 4u);
+                const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) {
+                    if (cnt > (uint32_t)(64 * q)) {
+                        const uint32_t i = (uint32_t)(64 * q + lane);
+                        const uint32_t key = s_stage[wave][0][i];
+                        const uint32_t val = s_stage[wave][1][i];
+                        uint32_t fin;
+                        if constexpr (MODE == 0) {
+                            const uint32_t left = wave_shift_up1(val);
+                            fin = val - (lane == 0 ? before : left);
+                            const uint32_t in_group = cnt - (uint32_t)(64 * q);
+                            before = (uint32_t)__builtin_amdgcn_readlane((int)val,
+                                                                         in_group >= 64u ? 63 : (int)in_group - 1);
+                        } else {
+                            // the segment's first head finishes a run that started
+                            // before the segment: it adds the value carried in
+                            fin = (first_of_seg && i == 0u) ? f2u(u2f(seed_value) + u2f(val)) : val;
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
+                        if (!first_of_array || i > 0u)
+                            __builtin_amdgcn_raw_buffer_store_b32(fin, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0,
+                                                                  0);
                     }
-                    __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
-                    if (!first_of_array || i > 0u)
-                        __builtin_amdgcn_raw_buffer_store_b32(fin, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0,
-                                                              0);
                 }
             }
+            __builtin_amdgcn_wave_barrier();
+            run0 += cnt;
         }
-        __builtin_amdgcn_wave_barrier();
-        run0 += cnt;
     }
     if (holds_last && lane == 0) {
         const uint32_t base_run = heads_before > 0u ? heads_before - 1u : 0u;
@@ -399,9 +485,12 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr uint32_t TILE = W * SEG;
     __shared__ V s_wave[W];
     __shared__ V s_prefix;
-    // per wave: keys, then positions, of one chunk's heads by rank, then one
-    // spare slot per lane that the chunk's other elements write to
-    __shared__ uint32_t s_stage[W][2][CH + 64];
+    // per wave: keys, then positions, of the segment's heads (or of one
+    // chunk's) by rank, then one spare slot per lane that the other elements
+    // write to
+    constexpr uint32_t PRE = SEG < 2048u ? 0u : (SEG < kRunPreHeads ? SEG : kRunPreHeads);
+    constexpr uint32_t SLOTS = PRE > CH ? PRE : CH;
+    __shared__ uint32_t s_stage[W][2][SLOTS + 64];
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
@@ -511,6 +600,40 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
         }
         if (lane == 0) s_prefix = prefix;
     }
+    // a segment with few heads stages all of them now (key and position at
+    // the head's rank in the segment)
+    const bool pre = PRE > 0u && (SEG <= PRE || h_seg <= PRE);
+    uint32_t pos_lane = (uint32_t)lane * VEC;
+    asm volatile("" : "+v"(pos_lane));   // formed here, not held through the look-back
+    if (pre) {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+        uint32_t base = 0u;   // heads of the segment before chunk c (uniform)
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            bool hd[VEC];
+            uint64_t m[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+                m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+            }
+            uint32_t r = base;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t slot = hd[e] ? r : SLOTS + (uint32_t)lane;
+                s_stage[wave][0][slot] = k[c][e];
+                s_stage[wave][1][slot] = (uint32_t)(c * CH + e) + pos_lane;
+                r += hd[e] ? 1u : 0u;
+            }
+            base = uniform((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+        }
+    }
     __syncthreads();
     const V tile_prefix = s_prefix;
     const V seed = Op::combine(tile_prefix, wave_pre);
@@ -519,74 +642,96 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
     const uint32_t heads_before = uniform(tile_prefix.w[0]);
     const uint32_t tile_heads = uniform(agg.w[0]);
 
-    // second pass
-    uint32_t pos_lane = (uint32_t)lane * VEC;
-    asm volatile("" : "+v"(pos_lane));   // formed here, not held through the look-back
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
-    uint32_t run0 = seed_heads;          // run of the chunk's first head (uniform)
-    uint32_t before = 0u - seed_value;   // position of the head before the chunk's first head
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        bool hd[VEC];
-        uint64_t m[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
-            m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+    if (pre) {
+        // head i of the segment is run seed_heads + i: its key goes to
+        // unique_keys[seed_heads + i], and it finishes run seed_heads + i - 1
+        // (the array's first head finishes none, so its lane stores no length)
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + seed_heads, h_seg * 4u);
+        const bool first_of_array = seed_heads == 0u;
+        const uint32_t abase = uniform(first_of_array ? 0u : seed_heads - 1u);
+        const uint32_t arange = uniform(first_of_array ? (h_seg > 0u ? h_seg * 4u - 4u : 0u) : h_seg * 4u);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+        uint32_t before = 0u - seed_value;   // position of the head before this group's first
+        for (uint32_t g = 0u; g < h_seg; g += 64u) {
+            const uint32_t i = g + (uint32_t)lane;
+            const uint32_t key = s_stage[wave][0][i];
+            const uint32_t pos = s_stage[wave][1][i];
+            const uint32_t left = wave_shift_up1(pos);
+            const uint32_t len = pos - (lane == 0 ? before : left);
+            __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
+            if (!first_of_array || i > 0u)
+                __builtin_amdgcn_raw_buffer_store_b32(len, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0, 0);
+            before = (uint32_t)__builtin_amdgcn_readlane((int)pos, 63);
         }
-        // rank among the chunk's heads: heads in lower lanes, then the lane's
-        // own; every element writes, the others to their lane's spare slot
-        // (one write per element without a branch measured 2 to 3% faster at
-        // mean run 16 than writing the heads alone under an execution mask)
-        uint32_t r = 0u;
+    } else {
+        // the chunk path
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+        for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t slot = hd[e] ? r : CH + (uint32_t)lane;
-            s_stage[wave][0][slot] = k[c][e];
-            s_stage[wave][1][slot] = pos_lane + (uint32_t)e;
-            r += hd[e] ? 1u : 0u;
-        }
-        // the chunk's head count: lane 63's rank after its own heads
-        const uint32_t cnt = uniform((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
-        // the wave's LDS accesses run in order: the reads below see every
-        // lane's writes above (and the next chunk's writes follow the reads)
-        __builtin_amdgcn_wave_barrier();
-        if (cnt > 0u) {
-            // head q of the chunk is run run0 + q: its key goes to
-            // unique_keys[run0 + q], and it finishes run run0 + q - 1 (the
-            // array's first head finishes none, so its lane stores no length)
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
-            const bool first_of_array = run0 == 0u;
-            const uint32_t abase = uniform(first_of_array ? 0u : run0 - 1u);
-            const uint32_t arange = uniform(first_of_array ? cnt * 4u - 4u : cnt * 4u);
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+            for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(k[c][e]));
+        uint32_t run0 = seed_heads;          // run of the chunk's first head (uniform)
+        uint32_t before = 0u - seed_value;   // position of the head before the chunk's first head
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) {
-                if (cnt > (uint32_t)(64 * q)) {
-                    const uint32_t i = (uint32_t)(64 * q + lane);
-                    const uint32_t key = s_stage[wave][0][i];
-                    const uint32_t pos = s_stage[wave][1][i] + (uint32_t)(c * CH);
-                    const uint32_t left = wave_shift_up1(pos);
-                    const uint32_t len = pos - (lane == 0 ? before : left);
-                    __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
-                    if (!first_of_array || i > 0u)
-                        __builtin_amdgcn_raw_buffer_store_b32(len, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0,
-                                                              0);
-                    // the last head of this group of 64 is the next group's
-                    // (or the next chunk's) head before
-                    const uint32_t in_group = cnt - (uint32_t)(64 * q);
-                    before = (uint32_t)__builtin_amdgcn_readlane((int)pos, in_group >= 64u ? 63 : (int)in_group - 1);
+        for (int c = 0; c < CHUNKS; ++c) {
+            bool hd[VEC];
+            uint64_t m[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                hd[e] = k[c][e] != (e > 0 ? k[c][e - 1] : fprev[c]);
+                m[e] = __builtin_amdgcn_ballot_w64(hd[e]);
+            }
+            // rank among the chunk's heads: heads in lower lanes, then the lane's
+            // own; every element writes, the others to their lane's spare slot
+            // (one write per element without a branch measured 2 to 3% faster at
+            // mean run 16 than writing the heads alone under an execution mask)
+            uint32_t r = 0u;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], r));
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t slot = hd[e] ? r : CH + (uint32_t)lane;
+                s_stage[wave][0][slot] = k[c][e];
+                s_stage[wave][1][slot] = pos_lane + (uint32_t)e;
+                r += hd[e] ? 1u : 0u;
+            }
+            // the chunk's head count: lane 63's rank after its own heads
+            const uint32_t cnt = uniform((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+            // the wave's LDS accesses run in order: the reads below see every
+            // lane's writes above (and the next chunk's writes follow the reads)
+            __builtin_amdgcn_wave_barrier();
+            if (cnt > 0u) {
+                // head q of the chunk is run run0 + q: its key goes to
+                // unique_keys[run0 + q], and it finishes run run0 + q - 1 (the
+                // array's first head finishes none, so its lane stores no length)
+                const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.ukeys + run0, cnt * 4u);
+                const bool first_of_array = run0 == 0u;
+                const uint32_t abase = uniform(first_of_array ? 0u : run0 - 1u);
+                const uint32_t arange = uniform(first_of_array ? cnt * 4u - 4u : cnt * 4u);
+                const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aggs + abase, arange);
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) {
+                    if (cnt > (uint32_t)(64 * q)) {
+                        const uint32_t i = (uint32_t)(64 * q + lane);
+                        const uint32_t key = s_stage[wave][0][i];
+                        const uint32_t pos = s_stage[wave][1][i] + (uint32_t)(c * CH);
+                        const uint32_t left = wave_shift_up1(pos);
+                        const uint32_t len = pos - (lane == 0 ? before : left);
+                        __builtin_amdgcn_raw_buffer_store_b32(key, rk, (int)(i * 4u), 0, 0);
+                        if (!first_of_array || i > 0u)
+                            __builtin_amdgcn_raw_buffer_store_b32(len, ra, (int)((first_of_array ? i - 1u : i) * 4u), 0,
+                                                                  0);
+                        // the last head of this group of 64 is the next group's
+                        // (or the next chunk's) head before
+                        const uint32_t in_group = cnt - (uint32_t)(64 * q);
+                        before = (uint32_t)__builtin_amdgcn_readlane((int)pos,
+                                                                     in_group >= 64u ? 63 : (int)in_group - 1);
+                    }
                 }
             }
+            __builtin_amdgcn_wave_barrier();
+            run0 += cnt;
         }
-        __builtin_amdgcn_wave_barrier();
-        run0 += cnt;
     }
     if (holds_last && lane == 0) {
         // the array's last run has no head after it: its length is the value

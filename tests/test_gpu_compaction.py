@@ -152,6 +152,52 @@ def test_run_boundaries(gpu):
             _run_both(wl.run_keys(n, mean_run, seed=n + mean_run), vals, f"mean run {mean_run} n={n}")
 
 
+def _threshold_keys(n):
+    """Keys whose 4,096-element blocks (a run-length wave segment; two of
+    reduce-by-key's 2,048) cycle through head counts on either side of the
+    1,024 heads up to which a segment stages all of its heads before the
+    look-back: exactly 1,024 heads, 1,025, about 1,365 (random runs of 1 to
+    5), 4,096 (all distinct) and 1 (one run across the block, so the next
+    block's first run starts elsewhere)."""
+    rng = np.random.default_rng(n)
+    lengths = []
+    for b in range(n // 4096 + 1):
+        kind = b % 5
+        if kind == 0:
+            lengths += [4] * 1024
+        elif kind == 1:
+            lengths += [4] * 1023 + [2, 2]
+        elif kind == 2:
+            left = 4096
+            while left > 0:
+                r = int(min(left, rng.integers(1, 6)))
+                lengths.append(r)
+                left -= r
+        elif kind == 3:
+            lengths += [1] * 4096
+        else:
+            lengths.append(4096)
+    run = np.repeat(np.arange(len(lengths), dtype=np.uint64), lengths)[:n]
+    return ((run * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+
+
+def test_stage_threshold(gpu):
+    # wave segments on both sides of the staging threshold inside the same
+    # tiles, with runs that cross segments, waves and tiles; integer and fp32
+    # sums and run lengths
+    import torch
+    for n in ((1 << 22) + 3 * 4096 + 5, (1 << 25) + 7):
+        keys = _threshold_keys(n)
+        note(f"staging threshold n={n}")
+        _run_both(keys, wl.generate("u32_full", n, n + 11), f"threshold n={n}")
+        vals = wl.generate("f32_pm1", n, n + 12)
+        kd, vd, uk, ag, cnt = _dev(keys), _dev(vals), _empty(n), _empty(n), _count()
+        st = dws.load_library().dws_reduce_by_key(kd.data_ptr(), vd.data_ptr(), uk.data_ptr(), ag.data_ptr(), n,
+                                                  dws.FLOAT32, cnt.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == dws.OK, dws.status_string(st)
+        _check_runs(f"threshold fp32 n={n}", keys, uk.cpu().numpy(), ag.cpu().numpy(), int(cnt.item()), vals)
+
+
 def test_reduce_by_key_unaligned_and_special_keys(gpu):
     import torch
     # keys and values one element off 16-byte alignment (scalar-load kernel),
