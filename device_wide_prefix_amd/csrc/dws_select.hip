@@ -39,8 +39,10 @@
 // Partition (section A5, partition-if) is the same kernel with one more
 // store: the rejected elements go to the back of the output in reverse input
 // order, element i to out[n - 1 - (number of rejected elements before i)],
-// which needs no total count. Those writes land past the input's unread part,
-// so the partition is never in place.
+// which needs no total count. A wave stages its rejected elements from the
+// back of its LDS stage, so they leave as one more contiguous block. Those
+// writes land past the input's unread part, so the partition is never in
+// place.
 #include <type_traits>
 
 #include "dws_device.hpp"
@@ -75,18 +77,10 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     __shared__ uint32_t s_draw, s_epoch;
     __shared__ uint32_t s_wave[W];
     __shared__ uint32_t s_prefix;
-    // Select stages the whole segment's selected elements by rank while wave
-    // 0 waits in the look-back (wave 0 after it), leaving only the stores for
-    // after it; measured 2.5% faster out of place and 5.8% in place at
-    // 2^30 - 12,345 elements, 2 and 4% at 2^25. A partition stages one chunk
-    // at a time after the look-back (its rejected elements, reversed, need a
-    // second array).
-    constexpr bool PRE = !PARTITION;
-    constexpr uint32_t SLOTS = PRE ? SEG : CH;
-    // per wave: the selected elements by rank (and, for a partition, the
-    // chunk's rejected elements, reversed), then one slot per lane that the
-    // other elements write to
-    __shared__ uint32_t s_stage[W][PARTITION ? 2 : 1][SLOTS + 64];
+    // per wave: the segment's selected elements by rank from the front (a
+    // partition's rejected elements by rank from the back), then one spare
+    // slot per lane that elements past n write to
+    __shared__ uint32_t s_stage[W][SEG + 64];
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
@@ -174,96 +168,48 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
         }
         if (lane == 0) s_prefix = prefix;
     }
-    if constexpr (PRE) {
-        // each selected element at its rank in the segment (r holds the
-        // exclusive scan of the segment's selection bits)
+    // While wave 0 waits in the look-back (wave 0 after it), every wave
+    // stages its segment: a selected element at its rank in the segment (r
+    // holds the exclusive scan of the selection bits), a partition's rejected
+    // element j of the segment at SEG - 1 - j. Only the stores are left for
+    // after the look-back. Against staging chunk by chunk after it, select
+    // measured 2.5% faster out of place and 5.8% in place at 2^30 - 12,345
+    // elements, 2 and 4% at 2^25.
+    const uint32_t seg_elems = seg_valid / 4u;
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c)
+    for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const bool sel = (selected >> (c * VEC + e)) & 1u;
-                s_stage[wave][0][sel ? r[c][e] : SLOTS + (uint32_t)lane] = x[c][e];
+        for (int e = 0; e < VEC; ++e) {
+            const bool sel = (selected >> (c * VEC + e)) & 1u;
+            uint32_t slot = sel ? r[c][e] : SEG + (uint32_t)lane;
+            if constexpr (PARTITION) {
+                const uint32_t idx = (uint32_t)(c * CH) + (uint32_t)(lane * VEC + e);
+                if (!sel && idx < seg_elems) slot = SEG - 1u - (idx - r[c][e]);
             }
-    }
+            s_stage[wave][slot] = x[c][e];
+        }
     __syncthreads();
     const uint32_t prefix = uniform(s_prefix);
-    if constexpr (PRE) {
-        // the segment's selected elements fill out[prefix + wave_pre ..): one
-        // lane-contiguous store per 64 of them
-        const uint32_t seg_n = uniform(seg_count);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.out + ((uint64_t)prefix + wave_pre), seg_n * 4u);
-        for (uint32_t g = 0u; g < seg_n; g += 64u) {
-            const uint32_t i = g + (uint32_t)lane;
-            __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][0][i], rs, (int)(i * 4u), 0, 0);
-        }
-        if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.count = (unsigned long long)prefix + count;
-        return;
+    // the segment's selected elements fill out[prefix + wave_pre ..): one
+    // lane-contiguous store per 64 of them
+    const uint32_t seg_n = uniform(seg_count);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.out + ((uint64_t)prefix + wave_pre), seg_n * 4u);
+    for (uint32_t g = 0u; g < seg_n; g += 64u) {
+        const uint32_t i = g + (uint32_t)lane;
+        __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][i], rs, (int)(i * 4u), 0, 0);
     }
-
-    // A partition's stores, chunk by chunk. The selected elements of one
-    // chunk of a wave (64 x VEC elements) have consecutive ranks, so they fill
-    // one contiguous range of the output: each writes itself into the wave's
-    // LDS stage at its rank within the chunk, and the wave stores the range
-    // with lane-contiguous dword stores, one instruction per 64 elements. The
-    // rejected elements of the chunk fill one contiguous range at the back in
-    // reverse order, staged reversed the same way.
-    const uint64_t tile_first = (uint64_t)tile * TILE;
-    const uint64_t left = p.n - tile_first;
-    const uint32_t valid_local = left < TILE ? (uint32_t)left : TILE;
-    const uint64_t rejected_before = tile_first - prefix;
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        const uint32_t sel_before = uniform(r[c][0]);   // lane 0: selected in the segment before chunk c
-        const uint32_t chunk_local = (uint32_t)wave * SEG + (uint32_t)c * CH;
-        uint32_t csel = 0u;
-        bool sel[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            sel[e] = (selected >> (c * VEC + e)) & 1u;
-            csel += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(sel[e]));
+    if constexpr (PARTITION) {
+        // the segment's rejected elements, rejected ranks rb .. rb + rej - 1
+        // of the array, go to out[n - 1 - rank]: one contiguous block
+        // starting at n - rb - rej, in the order they sit in slots
+        // SEG - rej .. SEG - 1
+        const uint32_t rej = uniform(seg_elems - seg_n);
+        const uint64_t rb = seg_first - ((uint64_t)prefix + wave_pre);   // rejected before the segment
+        const __amdgpu_buffer_rsrc_t rj = make_rsrc(p.out + (p.n - rb - rej), rej * 4u);
+        for (uint32_t g = 0u; g < rej; g += 64u) {
+            const uint32_t i = g + (uint32_t)lane;
+            __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][SEG - rej + i], rj, (int)(i * 4u), 0, 0);
         }
-        csel = uniform(csel);
-        const uint32_t valid_c = valid_local > chunk_local ? (valid_local - chunk_local < CH ? valid_local - chunk_local
-                                                                                          : CH)
-                                                           : 0u;
-        const uint32_t crej = valid_c - csel;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t in_chunk = (uint32_t)(lane * VEC + e);
-            const uint32_t rank = r[c][e] - sel_before;   // selected before it in the chunk
-            s_stage[wave][0][sel[e] ? rank : CH + (uint32_t)lane] = x[c][e];
-            if constexpr (PARTITION) {
-                const uint32_t j = in_chunk - rank;         // rejected before it in the chunk
-                const bool rej = !sel[e] && in_chunk < valid_c;
-                s_stage[wave][1][rej ? crej - 1u - j : CH + (uint32_t)lane] = x[c][e];
-            }
-        }
-        // the wave's LDS accesses run in order: the reads below see every
-        // lane's writes above (and the next chunk's writes follow the reads)
-        __builtin_amdgcn_wave_barrier();
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.out + ((uint64_t)prefix + wave_pre + sel_before), csel * 4u);
-#pragma unroll
-        for (int q = 0; q < (int)(CH / 64u); ++q) {
-            if (csel > (uint32_t)(64 * q)) {
-                const uint32_t i = (uint32_t)(64 * q + lane);
-                __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][0][i], rs, (int)(i * 4u), 0, 0);
-            }
-        }
-        if constexpr (PARTITION) {
-            // tile rejected ranks rr0 .. rr0 + crej - 1 land at the back in
-            // reverse: element index n - rejected_before - 1 - rr, so the
-            // chunk's block starts at n - rejected_before - rr0 - crej
-            const uint32_t rr0 = chunk_local - (wave_pre + sel_before);
-            const __amdgpu_buffer_rsrc_t rj = make_rsrc(p.out + (p.n - rejected_before - rr0 - crej), crej * 4u);
-#pragma unroll
-            for (int q = 0; q < (int)(CH / 64u); ++q) {
-                if (crej > (uint32_t)(64 * q)) {
-                    const uint32_t i = (uint32_t)(64 * q + lane);
-                    __builtin_amdgcn_raw_buffer_store_b32(s_stage[wave][1][i], rj, (int)(i * 4u), 0, 0);
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
     }
     if (tile == p.num_tiles - 1u && threadIdx.x == 0) *p.count = (unsigned long long)prefix + count;
 }
@@ -335,7 +281,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     if (a.partition)
         fn = drawn ? select_kernel<true, kTileDrawn, true>(s) : select_kernel<true, kTileDispatch>(s);
     else if (alias)
-        fn = drawn ? select_kernel<false, kTileDrawn, true, true>(s) : select_kernel<false, kTileDispatch, false, true>(s);
+        fn = drawn ? select_kernel<false, kTileDrawn, true, true>(s)
+                   : select_kernel<false, kTileDispatch, false, true>(s);
     else
         fn = drawn ? select_kernel<false, kTileDrawn, true>(s) : select_kernel<false, kTileDispatch>(s);
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
