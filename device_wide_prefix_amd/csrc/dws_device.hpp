@@ -338,7 +338,12 @@ __device__ __forceinline__ uint32_t draw_tile(unsigned long long* counter, uint3
 // K independent loads per lane in flight at once. The nearest P is the lowest
 // lane of the lowest slot that holds one. If any descriptor from tile - 1 back
 // to that P (or back through the whole window when there is none) is still X,
-// the window is polled again. Otherwise those descriptors' values are summed
+// the window is polled again. With RELOAD_ALL false the poll reloads only
+// those X descriptors (the others keep what they read: an A stays a valid
+// aggregate, a P a valid prefix); that measured 1.2 to 1.7% faster for the
+// compaction on the 2^30 - 12,345 flags and the workgroup-index scan of 2^26
+// elements, and 0.9% slower for the drawn-index scan of 2^28, which reloads
+// the whole window. Otherwise those descriptors' values are summed
 // into the running exclusive prefix (aggregates of the A tiles plus the
 // inclusive prefix of the nearest P); with a P the look-back ends, without one
 // the window slides back by 64 K. Indices below 0 read as P with value 0, so
@@ -353,7 +358,7 @@ __device__ __forceinline__ uint32_t draw_tile(unsigned long long* counter, uint3
 //
 // Back-off: a blocked window is polled again at once, then after the pause
 // of level `backoff` (lookback_pause) before every further poll.
-template <class T, int ORDER, int K>
+template <class T, int ORDER, int K, bool RELOAD_ALL = false>
 __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t epoch,
                                unsigned int* watchdog, uint32_t backoff = 0u)
 {
@@ -363,12 +368,19 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
     int64_t hi = (int64_t)tile - 1;
     const uint64_t t0 = realtime();
     bool repolled = false;
+    uint64_t d[K];
+    // lanes of each slot that the next poll loads: all of a new window; after
+    // a blocked poll only the descriptors still awaited (the rest keep what
+    // they read: an A stays a valid aggregate, a P a valid prefix)
+    uint64_t reload[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) reload[j] = ~0ull;
     for (;;) {
-        uint64_t d[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int64_t idx = hi - (int64_t)(j * 64 + lane);
-            d[j] = (idx >= 0) ? desc_load<ORDER>(desc_at(desc, (uint64_t)idx)) : desc_pack(epoch, kStatusP, 0u);
+            if (reload[j] & lane_bit)
+                d[j] = (idx >= 0) ? desc_load<ORDER>(desc_at(desc, (uint64_t)idx)) : desc_pack(epoch, kStatusP, 0u);
         }
         uint64_t has_p[K], has_x[K];
 #pragma unroll
@@ -402,7 +414,13 @@ __device__ T lookback_decoupled(const uint64_t* desc, uint32_t tile, uint32_t ep
             prefix = prefix + wave_sum(v);
             if (jp < K) return prefix;
             hi -= 64 * K;
+#pragma unroll
+            for (int j = 0; j < K; ++j) reload[j] = ~0ull;
             continue;
+        }
+        if constexpr (!RELOAD_ALL) {
+#pragma unroll
+            for (int j = 0; j < K; ++j) reload[j] = j < jp ? has_x[j] : (j == jp ? has_x[j] & need_p : 0ull);
         }
         if (realtime() - t0 > kWatchdogTicks) {
             if (lane == 0) atomicAdd(watchdog, 1u);

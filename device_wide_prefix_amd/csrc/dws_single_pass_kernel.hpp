@@ -106,8 +106,8 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)
                         desc_store<ORDER>(desc_at(p.desc, tile), desc_pack(epoch, kStatusA, Elem<T>::bits(agg)));
-                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots>(p.desc, tile, epoch, p.watchdog,
-                                                                          p.backoff);
+                    prefix = lookback_decoupled<T, ORDER, kLookbackSlots, TILE_INDEX == kTileDrawn>(
+                        p.desc, tile, epoch, p.watchdog, p.backoff);
                 } else {
                     prefix = lookback_chained<T, ORDER>(p.desc, tile, epoch, p.watchdog);
                 }
