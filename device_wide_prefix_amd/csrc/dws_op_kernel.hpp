@@ -329,6 +329,19 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
 #pragma unroll
     for (int j = 0; j < K; ++j) reload[j] = ~0ull;
     for (;;) {
+        // every slot's loads are issued before any is examined: one round
+        // trip per poll whatever K is
+        uint64_t wd[K][W];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t idx = hi - (int64_t)(j * 64 + lane);
+#pragma unroll
+            for (int k = 0; k < W; ++k) wd[j][k] = 0ull;
+            if ((reload[j] & lane_bit) && idx >= 0) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) wd[j][k] = desc_load<kOrderRelaxed>(desc_at(desc, (uint64_t)idx) + k);
+            }
+        }
         uint64_t has_p[K], has_x[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -337,15 +350,12 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
                 st[j] = kStatusP;
                 d[j] = Op::identity();
                 if (idx >= 0) {
-                    uint64_t wd[W];
-#pragma unroll
-                    for (int k = 0; k < W; ++k) wd[k] = desc_load<kOrderRelaxed>(desc_at(desc, (uint64_t)idx) + k);
-                    st[j] = desc_status(wd[0], epoch);
+                    st[j] = desc_status(wd[j][0], epoch);
 #pragma unroll
                     for (int k = 1; k < W; ++k)
-                        if ((wd[k] >> 32) != (wd[0] >> 32)) st[j] = kStatusX;
+                        if ((wd[j][k] >> 32) != (wd[j][0] >> 32)) st[j] = kStatusX;
 #pragma unroll
-                    for (int k = 0; k < W; ++k) d[j].w[k] = (uint32_t)wd[k];
+                    for (int k = 0; k < W; ++k) d[j].w[k] = (uint32_t)wd[j][k];
                 }
             }
             has_p[j] = __builtin_amdgcn_ballot_w64(st[j] == kStatusP);

@@ -56,12 +56,15 @@ struct RbkParams {
     uint32_t backoff;         // pause level between blocked look-back polls (kPause*)
 };
 
-// Look-back slots per lane for the run kernels: one, 64 predecessors per
-// poll. Against two slots (whose loads wait one after the other here, two
-// round trips per poll) it measured 1.4 to 2.8% faster at 2^25 keys with mean
-// run 16 and equal with all keys distinct, and 2.2 to 6% faster at 2^28. More
-// slots do not fit: with four, the kernels spill registers to scratch memory.
-constexpr int kRunLookbackSlots = 1;
+// Look-back slots per lane for the run kernels, with every slot's loads issued
+// before any is examined (one round trip per poll): two, 128 predecessors per
+// poll, for run-length encoding and integer sums. Against one slot, alternating
+// builds at 2^25 keys (three runs each): run-length encoding 1.5% faster at mean
+// run 16 and 0.9% with all keys distinct, integer sums 0.8 to 1% faster. The
+// fp32 sums kernel measured 1.4% slower with two slots with all keys distinct
+// (equal at mean run 16) and keeps one. Four slots spill registers.
+constexpr int kRunLookbackSlots = 2;
+constexpr int kRunF32LookbackSlots = 1;
 
 // A wave segment of the large shapes (2,048 elements or more) with at most
 // this many heads stages all of them in LDS right after publishing its
@@ -285,7 +288,8 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
                 if (lane == 0) desc_store_val<2>(p.desc, 0u, epoch, kStatusP, agg);
             } else {
                 if (lane == 0) desc_store_val<2>(p.desc, tile, epoch, kStatusA, agg);
-                prefix = lookback_op<Op, kRunLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.backoff);
+                constexpr int K = MODE == 1 ? kRunF32LookbackSlots : kRunLookbackSlots;
+                prefix = lookback_op<Op, K>(p.desc, tile, epoch, p.watchdog, p.backoff);
                 if (lane == 0) {
                     desc_store_val<2>(p.desc, tile, epoch, kStatusP, Op::combine(prefix, agg));
                     if (tile == p.num_tiles - 1u) advance_epoch(p.epoch, epoch);
