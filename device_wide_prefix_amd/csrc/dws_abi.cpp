@@ -233,24 +233,32 @@ dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool
     const bool aligned = aligned16(in, out);
     // non-temporal loads are a hint, built for aligned pointers only: 1 asks
     // for them, 2 never uses them, 0 leaves it to the library, which uses them
-    // on the automatic drawn relaxed single pass from kNtLoadMin elements, or
-    // from kNtLoadOutOfPlaceMin when the output is another buffer
+    // on the automatic relaxed single pass from kNtLoadMin elements
     bool nt = false;
     if (o.nontemporal == 1) {
         nt = aligned;
     } else if (o.nontemporal == 0) {
-        const uint64_t nt_min = in == out ? kNtLoadMin : kNtLoadOutOfPlaceMin;
-        nt = aligned && n >= nt_min && o.tile_shape == 0 && mode == kModeDecoupled &&
-             o.memory_order == DWS_ORDER_RELAXED && o.tile_index != DWS_TILE_DISPATCH;
+        nt = aligned && n >= kNtLoadMin && o.tile_shape == 0 && mode == kModeDecoupled &&
+             o.memory_order == DWS_ORDER_RELAXED;
     }
     const int shape = resolve_shape(o.tile_shape, n, aligned);
     if (shape < 0) return DWS_ERR_INVALID_ARG;
     // automatic: the workgroup index below kAutoDrawnMin elements where that
-    // kernel is built (relaxed decoupled look-back, no non-temporal access)
+    // kernel is built (relaxed decoupled look-back)
     int tile_index = o.tile_index == DWS_TILE_DISPATCH ? kTileDispatch : kTileDrawn;
-    if (o.tile_index == DWS_TILE_AUTO && mode == kModeDecoupled && o.memory_order == DWS_ORDER_RELAXED && !nt)
+    if (o.tile_index == DWS_TILE_AUTO && mode == kModeDecoupled && o.memory_order == DWS_ORDER_RELAXED)
         tile_index = auto_tile_index(n);
-    const int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt, tile_index, stamps != nullptr);
+    const bool instr = stamps != nullptr;
+    int cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt, tile_index, instr);
+    // the workgroup index has non-temporal kernels for the 32,768- and
+    // 65,536-element tiles only: elsewhere non-temporal loads asked for with
+    // the automatic tile index take the drawn index, and the library's own
+    // choice with a forced workgroup index drops them
+    if (cfg < 0 && nt && tile_index == kTileDispatch) {
+        if (o.tile_index == DWS_TILE_AUTO) tile_index = kTileDrawn;
+        else if (o.nontemporal == 0) nt = false;
+        cfg = find_single_pass_cfg(shape, aligned, o.memory_order, mode, nt, tile_index, instr);
+    }
     if (cfg < 0) return DWS_ERR_UNSUPPORTED;
     const TileShape ts = cfg_shape(kCfgs[cfg]);
     const uint64_t num_tiles = ceil_div(n, (uint64_t)ts.elems());

@@ -113,18 +113,17 @@ constexpr uint64_t kScanBackoffMin = (uint64_t)1 << 27;
 
 constexpr uint32_t scan_backoff(uint64_t n) { return n >= kScanBackoffMin ? kPause64 : kPauseShort; }
 // From here the automatic choice loads the input with non-temporal loads (each
-// element is read once); stores stay ordinary. Measured on MI355X with the
-// 65,536-element drawn kernel, alternating builds on two MI355X GPUs: 3.4 to
-// 3.9% faster at 2^28 elements, 3.0 to 3.2% at 2^29, 3.3% at 2^30; with spread
-// descriptors 0.7% faster at 2^27 in place and 5% out of place. Below 2^27 the
-// workgroup-index kernel (built without them) is faster still. Non-temporal
-// stores, alone or with the loads, were slower at every size measured. The
-// generic operators, select, partition and the run kernels measured faster
-// from 2^25 elements and load non-temporally from there (with their drawn or
-// large-tile kernels).
-constexpr uint64_t kNtLoadMin = (uint64_t)1 << 27;
-// The same threshold when the output is another buffer.
-constexpr uint64_t kNtLoadOutOfPlaceMin = (uint64_t)1 << 27;
+// element is read once), in place or not; stores stay ordinary. Measured on
+// MI355X: with the 65,536-element drawn kernel, alternating builds on two
+// GPUs, 3.4 to 3.9% faster at 2^28 elements, 3.0 to 3.2% at 2^29, 3.3% at 2^30;
+// with descriptors 64 bytes apart and the workgroup index (cold caches, three
+// rounds of 30 to 40 calls), 2.5 to 3.5% faster at 2^23 (32,768-element
+// tiles), 2% at 2^24, 4.5% at 2^25, 2.7% at 2^26 in place and 4.9% out of
+// place, and equal at 2^20 to 2^22. Non-temporal stores, alone or with the
+// loads, were slower at every size measured. The generic operators, select,
+// partition and the run kernels measured faster from 2^25 elements and load
+// non-temporally from there (with their drawn or large-tile kernels).
+constexpr uint64_t kNtLoadMin = (uint64_t)1 << 23;
 
 constexpr int auto_shape(uint64_t n)
 {
@@ -181,6 +180,10 @@ constexpr KernelCfg kCfgs[] = {
     // with scalar loads
     DWS_DISPATCH(0, 4), DWS_DISPATCH(1, 4), DWS_DISPATCH(2, 4), DWS_DISPATCH(3, 4), DWS_DISPATCH(4, 4),
     DWS_DISPATCH(5, 4), DWS_DISPATCH(0, 1), DWS_DISPATCH(2, 1), DWS_DISPATCH(4, 1), DWS_DISPATCH(5, 1),
+    // the same with non-temporal loads: the automatic choice from kNtLoadMin
+    // below kAutoDrawnMin (32,768- and 65,536-element tiles)
+    {4, 4, kOrderRelaxed, kModeDecoupled, true, kTileDispatch},
+    {5, 4, kOrderRelaxed, kModeDecoupled, true, kTileDispatch},
     // instrumented (time stamps), aligned automatic shapes, both sources
     {0, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
     {2, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
@@ -191,6 +194,8 @@ constexpr KernelCfg kCfgs[] = {
     {2, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
     {4, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
     {5, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
+    {4, 4, kOrderRelaxed, kModeDecoupled, true, kTileDispatch, true},
+    {5, 4, kOrderRelaxed, kModeDecoupled, true, kTileDispatch, true},
 };
 #undef DWS_AUTO_SHAPES
 #undef DWS_DISPATCH

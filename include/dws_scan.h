@@ -149,7 +149,9 @@ typedef enum dws_memory_order {
 /* Where a tile's index comes from in the single-pass and chained kernels. */
 typedef enum dws_tile_index {
     /* the library's choice: DWS_TILE_DISPATCH below 2^27 elements for the
-     * relaxed single pass without non-temporal access, else DWS_TILE_DRAWN */
+     * relaxed single pass (non-temporal loads asked for on a shape whose
+     * workgroup-index kernel has none take DWS_TILE_DRAWN), else
+     * DWS_TILE_DRAWN */
     DWS_TILE_AUTO = 0,
     /* one atomic add on a device-wide counter per workgroup, in the order the
      * workgroups start (PMPP 11.3 notes, dynamic block index; Merrill &
@@ -173,8 +175,8 @@ typedef struct dws_options {
                            the single-pass kernel, for sweeps */
     int nontemporal;    /* non-temporal (streaming) loads of the input:
                            0 = the library's choice (for the automatic
-                           single pass: on from 2^28 elements in place,
-                           from 2^26 out of place),
+                           relaxed single pass: on from 2^23 elements,
+                           in place or not),
                            1 = on, 2 = off; stores are never
                            non-temporal */
     int tile_index;     /* dws_tile_index; default DWS_TILE_AUTO */
@@ -202,7 +204,8 @@ dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
  *   reduce-then-scan, scan-then-propagate: tile_shape 0, nontemporal 0
  *                or 2, tile_index 0 (memory_order ignored);
  *   DWS_TILE_DISPATCH: single pass with relaxed order, every tile_shape,
- *                nontemporal 0 or 2.
+ *                nontemporal 0 or 2; nontemporal 1 with the automatic
+ *                32768- and 65536-element shapes.
  * Pointers that are not both 16-byte aligned use scalar loads; a forced
  * shape without a scalar-load kernel then falls back to the automatic one,
  * and nontemporal is ignored.

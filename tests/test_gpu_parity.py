@@ -66,8 +66,8 @@ def test_wave_primitives_lane_layout(gpu, dtype):
 # ---------------------------------------------------------------------------
 # sizes around wave and tile boundaries of every automatic tile size (4096
 # below 2^20, 16384 from 2^20, 32768 from 2^23, 65536 from 2^24), around the
-# back-off switch at 2^25 and the switch from workgroup-index tiles to drawn
-# tiles with non-temporal loads at 2^27
+# switch to non-temporal loads at 2^23 and the switch from workgroup-index
+# tiles to drawn tiles with the 64-unit back-off at 2^27
 M, L, H = 16384, 32768, 65536
 EDGE_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, TILE - 1, TILE, TILE + 1,
               2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 255 * TILE + 3,
@@ -224,6 +224,19 @@ def test_order_and_nontemporal(gpu, opts):
     x = wl.random_input("float32", 3 * TILE + 1, seed=1)
     y = _roundtrip(x, "float32", True, offset=1, **opts)   # non-temporal is a hint; unaligned ignores it
     check(x, y, "float32", True)
+
+
+def test_dispatch_nontemporal(gpu):
+    # non-temporal loads with the workgroup index, built for the 32,768- and
+    # 65,536-element tiles: the automatic choice from 2^23 elements, here also
+    # asked for explicitly, in and out of place, with ragged last tiles
+    for n in ((1 << 23) + 5, (1 << 24) - 3, (1 << 25) + 65536 + 7):
+        for dtype in DTYPES:
+            for exclusive in (False, True):
+                note(f"dispatch non-temporal dtype={dtype} excl={exclusive} n={n}")
+                x = wl.random_input(dtype, n, seed=n + 11)
+                y = _roundtrip(x, dtype, exclusive, in_place=exclusive, nt=1, tile_index=dws.TILE_DISPATCH)
+                check(x, y, dtype, exclusive, label=f"dispatch nt n={n}")
 
 
 # ---------------------------------------------------------------------------
