@@ -693,7 +693,7 @@ def main():
     ap.add_argument("--order", default="relaxed", choices=sorted(ORDERS))
     ap.add_argument("--tile-shape", type=int, default=0)
     ap.add_argument("--nontemporal", default="auto", choices=sorted(NONTEMPORAL),
-                    help="non-temporal loads: the library's choice (on from 2^28 elements), on or off")
+                    help="non-temporal loads: the library's choice (on from 2^23 elements), on or off")
     ap.add_argument("--tile-index", default="auto", choices=sorted(TILE_INDEX))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",

@@ -243,8 +243,8 @@ dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool
     }
     const int shape = resolve_shape(o.tile_shape, n, aligned);
     if (shape < 0) return DWS_ERR_INVALID_ARG;
-    // automatic: the workgroup index below kAutoDrawnMin elements where that
-    // kernel is built (relaxed decoupled look-back)
+    // automatic: the workgroup index where that kernel is built (relaxed
+    // decoupled look-back)
     int tile_index = o.tile_index == DWS_TILE_DISPATCH ? kTileDispatch : kTileDrawn;
     if (o.tile_index == DWS_TILE_AUTO && mode == kModeDecoupled && o.memory_order == DWS_ORDER_RELAXED)
         tile_index = auto_tile_index(n);
@@ -270,7 +270,7 @@ dws_status plan_single_pass(const void* in, void* out, size_t n, int dtype, bool
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
     p.stamps = stamps;
-    p.backoff = scan_backoff(n);
+    p.backoff = scan_backoff(n, kCfgs[cfg].tile_index);
     plan->cfg = cfg;
     plan->f32 = kind_of(dtype) == kKindF32;
     plan->exclusive = excl;
@@ -432,19 +432,18 @@ int op_kind(int dtype, int op)
     }
 }
 
-hipError_t launch_op_kind(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
-                          hipStream_t stream)
+hipError_t launch_op_kind(int kind, bool exclusive, int shape, bool nt, const OpScanParams& p, hipStream_t stream)
 {
     switch (kind) {
     case kOpMaxI32:
     case kOpMaxU32:
     case kOpMinI32:
-    case kOpMinU32: return launch_op_minmax(kind, exclusive, shape, tile_index, nt, p, stream);
+    case kOpMinU32: return launch_op_minmax(kind, exclusive, shape, nt, p, stream);
     case kOpSumPairIF:
-    case kOpSumPairU32: return launch_op_pairsum(kind, exclusive, shape, tile_index, nt, p, stream);
-    case kOpAffineU32: return launch_op_affine(kind, exclusive, shape, tile_index, nt, p, stream);
+    case kOpSumPairU32: return launch_op_pairsum(kind, exclusive, shape, nt, p, stream);
+    case kOpAffineU32: return launch_op_affine(kind, exclusive, shape, nt, p, stream);
     case kOpSegSumIF:
-    case kOpSegSumU32: return launch_op_segsum(kind, exclusive, shape, tile_index, nt, p, stream);
+    case kOpSegSumU32: return launch_op_segsum(kind, exclusive, shape, nt, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -454,11 +453,13 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     const int words = op_kind_words(kind);
     const bool aligned = aligned16(in, out);
     const int shape = op_auto_shape(n, aligned);
-    const int tile_index = (shape == kOpShapeLarge && n >= kOpDrawnMin) ? kTileDrawn : kTileDispatch;
-    // non-temporal loads with the drawn tile index (from 2^25 elements, the
-    // large shape): each input word is read once. Measured 2 to 3% faster on
-    // 128 and 256 MB inputs, 4.6 to 5.1% on 512 MB and 1 GiB.
-    const bool nt = tile_index == kTileDrawn;
+    // The tile index is the workgroup index. Non-temporal loads from kOpNtMin
+    // elements (the large shape): each input word is read once. With a drawn
+    // index they measured 2 to 3% faster on 128 and 256 MB inputs, 4.6 to
+    // 5.1% on 512 MB and 1 GiB; the workgroup index with them (and the short
+    // pause) then measured 5.6 to 7.3% faster than the drawn index with them
+    // on 1 GiB inputs (three alternating runs of whole library builds).
+    const bool nt = shape == kOpShapeLarge && n >= kOpNtMin;
     const uint64_t num_tiles = ceil_div(n, op_tile_elems(words, shape));
     if (num_tiles > 0xffffffffull || num_tiles * op_tile_threads(shape) > kMaxGridThreads)
         return DWS_ERR_UNSUPPORTED;
@@ -468,7 +469,7 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
     p.backoff = op_backoff(n);
-    if (num_tiles == 1) return from_hip(launch_op_kind(kind, excl, shape, tile_index, false, p, stream));
+    if (num_tiles == 1) return from_hip(launch_op_kind(kind, excl, shape, false, p, stream));
     Workspace* ws = nullptr;
     dws_status s = get_workspace(stream, &ws);
     if (s != DWS_OK) return s;
@@ -479,9 +480,8 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     if (s != DWS_OK) return s;
     p.epoch = ws->epoch();
     p.desc = ws->desc;
-    p.counter = ws->counter();
     p.watchdog = ws->watchdog();
-    return from_hip(launch_op_kind(kind, excl, shape, tile_index, nt, p, stream));
+    return from_hip(launch_op_kind(kind, excl, shape, nt, p, stream));
 }
 
 }  // namespace

@@ -4,11 +4,11 @@
 
 namespace dws {
 
-hipError_t launch_op_affine(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
+hipError_t launch_op_affine(int kind, bool exclusive, int shape, bool nt, const OpScanParams& p,
                             hipStream_t stream)
 {
     if (kind != kOpAffineU32) return hipErrorInvalidValue;
-    return launch_op_typed<OpAffineU32>(exclusive, shape, tile_index, nt, p, stream);
+    return launch_op_typed<OpAffineU32>(exclusive, shape, nt, p, stream);
 }
 
 }  // namespace dws

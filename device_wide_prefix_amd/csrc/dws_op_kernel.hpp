@@ -406,7 +406,7 @@ __device__ typename Op::V lookback_op(const uint64_t* desc, uint32_t tile, uint3
 // The kernel. LOADW words per lane per chunk load (4: dwordx4), E = LOADW / W
 // elements per lane per chunk.
 // ---------------------------------------------------------------------------
-template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, int TILE_INDEX, bool NT = false>
+template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, bool NT = false>
 __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
 {
     using V = typename Op::V;
@@ -417,43 +417,24 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     constexpr uint32_t SEG = 64u * E * CHUNKS;
     constexpr uint32_t TILE = WAVES * SEG;
     constexpr uint32_t ESIZE = 4u * W;
-    __shared__ uint32_t s_draw, s_epoch;
     __shared__ V s_wave[WAVES];
     __shared__ V s_prefix;
 
     const int lane = lane_id();
     const int wave = (int)uniform(threadIdx.x >> 6);
     const bool multi = p.num_tiles > 1u;
-    // the descriptor epoch is read with the draw, or after the tile loads,
-    // so that it never costs a round trip of its own (needed only to publish)
+    // the descriptor epoch is read in wave 0 after the tile loads are issued:
+    // it is needed only to publish, and never costs a round trip of its own
     uint32_t epoch_v = 0u;
-
-    uint32_t tile = 0u;
-    if (multi) {
-        if constexpr (TILE_INDEX == kTileDispatch) {
-            tile = blockIdx.x;
-        } else {
-            if (threadIdx.x == 0) {
-                const uint32_t e = load_epoch_async(p.epoch);
-                s_draw = draw_tile(p.counter, p.num_tiles);
-                s_epoch = e;
-            }
-            __syncthreads();
-            tile = uniform(s_draw);
-            epoch_v = s_epoch;
-            if (tile >= p.num_tiles) {   // counter not put back to 0: never index past the grid
-                if (threadIdx.x == 0) atomicAdd(p.watchdog, 1u);
-                return;
-            }
-        }
-    }
+    // the tile index is the workgroup index (each XCD starts its workgroups
+    // in index order; the watchdog bounds every wait)
+    const uint32_t tile = multi ? (uint32_t)blockIdx.x : 0u;
 
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t vb = valid_bytes_sized(seg_first, SEG, p.n, ESIZE);
     uint32_t raw[CHUNKS][LOADW];
     load_words<LOADW, CHUNKS, NT>(make_rsrc(static_cast<const char*>(p.in) + seg_first * ESIZE, vb), lane, raw);
-    if constexpr (TILE_INDEX == kTileDispatch)
-        if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
+    if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
 
     V x[CHUNKS][E];
 #pragma unroll
@@ -515,39 +496,37 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
 // Shapes and launch. Shapes are (threads, words per load, loads per lane);
 // the unaligned shape loads one element per access.
 // ---------------------------------------------------------------------------
-template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, int TILE_INDEX, bool NT = false>
+template <class Op, bool EXCL, int BLOCK, int LOADW, int CHUNKS, bool NT = false>
 static hipError_t launch_op_shape(const OpScanParams& p, hipStream_t stream)
 {
     OpScanParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_scan_op<Op, EXCL, BLOCK, LOADW, CHUNKS, TILE_INDEX, NT>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_scan_op<Op, EXCL, BLOCK, LOADW, CHUNKS, NT>),
                            dim3(p.num_tiles), dim3(BLOCK), args, 0, stream);
 }
 
 template <class Op, bool EXCL>
-static hipError_t launch_op_excl(int shape, int tile_index, bool nt, const OpScanParams& p, hipStream_t stream)
+static hipError_t launch_op_excl(int shape, bool nt, const OpScanParams& p, hipStream_t stream)
 {
     constexpr int W = Op::kWords;
     switch (shape) {
-    case kOpShapeSmall: return launch_op_shape<Op, EXCL, 256, 4, 4, kTileDispatch>(p, stream);
-    case kOpShapeMedium: return launch_op_shape<Op, EXCL, 512, 4, 8, kTileDispatch>(p, stream);
+    case kOpShapeSmall: return launch_op_shape<Op, EXCL, 256, 4, 4>(p, stream);
+    case kOpShapeMedium: return launch_op_shape<Op, EXCL, 512, 4, 8>(p, stream);
     case kOpShapeLarge:
-        // non-temporal loads are built for the drawn large shape only, which
-        // the caller uses from 2^25 elements
-        if (tile_index == kTileDrawn)
-            return nt ? launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn, true>(p, stream)
-                      : launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDrawn>(p, stream);
-        return launch_op_shape<Op, EXCL, 1024, 4, 16, kTileDispatch>(p, stream);
-    case kOpShapeUnaligned: return launch_op_shape<Op, EXCL, 256, W, 16, kTileDispatch>(p, stream);
+        // non-temporal loads are built for the large shape only, which the
+        // caller uses them with from kOpNtMin elements
+        return nt ? launch_op_shape<Op, EXCL, 1024, 4, 16, true>(p, stream)
+                  : launch_op_shape<Op, EXCL, 1024, 4, 16>(p, stream);
+    case kOpShapeUnaligned: return launch_op_shape<Op, EXCL, 256, W, 16>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <class Op>
-hipError_t launch_op_typed(bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p, hipStream_t stream)
+hipError_t launch_op_typed(bool exclusive, int shape, bool nt, const OpScanParams& p, hipStream_t stream)
 {
-    return exclusive ? launch_op_excl<Op, true>(shape, tile_index, nt, p, stream)
-                     : launch_op_excl<Op, false>(shape, tile_index, nt, p, stream);
+    return exclusive ? launch_op_excl<Op, true>(shape, nt, p, stream)
+                     : launch_op_excl<Op, false>(shape, nt, p, stream);
 }
 
 }  // namespace dws

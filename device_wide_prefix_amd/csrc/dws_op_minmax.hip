@@ -4,14 +4,14 @@
 
 namespace dws {
 
-hipError_t launch_op_minmax(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
+hipError_t launch_op_minmax(int kind, bool exclusive, int shape, bool nt, const OpScanParams& p,
                             hipStream_t stream)
 {
     switch (kind) {
-    case kOpMaxI32: return launch_op_typed<OpMaxI32>(exclusive, shape, tile_index, nt, p, stream);
-    case kOpMaxU32: return launch_op_typed<OpMaxU32>(exclusive, shape, tile_index, nt, p, stream);
-    case kOpMinI32: return launch_op_typed<OpMinI32>(exclusive, shape, tile_index, nt, p, stream);
-    case kOpMinU32: return launch_op_typed<OpMinU32>(exclusive, shape, tile_index, nt, p, stream);
+    case kOpMaxI32: return launch_op_typed<OpMaxI32>(exclusive, shape, nt, p, stream);
+    case kOpMaxU32: return launch_op_typed<OpMaxU32>(exclusive, shape, nt, p, stream);
+    case kOpMinI32: return launch_op_typed<OpMinI32>(exclusive, shape, nt, p, stream);
+    case kOpMinU32: return launch_op_typed<OpMinU32>(exclusive, shape, nt, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -4,12 +4,12 @@
 
 namespace dws {
 
-hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
+hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, bool nt, const OpScanParams& p,
                              hipStream_t stream)
 {
     switch (kind) {
-    case kOpSumPairIF: return launch_op_typed<OpSumPairIF>(exclusive, shape, tile_index, nt, p, stream);
-    case kOpSumPairU32: return launch_op_typed<OpSumPairU32>(exclusive, shape, tile_index, nt, p, stream);
+    case kOpSumPairIF: return launch_op_typed<OpSumPairIF>(exclusive, shape, nt, p, stream);
+    case kOpSumPairU32: return launch_op_typed<OpSumPairU32>(exclusive, shape, nt, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

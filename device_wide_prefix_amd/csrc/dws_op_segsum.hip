@@ -4,12 +4,12 @@
 
 namespace dws {
 
-hipError_t launch_op_segsum(int kind, bool exclusive, int shape, int tile_index, bool nt, const OpScanParams& p,
+hipError_t launch_op_segsum(int kind, bool exclusive, int shape, bool nt, const OpScanParams& p,
                             hipStream_t stream)
 {
     switch (kind) {
-    case kOpSegSumIF: return launch_op_typed<OpSegSumIF>(exclusive, shape, tile_index, nt, p, stream);
-    case kOpSegSumU32: return launch_op_typed<OpSegSumU32>(exclusive, shape, tile_index, nt, p, stream);
+    case kOpSegSumIF: return launch_op_typed<OpSegSumIF>(exclusive, shape, nt, p, stream);
+    case kOpSegSumU32: return launch_op_typed<OpSegSumU32>(exclusive, shape, nt, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -85,19 +85,12 @@ constexpr TileShape kShapes[] = {
 };
 constexpr int kNumShapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
 
-// Automatic shape and tile index source, from a sweep of every shape with
-// both sources at n = 2^16 .. 2^28 on MI355X (fp32, exclusive, in place,
-// caches flushed): the best tile grows with n as long as every CU still gets
-// tiles. Below 2^27 elements (at most 2,048 tiles) the workgroup index is the
-// better tile index: no atomic on the critical path (with spread descriptors:
-// 1.5-2% faster than drawn at 2^25, 2-3% at 2^26). From 2^27 the drawn index
-// wins (3% at 2^27, 2-11% at 2^28 and up): many workgroups run one after
-// another on each CU, and a drawn index follows the order in which they
-// really start, so a tile rarely waits on a predecessor that started after it.
+// Automatic shape, from a sweep of every shape with both tile index sources
+// at n = 2^16 .. 2^28 on MI355X (fp32, exclusive, in place, caches flushed):
+// the best tile grows with n as long as every CU still gets tiles.
 constexpr uint64_t kAutoHugeMin = (uint64_t)1 << 24;    // 65536-element tiles
 constexpr uint64_t kAutoLargeMin = (uint64_t)1 << 23;   // 32768
 constexpr uint64_t kAutoMediumMin = (uint64_t)1 << 20;  // 16384 (512 threads)
-constexpr uint64_t kAutoDrawnMin = (uint64_t)1 << 27;   // drawn tile index from here
 // Back-off levels of a look-back that is still blocked after its first,
 // immediate re-poll (lookback_pause): 0 a short pause (s_sleep 1), then 64,
 // 127 or 190 units of 64 clocks before every further poll.
@@ -105,13 +98,17 @@ constexpr uint32_t kPauseShort = 0u;
 constexpr uint32_t kPause64 = 1u;
 constexpr uint32_t kPause127 = 2u;
 constexpr uint32_t kPause190 = 3u;
-// The + scan backs off from here, where tiles take a drawn index: 64 units,
-// the best of 16 / 32 / 64 / 127 at 2^27 to 2^30 with spread descriptors (127
-// equal). With the workgroup index (below 2^27) the short pause measured 1.3
-// to 3.4% faster than 64 units at 2^24, 2^25 and 2^26 elements.
+// A + scan with a drawn tile index backs off from here: 64 units, the best of
+// 16 / 32 / 64 / 127 at 2^27 to 2^30 with spread descriptors (127 equal). The
+// workgroup-index scan keeps the short pause at every size: 1.3 to 3.4% faster
+// than 64 units at 2^24 to 2^26 elements, 2% at 2^28 (6,540 against 6,413 GB/s,
+// three alternating runs each) and 0.7% at 2^30 - 12,345.
 constexpr uint64_t kScanBackoffMin = (uint64_t)1 << 27;
 
-constexpr uint32_t scan_backoff(uint64_t n) { return n >= kScanBackoffMin ? kPause64 : kPauseShort; }
+constexpr uint32_t scan_backoff(uint64_t n, int tile_index)
+{
+    return tile_index == kTileDrawn && n >= kScanBackoffMin ? kPause64 : kPauseShort;
+}
 // From here the automatic choice loads the input with non-temporal loads (each
 // element is read once), in place or not; stores stay ordinary. Measured on
 // MI355X: with the 65,536-element drawn kernel, alternating builds on two
@@ -122,7 +119,7 @@ constexpr uint32_t scan_backoff(uint64_t n) { return n >= kScanBackoffMin ? kPau
 // place, and equal at 2^20 to 2^22. Non-temporal stores, alone or with the
 // loads, were slower at every size measured. The generic operators, select,
 // partition and the run kernels measured faster from 2^25 elements and load
-// non-temporally from there (with their drawn or large-tile kernels).
+// non-temporally from there (with their large-tile kernels).
 constexpr uint64_t kNtLoadMin = (uint64_t)1 << 23;
 
 constexpr int auto_shape(uint64_t n)
@@ -130,7 +127,18 @@ constexpr int auto_shape(uint64_t n)
     return n >= kAutoHugeMin ? 5 : (n >= kAutoLargeMin ? 4 : (n >= kAutoMediumMin ? 2 : 0));
 }
 
-constexpr int auto_tile_index(uint64_t n) { return n >= kAutoDrawnMin ? kTileDrawn : kTileDispatch; }
+// Automatic tile index of the relaxed single pass: the workgroup index, at
+// every size. It needs no atomic on the critical path. With non-temporal loads
+// in both kernels it measured 4.4% faster than a drawn index at 2^28 elements
+// in place (6,540 against 6,265 GB/s, three alternating runs each) and 6.9% at
+// 2^30 - 12,345 (6,506 against 6,087), 1.5 to 3% at 2^25 and 2^26. Earlier
+// comparisons that favoured the drawn index from 2^27 set a drawn kernel with
+// non-temporal loads against a workgroup-index kernel without them. The
+// workgroup index relies on the GPU starting each XCD's workgroups in index
+// order (the lowest unfinished tile is then always running); the watchdog
+// bounds every wait. The drawn index stays selectable (DWS_TILE_DRAWN), and
+// the chained and release/acquire kernels always draw.
+constexpr int auto_tile_index(uint64_t) { return kTileDispatch; }
 
 // Scalar-load version of a shape: one element per load, at most 16 loads per
 // lane (each load is one wave scan; more would spill registers).
@@ -181,15 +189,10 @@ constexpr KernelCfg kCfgs[] = {
     DWS_DISPATCH(0, 4), DWS_DISPATCH(1, 4), DWS_DISPATCH(2, 4), DWS_DISPATCH(3, 4), DWS_DISPATCH(4, 4),
     DWS_DISPATCH(5, 4), DWS_DISPATCH(0, 1), DWS_DISPATCH(2, 1), DWS_DISPATCH(4, 1), DWS_DISPATCH(5, 1),
     // the same with non-temporal loads: the automatic choice from kNtLoadMin
-    // below kAutoDrawnMin (32,768- and 65,536-element tiles)
+    // (32,768- and 65,536-element tiles)
     {4, 4, kOrderRelaxed, kModeDecoupled, true, kTileDispatch},
     {5, 4, kOrderRelaxed, kModeDecoupled, true, kTileDispatch},
-    // instrumented (time stamps), aligned automatic shapes, both sources
-    {0, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
-    {2, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
-    {4, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
-    {5, 4, kOrderRelaxed, kModeDecoupled, false, kTileDrawn, true},
-    {5, 4, kOrderRelaxed, kModeDecoupled, true, kTileDrawn, true},   // the automatic choice from kNtLoadMin
+    // instrumented (time stamps): the automatic configurations
     {0, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
     {2, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},
     {4, 4, kOrderRelaxed, kModeDecoupled, false, kTileDispatch, true},

@@ -5,9 +5,9 @@
 // tile writes, so the output may overwrite the input) and section A5
 // (select-if fused with the scan, no extra pass).
 //
-// Per tile (one workgroup; tile index drawn from the workspace counter from
-// 2^25 elements, the workgroup index below; same descriptor protocol and
-// workspace as the scan):
+// Per tile (one workgroup; the tile index is the workgroup index, or for an
+// in-place select from 2^25 elements drawn from the workspace counter; same
+// descriptor protocol and workspace as the scan):
 //   1. load the flags, then the values of the tile (coalesced, in registers);
 //   2. exclusive scan of the 0/1 flags in the tile -> each element's rank
 //      among the tile's selected elements, and the tile's selected count;
@@ -265,26 +265,30 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
                    a.epoch,
                    select_backoff(a.n)};
     void* args[] = {&p};
-    // the workgroup index as the tile index below kSelectDrawnMin, as for the
-    // scan: no atomic on the critical path while there are few tiles per CU;
-    // the watchdog still bounds every wait.
-    // With a drawn tile index (from 2^25 elements) the values and flags are
-    // loaded non-temporally, each being read once: measured 0.5 to 2% faster
-    // at 2^25, 3 to 5.6% at 2^26 and 2^27, 3% at 2^30 - 12,345. Those sizes run
-    // the large shape when the pointers are aligned (the small and scalar
-    // shapes have no non-temporal build).
+    // The tile index is the workgroup index, as for the scan: no atomic on the
+    // critical path; the watchdog still bounds every wait. From kSelectNtMin
+    // elements (the large shape) the values and flags are loaded
+    // non-temporally, each being read once. Against a drawn index with
+    // non-temporal loads, alternating whole library builds in one session
+    // measured partition 81.7 -> 76.8 us and select 67.6 -> 66.9 us at 2^25,
+    // and select 1,797.7 -> 1,789.7 us at 2^30 - 12,345.
     // In place (select only) the kernel waits for its values before it
-    // publishes, which is what makes writing over the input safe.
-    const bool drawn = a.n >= kSelectDrawnMin;
+    // publishes, which is what makes writing over the input safe. There the
+    // drawn index stays from kSelectDrawnMin (with non-temporal loads): with
+    // the workgroup index the in-place select of the 2^30 - 12,345 flags
+    // measured 1.84 to 2.01 ms (mean 1.943) against 1.795 to 1.930 (mean
+    // 1.844).
+    const bool nt = a.n >= kSelectNtMin;
     const bool alias = !a.partition && a.out == a.in;
     const void* fn;
-    if (a.partition)
-        fn = drawn ? select_kernel<true, kTileDrawn, true>(s) : select_kernel<true, kTileDispatch>(s);
-    else if (alias)
-        fn = drawn ? select_kernel<false, kTileDrawn, true, true>(s)
-                   : select_kernel<false, kTileDispatch, false, true>(s);
-    else
-        fn = drawn ? select_kernel<false, kTileDrawn, true>(s) : select_kernel<false, kTileDispatch>(s);
+    if (a.partition) {
+        fn = nt ? select_kernel<true, kTileDispatch, true>(s) : select_kernel<true, kTileDispatch>(s);
+    } else if (alias) {
+        fn = a.n >= kSelectDrawnMin ? select_kernel<false, kTileDrawn, true, true>(s)
+                                    : select_kernel<false, kTileDispatch, false, true>(s);
+    } else {
+        fn = nt ? select_kernel<false, kTileDispatch, true>(s) : select_kernel<false, kTileDispatch>(s);
+    }
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 

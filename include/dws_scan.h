@@ -148,10 +148,10 @@ typedef enum dws_memory_order {
 
 /* Where a tile's index comes from in the single-pass and chained kernels. */
 typedef enum dws_tile_index {
-    /* the library's choice: DWS_TILE_DISPATCH below 2^27 elements for the
-     * relaxed single pass (non-temporal loads asked for on a shape whose
-     * workgroup-index kernel has none take DWS_TILE_DRAWN), else
-     * DWS_TILE_DRAWN */
+    /* the library's choice: DWS_TILE_DISPATCH for the relaxed single pass
+     * (non-temporal loads asked for on a shape whose workgroup-index kernel
+     * has none take DWS_TILE_DRAWN), DWS_TILE_DRAWN for the chained scan and
+     * release/acquire descriptors */
     DWS_TILE_AUTO = 0,
     /* one atomic add on a device-wide counter per workgroup, in the order the
      * workgroups start (PMPP 11.3 notes, dynamic block index; Merrill &

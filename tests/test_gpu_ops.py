@@ -30,8 +30,7 @@ COMBOS = {
 
 # around the tile sizes of every shape (small 4096 / 2048, medium 16384 / 8192
 # from 2^20, large 65536 / 32768 from 2^24, elements of one / two words) and
-# the switch to drawn tile indices at 2^25, and the look-back's long back-off
-# from 2^26
+# the switch to non-temporal loads at 2^25
 SIZES = [1, 2, 63, 64, 65, 2047, 2048, 2049, 4095, 4096, 4097, 3 * 4096 + 5, 100_003,
          (1 << 20) - 1, (1 << 20) + 7, 3 * (1 << 20) + 5, (1 << 24) - 3, (1 << 24) + 5, (1 << 25) + 9,
          (1 << 26) + 3]

@@ -66,8 +66,7 @@ def test_wave_primitives_lane_layout(gpu, dtype):
 # ---------------------------------------------------------------------------
 # sizes around wave and tile boundaries of every automatic tile size (4096
 # below 2^20, 16384 from 2^20, 32768 from 2^23, 65536 from 2^24), around the
-# switch to non-temporal loads at 2^23 and the switch from workgroup-index
-# tiles to drawn tiles with the 64-unit back-off at 2^27
+# switch to non-temporal loads at 2^23 and around 2^27
 M, L, H = 16384, 32768, 65536
 EDGE_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, TILE - 1, TILE, TILE + 1,
               2 * TILE - 1, 2 * TILE, 2 * TILE + 1, 17 * TILE + 333, 64 * TILE + 17, 255 * TILE + 3,
@@ -528,11 +527,12 @@ def test_select_sizes_and_densities(gpu, density, in_place):
         _check_select(x, flags, got, cnt, in_place, f"n={n} d={density}")
 
 
-def test_select_drawn_tiles(gpu):
-    # the drawn tile index with non-temporal loads (from 2^25): either side of
-    # the threshold, and a size past 2^27 with a ragged last tile, in and out
-    # of place
-    for n in ((1 << 25) - 1, (1 << 25) + SEL_TILE_LARGE + 5, (1 << 27) + SEL_TILE_LARGE + 5):
+def test_select_nontemporal_tiles(gpu):
+    # the large tiles with non-temporal loads (from 2^23): either side of the
+    # threshold, and sizes past 2^25 and 2^27 with a ragged last tile, in and
+    # out of place
+    for n in ((1 << 23) - 1, (1 << 23) + SEL_TILE_LARGE + 5, (1 << 25) + SEL_TILE_LARGE + 5,
+              (1 << 27) + SEL_TILE_LARGE + 5):
         x = wl.generate("i32_full", n, seed=n + 1)
         flags = wl.selection_flags(n, 0.5, seed=n + 2, any_nonzero=True)
         for in_place in (False, True):
@@ -646,12 +646,14 @@ def test_random_sizes(gpu):
         check(x, y, dtype, exclusive, label=f"random case {case} n={n}")
 
 
-@pytest.mark.parametrize("n", [(1 << 22) + 7, (1 << 27) + 3], ids=["dispatch_tiles", "drawn_tiles"])
+@pytest.mark.parametrize("n", [(1 << 22) + 7, (1 << 27) + 3], ids=["mid", "large"])
 def test_graph_replays(gpu, n):
     # a captured call replays with the arguments it was captured with; the
     # descriptor epoch comes from the workspace, so every replay still sees
-    # only its own descriptors. Eager work (new inputs, an uncaptured scan on
-    # the same stream) runs between replays, and every replay is checked.
+    # only its own descriptors, and a drawn-index scan's last draw puts the
+    # tile counter back for the next one. Eager work (new inputs, an
+    # uncaptured scan on the same stream) runs between replays, and every
+    # replay is checked.
     import torch
     s = torch.cuda.Stream()
     x = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -661,15 +663,18 @@ def test_graph_replays(gpu, n):
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     pairs = torch.empty((n, 2), dtype=torch.int32, device="cuda")
     pout = torch.empty_like(pairs)
+    dout = torch.empty_like(x)
     dws.reserve(n, stream=s.cuda_stream)
     with torch.cuda.stream(s):          # warm-up outside the capture
         dws.scan_exclusive(x, out)
+        dws.scan_opts(x, dout, tile_index=dws.TILE_DRAWN)
         dws.select_flagged(x, flags, out=sel, count=cnt)
         dws.scan_op(pairs, dws.OP_AFFINE, dws.PAIR_U32, out=pout)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         dws.scan_exclusive(x, out)
+        dws.scan_opts(x, dout, tile_index=dws.TILE_DRAWN)
         dws.select_flagged(x, flags, out=sel, count=cnt)
         dws.scan_op(pairs, dws.OP_AFFINE, dws.PAIR_U32, out=pout)
     for rep in range(4):
@@ -686,6 +691,7 @@ def test_graph_replays(gpu, n):
         g.replay()
         torch.cuda.synchronize()
         check(data, from_device(out, "int32"), "int32", True, label=f"replay {rep}")
+        check(data, from_device(dout, "int32"), "int32", False, label=f"drawn replay {rep}")
         want = oracle.select_flagged(data, fl)
         assert int(cnt.item()) == want.size
         assert np.array_equal(sel[:want.size].cpu().numpy(), want)

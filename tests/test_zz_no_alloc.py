@@ -56,8 +56,8 @@ def _compare(x, a, b, dtype, exclusive, label):
         assert np.array_equal(a, b), label
 
 
-# sizes: two drawn-index sizes (tile counter in the array), workgroup-index
-# sizes across the automatic shapes, a ragged multi-tile size and one tile
+# sizes: the automatic shapes with and without non-temporal loads, ragged
+# multi-tile sizes and one tile
 SIZES_FIRST_SECOND = [((1 << 25) + 777, (1 << 22) + 3), ((1 << 23) + 5, 70_001), (300_001, 4097)]
 
 
