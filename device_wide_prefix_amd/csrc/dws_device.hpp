@@ -255,19 +255,15 @@ __device__ __forceinline__ const uint64_t* desc_at(const uint64_t* desc, uint64_
 }
 
 // Pause before re-polling a blocked look-back window. The first re-poll comes
-// at once (`first`); after that, level kPauseShort keeps a short pause and the
-// other levels sleep 64, 127 or 190 x 64 clocks: fewer polls while many tiles
-// wait leave the memory system to the loads of the tiles being waited on.
+// at once (`first`); after that, level kPauseShort keeps a short pause and
+// kPause64 sleeps 64 x 64 clocks: fewer polls while many tiles wait leave the
+// memory system to the loads of the tiles being waited on.
 __device__ __forceinline__ void lookback_pause(uint32_t level, bool first)
 {
-    if (first || level == kPauseShort) {
+    if (first || level == kPauseShort)
         __builtin_amdgcn_s_sleep(1);
-    } else if (level == kPause64) {
+    else
         __builtin_amdgcn_s_sleep(64);
-    } else {
-        __builtin_amdgcn_s_sleep(127);
-        if (level == kPause190) __builtin_amdgcn_s_sleep(63);
-    }
 }
 
 template <int ORDER>

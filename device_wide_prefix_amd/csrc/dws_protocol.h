@@ -92,12 +92,11 @@ constexpr uint64_t kAutoHugeMin = (uint64_t)1 << 24;    // 65536-element tiles
 constexpr uint64_t kAutoLargeMin = (uint64_t)1 << 23;   // 32768
 constexpr uint64_t kAutoMediumMin = (uint64_t)1 << 20;  // 16384 (512 threads)
 // Back-off levels of a look-back that is still blocked after its first,
-// immediate re-poll (lookback_pause): 0 a short pause (s_sleep 1), then 64,
-// 127 or 190 units of 64 clocks before every further poll.
+// immediate re-poll (lookback_pause): a short pause (s_sleep 1), or 64 units
+// of 64 clocks before every further poll. (Sleeps of 127 and 190 units paid
+// only while descriptors were packed 8 bytes apart.)
 constexpr uint32_t kPauseShort = 0u;
 constexpr uint32_t kPause64 = 1u;
-constexpr uint32_t kPause127 = 2u;
-constexpr uint32_t kPause190 = 3u;
 // A + scan with a drawn tile index backs off from here: 64 units, the best of
 // 16 / 32 / 64 / 127 at 2^27 to 2^30 with spread descriptors (127 equal). The
 // workgroup-index scan keeps the short pause at every size: 1.3 to 3.4% faster

@@ -6,9 +6,9 @@
 // One workgroup per tile; the kernel is the whole call (no init launch: every
 // launch reads a new descriptor epoch from the workspace, and the owner of the
 // last tile advances it):
-//   1. lane 0 draws the tile index from the workspace counter (dynamic tile
-//      index, PMPP 11.3 notes), or the tile is the workgroup index
-//      (TILE_INDEX == kTileDispatch);
+//   1. the tile is the workgroup index (TILE_INDEX == kTileDispatch, the
+//      automatic choice), or lane 0 draws it from the workspace counter
+//      (dynamic tile index, PMPP 11.3 notes; kTileDrawn);
 //   2. every wave loads its segment of the tile with coalesced vector loads,
 //      CHUNKS x VEC elements per lane kept in registers (thread coarsening,
 //      PMPP 11.2 notes); with NT the loads are non-temporal (the input is read
