@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
-    "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc",
+    "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc", "dws_scan_plan",
 )
 
 
@@ -56,6 +56,12 @@ class DwsOptions(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("memory_order", ctypes.c_int),
                 ("tile_shape", ctypes.c_int), ("nontemporal", ctypes.c_int),
                 ("tile_index", ctypes.c_int)]
+
+
+class LaunchPlan(ctypes.Structure):
+    """dws_launch_plan: what a single-pass or chained call would launch."""
+    _fields_ = [("threads", ctypes.c_uint), ("tile_elems", ctypes.c_uint), ("num_tiles", ctypes.c_uint),
+                ("tile_index", ctypes.c_int), ("nontemporal", ctypes.c_int), ("pause_units", ctypes.c_int)]
 
 
 _lib = None
@@ -85,6 +91,8 @@ def load_library():
     lib.dws_scan_opts.restype = ci
     lib.dws_scan_noalloc.argtypes = [vp, vp, sz, ci, ci, vp]
     lib.dws_scan_noalloc.restype = ci
+    lib.dws_scan_plan.argtypes = [vp, vp, sz, ci, ci, ctypes.POINTER(DwsOptions), ctypes.POINTER(LaunchPlan)]
+    lib.dws_scan_plan.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -153,6 +161,16 @@ def scan_opts_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,
                   options: DwsOptions | None, stream: int = 0) -> int:
     opt = ctypes.byref(options) if options is not None else None
     return load_library().dws_scan_opts(d_in, d_out, n, dtype, int(bool(exclusive)), opt, stream)
+
+
+def scan_plan_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,
+                  options: DwsOptions | None = None) -> tuple[int, LaunchPlan]:
+    """dws_scan_plan: (status, plan) for what dws_scan_opts would launch with
+    these arguments; the pointers are only compared and checked for alignment."""
+    plan = LaunchPlan()
+    opt = ctypes.byref(options) if options is not None else None
+    st = load_library().dws_scan_plan(d_in, d_out, n, dtype, int(bool(exclusive)), opt, ctypes.byref(plan))
+    return st, plan
 
 
 # ---- torch-tensor entry points --------------------------------------------

@@ -382,21 +382,30 @@ dws_status run_stp(const void* in, void* out, size_t n, int dtype, bool excl, hi
     return from_hip(launch_stp(a, stream));
 }
 
+// Options checked before the arguments: unknown values are invalid, a tile
+// index source other than automatic exists for the single pass and the
+// chained scan only.
+dws_status check_options(const dws_options& o)
+{
+    if (o.variant < DWS_VARIANT_SINGLE_PASS || o.variant > DWS_VARIANT_SCAN_THEN_PROPAGATE) return DWS_ERR_INVALID_ARG;
+    if (o.memory_order != DWS_ORDER_RELAXED && o.memory_order != DWS_ORDER_ACQ_REL) return DWS_ERR_INVALID_ARG;
+    if (o.tile_shape < 0 || o.tile_shape > kNumShapes) return DWS_ERR_INVALID_ARG;
+    if (o.nontemporal < 0 || o.nontemporal > 2) return DWS_ERR_INVALID_ARG;
+    if (o.tile_index < DWS_TILE_AUTO || o.tile_index > DWS_TILE_DISPATCH) return DWS_ERR_INVALID_ARG;
+    if (o.tile_index != DWS_TILE_AUTO && o.variant != DWS_VARIANT_SINGLE_PASS && o.variant != DWS_VARIANT_CHAINED)
+        return DWS_ERR_UNSUPPORTED;
+    return DWS_OK;
+}
+
 dws_status scan_entry(const void* in, void* out, size_t n, int dtype, int exclusive, const dws_options* opt,
                       hipStream_t stream)
 {
     try {
         dws_options o{};
         if (opt != nullptr) o = *opt;
-        if (o.variant < DWS_VARIANT_SINGLE_PASS || o.variant > DWS_VARIANT_SCAN_THEN_PROPAGATE) return DWS_ERR_INVALID_ARG;
-        if (o.memory_order != DWS_ORDER_RELAXED && o.memory_order != DWS_ORDER_ACQ_REL)
-            return DWS_ERR_INVALID_ARG;
-        if (o.tile_shape < 0 || o.tile_shape > kNumShapes) return DWS_ERR_INVALID_ARG;
-        if (o.nontemporal < 0 || o.nontemporal > 2) return DWS_ERR_INVALID_ARG;
-        if (o.tile_index < DWS_TILE_AUTO || o.tile_index > DWS_TILE_DISPATCH) return DWS_ERR_INVALID_ARG;
-        if (o.tile_index != DWS_TILE_AUTO && o.variant != DWS_VARIANT_SINGLE_PASS && o.variant != DWS_VARIANT_CHAINED)
-            return DWS_ERR_UNSUPPORTED;
-        dws_status s = validate(in, out, n, dtype);
+        dws_status s = check_options(o);
+        if (s != DWS_OK) return s;
+        s = validate(in, out, n, dtype);
         if (s != DWS_OK || n == 0) return s;
         const bool excl = exclusive != 0;
         switch (o.variant) {
@@ -531,6 +540,41 @@ dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtyp
                          const dws_options* opt, hipStream_t stream)
 {
     return scan_entry(d_in, d_out, n, enum_arg(dtype), exclusive, opt, stream);
+}
+
+dws_status dws_scan_plan(const void* d_in, const void* d_out, size_t n, dws_dtype dtype, int exclusive,
+                         const dws_options* opt, dws_launch_plan* plan)
+{
+    try {
+        if (plan == nullptr) return DWS_ERR_INVALID_ARG;
+        dws_options o{};
+        if (opt != nullptr) o = *opt;
+        dws_status s = check_options(o);
+        if (s != DWS_OK) return s;
+        if (o.variant != DWS_VARIANT_SINGLE_PASS && o.variant != DWS_VARIANT_CHAINED) return DWS_ERR_UNSUPPORTED;
+        const int dt = enum_arg(dtype);
+        s = validate(d_in, d_out, n, dt);
+        if (s != DWS_OK) return s;
+        dws_launch_plan out{};
+        if (n > 0) {
+            SinglePassPlan sp{};
+            const int mode = o.variant == DWS_VARIANT_CHAINED ? kModeChained : kModeDecoupled;
+            s = plan_single_pass(d_in, const_cast<void*>(d_out), n, dt, exclusive != 0, mode, o, nullptr, &sp);
+            if (s != DWS_OK) return s;
+            const KernelCfg& c = kCfgs[sp.cfg];
+            const TileShape ts = cfg_shape(c);
+            out.threads = (unsigned)ts.threads;
+            out.tile_elems = (unsigned)ts.elems();
+            out.num_tiles = sp.params.num_tiles;
+            out.tile_index = c.tile_index == kTileDrawn ? DWS_TILE_DRAWN : DWS_TILE_DISPATCH;
+            out.nontemporal = c.nt ? 1 : 0;
+            out.pause_units = sp.params.backoff == kPause64 ? 64 : 1;
+        }
+        *plan = out;
+        return DWS_OK;
+    } catch (...) {
+        return DWS_ERR_INVALID_ARG;
+    }
 }
 
 const char* dws_status_string(dws_status status)

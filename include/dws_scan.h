@@ -213,6 +213,34 @@ dws_status dws_scan_ex(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
 dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                          int exclusive, const dws_options* opt, hipStream_t stream);
 
+/* The launch a single-pass or chained dws_scan_opts call with the same
+ * arguments would make. */
+typedef struct dws_launch_plan {
+    unsigned threads;      /* threads per workgroup */
+    unsigned tile_elems;   /* elements per tile (one workgroup each) */
+    unsigned num_tiles;    /* workgroups launched (0 when n == 0) */
+    int tile_index;        /* DWS_TILE_DRAWN or DWS_TILE_DISPATCH */
+    int nontemporal;       /* 1: the input is read with non-temporal loads */
+    int pause_units;       /* sleep between blocked look-back polls after the
+                              first re-poll, in units of 64 clocks (1: the
+                              short pause) */
+} dws_launch_plan;
+
+/*
+ * Describe, without launching anything or making any HIP call, what
+ * dws_scan_opts(d_in, d_out, n, dtype, exclusive, opt, ...) would launch for
+ * the single pass or the chained scan: the tile shape, the tile index source
+ * (the dynamic index of the PMPP 11.3 notes and section 4.4 of the Merrill &
+ * Garland notes, or the workgroup index), non-temporal loads and the
+ * look-back's back-off, as the library chooses them. d_in and
+ * d_out are only compared and checked for alignment, never dereferenced.
+ * Validation and status codes are those of dws_scan_opts; the other variants
+ * give DWS_ERR_UNSUPPORTED, plan == NULL gives DWS_ERR_INVALID_ARG. The
+ * caller owns *plan, which is written only on DWS_OK.
+ */
+dws_status dws_scan_plan(const void* d_in, const void* d_out, size_t n, dws_dtype dtype,
+                         int exclusive, const dws_options* opt, dws_launch_plan* plan);
+
 /* Tiles the fixed device array of dws_scan_noalloc has descriptors for (64
  * bytes each), so n may be up to 2^32 elements when both pointers are 16-byte
  * aligned (65,536-element tiles) and up to 2^30 otherwise (16,384). */

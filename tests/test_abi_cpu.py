@@ -365,3 +365,86 @@ def test_noalloc_validation_and_limit(lib):
     assert f(FAKE, big, max_tiles * 65536 + 1, dws.FLOAT32, 1, None) == dws.ERR_UNSUPPORTED
     assert dws.tile_elems(0, max_tiles * 16384, False) == 16384
     assert f(FAKE + 4, big, max_tiles * 16384 + 1, dws.FLOAT32, 1, None) == dws.ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# the launch the library chooses (dws_scan_plan: no HIP call, no launch)
+# ---------------------------------------------------------------------------
+def _plan(lib, n, dtype=dws.FLOAT32, in_place=False, offset=0, exclusive=False, **kw):
+    d_in = FAKE + offset
+    d_out = d_in if in_place else d_in + (1 << 40)
+    o = dws.DwsOptions(kw.get("variant", 0), kw.get("order", 0), kw.get("shape", 0), kw.get("nt", 0),
+                       kw.get("tile_index", 0))
+    return dws.scan_plan_ptr(d_in, d_out, n, dtype, exclusive, o)
+
+
+def _auto_tile(n):
+    """The automatic tile: (threads, elements) by n."""
+    if n >= 1 << 24:
+        return 1024, 65536
+    if n >= 1 << 23:
+        return 1024, 32768
+    if n >= 1 << 20:
+        return 512, 16384
+    return 256, 4096
+
+
+@pytest.mark.parametrize("in_place", [False, True], ids=["out_of_place", "in_place"])
+def test_plan_automatic_policy(lib, in_place):
+    # every size takes the workgroup index and the short pause; non-temporal
+    # loads from 2^23 elements, in place or not
+    for n in (1, 4096, 4097, (1 << 20) - 1, 1 << 20, (1 << 23) - 1, 1 << 23, (1 << 24) - 3, 1 << 24,
+              (1 << 27) + 1, 1 << 28, (1 << 30) - 12345, 1 << 32):
+        st, p = _plan(lib, n, in_place=in_place)
+        assert st == dws.OK, n
+        threads, tile = _auto_tile(n)
+        assert (p.threads, p.tile_elems) == (threads, tile), n
+        assert p.num_tiles == -(-n // tile), n
+        assert p.tile_index == dws.TILE_DISPATCH, n
+        assert p.nontemporal == (1 if n >= 1 << 23 else 0), n
+        assert p.pause_units == 1, n
+
+
+def test_plan_explicit_choices(lib):
+    big = 1 << 28
+    # a drawn index: the 64-unit back-off from 2^27, the short pause below it
+    st, p = _plan(lib, big, tile_index=dws.TILE_DRAWN)
+    assert st == dws.OK and (p.tile_index, p.nontemporal, p.pause_units) == (dws.TILE_DRAWN, 1, 64)
+    st, p = _plan(lib, 1 << 26, tile_index=dws.TILE_DRAWN)
+    assert st == dws.OK and (p.tile_index, p.nontemporal, p.pause_units) == (dws.TILE_DRAWN, 1, 1)
+    # the chained scan and release/acquire descriptors always draw, without
+    # non-temporal loads unless asked for
+    for kw in (dict(variant=dws.CHAINED), dict(order=dws.ORDER_ACQ_REL)):
+        st, p = _plan(lib, big, **kw)
+        assert st == dws.OK and (p.tile_index, p.nontemporal) == (dws.TILE_DRAWN, 0), kw
+    # non-temporal loads off; on for a small automatic shape (only its drawn
+    # kernel has them); on with the workgroup index where it has them
+    st, p = _plan(lib, big, nt=2)
+    assert st == dws.OK and (p.tile_index, p.nontemporal) == (dws.TILE_DISPATCH, 0)
+    st, p = _plan(lib, 1 << 16, nt=1)
+    assert st == dws.OK and (p.tile_index, p.nontemporal, p.tile_elems) == (dws.TILE_DRAWN, 1, 4096)
+    st, p = _plan(lib, 1 << 24, nt=1, tile_index=dws.TILE_DISPATCH)
+    assert st == dws.OK and (p.tile_index, p.nontemporal) == (dws.TILE_DISPATCH, 1)
+    assert _plan(lib, 1 << 16, nt=1, tile_index=dws.TILE_DISPATCH)[0] == dws.ERR_UNSUPPORTED
+    # a forced shape does not take the automatic non-temporal loads
+    st, p = _plan(lib, big, shape=5)
+    assert st == dws.OK and (p.tile_elems, p.nontemporal, p.tile_index) == (32768, 0, dws.TILE_DISPATCH)
+    # pointers that are not 16-byte aligned: scalar loads, 16 per lane, no
+    # non-temporal loads
+    st, p = _plan(lib, big, offset=4)
+    assert st == dws.OK and (p.threads, p.tile_elems, p.nontemporal) == (1024, 16384, 0)
+
+
+def test_plan_validation(lib):
+    o = dws.DwsOptions(0, 0, 0, 0, 0)
+    f = lib.dws_scan_plan
+    assert f(FAKE, FAKE + (1 << 20), 100, dws.FLOAT32, 0, ctypes.byref(o), None) == dws.ERR_INVALID_ARG
+    st, p = _plan(lib, 0)
+    assert st == dws.OK and p.num_tiles == 0
+    assert _plan(lib, 100, dtype=9)[0] == dws.ERR_INVALID_ARG
+    assert _plan(lib, 100, offset=2)[0] == dws.ERR_MISALIGNED
+    assert _plan(lib, 1 << 20, variant=dws.REDUCE_THEN_SCAN)[0] == dws.ERR_UNSUPPORTED
+    assert _plan(lib, 1 << 20, variant=dws.SCAN_THEN_PROPAGATE)[0] == dws.ERR_UNSUPPORTED
+    assert _plan(lib, 1 << 20, variant=7)[0] == dws.ERR_INVALID_ARG
+    st = dws.scan_plan_ptr(FAKE, FAKE + 4, 100, dws.INT32, False)[0]
+    assert st == dws.ERR_OVERLAP
