@@ -448,3 +448,11 @@ def test_plan_validation(lib):
     assert _plan(lib, 1 << 20, variant=7)[0] == dws.ERR_INVALID_ARG
     st = dws.scan_plan_ptr(FAKE, FAKE + 4, 100, dws.INT32, False)[0]
     assert st == dws.ERR_OVERLAP
+
+
+def test_plan_agrees_with_the_profiled_scan(lib):
+    # the instrumented scan sizes its stamp buffer by its own tile count
+    for n in (5, 4097, (1 << 20) + 3, (1 << 23) + 1, (1 << 24) + 77, (1 << 28) + 5):
+        st, p = _plan(lib, n)
+        assert st == dws.OK
+        assert p.num_tiles == dws.profiled_num_tiles(n), n
