@@ -16,11 +16,12 @@ library launches on. The call is a single kernel launch, so the event time is
 the kernel's launch duration.
 
 Options: --workload NAME (a key of scan_workloads.WORKLOADS),
-         --variant single_pass|reduce_then_scan|chained|scan_then_propagate,
+--variant single_pass|reduce_then_scan|chained|scan_then_propagate,
 --order relaxed|acq_rel, --tile-shape K, --nontemporal auto|on|off, --no-cpu-baseline,
 --all (extra JSON lines for every workload and variant on stderr), --sweep
 (N = 2^10..2^30, every variant and memcpy, cold and warm caches; stderr),
---select (stream compaction on the 2^30-12345 flag workload; stderr), --ops
+--shards G (one device's share of the headline scan split into G shards:
+reduce, seeded scan and both together; stderr), --select (stream compaction on the 2^30-12345 flag workload; stderr), --ops
 (generic-operator scans: max, min, {int32, fp32} pair sum, affine maps,
 segmented sum, on 1 GiB inputs; stderr), --compaction (select, partition,
 reduce-by-key, run-length encoding on 2^25 items, beside PyTorch; stderr).
@@ -175,12 +176,22 @@ def run_workload(w: wl.Workload, variant: int, order: int, shape: int, nt: int, 
         if st != dws.OK:
             raise RuntimeError(f"scan failed: {dws.status_string(st)}")
 
+    launch = None
+    if variant in (0, 2):
+        # what the library resolves the options to for these buffers
+        st, plan = dws.scan_plan_ptr(work.data_ptr(), out.data_ptr(), w.n, code, w.exclusive, opt)
+        if st != dws.OK:
+            raise RuntimeError(f"scan plan failed: {dws.status_string(st)}")
+        launch = {"threads": plan.threads, "tile_elems": plan.tile_elems, "num_tiles": plan.num_tiles,
+                  "tile_index": "drawn" if plan.tile_index == dws.TILE_DRAWN else "dispatch",
+                  "nontemporal": bool(plan.nontemporal), "pause_units": plan.pause_units}
+
     trips_before = dws.watchdog_trips()
     times = time_steps(scan, prepare, steps, warmup)
     # a look-back wait that timed out leaves wrong output behind a DWS_OK
     # status: count the trips of the timed steps and fail the check on any
     trips = dws.watchdog_trips() - trips_before
-    result = {"times_ms": times, "watchdog_trips": int(trips)}
+    result = {"times_ms": times, "watchdog_trips": int(trips), "launch": launch}
 
     # property checks that hold at any size (no oracle here)
     y = out.cpu().numpy()
@@ -428,6 +439,82 @@ def run_ops(steps: int, warmup: int, with_oracle: bool = True):
     return rows
 
 
+def run_shards(steps: int, warmup: int, shards: int):
+    """One device's share of the headline scan split into `shards` contiguous
+    shards (2^28 / shards fp32 elements, exclusive, in place), cold caches:
+      reduce     the shard's total (dws_reduce; 4 bytes per element read)
+      seeded     the shard's scan seeded with a device element (8 bytes)
+      unseeded   scan_exclusive of the same shard, for comparison
+      sequence   reduce, exclusive scan of the `shards` totals, seeded scan:
+                 what each device runs besides the exchange of the totals
+                 (12 bytes per element, ~3n/G per device)
+      torch_sum  torch.sum of the shard (the library reduction), for comparison
+    One SHARD line on stderr."""
+    import torch
+    import device_wide_prefix_amd as dws
+    w = wl.WORKLOADS["f32_2p28_excl_inplace"]
+    m = w.n // shards
+    x = wl.generate_workload(w)[:m].copy()
+    pristine = torch.from_numpy(x).to("cuda")
+    work = torch.empty_like(pristine)
+    totals = torch.zeros(shards, dtype=torch.float32, device="cuda")
+    offsets = torch.zeros_like(totals)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    dws.reserve(m)
+
+    def prepare():
+        work.copy_(pristine)
+        flush.sum()
+
+    def ok(st):
+        if st != dws.OK:
+            raise RuntimeError(dws.status_string(st))
+
+    def reduce():
+        ok(dws.reduce_ptr(work.data_ptr(), m, dws.FLOAT32, totals.data_ptr(), stream))
+
+    def seeded():
+        ok(dws.scan_seeded_ptr(work.data_ptr(), work.data_ptr(), m, dws.FLOAT32, True, offsets.data_ptr(), stream))
+
+    def unseeded():
+        ok(dws.scan_exclusive_ptr(work.data_ptr(), work.data_ptr(), m, dws.FLOAT32, stream))
+
+    def sequence():
+        reduce()
+        ok(dws.scan_exclusive_ptr(totals.data_ptr(), offsets.data_ptr(), shards, dws.FLOAT32, stream))
+        seeded()
+
+    def torch_sum():
+        torch.sum(work, 0, out=totals[:1].view(()))
+
+    row = {"workload": f"{w.description}, one of {shards} shards", "shards": shards, "n": m}
+    trips = dws.watchdog_trips()
+    for name, fn, per_elem in (("reduce", reduce, 4), ("seeded", seeded, 8), ("unseeded", unseeded, 8),
+                               ("torch_sum", torch_sum, 4), ("sequence", sequence, 12)):
+        times = time_steps(fn, prepare, steps, warmup)
+        mean = float(np.mean(times))
+        gbps = per_elem * m / (mean * 1e-3) / 1e9
+        row[name] = {"us_mean": round(mean * 1e3, 3), "us_min": round(float(np.min(times)) * 1e3, 3),
+                     "bytes_per_element": per_elem, "gbps": round(gbps, 1),
+                     "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    # the last timed step ran the whole sequence on the shard: its total and
+    # the ends of its seeded scan agree with a float64 sum (offsets[0], the
+    # seed of the first shard, is 0)
+    sequence_out = work.cpu().numpy()
+    total = float(totals[0].item())
+    ref = float(np.sum(x, dtype=np.float64))
+    bound = 1e-4 * float(np.sum(np.abs(x), dtype=np.float64)) + 1e-6
+    seed0 = float(offsets[0].item())
+    row["property_check"] = bool(abs(total - ref) <= bound and seed0 == 0.0 and sequence_out[0] == 0.0
+                                 and abs(float(sequence_out[-1]) + float(x[-1]) - ref) <= bound)
+    row["watchdog_trips"] = int(dws.watchdog_trips() - trips)
+    log("SHARD " + json.dumps(row))
+    del pristine, work, flush
+    torch.cuda.empty_cache()
+    return row
+
+
 COMPACTION_N = 1 << 25   # the 32M-item size the pages measure the compaction family on
 
 
@@ -638,7 +725,7 @@ def summarize(w, res, variant_name, args):
     out = {"workload": w.name, "variant": variant_name, "ms_mean": mean_ms, "ms_min": float(np.min(times)),
            "ms_median": float(np.median(times)), "gbps": gbps, "property_check": res["property_check"],
            "watchdog_trips": res["watchdog_trips"]}
-    for key in ("lookback_stall_share", "phase_mean_us", "tiles"):
+    for key in ("lookback_stall_share", "phase_mean_us", "tiles", "launch"):
         if key in res:
             out[key] = res[key]
     if "memcpy_times_ms" in res:
@@ -677,7 +764,8 @@ def config_row(w: wl.Workload, s: dict, oracle_row) -> dict:
            "us_min": round(s["ms_min"] * 1e3, 3), "gbps": round(gbps, 2),
            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
            "memcpy_gbps": round(s["memcpy_gbps"], 2), "frac_memcpy": round(gbps / s["memcpy_gbps"], 4),
-           "property_check": s["property_check"], "watchdog_trips": s["watchdog_trips"]}
+           "property_check": s["property_check"], "watchdog_trips": s["watchdog_trips"],
+           "launch": s.get("launch")}
     if oracle_row is not None:
         row["oracle"] = oracle_row
     return row
@@ -705,6 +793,9 @@ def main():
                     help="also measure stream compaction on the 2^30-12345 flag workload (stderr)")
     ap.add_argument("--ops", action="store_true",
                     help="also measure the generic-operator scans on 1 GiB inputs (stderr)")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="also time one device's share of the headline scan split into this many shards: "
+                         "reduce, seeded scan and the two together (stderr)")
     ap.add_argument("--compaction", action="store_true",
                     help="also measure select, partition, reduce-by-key and run-length encoding on 2^25 items "
                          "(stderr)")
@@ -773,6 +864,7 @@ def main():
         "watchdog_trips": s["watchdog_trips"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "launch": s.get("launch"),
         "lookback_stall_share": s.get("lookback_stall_share"),
         "tile_phase_mean_us": s.get("phase_mean_us"),
         "device": device_info(),
@@ -823,6 +915,8 @@ def main():
         run_ops(args.steps, args.warmup, timed_oracle)
     if args.compaction:
         run_compaction(args.steps, args.warmup, timed_oracle)
+    if args.shards:
+        run_shards(args.steps, args.warmup, args.shards)
     if args.select:
         for in_place in (False, True):
             log("SELECT " + json.dumps(run_select(args.steps, args.warmup, in_place, timed_oracle and not in_place)))

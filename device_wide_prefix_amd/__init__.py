@@ -9,6 +9,8 @@ fallback; if the library is not built, importing the binding's functions raises.
     scan_ex(x, out=None, exclusive=False, variant=SINGLE_PASS) -> out
     scan_opts(x, out=None, exclusive=False, variant=..., memory_order=...,
               tile_shape=0, nontemporal=None, tile_index=...) -> out
+    scan_seeded(x, seed, exclusive=False, out=None) -> out  (seed: 1-element GPU tensor)
+    reduce(x, out=None)                    -> 1-element GPU tensor holding the + of x
     scan_debug(x, out, tile_elems, ...)    -> descriptor words (numpy uint64)
     watchdog_trips()                       -> int
     selftest_wave(x)                       -> (incl, shift)
@@ -42,7 +44,8 @@ EXPORTED_SYMBOLS = (
     "dws_num_tile_shapes", "dws_tile_elems", "dws_tile_threads", "dws_reserve",
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
-    "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc", "dws_scan_plan",
+    "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc", "dws_scan_plan", "dws_scan_seeded",
+    "dws_reduce",
 )
 
 
@@ -93,6 +96,10 @@ def load_library():
     lib.dws_scan_noalloc.restype = ci
     lib.dws_scan_plan.argtypes = [vp, vp, sz, ci, ci, ctypes.POINTER(DwsOptions), ctypes.POINTER(LaunchPlan)]
     lib.dws_scan_plan.restype = ci
+    lib.dws_scan_seeded.argtypes = [vp, vp, sz, ci, ci, vp, vp]
+    lib.dws_scan_seeded.restype = ci
+    lib.dws_reduce.argtypes = [vp, sz, ci, vp, vp]
+    lib.dws_reduce.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -155,6 +162,15 @@ def scan_ex_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool, vari
 
 def scan_noalloc_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool, stream: int = 0) -> int:
     return load_library().dws_scan_noalloc(d_in, d_out, n, dtype, int(bool(exclusive)), stream)
+
+
+def scan_seeded_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool, d_seed: int,
+                    stream: int = 0) -> int:
+    return load_library().dws_scan_seeded(d_in, d_out, n, dtype, int(bool(exclusive)), d_seed, stream)
+
+
+def reduce_ptr(d_in: int, n: int, dtype: int, d_total: int, stream: int = 0) -> int:
+    return load_library().dws_reduce(d_in, n, dtype, d_total, stream)
 
 
 def scan_opts_ptr(d_in: int, d_out: int, n: int, dtype: int, exclusive: bool,
@@ -246,6 +262,38 @@ def scan_opts(x, out=None, exclusive=False, variant=SINGLE_PASS, memory_order=OR
     with _device_of(x):
         _check(scan_opts_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, opt,
                              _stream(x, stream)), "dws_scan_opts")
+    return out
+
+
+def scan_seeded(x, seed, exclusive=False, out=None, stream=None):
+    """Scan of x with the 1-element GPU tensor ``seed`` (dtype of x) as the
+    prefix of the whole array (dws_scan_seeded); returns ``out`` (may be x)."""
+    import torch
+    code, out = _prepare(x, out)
+    if not isinstance(seed, torch.Tensor) or seed.device != x.device or seed.dtype != x.dtype or \
+            seed.numel() != 1:
+        raise ValueError("seed must be a 1-element tensor with the dtype and device of x")
+    with _device_of(x):
+        _check(scan_seeded_ptr(x.data_ptr(), out.data_ptr(), x.numel(), code, exclusive, seed.data_ptr(),
+                               _stream(x, stream)), "dws_scan_seeded")
+    return out
+
+
+def reduce(x, out=None, stream=None):
+    """+ of every element of x (dws_reduce) into the 1-element GPU tensor
+    ``out`` (a new one by default); returns ``out``."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("reduce expects a GPU tensor (there is no CPU path)")
+    if not x.is_contiguous():
+        raise ValueError("input tensor must be contiguous")
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty(1, dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or out.numel() != 1 or out.device != x.device:
+        raise ValueError("out must be a 1-element tensor with the dtype and device of x")
+    with _device_of(x):
+        _check(reduce_ptr(x.data_ptr(), x.numel(), code, out.data_ptr(), _stream(x, stream)), "dws_reduce")
     return out
 
 

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libdws_scan.so")
 ARCH = "gfx950"
 
-SOURCES = ["dws_sp_u32.hip", "dws_sp_f32.hip", "dws_aux.hip", "dws_stp.hip", "dws_select.hip",
+SOURCES = ["dws_sp_u32.hip", "dws_sp_f32.hip", "dws_aux.hip", "dws_stp.hip", "dws_select.hip", "dws_reduce.hip",
            "dws_op_minmax.hip", "dws_op_pairsum.hip", "dws_op_affine.hip", "dws_op_segsum.hip", "dws_rbk.hip",
            "dws_static.hip", "dws_single_pass_host.cpp", "dws_abi.cpp"]
 

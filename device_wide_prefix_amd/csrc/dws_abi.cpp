@@ -296,11 +296,13 @@ hipError_t launch_single_pass_plan(const SinglePassPlan& plan, const LookbackSta
 namespace {
 
 dws_status run_single_pass(const void* in, void* out, size_t n, int dtype, bool excl, int mode,
-                           const dws_options& o, hipStream_t stream, unsigned long long* stamps = nullptr)
+                           const dws_options& o, hipStream_t stream, unsigned long long* stamps = nullptr,
+                           const void* seed = nullptr)
 {
     SinglePassPlan plan{};
     dws_status s = plan_single_pass(in, out, n, dtype, excl, mode, o, stamps, &plan);
     if (s != DWS_OK) return s;
+    plan.params.seed = seed;
     // one tile: no predecessors, no descriptors, no counter
     if (plan.params.num_tiles == 1) return from_hip(launch_single_pass_plan(plan, nullptr, stream));
     Workspace* ws = nullptr;
@@ -340,6 +342,41 @@ dws_status run_rts(const void* in, void* out, size_t n, int dtype, bool excl, hi
     a.groups = (uint32_t)groups;
     a.tiles_per_group = (uint32_t)tpg;
     return from_hip(launch_rts(a, stream));
+}
+
+// Device-wide + reduction into one element (validated arguments). The grid
+// depends on n only: at most kReduceMaxGroups workgroups, each summing the
+// same number of consecutive tiles.
+dws_status run_reduce(const void* in, size_t n, int dtype, void* total, hipStream_t stream)
+{
+    const uint64_t num_tiles = ceil_div(n, kReduceTileElems);
+    if (num_tiles > 0xffffffffull) return DWS_ERR_UNSUPPORTED;
+    uint64_t groups = std::max<uint64_t>(1u, std::min<uint64_t>(num_tiles, kReduceMaxGroups));
+    const uint64_t tpg = ceil_div(num_tiles, groups);
+    if (tpg > 0) groups = ceil_div(num_tiles, tpg);
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_desc(ws, groups * kDescStride);
+    if (s != DWS_OK) return s;
+    s = before_lookback_launch(ws);
+    if (s != DWS_OK) return s;
+    ReduceArgs a{};
+    a.in = in;
+    a.n = n;
+    a.kind = kind_of(dtype);
+    a.aligned = (reinterpret_cast<uintptr_t>(in) & 15u) == 0;
+    // each input word is read once, as in the scan's tiles
+    a.nontemporal = a.aligned && n >= kNtLoadMin;
+    a.desc = ws->desc;
+    a.epoch = ws->epoch();
+    a.watchdog = ws->watchdog();
+    a.total = total;
+    a.num_tiles = (uint32_t)num_tiles;
+    a.groups = (uint32_t)groups;
+    a.tiles_per_group = (uint32_t)tpg;
+    return from_hip(launch_reduce(a, stream));
 }
 
 // Grow the scan-then-propagate scratch (call with ws->mu held).
@@ -540,6 +577,49 @@ dws_status dws_scan_opts(const void* d_in, void* d_out, size_t n, dws_dtype dtyp
                          const dws_options* opt, hipStream_t stream)
 {
     return scan_entry(d_in, d_out, n, enum_arg(dtype), exclusive, opt, stream);
+}
+
+dws_status dws_scan_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dtype, int exclusive,
+                           const void* d_seed, hipStream_t stream)
+{
+    try {
+        const int dt = enum_arg(dtype);
+        dws_status s = validate(d_in, d_out, n, dt);
+        if (s != DWS_OK || n == 0) return s;
+        if (d_seed == nullptr) return DWS_ERR_INVALID_ARG;
+        const uintptr_t sd = reinterpret_cast<uintptr_t>(d_seed);
+        if (sd % kElemBytes != 0) return DWS_ERR_MISALIGNED;
+        // tile 0 reads the seed before it publishes, and every store of the
+        // call follows that publication; an output range that held the seed
+        // would still be an error, so it is refused outright
+        const uintptr_t ob = reinterpret_cast<uintptr_t>(d_out);
+        if (sd + kElemBytes > ob && sd < ob + (uintptr_t)n * kElemBytes) return DWS_ERR_OVERLAP;
+        const dws_options o{};
+        return run_single_pass(d_in, d_out, n, dt, exclusive != 0, kModeDecoupled, o, stream, nullptr, d_seed);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_reduce(const void* d_in, size_t n, dws_dtype dtype, void* d_total, hipStream_t stream)
+{
+    try {
+        const int dt = enum_arg(dtype);
+        if (!valid_dtype(dt)) return DWS_ERR_INVALID_ARG;
+        if (d_total == nullptr || (n > 0 && d_in == nullptr)) return DWS_ERR_INVALID_ARG;
+        if (n > DWS_MAX_ELEMENTS) return DWS_ERR_UNSUPPORTED;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(d_in);
+        const uintptr_t t = reinterpret_cast<uintptr_t>(d_total);
+        if (a % kElemBytes != 0 || t % kElemBytes != 0) return DWS_ERR_MISALIGNED;
+        if (n > 0 && t + kElemBytes > a && t < a + (uintptr_t)n * kElemBytes) return DWS_ERR_OVERLAP;
+        return run_reduce(d_in, n, dt, d_total, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
 }
 
 dws_status dws_scan_plan(const void* d_in, const void* d_out, size_t n, dws_dtype dtype, int exclusive,

@@ -74,6 +74,30 @@ struct RtsArgs {
 constexpr uint32_t kRtsTileElems = 4096u;
 hipError_t launch_rts(const RtsArgs& a, hipStream_t stream);
 
+// Device-wide + reduction to one element (dws_reduce.hip): G workgroups of
+// kReduceThreads threads, each summing tiles_per_group consecutive tiles of
+// kReduceTileElems elements and publishing the partial in its descriptor; the
+// highest-indexed one adds the G partials. A look-back launch of the
+// workspace: it reads the epoch word and advances it.
+struct ReduceArgs {
+    const void* in;
+    uint64_t n;
+    int kind;
+    bool aligned;            // in is 16-byte aligned: dwordx4 loads
+    bool nontemporal;        // non-temporal loads (aligned only)
+    uint64_t* desc;          // >= groups descriptor slots
+    unsigned int* epoch;     // the workspace epoch word
+    unsigned int* watchdog;
+    void* total;             // one element
+    uint32_t num_tiles;
+    uint32_t groups;
+    uint32_t tiles_per_group;
+};
+constexpr int kReduceThreads = 512;
+constexpr uint32_t kReduceTileElems = 16384u;
+constexpr uint32_t kReduceMaxGroups = 1024u;
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
 // Scan-then-propagate: per-tile scans, recursive scan of the tile sums,
 // propagation of the scanned sums (dws_stp.hip).
 struct StpArgs {

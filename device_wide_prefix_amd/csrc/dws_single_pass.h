@@ -20,6 +20,7 @@ struct SinglePassParams {
     uint32_t num_tiles;
     unsigned int* epoch;          // the workspace's epoch word (unused when num_tiles == 1)
     uint32_t backoff;             // pause level between blocked look-back polls (kPause*)
+    const void* seed;             // one element: tile 0's prefix (null: the identity)
 };
 
 // Launch built configuration `cfg` (index into kCfgs) for element type T

@@ -15,9 +15,10 @@
 //      once), the stores never are;
 //   3. lane-serial totals -> wave64 DPP scans -> the wave totals go through
 //      LDS, giving each wave its prefix inside the tile and the tile aggregate;
-//   4. wave 0 publishes {A, aggregate} (tile 0: {P, aggregate}), looks back
-//      over 64 predecessor descriptors per step until the nearest P, and
-//      publishes {P, prefix + aggregate};
+//   4. wave 0 publishes {A, aggregate} (tile 0: {P, seed + aggregate}, the
+//      seed being the caller's one-element prefix of the whole array, or 0),
+//      looks back over 64 predecessor descriptors per step until the nearest
+//      P, and publishes {P, prefix + aggregate};
 //   5. every element gets prefix + wave prefix + chunk/lane prefix + its
 //      serial in-lane prefix, and the tile is stored. The whole tile is in
 //      registers before the first store, so d_out == d_in is safe.
@@ -82,6 +83,10 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     load_segment<T, VEC, CHUNKS, NT>(make_rsrc(static_cast<const T*>(p.in) + seg_first, seg_valid), lane, x);
     if constexpr (TILE_INDEX == kTileDispatch)
         if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
+    // a seeded scan: tile 0's prefix is the caller's element, read while the
+    // tile's loads are in flight
+    uint32_t seed_bits = 0u;
+    if (p.seed != nullptr && tile == 0u && wave == 0) seed_bits = *static_cast<const uint32_t*>(p.seed);
 
     const T seg_total = scan_segment_local<T, EXCL, VEC, CHUNKS>(x);
     pin_in_registers<T, VEC, CHUNKS>(x);
@@ -97,11 +102,12 @@ __global__ void __launch_bounds__(BLOCK) k_single_pass(SinglePassParams p)
     }
 
     if (wave == 0) {
-        T prefix = T(0);
+        T prefix = Elem<T>::from(uniform(seed_bits));
         if (multi) {
             const uint32_t epoch = uniform(epoch_v);
             if (tile == 0u) {
-                if (lane == 0) desc_store<ORDER>(desc_at(p.desc, 0u), desc_pack(epoch, kStatusP, Elem<T>::bits(agg)));
+                if (lane == 0)
+                    desc_store<ORDER>(desc_at(p.desc, 0u), desc_pack(epoch, kStatusP, Elem<T>::bits(prefix + agg)));
             } else {
                 if constexpr (MODE == kModeDecoupled) {
                     if (lane == 0)

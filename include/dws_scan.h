@@ -241,6 +241,56 @@ typedef struct dws_launch_plan {
 dws_status dws_scan_plan(const void* d_in, const void* d_out, size_t n, dws_dtype dtype,
                          int exclusive, const dws_options* opt, dws_launch_plan* plan);
 
+/*
+ * Seeded scan: the single-pass scan of d_in with the DEVICE element *d_seed
+ * (one element of dtype, 4-byte aligned) as the prefix of the whole array:
+ *   inclusive (exclusive == 0): d_out[i] = *d_seed + x[0] + ... + x[i]
+ *   exclusive (exclusive != 0): d_out[i] = *d_seed + x[0] + ... + x[i-1],
+ *                               so d_out[0] = *d_seed
+ * that is, the scan of the sequence *d_seed, x[0], ..., x[n-1] without its
+ * first (inclusive) or last (exclusive) element. It is the last stage of a
+ * reduce-then-scan decomposition taken one level up (Merrill & Garland,
+ * section 3.2 and Fig 3: each block's downsweep scan starts from the scanned
+ * block aggregates): a scan split into contiguous shards scans each shard
+ * seeded with the + of the shards before it (dws_reduce gives each shard's
+ * total). The seed enters as the prefix of tile 0, which reads it while its
+ * loads are in flight; the other tiles receive it through the look-back, so
+ * the call costs what scan_inclusive / scan_exclusive cost. int32 / uint32
+ * wrap mod 2^32; fp32 adds in fp32 (the seed is added to tile 0's aggregate
+ * first). Same validation, kernels and workspace as scan_inclusive; in
+ * addition d_seed == NULL gives DWS_ERR_INVALID_ARG, a d_seed that is not
+ * 4-byte aligned DWS_ERR_MISALIGNED, and a d_seed inside d_out's n elements
+ * DWS_ERR_OVERLAP (it may lie inside d_in when d_out != d_in). n == 0 is a
+ * no-op that does not read *d_seed. The seed is read on `stream` in order
+ * with the caller's earlier work there, so it may be written by a kernel
+ * enqueued just before (dws_reduce, or a scan of shard totals).
+ */
+dws_status dws_scan_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                           int exclusive, const void* d_seed, hipStream_t stream);
+
+/*
+ * Device-wide + reduction: writes x[0] + ... + x[n-1] to the DEVICE element
+ * *d_total (one element of dtype, 4-byte aligned; 0 when n == 0). The first
+ * stage of the reduce-then-scan decomposition (Merrill & Garland, section 3.2
+ * and Fig 3, block-wide reduction), used one level up to give each shard of a
+ * split scan its total. One kernel launch reading the input once (4 bytes per
+ * element): at most 1,024 workgroups each add a contiguous run of
+ * 16,384-element tiles, and the workgroup with the highest index then adds
+ * their partials in index order. int32 / uint32 wrap mod 2^32; fp32 adds in fp32 in an order
+ * fixed by n and by whether d_in is 16-byte aligned, so repeated calls give
+ * the same bits. Validation before any HIP call: an invalid dtype, d_total ==
+ * NULL or d_in == NULL with n > 0 give DWS_ERR_INVALID_ARG; pointers that are
+ * not 4-byte aligned DWS_ERR_MISALIGNED; n above DWS_MAX_ELEMENTS
+ * DWS_ERR_UNSUPPORTED; d_total inside d_in's n elements DWS_ERR_OVERLAP. Each
+ * workgroup publishes its partial as a look-back descriptor of the
+ * per-(device, stream) workspace of the scans, so calls in order on one
+ * stream are safe. Only the highest-indexed workgroup waits, and only on
+ * workgroups that never wait; the wait is bounded like a look-back wait and
+ * counts in dws_watchdog_trips when it expires (the total is then wrong).
+ * Asynchronous on `stream`.
+ */
+dws_status dws_reduce(const void* d_in, size_t n, dws_dtype dtype, void* d_total, hipStream_t stream);
+
 /* Tiles the fixed device array of dws_scan_noalloc has descriptors for (64
  * bytes each), so n may be up to 2^32 elements when both pointers are 16-byte
  * aligned (65,536-element tiles) and up to 2^30 otherwise (16,384). */

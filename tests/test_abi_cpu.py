@@ -367,6 +367,56 @@ def test_noalloc_validation_and_limit(lib):
     assert f(FAKE + 4, big, max_tiles * 16384 + 1, dws.FLOAT32, 1, None) == dws.ERR_UNSUPPORTED
 
 
+def test_scan_seeded_validation(lib):
+    """dws_scan_seeded: the scans' argument checks, then the seed's, all before
+    any HIP call."""
+    f = lib.dws_scan_seeded
+    seed = FAKE + (1 << 41)
+    # n == 0 is a no-op that reads nothing, even the seed
+    assert f(None, None, 0, dws.INT32, 0, None, None) == dws.OK
+    assert f(None, FAKE, 10, dws.INT32, 0, seed, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, 7, 1, seed, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE + 2, FAKE + 4096, 10, dws.UINT32, 0, seed, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, FAKE + 4, 10, dws.INT32, 0, seed, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE + (1 << 40), (1 << 35) + 1, dws.INT32, 0, seed, None) == dws.ERR_UNSUPPORTED
+    # the seed itself
+    assert f(FAKE, FAKE + 4096, 10, dws.FLOAT32, 0, None, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, dws.FLOAT32, 1, seed + 2, None) == dws.ERR_MISALIGNED
+    # inside the output's n elements (first, last), in place or not
+    out = FAKE + 4096
+    assert f(FAKE, out, 10, dws.INT32, 0, out, None) == dws.ERR_OVERLAP
+    assert f(FAKE, out, 10, dws.INT32, 0, out + 36, None) == dws.ERR_OVERLAP
+    assert f(FAKE, FAKE, 10, dws.INT32, 1, FAKE + 8, None) == dws.ERR_OVERLAP
+    # (a seed just outside the output, or inside an input that is not the
+    # output, passes these checks: the GPU tests run such calls)
+
+
+def test_reduce_validation(lib):
+    """dws_reduce: argument checks before any HIP call."""
+    f = lib.dws_reduce
+    total = FAKE + (1 << 41)
+    assert f(FAKE, 10, 7, total, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, 10, -1, total, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, 10, dws.INT32, None, None) == dws.ERR_INVALID_ARG
+    assert f(None, 10, dws.INT32, total, None) == dws.ERR_INVALID_ARG
+    assert f(None, 0, dws.INT32, None, None) == dws.ERR_INVALID_ARG   # the total is written even for n == 0
+    assert f(FAKE + 2, 10, dws.FLOAT32, total, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, 10, dws.FLOAT32, total + 1, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, (1 << 35) + 1, dws.UINT32, total, None) == dws.ERR_UNSUPPORTED
+    # the total inside the input's n elements
+    assert f(FAKE, 10, dws.INT32, FAKE, None) == dws.ERR_OVERLAP
+    assert f(FAKE, 10, dws.INT32, FAKE + 36, None) == dws.ERR_OVERLAP
+
+
+def test_seeded_and_reduce_bindings_refuse_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(8, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        dws.reduce(x)
+    with pytest.raises(TypeError):
+        dws.scan_seeded(x, torch.zeros(1))
+
+
 # ---------------------------------------------------------------------------
 # the launch the library chooses (dws_scan_plan: no HIP call, no launch)
 # ---------------------------------------------------------------------------
