@@ -258,5 +258,36 @@ def test_sharded_headline_scan(gpu):
     note(f"sharded headline scan: parity ok, max fp32 tolerance ratio {worst:.3g}")
 
 
+def test_sharded_scan_graph_replays(gpu):
+    """The per-device steps captured in one graph: every replay reads the
+    epoch word the previous launch on the workspace advanced, so it sees only
+    its own partials and descriptors. Eager launches on the same workspace run
+    between replays, and every replay is checked against the oracle."""
+    import torch
+    n = (1 << 22) + 7
+    cut = [1_000_003, 1_000_003 + (1 << 21)]
+    s = torch.cuda.Stream()
+    x = torch.empty(n, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(x)
+    dws.reserve(n, stream=s.cuda_stream)
+    with torch.cuda.stream(s):          # warm-up outside the capture
+        _sharded_scan(x, out, n, "int32", True, cut)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _sharded_scan(x, out, n, "int32", True, cut)
+    for rep in range(4):
+        note(f"sharded graph replay rep={rep}")
+        data = wl.random_input("int32", n, seed=400 + rep)
+        x.copy_(torch.from_numpy(data))
+        with torch.cuda.stream(s):        # eager launches on the workspace between replays
+            dws.reduce(x)
+            dws.scan_inclusive(x, torch.empty_like(x))
+        s.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_chunked(data, from_device(out, "int32"), "int32", True, label=f"replay {rep}")
+
+
 def test_zz_shard_watchdog_never_tripped(gpu):
     assert dws.watchdog_trips() == 0
