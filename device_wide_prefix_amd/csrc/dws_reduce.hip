@@ -14,10 +14,10 @@
 // index order, writes the total and advances the epoch. It is the only
 // workgroup that waits, and only on workgroups that never wait, so the wait
 // ends whatever order the workgroups run in (the watchdog bounds it all the
-// same). Electing the last to finish with a counter instead measured 2.5 to
-// 3.7 times slower at 2^25 elements: the 1,024 to 2,048 device-scope atomics
+// same). Electing the last to finish with a counter instead measured 1.75 to
+// 3.5 times slower at 2^25 elements: the 1,024 to 2,048 device-scope atomics
 // on one word, issued in one burst as the workgroups finish together,
-// serialise at about 40 to 50 ns each. Every addition's operands and order
+// serialise at about 11 to 32 ns each. Every addition's operands and order
 // depend on n and on whether the input is 16-byte aligned only, so repeated
 // calls return the same bits for fp32.
 #include "dws_device.hpp"
