@@ -1,8 +1,10 @@
 /*
  * Calling the scan library from C through its C ABI (include/dws_scan.h):
  * device buffers from hipMalloc, a stream, an exclusive scan in place, a
- * compaction with its count in device memory, and a check of both results on
- * the host with exact integer arithmetic. Exit status 0 on success.
+ * compaction with its count in device memory, the same scan split into two
+ * shards (each shard's total, the scan of the totals, each shard scanned seeded
+ * with its offset), and a check of every result on the host with exact
+ * integer arithmetic. Exit status 0 on success.
  *
  * Build: hipcc -I include scan_from_c.c -L device_wide_prefix_amd -ldws_scan
  *        -Wl,-rpath,<that directory> -o scan_from_c
@@ -96,6 +98,31 @@ int main(int argc, char** argv)
         return 1;
     }
 
+    /* the exclusive scan again, as two shards of n / 2 and n - n / 2 elements:
+     * totals (dws_reduce), their exclusive scan, then each shard scanned
+     * seeded with its offset (dws_scan_seeded), all enqueued on the stream */
+    uint32_t *d_tot, *d_off;
+    CHECK_HIP(hipMalloc((void**)&d_tot, 2 * sizeof(uint32_t)));
+    CHECK_HIP(hipMalloc((void**)&d_off, 2 * sizeof(uint32_t)));
+    const size_t half = n / 2;
+    CHECK_DWS(dws_reduce(d_x, half, DWS_UINT32, d_tot, stream));
+    CHECK_DWS(dws_reduce(d_x + half, n - half, DWS_UINT32, d_tot + 1, stream));
+    CHECK_DWS(scan_exclusive(d_tot, d_off, 2, DWS_UINT32, stream));
+    CHECK_DWS(dws_scan_seeded(d_x, d_out, half, DWS_UINT32, 1, d_off, stream));
+    CHECK_DWS(dws_scan_seeded(d_x + half, d_out + half, n - half, DWS_UINT32, 1, d_off + 1, stream));
+    CHECK_HIP(hipMemcpyAsync(h_y, d_out, n * sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    running = 0u;
+    for (size_t i = 0; i < n; ++i) {
+        if (h_y[i] != running) {
+            fprintf(stderr, "two-shard scan mismatch at %zu: %u != %u\n", i, h_y[i], running);
+            return 1;
+        }
+        running += h_x[i];
+    }
+    CHECK_HIP(hipFree(d_tot));
+    CHECK_HIP(hipFree(d_off));
+
     /* errors come back as status codes, before any work is enqueued: with
      * n >= 2, d_x + 1 .. d_x + n overlaps d_x .. d_x + n - 1 without equalling it */
     if (n >= 2 && scan_exclusive(d_x, d_x + 1, n, DWS_UINT32, stream) != DWS_ERR_OVERLAP) {
@@ -109,7 +136,7 @@ int main(int argc, char** argv)
     CHECK_HIP(hipFree(d_count));
     CHECK_DWS(dws_release_workspaces());
     CHECK_HIP(hipStreamDestroy(stream));
-    printf("scan_from_c: n=%zu exclusive scan and compaction (%llu selected) correct\n", n, count);
+    printf("scan_from_c: n=%zu exclusive scan, compaction (%llu selected) and two-shard scan correct\n", n, count);
     free(h_x);
     free(h_f);
     free(h_y);

@@ -1,6 +1,7 @@
 """The C ABI used from a C program (device_wide_prefix_amd/examples/
 scan_from_c.c): it compiles against include/dws_scan.h and the built library
-here; on a GPU it runs a scan and a compaction and checks them itself."""
+here; on a GPU it runs a scan, a compaction and a two-shard scan (dws_reduce,
+dws_scan_seeded) and checks them itself."""
 import os
 import subprocess
 
