@@ -1,5 +1,5 @@
-"""GPU scans past 2^32 elements and at the largest supported count (2^35,
-DWS_MAX_ELEMENTS in include/dws_scan.h), in place.
+"""GPU scans (and totals) past 2^32 elements and at the largest supported
+count (2^35, DWS_MAX_ELEMENTS in include/dws_scan.h), in place.
 
 An all-ones input has a closed form: the exclusive scan is y[i] = i and the
 inclusive one y[i] = i + 1, modulo 2^32 for 32-bit integers, so the result is
@@ -47,6 +47,33 @@ def test_all_ones_past_32_bits(gpu, n, exclusive):
         (dws.scan_exclusive if exclusive else dws.scan_inclusive)(x, out=x)
         torch.cuda.synchronize()
         _check_ramp(x, n, 0 if exclusive else 1, f"n={n} exclusive={exclusive}")
+    finally:
+        del x
+        torch.cuda.empty_cache()
+    assert dws.watchdog_trips() == 0
+
+
+@pytest.mark.parametrize("n", [(1 << 32) + 12345, MAX_ELEMENTS], ids=["2^32+12345", "2^35"])
+def test_reduce_and_seeded_scan_past_32_bits(gpu, n):
+    # the + of n ones is n (mod 2^32 for int32; fp32 within the bar of the
+    # scans), and the exclusive scan of ones seeded with s is s + i
+    import torch
+    _need(4 * n)
+    x = torch.ones(n, dtype=torch.int32, device="cuda")
+    try:
+        note(f"reduce of n={n} int32 ones")
+        assert int(dws.reduce(x).item()) & 0xFFFFFFFF == n & 0xFFFFFFFF
+        note(f"reduce of n={n} fp32 ones")
+        xf = x.view(torch.float32)
+        xf.fill_(1.0)
+        total = float(dws.reduce(xf).item())
+        assert abs(total - n) <= 1e-4 * n + 1e-6, total
+        note(f"seeded exclusive scan of n={n} int32 ones, seed 7, in place")
+        x.fill_(1)
+        seed = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+        dws.scan_seeded(x, seed, exclusive=True, out=x)
+        torch.cuda.synchronize()
+        _check_ramp(x, n, 7, f"seeded n={n}")
     finally:
         del x
         torch.cuda.empty_cache()
