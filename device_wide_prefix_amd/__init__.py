@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
     "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc", "dws_scan_plan", "dws_scan_seeded",
-    "dws_reduce",
+    "dws_reduce", "dws_scan_op_seeded",
 )
 
 
@@ -100,6 +100,8 @@ def load_library():
     lib.dws_scan_seeded.restype = ci
     lib.dws_reduce.argtypes = [vp, sz, ci, vp, vp]
     lib.dws_reduce.restype = ci
+    lib.dws_scan_op_seeded.argtypes = [vp, vp, sz, ci, ci, ci, vp, vp]
+    lib.dws_scan_op_seeded.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -350,12 +352,19 @@ def scan_op_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: b
     return load_library().dws_scan_op(d_in, d_out, n, dtype, op, int(bool(exclusive)), stream)
 
 
-def scan_op(x, op, dtype=None, exclusive=False, out=None, stream=None):
+def scan_op_seeded_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: bool, d_seed: int,
+                       stream: int = 0) -> int:
+    return load_library().dws_scan_op_seeded(d_in, d_out, n, dtype, op, int(bool(exclusive)), d_seed, stream)
+
+
+def scan_op(x, op, dtype=None, exclusive=False, out=None, stream=None, seed=None):
     """Scan of a contiguous GPU tensor under a generic operator (OP_*).
 
     For the 32-bit types dtype defaults from the tensor. Pair types
     (PAIR_I32_F32, PAIR_U32) take any contiguous tensor whose bytes hold the
     pairs, e.g. an (n, 2) int32 tensor of bits; n is its byte size / 8.
+    ``seed``: a GPU tensor on x's device whose bytes hold one element, the
+    initial value before the whole array (dws_scan_op_seeded).
     Returns ``out`` (same shape and dtype as x; may be x)."""
     import torch
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
@@ -372,6 +381,14 @@ def scan_op(x, op, dtype=None, exclusive=False, out=None, stream=None):
         out = torch.empty_like(x)
     if out.numel() * out.element_size() != nbytes or not out.is_contiguous() or out.device != x.device:
         raise ValueError("out must be a contiguous tensor of the same byte size on the device of x")
+    if seed is not None:
+        if not isinstance(seed, torch.Tensor) or seed.device != x.device or not seed.is_contiguous() or \
+                seed.numel() * seed.element_size() != esize:
+            raise ValueError(f"seed must be a contiguous tensor of {esize} bytes on the device of x")
+        with _device_of(x):
+            _check(scan_op_seeded_ptr(x.data_ptr(), out.data_ptr(), nbytes // esize, int(dtype), int(op),
+                                      exclusive, seed.data_ptr(), _stream(x, stream)), "dws_scan_op_seeded")
+        return out
     with _device_of(x):
         _check(scan_op_ptr(x.data_ptr(), out.data_ptr(), nbytes // esize, int(dtype), int(op), exclusive,
                            _stream(x, stream)), "dws_scan_op")

@@ -101,6 +101,21 @@ dws_status validate(const void* in, const void* out, size_t n, int dtype)
 
 int kind_of(int dtype) { return dtype == DWS_FLOAT32 ? kKindF32 : kKindU32; }
 
+// The seed of a seeded scan: one element of `esize` bytes, 4-byte aligned,
+// outside the output's n elements (tile 0 reads it before it publishes and
+// every store of the call follows that publication, but an output range that
+// held the seed would still be a caller's error, so it is refused outright).
+dws_status check_seed(const void* seed, const void* out, size_t n, size_t esize)
+{
+    if (seed == nullptr) return DWS_ERR_INVALID_ARG;
+    const uintptr_t sd = reinterpret_cast<uintptr_t>(seed);
+    if (sd % kElemBytes != 0) return DWS_ERR_MISALIGNED;
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(out);
+    if (sd + esize < sd) return DWS_ERR_INVALID_ARG;
+    if (sd + esize > ob && sd < ob + (uintptr_t)n * esize) return DWS_ERR_OVERLAP;
+    return DWS_OK;
+}
+
 bool aligned16(const void* in, const void* out)
 {
     return ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15u) == 0;
@@ -494,7 +509,8 @@ hipError_t launch_op_kind(int kind, bool exclusive, int shape, bool nt, const Op
     }
 }
 
-dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl, hipStream_t stream)
+dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl, hipStream_t stream,
+                       const void* seed = nullptr)
 {
     const int words = op_kind_words(kind);
     const bool aligned = aligned16(in, out);
@@ -515,6 +531,7 @@ dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl,
     p.n = n;
     p.num_tiles = (uint32_t)num_tiles;
     p.backoff = op_backoff(n);
+    p.seed = seed;
     if (num_tiles == 1) return from_hip(launch_op_kind(kind, excl, shape, false, p, stream));
     Workspace* ws = nullptr;
     dws_status s = get_workspace(stream, &ws);
@@ -586,16 +603,34 @@ dws_status dws_scan_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dt
         const int dt = enum_arg(dtype);
         dws_status s = validate(d_in, d_out, n, dt);
         if (s != DWS_OK || n == 0) return s;
-        if (d_seed == nullptr) return DWS_ERR_INVALID_ARG;
-        const uintptr_t sd = reinterpret_cast<uintptr_t>(d_seed);
-        if (sd % kElemBytes != 0) return DWS_ERR_MISALIGNED;
-        // tile 0 reads the seed before it publishes, and every store of the
-        // call follows that publication; an output range that held the seed
-        // would still be an error, so it is refused outright
-        const uintptr_t ob = reinterpret_cast<uintptr_t>(d_out);
-        if (sd + kElemBytes > ob && sd < ob + (uintptr_t)n * kElemBytes) return DWS_ERR_OVERLAP;
+        s = check_seed(d_seed, d_out, n, kElemBytes);
+        if (s != DWS_OK) return s;
         const dws_options o{};
         return run_single_pass(d_in, d_out, n, dt, exclusive != 0, kModeDecoupled, o, stream, nullptr, d_seed);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_scan_op_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_op op, int exclusive,
+                              const void* d_seed, hipStream_t stream)
+{
+    try {
+        const int dt = enum_arg(dtype), o = enum_arg(op);
+        if (dt < DWS_INT32 || dt > DWS_PAIR_U32) return DWS_ERR_INVALID_ARG;
+        if (o < DWS_OP_SUM || o > DWS_OP_SEGMENTED_SUM) return DWS_ERR_INVALID_ARG;
+        if (o == DWS_OP_SUM && valid_dtype(dt))
+            return dws_scan_seeded(d_in, d_out, n, dtype, exclusive, d_seed, stream);
+        const int kind = op_kind(dt, o);
+        if (kind < 0) return DWS_ERR_UNSUPPORTED;
+        const size_t esize = 4u * (size_t)op_kind_words(kind);
+        dws_status s = validate_sized(d_in, d_out, n, esize);
+        if (s != DWS_OK || n == 0) return s;
+        s = check_seed(d_seed, d_out, n, esize);
+        if (s != DWS_OK) return s;
+        return run_scan_op(d_in, d_out, n, kind, exclusive != 0, stream, d_seed);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

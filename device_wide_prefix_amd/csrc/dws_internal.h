@@ -192,6 +192,7 @@ struct OpScanParams {
     uint32_t num_tiles;
     unsigned int* epoch;     // the workspace epoch word
     uint32_t backoff;        // pause level between blocked look-back polls (kPause*)
+    const void* seed;        // one element (its words): tile 0's prefix (null: the identity)
 };
 enum OpKind : int {
     kOpMaxI32, kOpMaxU32, kOpMinI32, kOpMinU32,          // one word

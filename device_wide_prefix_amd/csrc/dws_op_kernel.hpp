@@ -435,6 +435,14 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     uint32_t raw[CHUNKS][LOADW];
     load_words<LOADW, CHUNKS, NT>(make_rsrc(static_cast<const char*>(p.in) + seg_first * ESIZE, vb), lane, raw);
     if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
+    // a seeded scan: tile 0's prefix is the caller's element, the earlier
+    // operand of every combine it enters, read while the tile's loads are in
+    // flight
+    V seed_v = Op::identity();
+    if (p.seed != nullptr && tile == 0u && wave == 0) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) seed_v.w[k] = static_cast<const uint32_t*>(p.seed)[k];
+    }
 
     V x[CHUNKS][E];
 #pragma unroll
@@ -462,11 +470,13 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
     }
 
     if (wave == 0) {
-        V prefix = Op::identity();
+        V prefix;
+#pragma unroll
+        for (int k = 0; k < W; ++k) prefix.w[k] = uniform(seed_v.w[k]);
         if (multi) {
             const uint32_t epoch = uniform(epoch_v);
             if (tile == 0u) {
-                if (lane == 0) desc_store_val<W>(p.desc, 0u, epoch, kStatusP, agg);
+                if (lane == 0) desc_store_val<W>(p.desc, 0u, epoch, kStatusP, Op::combine(prefix, agg));
             } else {
                 if (lane == 0) desc_store_val<W>(p.desc, tile, epoch, kStatusA, agg);
                 prefix = lookback_op<Op, kOpLookbackSlots>(p.desc, tile, epoch, p.watchdog, p.backoff);

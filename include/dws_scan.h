@@ -422,6 +422,28 @@ typedef enum dws_op {
 dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                        dws_op op, int exclusive, hipStream_t stream);
 
+/*
+ * dws_scan_op with an initial value: the DEVICE element *d_seed (one element
+ * of `dtype`: 4 bytes, or 8 for the pair types; 4-byte aligned) comes before
+ * the whole array, as the earlier operand of every combine it enters. The
+ * inclusive result is the scan of the sequence *d_seed, x[0], ..., x[n-1]
+ * without its first element, the exclusive one that scan without its last
+ * (so d_out[0] = *d_seed). For DWS_OP_AFFINE the seed map runs first, and for
+ * DWS_OP_SEGMENTED_SUM it is the running value of a segment that x[0]
+ * continues unless its flag is set. Together with an inclusive scan's last
+ * element as a shard's total, it gives every operator the sharded scan that
+ * dws_reduce and dws_scan_seeded give +. The seed enters as the prefix of tile
+ * 0 (Merrill & Garland, section 4.2: only contiguous partial results are
+ * combined, in input order); the other tiles receive it through the
+ * look-back. DWS_OP_SUM with the 32-bit scalar types is dws_scan_seeded.
+ * Validation and errors are those of dws_scan_op, then those of
+ * dws_scan_seeded for d_seed (NULL: DWS_ERR_INVALID_ARG; not 4-byte aligned:
+ * DWS_ERR_MISALIGNED; inside d_out's n elements: DWS_ERR_OVERLAP). n == 0 is a
+ * no-op that does not read *d_seed. Asynchronous on `stream`.
+ */
+dws_status dws_scan_op_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
+                              dws_op op, int exclusive, const void* d_seed, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* dws_status_string(dws_status status);
 

@@ -391,6 +391,31 @@ def test_scan_seeded_validation(lib):
     # output, passes these checks: the GPU tests run such calls)
 
 
+def test_scan_op_seeded_validation(lib):
+    """dws_scan_op_seeded: dws_scan_op's checks, then the seed's, before any
+    HIP call; + on a 32-bit scalar is dws_scan_seeded."""
+    f = lib.dws_scan_op_seeded
+    seed = FAKE + (1 << 41)
+    assert f(None, None, 0, dws.PAIR_U32, dws.OP_AFFINE, 0, None, None) == dws.OK
+    assert f(FAKE, FAKE + 4096, 10, 9, dws.OP_MAX, 0, seed, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, dws.INT32, 7, 0, seed, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4096, 10, dws.FLOAT32, dws.OP_MAX, 0, seed, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE + 4096, 10, dws.INT32, dws.OP_AFFINE, 0, seed, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE + 4, FAKE + 4096, 10, dws.PAIR_U32, dws.OP_AFFINE, 0, seed, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, FAKE + 8, 10, dws.PAIR_U32, dws.OP_AFFINE, 0, seed, None) == dws.ERR_OVERLAP
+    for op, dt in ((dws.OP_MAX, dws.INT32), (dws.OP_SEGMENTED_SUM, dws.PAIR_I32_F32), (dws.OP_SUM, dws.UINT32)):
+        esize = 4 if dt in (dws.INT32, dws.UINT32) else 8
+        out = FAKE + 4096
+        assert f(FAKE, out, 10, dt, op, 1, None, None) == dws.ERR_INVALID_ARG
+        assert f(FAKE, out, 10, dt, op, 1, seed + 2, None) == dws.ERR_MISALIGNED
+        # inside the output's 10 elements: first and last element
+        assert f(FAKE, out, 10, dt, op, 0, out, None) == dws.ERR_OVERLAP
+        assert f(FAKE, out, 10, dt, op, 0, out + 9 * esize, None) == dws.ERR_OVERLAP
+        # an 8-byte seed that straddles the output's first byte
+        if esize == 8:
+            assert f(FAKE, out, 10, dt, op, 0, out - 4, None) == dws.ERR_OVERLAP
+
+
 def test_reduce_validation(lib):
     """dws_reduce: argument checks before any HIP call."""
     f = lib.dws_reduce

@@ -56,9 +56,10 @@ def expected(name, x, exclusive):
     raise KeyError(name)
 
 
-def run_op(name, x, exclusive, in_place=False, offset_elems=0):
-    """Upload x, run dws_scan_op through the C ABI, return the result as
-    uint32 bits with x's shape."""
+def run_op(name, x, exclusive, in_place=False, offset_elems=0, seed=None):
+    """Upload x, run dws_scan_op (dws_scan_op_seeded with ``seed``, one
+    element of x's kind) through the C ABI, return the result as uint32 bits
+    with x's shape."""
     import torch
     op, dtype, _, words = COMBOS[name]
     n = x.shape[0]
@@ -73,13 +74,19 @@ def run_op(name, x, exclusive, in_place=False, offset_elems=0):
         ostore = torch.empty(flat.size + pad, dtype=torch.int32, device="cuda")
         out = ostore[pad:]
     stream = torch.cuda.current_stream().cuda_stream
-    st = dws.scan_op_ptr(xd.data_ptr(), out.data_ptr(), n, dtype, op, exclusive, stream)
+    if seed is None:
+        st = dws.scan_op_ptr(xd.data_ptr(), out.data_ptr(), n, dtype, op, exclusive, stream)
+    else:
+        sd = torch.from_numpy(np.ascontiguousarray(seed).view(np.uint32).reshape(-1).view(np.int32)).to("cuda")
+        st = dws.scan_op_seeded_ptr(xd.data_ptr(), out.data_ptr(), n, dtype, op, exclusive, sd.data_ptr(), stream)
     assert st == dws.OK, dws.status_string(st)
     return out.cpu().numpy().view(np.uint32).reshape(x.shape)
 
 
-def check_op(name, x, y, exclusive, label):
-    exact, yf, sabs = expected(name, x, exclusive)
+def check_op(name, x, y, exclusive, label, ref=None):
+    """y against the oracle's scan of x, or against ``ref`` (the same triple
+    expected() returns) when given."""
+    exact, yf, sabs = expected(name, x, exclusive) if ref is None else ref
     if yf is None:
         if not np.array_equal(y, exact):
             bad = np.flatnonzero(np.any((y != exact).reshape(y.shape[0], -1), axis=1))
@@ -123,6 +130,28 @@ def test_op_in_place_and_unaligned(gpu, name):
             check_op(name, x, run_op(name, x, exclusive, offset_elems=1), exclusive, f"{name} unaligned n={n}")
             check_op(name, x, run_op(name, x, exclusive, in_place=True, offset_elems=1), exclusive,
                      f"{name} unaligned in place n={n}")
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("name", list(COMBOS))
+def test_op_seeded(gpu, name, exclusive):
+    """dws_scan_op_seeded against the oracle's scan of the sequence seed,
+    x[0], ..., x[n-1] without its first (inclusive) or last (exclusive)
+    element: the seed is the earlier operand of every combine it enters."""
+    kind = COMBOS[name][2]
+    for i, n in enumerate((1, 5, 3 * 4096 + 5, (1 << 20) + 7, (1 << 25) + 9)):
+        x = wl.op_input(kind, n, seed=3 * n + 1)
+        seed = wl.op_input(kind, 1, seed=1000 + i)
+        if name.startswith("segsum") and i % 2 == 1:
+            seed[0, 0] = 0       # a seed without a head: x[0] continues its segment
+        in_place = i % 2 == 0
+        note(f"op={name} seeded excl={exclusive} n={n} in_place={in_place}")
+        y = run_op(name, x, exclusive, in_place=in_place, seed=seed)
+        z = np.concatenate([seed, x])
+        exact, yf, sabs = expected(name, z, False)
+        part = slice(0, -1) if exclusive else slice(1, None)
+        ref = (exact[part], None if yf is None else yf[part], None if sabs is None else sabs[part])
+        check_op(name, x, y, exclusive, f"{name} seeded n={n}", ref=ref)
 
 
 def test_segsum_head_densities(gpu):
