@@ -394,7 +394,9 @@ def op_property_check(name: str, x: np.ndarray, y: np.ndarray) -> bool:
 def run_ops(steps: int, warmup: int, with_oracle: bool = True):
     """Generic-operator scans of 1 GiB of input (2^28 32-bit or 2^27 pair
     elements), out of place, cold caches; GB/s counts 2 x the input bytes,
-    like the + scan, against a same-size memcpy. One OPS line per operator."""
+    like the + scan, against a same-size memcpy; and the reduction of the same
+    input under the operator (dws_reduce_op; GB/s counts the input bytes once).
+    One OPS line per operator."""
     import torch
     import device_wide_prefix_amd as dws
     rows = []
@@ -420,12 +422,34 @@ def run_ops(steps: int, warmup: int, with_oracle: bool = True):
         times = time_steps(scan, prepare, steps, warmup)
         y = out.cpu().numpy().view(np.uint32).reshape(x.shape)
         ok = op_property_check(name, x, y)
+        # the same input's total under the operator (dws_reduce_op, n * esize
+        # bytes read): the inclusive scan's last element, fp32 parts within
+        # the scans' bar
+        total = torch.zeros(esize // 4, dtype=torch.int32, device="cuda")
+
+        def reduce():
+            st = dws.reduce_op_ptr(xd.data_ptr(), n, dtype, op, total.data_ptr(), stream)
+            if st != dws.OK:
+                raise RuntimeError(f"{name} reduce: {dws.status_string(st)}")
+
+        rtimes = time_steps(reduce, prepare, steps, warmup)
+        tw = total.cpu().numpy().view(np.uint32)
+        last = y.reshape(n, -1)[-1]
+        if name in ("sum_pair_i32_f32", "segsum_i32_f32"):
+            xs = x.reshape(n, -1)[:, 1].view(np.float32).astype(np.float64)
+            scale = float(np.abs(xs).sum())
+            ok = ok and tw[0] == last[0] and abs(float(tw[1:2].view(np.float32)[0])
+                                               - float(last[1:2].view(np.float32)[0])) <= 2e-4 * scale + 1e-6
+        else:
+            ok = ok and np.array_equal(tw, last)
         mc = time_steps(lambda: hip.memcpy_d2d(out.data_ptr(), xd.data_ptr(), n * esize, stream), prepare,
                         steps, warmup)
         mean, mcm = float(np.mean(times)), float(np.mean(mc))
         row = {"op": name, "n": n, "element_bytes": esize, "ms_mean": mean, "ms_min": float(np.min(times)),
                "gbps": 2 * n * esize / (mean * 1e-3) / 1e9, "memcpy_gbps": 2 * n * esize / (mcm * 1e-3) / 1e9,
                "frac_memcpy": mcm / mean, "frac_hbm_peak": 2 * n * esize / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "reduce_ms_mean": float(np.mean(rtimes)),
+               "reduce_gbps": n * esize / (float(np.mean(rtimes)) * 1e-3) / 1e9,
                "property_check": ok}
         if with_oracle:
             m = min(n, ORACLE_SAMPLE // 4)

@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
     "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc", "dws_scan_plan", "dws_scan_seeded",
-    "dws_reduce", "dws_scan_op_seeded",
+    "dws_reduce", "dws_scan_op_seeded", "dws_reduce_op",
 )
 
 
@@ -102,6 +102,8 @@ def load_library():
     lib.dws_reduce.restype = ci
     lib.dws_scan_op_seeded.argtypes = [vp, vp, sz, ci, ci, ci, vp, vp]
     lib.dws_scan_op_seeded.restype = ci
+    lib.dws_reduce_op.argtypes = [vp, sz, ci, ci, vp, vp]
+    lib.dws_reduce_op.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -355,6 +357,35 @@ def scan_op_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: b
 def scan_op_seeded_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: bool, d_seed: int,
                        stream: int = 0) -> int:
     return load_library().dws_scan_op_seeded(d_in, d_out, n, dtype, op, int(bool(exclusive)), d_seed, stream)
+
+
+def reduce_op_ptr(d_in: int, n: int, dtype: int, op: int, d_total: int, stream: int = 0) -> int:
+    return load_library().dws_reduce_op(d_in, n, dtype, op, d_total, stream)
+
+
+def reduce_op(x, op, dtype=None, out=None, stream=None):
+    """Combination under ``op`` of every element of x in order (dws_reduce_op)
+    into ``out``: a GPU tensor of one element's bytes (a new int32 tensor of 1
+    or 2 words by default, bits as for scan_op). Returns ``out``."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("reduce_op expects a GPU tensor (there is no CPU path)")
+    if not x.is_contiguous():
+        raise ValueError("input tensor must be contiguous")
+    if dtype is None:
+        dtype = _dtype_code(x)
+    esize = 8 if dtype in (PAIR_I32_F32, PAIR_U32) else 4
+    nbytes = x.numel() * x.element_size()
+    if nbytes % esize:
+        raise ValueError(f"tensor of {nbytes} bytes does not hold whole {esize}-byte elements")
+    if out is None:
+        out = torch.empty(esize // 4, dtype=torch.int32, device=x.device)
+    if out.numel() * out.element_size() != esize or not out.is_contiguous() or out.device != x.device:
+        raise ValueError(f"out must be a contiguous tensor of {esize} bytes on the device of x")
+    with _device_of(x):
+        _check(reduce_op_ptr(x.data_ptr(), nbytes // esize, int(dtype), int(op), out.data_ptr(),
+                             _stream(x, stream)), "dws_reduce_op")
+    return out
 
 
 def scan_op(x, op, dtype=None, exclusive=False, out=None, stream=None, seed=None):

@@ -509,6 +509,55 @@ hipError_t launch_op_kind(int kind, bool exclusive, int shape, bool nt, const Op
     }
 }
 
+hipError_t launch_reduce_op_kind(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream)
+{
+    switch (kind) {
+    case kOpMaxI32:
+    case kOpMaxU32:
+    case kOpMinI32:
+    case kOpMinU32: return launch_reduce_op_minmax(kind, aligned, nt, p, stream);
+    case kOpSumPairIF:
+    case kOpSumPairU32: return launch_reduce_op_pairsum(kind, aligned, nt, p, stream);
+    case kOpAffineU32: return launch_reduce_op_affine(kind, aligned, nt, p, stream);
+    case kOpSegSumIF:
+    case kOpSegSumU32: return launch_reduce_op_segsum(kind, aligned, nt, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Reduction under an operator into one element (validated arguments): the
+// grid of run_reduce, with the operator's tile size.
+dws_status run_reduce_op(const void* in, size_t n, int kind, void* total, hipStream_t stream)
+{
+    const int words = op_kind_words(kind);
+    const bool aligned = (reinterpret_cast<uintptr_t>(in) & 15u) == 0;
+    const uint64_t num_tiles = ceil_div(n, op_reduce_tile_elems(words, aligned));
+    if (num_tiles > 0xffffffffull) return DWS_ERR_UNSUPPORTED;
+    uint64_t groups = std::max<uint64_t>(1u, std::min<uint64_t>(num_tiles, kReduceMaxGroups));
+    const uint64_t tpg = ceil_div(num_tiles, groups);
+    if (tpg > 0) groups = ceil_div(num_tiles, tpg);
+    Workspace* ws = nullptr;
+    dws_status s = get_workspace(stream, &ws);
+    if (s != DWS_OK) return s;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    s = ensure_desc(ws, groups * kDescStride);
+    if (s != DWS_OK) return s;
+    s = before_lookback_launch(ws);
+    if (s != DWS_OK) return s;
+    OpReduceParams p{};
+    p.in = in;
+    p.n = n;
+    p.num_tiles = (uint32_t)num_tiles;
+    p.tiles_per_group = (uint32_t)tpg;
+    p.groups = (uint32_t)groups;
+    p.desc = ws->desc;
+    p.epoch = ws->epoch();
+    p.watchdog = ws->watchdog();
+    p.total = total;
+    // each input word is read once, as in the operator scans' tiles
+    return from_hip(launch_reduce_op_kind(kind, aligned, aligned && n >= kOpNtMin, p, stream));
+}
+
 dws_status run_scan_op(const void* in, void* out, size_t n, int kind, bool excl, hipStream_t stream,
                        const void* seed = nullptr)
 {
@@ -650,6 +699,32 @@ dws_status dws_reduce(const void* d_in, size_t n, dws_dtype dtype, void* d_total
         if (a % kElemBytes != 0 || t % kElemBytes != 0) return DWS_ERR_MISALIGNED;
         if (n > 0 && t + kElemBytes > a && t < a + (uintptr_t)n * kElemBytes) return DWS_ERR_OVERLAP;
         return run_reduce(d_in, n, dt, d_total, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_reduce_op(const void* d_in, size_t n, dws_dtype dtype, dws_op op, void* d_total,
+                         hipStream_t stream)
+{
+    try {
+        const int dt = enum_arg(dtype), o = enum_arg(op);
+        if (dt < DWS_INT32 || dt > DWS_PAIR_U32) return DWS_ERR_INVALID_ARG;
+        if (o < DWS_OP_SUM || o > DWS_OP_SEGMENTED_SUM) return DWS_ERR_INVALID_ARG;
+        if (o == DWS_OP_SUM && valid_dtype(dt)) return dws_reduce(d_in, n, dtype, d_total, stream);
+        const int kind = op_kind(dt, o);
+        if (kind < 0) return DWS_ERR_UNSUPPORTED;
+        const size_t esize = 4u * (size_t)op_kind_words(kind);
+        if (d_total == nullptr || (n > 0 && d_in == nullptr)) return DWS_ERR_INVALID_ARG;
+        if (n > DWS_MAX_ELEMENTS) return DWS_ERR_UNSUPPORTED;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(d_in);
+        const uintptr_t t = reinterpret_cast<uintptr_t>(d_total);
+        if (a % esize != 0 || t % kElemBytes != 0) return DWS_ERR_MISALIGNED;
+        if (a + (uintptr_t)n * esize < a || t + esize < t) return DWS_ERR_INVALID_ARG;
+        if (n > 0 && t + esize > a && t < a + (uintptr_t)n * esize) return DWS_ERR_OVERLAP;
+        return run_reduce_op(d_in, n, kind, d_total, stream);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

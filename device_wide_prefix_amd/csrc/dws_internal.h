@@ -194,6 +194,20 @@ struct OpScanParams {
     uint32_t backoff;        // pause level between blocked look-back polls (kPause*)
     const void* seed;        // one element (its words): tile 0's prefix (null: the identity)
 };
+// Reduction under an operator (k_reduce_op in dws_op_kernel.hpp): the grid of
+// the + reduction (kReduceThreads threads, at most kReduceMaxGroups groups of
+// tiles_per_group consecutive tiles).
+struct OpReduceParams {
+    const void* in;
+    uint64_t n;                   // elements
+    uint32_t num_tiles;
+    uint32_t tiles_per_group;
+    uint32_t groups;
+    uint64_t* desc;               // >= groups descriptor slots
+    unsigned int* epoch;          // the workspace epoch word
+    unsigned int* watchdog;
+    void* total;                  // one element (its words)
+};
 enum OpKind : int {
     kOpMaxI32, kOpMaxU32, kOpMinI32, kOpMinU32,          // one word
     kOpSumPairIF, kOpSumPairU32, kOpAffineU32, kOpSegSumIF, kOpSegSumU32,   // two words
@@ -229,6 +243,18 @@ constexpr uint32_t op_tile_threads(int shape)
 {
     return shape == kOpShapeMedium ? 512u : (shape == kOpShapeLarge ? 1024u : 256u);
 }
+// Elements per tile of the reduction under an operator: kReduceThreads threads
+// loading 4 words 8 times (16-byte aligned input) or one element 16 times.
+constexpr uint32_t op_reduce_tile_elems(int words, bool aligned)
+{
+    return aligned ? (uint32_t)kReduceThreads * (4u / words) * 8u : (uint32_t)kReduceThreads * 16u;
+}
+// Reductions under the operators of each file (k_reduce_op), non-temporal
+// loads as asked (aligned inputs only).
+hipError_t launch_reduce_op_minmax(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream);
+hipError_t launch_reduce_op_pairsum(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream);
+hipError_t launch_reduce_op_affine(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream);
+hipError_t launch_reduce_op_segsum(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream);
 // The tile index is the workgroup index; only the large shape is built with
 // non-temporal loads (used from kOpNtMin elements).
 hipError_t launch_op_minmax(int kind, bool exclusive, int shape, bool nt, const OpScanParams& p,

@@ -11,4 +11,12 @@ hipError_t launch_op_affine(int kind, bool exclusive, int shape, bool nt, const 
     return launch_op_typed<OpAffineU32>(exclusive, shape, nt, p, stream);
 }
 
+hipError_t launch_reduce_op_affine(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream)
+{
+    switch (kind) {
+    case kOpAffineU32: return launch_reduce_op_typed<OpAffineU32>(aligned, nt, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace dws

@@ -503,6 +503,176 @@ __global__ void __launch_bounds__(BLOCK) k_scan_op(OpScanParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Reduction under Op to one element (the shard total of a split scan, as
+// dws_reduce for +). The grid and the partials follow the + reduction: at
+// most kReduceMaxGroups workgroups of BLOCK threads each combine a contiguous
+// run of tiles and publish the result as a descriptor of W tagged words; the
+// highest-indexed workgroup combines the partials in index order and writes
+// the total. Every combine keeps input order: a wave's segment is combined
+// chunk by chunk (in-lane, then across lanes by an in-order wave scan), a
+// tile's segments wave by wave through LDS, the group's tiles one after the
+// other, and the partials in index order (thread q of the last group takes
+// partials q PER .. q PER + PER - 1, lanes and waves in order).
+// ---------------------------------------------------------------------------
+template <class Op, int BLOCK, int LOADW, int CHUNKS, bool NT>
+__global__ void __launch_bounds__(BLOCK) k_reduce_op(OpReduceParams p)
+{
+    using V = typename Op::V;
+    constexpr int W = Op::kWords;
+    static_assert(LOADW % W == 0, "whole elements per load");
+    constexpr int E = LOADW / W;
+    constexpr int WAVES = BLOCK / 64;
+    constexpr uint32_t SEG = 64u * E * CHUNKS;
+    constexpr uint32_t TILE = WAVES * SEG;
+    constexpr uint32_t ESIZE = 4u * W;
+    constexpr int PER = (int)(kReduceMaxGroups / BLOCK);
+    static_assert(PER * BLOCK == (int)kReduceMaxGroups, "the last group reads every partial in one round");
+    // double-buffered: tile i + 2 overwrites a buffer only after every wave has
+    // passed the barrier of tile i + 1, i.e. has read tile i's totals
+    __shared__ V s_wave[2][WAVES];
+    __shared__ V s_fin[WAVES];
+    __shared__ uint32_t s_epoch;
+    const int lane = lane_id();
+    const int wave = (int)uniform(threadIdx.x >> 6);
+    const uint32_t g = blockIdx.x;
+    const uint64_t t0 = (uint64_t)g * p.tiles_per_group;
+    const uint64_t t_end = t0 + p.tiles_per_group;
+    const uint64_t t1 = t_end < (uint64_t)p.num_tiles ? t_end : (uint64_t)p.num_tiles;
+    uint32_t epoch_v = 0u;
+    if (wave == 0) epoch_v = load_epoch_async(p.epoch);
+
+    V acc = Op::identity();
+    uint32_t it = 0;
+    for (uint64_t t = t0; t < t1; ++t, ++it) {
+        const uint64_t seg_first = t * TILE + (uint64_t)wave * SEG;
+        const uint32_t vb = valid_bytes_sized(seg_first, SEG, p.n, ESIZE);
+        uint32_t raw[CHUNKS][LOADW];
+        load_words<LOADW, CHUNKS, NT>(make_rsrc(static_cast<const char*>(p.in) + seg_first * ESIZE, vb), lane, raw);
+        // words past n load as 0, which is not every operator's identity: a
+        // ragged segment (the array's last, uniform test) puts the identity
+        // in their place
+        if (vb < SEG * ESIZE) {
+            const uint32_t valid = vb / ESIZE;
+            const V id = Op::identity();
+#pragma unroll
+            for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if ((uint32_t)((c * 64 + lane) * E + e) >= valid) {
+#pragma unroll
+                        for (int k = 0; k < W; ++k) raw[c][e * W + k] = id.w[k];
+                    }
+        }
+        V seg = Op::identity();
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            V lane_total;
+#pragma unroll
+            for (int k = 0; k < W; ++k) lane_total.w[k] = raw[c][k];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                V xe;
+#pragma unroll
+                for (int k = 0; k < W; ++k) xe.w[k] = raw[c][e * W + k];
+                lane_total = Op::combine(lane_total, xe);
+            }
+            seg = Op::combine(seg, wave_read_lane_op<Op>(wave_scan_op<Op>(lane_total), 63));
+        }
+        V* buf = s_wave[it & 1u];
+        if (lane == 0) buf[wave] = seg;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) acc = Op::combine(acc, buf[w]);
+    }
+
+    if (threadIdx.x == 0) {
+        const uint32_t e = uniform(epoch_v);
+        desc_store_val<W>(p.desc, g, e, kStatusP, acc);
+        s_epoch = e;
+    }
+    if (g != p.groups - 1u) return;
+    __syncthreads();
+    const uint32_t epoch = uniform(s_epoch);
+
+    // the last group: thread q combines partials q PER .. q PER + PER - 1
+    const uint32_t q0 = threadIdx.x * (uint32_t)PER;
+    uint64_t d[PER][W];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+#pragma unroll
+        for (int k = 0; k < W; ++k)
+            d[j][k] = q0 + j < p.groups ? desc_load<kOrderRelaxed>(desc_at(p.desc, q0 + j) + k)
+                                        : desc_pack(epoch, kStatusP, Op::identity().w[k]);
+    const uint64_t start = realtime();
+    for (;;) {
+        bool waiting = false;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            bool torn = false;
+#pragma unroll
+            for (int k = 1; k < W; ++k) torn = torn || (d[j][k] >> 32) != (d[j][0] >> 32);
+            if (torn || desc_status(d[j][0], epoch) == kStatusX) waiting = true;
+        }
+        if (!waiting) break;
+        if (realtime() - start > kWatchdogTicks) {
+            atomicAdd(p.watchdog, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            bool torn = false;
+#pragma unroll
+            for (int k = 1; k < W; ++k) torn = torn || (d[j][k] >> 32) != (d[j][0] >> 32);
+            if (torn || desc_status(d[j][0], epoch) == kStatusX) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) d[j][k] = desc_load<kOrderRelaxed>(desc_at(p.desc, q0 + j) + k);
+            }
+        }
+    }
+    V v = Op::identity();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        V pj;
+#pragma unroll
+        for (int k = 0; k < W; ++k) pj.w[k] = (uint32_t)d[j][k];
+        v = Op::combine(v, pj);
+    }
+    const V wv = wave_read_lane_op<Op>(wave_scan_op<Op>(v), 63);
+    if (lane == 0) s_fin[wave] = wv;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        V total = Op::identity();
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) total = Op::combine(total, s_fin[w]);
+#pragma unroll
+        for (int k = 0; k < W; ++k) static_cast<uint32_t*>(p.total)[k] = total.w[k];
+        advance_epoch(p.epoch, epoch);
+    }
+}
+
+template <class Op, int BLOCK, int LOADW, int CHUNKS, bool NT = false>
+static hipError_t launch_reduce_op_shape(const OpReduceParams& p, hipStream_t stream)
+{
+    OpReduceParams arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_reduce_op<Op, BLOCK, LOADW, CHUNKS, NT>),
+                           dim3(p.groups), dim3(BLOCK), args, 0, stream);
+}
+
+// The reduction's shapes: 16-byte aligned inputs load dwordx4 (8 loads per
+// lane, non-temporal as the caller asks), others one element per access
+// (16 per lane); kReduceThreads threads either way (op_reduce_tile_elems).
+template <class Op>
+hipError_t launch_reduce_op_typed(bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream)
+{
+    constexpr int W = Op::kWords;
+    if (!aligned) return launch_reduce_op_shape<Op, kReduceThreads, W, 16>(p, stream);
+    return nt ? launch_reduce_op_shape<Op, kReduceThreads, 4, 8, true>(p, stream)
+              : launch_reduce_op_shape<Op, kReduceThreads, 4, 8>(p, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Shapes and launch. Shapes are (threads, words per load, loads per lane);
 // the unaligned shape loads one element per access.
 // ---------------------------------------------------------------------------

@@ -16,4 +16,15 @@ hipError_t launch_op_minmax(int kind, bool exclusive, int shape, bool nt, const 
     }
 }
 
+hipError_t launch_reduce_op_minmax(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream)
+{
+    switch (kind) {
+    case kOpMaxI32: return launch_reduce_op_typed<OpMaxI32>(aligned, nt, p, stream);
+    case kOpMaxU32: return launch_reduce_op_typed<OpMaxU32>(aligned, nt, p, stream);
+    case kOpMinI32: return launch_reduce_op_typed<OpMinI32>(aligned, nt, p, stream);
+    case kOpMinU32: return launch_reduce_op_typed<OpMinU32>(aligned, nt, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace dws

@@ -14,4 +14,13 @@ hipError_t launch_op_pairsum(int kind, bool exclusive, int shape, bool nt, const
     }
 }
 
+hipError_t launch_reduce_op_pairsum(int kind, bool aligned, bool nt, const OpReduceParams& p, hipStream_t stream)
+{
+    switch (kind) {
+    case kOpSumPairIF: return launch_reduce_op_typed<OpSumPairIF>(aligned, nt, p, stream);
+    case kOpSumPairU32: return launch_reduce_op_typed<OpSumPairU32>(aligned, nt, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace dws

@@ -430,9 +430,9 @@ dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
  * without its first element, the exclusive one that scan without its last
  * (so d_out[0] = *d_seed). For DWS_OP_AFFINE the seed map runs first, and for
  * DWS_OP_SEGMENTED_SUM it is the running value of a segment that x[0]
- * continues unless its flag is set. Together with an inclusive scan's last
- * element as a shard's total, it gives every operator the sharded scan that
- * dws_reduce and dws_scan_seeded give +. The seed enters as the prefix of tile
+ * continues unless its flag is set. With dws_reduce_op for a shard's total,
+ * it gives every operator the sharded scan that dws_reduce and
+ * dws_scan_seeded give +. The seed enters as the prefix of tile
  * 0 (Merrill & Garland, section 4.2: only contiguous partial results are
  * combined, in input order); the other tiles receive it through the
  * look-back. DWS_OP_SUM with the 32-bit scalar types is dws_scan_seeded.
@@ -443,6 +443,29 @@ dws_status dws_scan_op(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
  */
 dws_status dws_scan_op_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dtype,
                               dws_op op, int exclusive, const void* d_seed, hipStream_t stream);
+
+/*
+ * Reduction under `op`: writes the combination of x[0], ..., x[n-1] in input
+ * order (the operator's identity when n == 0) to the DEVICE element *d_total
+ * (one element of `dtype`, 4-byte aligned), the last element an inclusive
+ * dws_scan_op would give. The first stage of the reduce-then-scan
+ * decomposition (Merrill & Garland, section 3.2 and Fig 3) under any
+ * associative operator (section 4.2): with dws_scan_op_seeded it shards every
+ * operator's scan as dws_reduce and dws_scan_seeded shard +. One launch
+ * reading the input once: the grid and the partials of dws_reduce, and every
+ * combine in input order (within a wave segment, across a tile's waves,
+ * along a workgroup's tiles and over the partials), so non-commutative
+ * operators are exact; fp32 parts are added in an order fixed by n and the
+ * input's alignment. Built combinations are those of dws_scan_op; DWS_OP_SUM
+ * with the 32-bit scalar types is dws_reduce. Validation before any HIP call:
+ * an unknown dtype or op, d_total == NULL or d_in == NULL with n > 0 give
+ * DWS_ERR_INVALID_ARG; other combinations, or n above DWS_MAX_ELEMENTS,
+ * DWS_ERR_UNSUPPORTED; d_in not aligned to the element size or d_total not
+ * 4-byte aligned DWS_ERR_MISALIGNED; d_total inside d_in's n elements
+ * DWS_ERR_OVERLAP. Workspace, watchdog and asynchrony as dws_reduce.
+ */
+dws_status dws_reduce_op(const void* d_in, size_t n, dws_dtype dtype, dws_op op, void* d_total,
+                         hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* dws_status_string(dws_status status);

@@ -416,6 +416,28 @@ def test_scan_op_seeded_validation(lib):
             assert f(FAKE, out, 10, dt, op, 0, out - 4, None) == dws.ERR_OVERLAP
 
 
+def test_reduce_op_validation(lib):
+    """dws_reduce_op: argument checks before any HIP call; + on a 32-bit
+    scalar is dws_reduce."""
+    f = lib.dws_reduce_op
+    total = FAKE + (1 << 41)
+    assert f(FAKE, 10, 9, dws.OP_MAX, total, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, 10, dws.INT32, 7, total, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, 10, dws.FLOAT32, dws.OP_MAX, total, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, 10, dws.UINT32, dws.OP_AFFINE, total, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE, 10, dws.PAIR_U32, dws.OP_AFFINE, None, None) == dws.ERR_INVALID_ARG
+    assert f(None, 10, dws.PAIR_U32, dws.OP_AFFINE, total, None) == dws.ERR_INVALID_ARG
+    assert f(None, 0, dws.PAIR_U32, dws.OP_AFFINE, None, None) == dws.ERR_INVALID_ARG
+    assert f(FAKE, (1 << 35) + 1, dws.PAIR_U32, dws.OP_SEGMENTED_SUM, total, None) == dws.ERR_UNSUPPORTED
+    assert f(FAKE + 4, 10, dws.PAIR_U32, dws.OP_AFFINE, total, None) == dws.ERR_MISALIGNED
+    assert f(FAKE, 10, dws.PAIR_I32_F32, dws.OP_SUM, total + 2, None) == dws.ERR_MISALIGNED
+    assert f(FAKE + 2, 10, dws.INT32, dws.OP_MIN, total, None) == dws.ERR_MISALIGNED
+    # the total inside the input's n elements (8-byte elements: 80 bytes)
+    assert f(FAKE, 10, dws.PAIR_U32, dws.OP_AFFINE, FAKE + 72, None) == dws.ERR_OVERLAP
+    assert f(FAKE, 10, dws.PAIR_U32, dws.OP_AFFINE, FAKE - 4, None) == dws.ERR_OVERLAP
+    assert f(FAKE, 10, dws.INT32, dws.OP_SUM, FAKE + 36, None) == dws.ERR_OVERLAP
+
+
 def test_reduce_validation(lib):
     """dws_reduce: argument checks before any HIP call."""
     f = lib.dws_reduce

@@ -154,6 +154,101 @@ def test_op_seeded(gpu, name, exclusive):
         check_op(name, x, y, exclusive, f"{name} seeded n={n}", ref=ref)
 
 
+def _upload(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.uint32).reshape(-1).view(np.int32)).to("cuda")
+
+
+def check_total(name, x, got, label):
+    """got (one element as uint32 words) against the last element of the
+    oracle's inclusive scan of x, or the identity when x is empty."""
+    exact, yf, sabs = expected(name, x, False)
+    words = COMBOS[name][3]
+    got = got.reshape(-1)
+    if x.shape[0] == 0:
+        return
+    if yf is None:
+        want = np.asarray(exact[-1]).reshape(-1).astype(np.uint32)
+        assert np.array_equal(got[:words], want), f"{label}: gpu {got} oracle {want}"
+        return
+    assert got[0] == exact[-1], f"{label}: integer part gpu {got[0]} oracle {exact[-1]}"
+    g = float(got[1:2].view(np.float32)[0])
+    assert abs(g - yf[-1]) <= RTOL * sabs[-1] + ATOL, f"{label}: fp32 part gpu {g!r} oracle {yf[-1]!r}"
+
+
+IDENTITY = {"max_i32": [0x80000000], "max_u32": [0], "min_i32": [0x7FFFFFFF], "min_u32": [0xFFFFFFFF],
+            "sum_pair_i32_f32": [0, 0], "sum_pair_u32": [0, 0], "affine_u32": [1, 0], "segsum_u32": [0, 0],
+            "segsum_i32_f32": [0, 0]}
+
+
+@pytest.mark.parametrize("name", list(COMBOS))
+def test_reduce_op(gpu, name):
+    """dws_reduce_op at sizes around every tile and group boundary, aligned
+    and not, against the oracle; the empty input gives the identity, and fp32
+    parts repeat bit for bit."""
+    import torch
+    op, dtype, kind, words = COMBOS[name]
+    for off in (0, 1):
+        for n in (0, 1, 5, 4097, 8192, 8193, 16385, 1_000_003, 1024 * 8192 + 3, (1 << 25) + 9):
+            if n == 0 and off:
+                continue
+            note(f"reduce_op={name} n={n} offset={off}")
+            x = wl.op_input(kind, n, seed=5 * n + off) if n else wl.op_input(kind, 1, seed=1)[:0]
+            flat = np.ascontiguousarray(x).view(np.uint32).reshape(-1).view(np.int32)
+            store = torch.empty(flat.size + off * words + 1, dtype=torch.int32, device="cuda")
+            xd = store[off * words:off * words + flat.size]
+            if n:
+                xd.copy_(torch.from_numpy(flat))
+            total = torch.full((words,), 12345, dtype=torch.int32, device="cuda")
+            stream = torch.cuda.current_stream().cuda_stream
+            st = dws.reduce_op_ptr(xd.data_ptr(), n, dtype, op, total.data_ptr(), stream)
+            assert st == dws.OK, dws.status_string(st)
+            first = total.cpu().numpy().view(np.uint32).copy()
+            if n == 0:
+                assert first.tolist() == IDENTITY[name], first
+                continue
+            check_total(name, x, first, f"{name} n={n} offset={off}")
+            st = dws.reduce_op_ptr(xd.data_ptr(), n, dtype, op, total.data_ptr(), stream)
+            assert st == dws.OK
+            assert np.array_equal(total.cpu().numpy().view(np.uint32), first), "not repeatable"
+
+
+@pytest.mark.parametrize("name", list(COMBOS))
+def test_sharded_op_scan(gpu, name):
+    """A generic-operator scan split into uneven shards (one empty, one
+    shorter than a tile): each shard's total (dws_reduce_op), the exclusive
+    scan of the totals (dws_scan_op), each shard scanned seeded with its
+    offset (dws_scan_op_seeded), reassembled and compared with the oracle's
+    scan of the whole array. The operators that are not commutative depend on
+    every shard keeping its place."""
+    import torch
+    op, dtype, kind, words = COMBOS[name]
+    n = (1 << 22) + 33
+    cuts = [0, 3, 700_001, 700_001, (1 << 21) + 5, n]
+    x = wl.op_input(kind, n, seed=77)
+    xd = _upload(x)
+    stream = torch.cuda.current_stream().cuda_stream
+    g = len(cuts) - 1
+    totals = torch.empty(g * words, dtype=torch.int32, device="cuda")
+    for i in range(g):
+        a, b = cuts[i], cuts[i + 1]
+        st = dws.reduce_op_ptr(xd[a * words:].data_ptr(), b - a, dtype, op, totals[i * words:].data_ptr(), stream)
+        assert st == dws.OK, dws.status_string(st)
+    offsets = torch.empty_like(totals)
+    assert dws.scan_op_ptr(totals.data_ptr(), offsets.data_ptr(), g, dtype, op, True, stream) == dws.OK
+    for exclusive in (False, True):
+        note(f"sharded op={name} excl={exclusive} shards={g}")
+        out = torch.empty_like(xd)
+        for i in range(g):
+            a, b = cuts[i], cuts[i + 1]
+            if b > a:
+                st = dws.scan_op_seeded_ptr(xd[a * words:].data_ptr(), out[a * words:].data_ptr(), b - a, dtype, op,
+                                            exclusive, offsets[i * words:].data_ptr(), stream)
+                assert st == dws.OK, dws.status_string(st)
+        y = out.cpu().numpy().view(np.uint32).reshape(x.shape)
+        check_op(name, x, y, exclusive, f"{name} sharded")
+
+
 def test_segsum_head_densities(gpu):
     # no heads (one long segment), every element a head, and sparse heads
     # whose segments span many tiles
