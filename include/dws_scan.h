@@ -44,8 +44,10 @@
  * dws_reserve), calls on that stream allocate nothing and may be captured
  * into a HIP graph. A call captured before that, which would have to create
  * or grow the workspace, returns DWS_ERR_UNSUPPORTED without allocating,
- * synchronising or enqueuing anything, so the capture stays valid. Replays stay correct: each launch takes its descriptor
- * epoch from a device word that the launch itself advances. The host clears
+ * synchronising or enqueuing anything, so the capture stays valid. Replays stay correct: each launch (the
+ * reductions dws_reduce and dws_reduce_op included, whose partials are
+ * descriptors of the same workspace) takes its descriptor epoch from a device
+ * word that the launch itself advances. The host clears
  * the descriptors before its own calls could wrap the 30-bit epoch, but
  * replays advance it unseen: after about 2^30 launches on one workspace,
  * replays included, call dws_release_workspaces (and capture again) so that
