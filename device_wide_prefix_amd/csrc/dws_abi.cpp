@@ -697,6 +697,7 @@ dws_status dws_reduce(const void* d_in, size_t n, dws_dtype dtype, void* d_total
         const uintptr_t a = reinterpret_cast<uintptr_t>(d_in);
         const uintptr_t t = reinterpret_cast<uintptr_t>(d_total);
         if (a % kElemBytes != 0 || t % kElemBytes != 0) return DWS_ERR_MISALIGNED;
+        if (a + (uintptr_t)n * kElemBytes < a || t + kElemBytes < t) return DWS_ERR_INVALID_ARG;
         if (n > 0 && t + kElemBytes > a && t < a + (uintptr_t)n * kElemBytes) return DWS_ERR_OVERLAP;
         return run_reduce(d_in, n, dt, d_total, stream);
     } catch (const std::bad_alloc&) {

@@ -281,7 +281,8 @@ dws_status dws_scan_seeded(const void* d_in, void* d_out, size_t n, dws_dtype dt
  * their partials in index order. int32 / uint32 wrap mod 2^32; fp32 adds in fp32 in an order
  * fixed by n and by whether d_in is 16-byte aligned, so repeated calls give
  * the same bits. Validation before any HIP call: an invalid dtype, d_total ==
- * NULL or d_in == NULL with n > 0 give DWS_ERR_INVALID_ARG; pointers that are
+ * NULL, d_in == NULL with n > 0 or an input range that wraps the address
+ * space give DWS_ERR_INVALID_ARG; pointers that are
  * not 4-byte aligned DWS_ERR_MISALIGNED; n above DWS_MAX_ELEMENTS
  * DWS_ERR_UNSUPPORTED; d_total inside d_in's n elements DWS_ERR_OVERLAP. Each
  * workgroup publishes its partial as a look-back descriptor of the
@@ -460,8 +461,8 @@ dws_status dws_scan_op_seeded(const void* d_in, void* d_out, size_t n, dws_dtype
  * operators are exact; fp32 parts are added in an order fixed by n and the
  * input's alignment. Built combinations are those of dws_scan_op; DWS_OP_SUM
  * with the 32-bit scalar types is dws_reduce. Validation before any HIP call:
- * an unknown dtype or op, d_total == NULL or d_in == NULL with n > 0 give
- * DWS_ERR_INVALID_ARG; other combinations, or n above DWS_MAX_ELEMENTS,
+ * an unknown dtype or op, d_total == NULL, d_in == NULL with n > 0 or an
+ * input range that wraps the address space give DWS_ERR_INVALID_ARG; other combinations, or n above DWS_MAX_ELEMENTS,
  * DWS_ERR_UNSUPPORTED; d_in not aligned to the element size or d_total not
  * 4-byte aligned DWS_ERR_MISALIGNED; d_total inside d_in's n elements
  * DWS_ERR_OVERLAP. Workspace, watchdog and asynchrony as dws_reduce.

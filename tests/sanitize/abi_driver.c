@@ -158,6 +158,45 @@ static void operators(void)
           DWS_ERR_UNSUPPORTED);
 }
 
+static void sharded_steps(void)
+{
+    const uint64_t seed = FAKE + (1ull << 41);
+    /* dws_scan_seeded: the scans' checks, then the seed's */
+    CHECK(dws_scan_seeded(NULL, NULL, 0, DWS_INT32, 0, NULL, NULL), DWS_OK);
+    CHECK(dws_scan_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_INT32, 0, NULL, NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_seeded(at(FAKE), at(FAKE + 4096), 10, (dws_dtype)5, 0, at(seed), NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_FLOAT32, 1, at(seed + 2), NULL), DWS_ERR_MISALIGNED);
+    CHECK(dws_scan_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_INT32, 0, at(FAKE + 4096 + 36), NULL), DWS_ERR_OVERLAP);
+    CHECK(dws_scan_seeded(at(FAKE), at(FAKE), 10, DWS_INT32, 1, at(FAKE), NULL), DWS_ERR_OVERLAP);
+    CHECK(dws_scan_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_INT32, 0, at(UINT64_MAX - 1), NULL), DWS_ERR_MISALIGNED);
+    /* dws_reduce */
+    CHECK(dws_reduce(NULL, 0, DWS_INT32, NULL, NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_reduce(NULL, 10, DWS_INT32, at(seed), NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_reduce(at(FAKE), 10, (dws_dtype)-2, at(seed), NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_reduce(at(FAKE), 10, DWS_FLOAT32, at(seed + 1), NULL), DWS_ERR_MISALIGNED);
+    CHECK(dws_reduce(at(FAKE), DWS_MAX_ELEMENTS + 1, DWS_UINT32, at(seed), NULL), DWS_ERR_UNSUPPORTED);
+    CHECK(dws_reduce(at(FAKE), 10, DWS_INT32, at(FAKE + 36), NULL), DWS_ERR_OVERLAP);
+    CHECK(dws_reduce(at(UINT64_MAX - 15), 100, DWS_INT32, at(seed), NULL), DWS_ERR_INVALID_ARG);
+    /* under the generic operators */
+    CHECK(dws_scan_op_seeded(NULL, NULL, 0, DWS_PAIR_U32, DWS_OP_AFFINE, 0, NULL, NULL), DWS_OK);
+    CHECK(dws_scan_op_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_PAIR_U32, (dws_op)9, 0, at(seed), NULL),
+          DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_op_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_FLOAT32, DWS_OP_MAX, 0, at(seed), NULL),
+          DWS_ERR_UNSUPPORTED);
+    CHECK(dws_scan_op_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_PAIR_U32, DWS_OP_AFFINE, 1, NULL, NULL),
+          DWS_ERR_INVALID_ARG);
+    CHECK(dws_scan_op_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_PAIR_U32, DWS_OP_AFFINE, 1, at(FAKE + 4092), NULL),
+          DWS_ERR_OVERLAP);
+    CHECK(dws_scan_op_seeded(at(FAKE), at(FAKE + 4096), 10, DWS_PAIR_I32_F32, DWS_OP_SEGMENTED_SUM, 0,
+                             at(FAKE + 4096 + 72), NULL), DWS_ERR_OVERLAP);
+    CHECK(dws_reduce_op(at(FAKE), 10, DWS_PAIR_U32, DWS_OP_AFFINE, NULL, NULL), DWS_ERR_INVALID_ARG);
+    CHECK(dws_reduce_op(at(FAKE), 10, DWS_INT32, DWS_OP_AFFINE, at(seed), NULL), DWS_ERR_UNSUPPORTED);
+    CHECK(dws_reduce_op(at(FAKE + 4), 10, DWS_PAIR_U32, DWS_OP_SUM, at(seed), NULL), DWS_ERR_MISALIGNED);
+    CHECK(dws_reduce_op(at(FAKE), 10, DWS_PAIR_U32, DWS_OP_SUM, at(FAKE + 76), NULL), DWS_ERR_OVERLAP);
+    CHECK(dws_reduce_op(at(FAKE), DWS_MAX_ELEMENTS + 1, DWS_INT32, DWS_OP_MAX, at(seed), NULL), DWS_ERR_UNSUPPORTED);
+    CHECK(dws_reduce_op(at(UINT64_MAX - 7), 10, DWS_PAIR_U32, DWS_OP_AFFINE, at(seed), NULL), DWS_ERR_INVALID_ARG);
+}
+
 static void diagnostics(void)
 {
     CHECK(dws_scan_debug(at(FAKE), at(FAKE + 4096), 16, DWS_INT32, 0, 0, 0, 0, 0, 0, NULL, NULL),
@@ -182,6 +221,7 @@ static void diagnostics(void)
 int main(void)
 {
     status_and_geometry();
+    sharded_steps();
     scans();
     compaction();
     operators();

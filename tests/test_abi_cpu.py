@@ -453,6 +453,8 @@ def test_reduce_validation(lib):
     # the total inside the input's n elements
     assert f(FAKE, 10, dws.INT32, FAKE, None) == dws.ERR_OVERLAP
     assert f(FAKE, 10, dws.INT32, FAKE + 36, None) == dws.ERR_OVERLAP
+    # an input range that wraps the address space
+    assert f(2**64 - 16, 100, dws.INT32, total, None) == dws.ERR_INVALID_ARG
 
 
 def test_seeded_and_reduce_bindings_refuse_cpu_tensors(lib):
