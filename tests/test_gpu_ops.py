@@ -249,6 +249,53 @@ def test_sharded_op_scan(gpu, name):
         check_op(name, x, y, exclusive, f"{name} sharded")
 
 
+def test_sharded_op_scan_graph_replays(gpu):
+    """The operator steps of a split scan (affine maps: not commutative)
+    captured in one graph and replayed with new inputs and eager launches on
+    the same workspace between replays; every replay is checked."""
+    import torch
+    op, dtype, kind, words = COMBOS["affine_u32"]
+    n = (1 << 21) + 7
+    cuts = [0, 500_001, (1 << 20) + 3, n]
+    g = len(cuts) - 1
+    s = torch.cuda.Stream()
+    xd = torch.empty(n * words, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(xd)
+    totals = torch.empty(g * words, dtype=torch.int32, device="cuda")
+    offsets = torch.empty_like(totals)
+    dws.reserve(n, stream=s.cuda_stream)
+
+    def steps():
+        st = s.cuda_stream
+        for i in range(g):
+            a, b = cuts[i], cuts[i + 1]
+            assert dws.reduce_op_ptr(xd[a * words:].data_ptr(), b - a, dtype, op, totals[i * words:].data_ptr(),
+                                     st) == dws.OK
+        assert dws.scan_op_ptr(totals.data_ptr(), offsets.data_ptr(), g, dtype, op, True, st) == dws.OK
+        for i in range(g):
+            a, b = cuts[i], cuts[i + 1]
+            assert dws.scan_op_seeded_ptr(xd[a * words:].data_ptr(), out[a * words:].data_ptr(), b - a, dtype, op,
+                                          False, offsets[i * words:].data_ptr(), st) == dws.OK
+
+    with torch.cuda.stream(s):          # warm-up outside the capture
+        steps()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        steps()
+    for rep in range(3):
+        note(f"sharded affine graph replay rep={rep}")
+        x = wl.op_input(kind, n, seed=500 + rep)
+        xd.copy_(_upload(x))
+        with torch.cuda.stream(s):        # eager launches on the workspace between replays
+            dws.reduce_op(xd, op, dtype)
+            dws.scan_op(xd, op, dtype)
+        s.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check_op("affine_u32", x, out.cpu().numpy().view(np.uint32).reshape(x.shape), False, f"replay {rep}")
+
+
 def test_segsum_head_densities(gpu):
     # no heads (one long segment), every element a head, and sparse heads
     # whose segments span many tiles
