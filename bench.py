@@ -8,6 +8,9 @@ decoupled look-back kernel). Prints ONE JSON line on stdout:
   memcpy       a same-run device-to-device hipMemcpyAsync of N * 4 bytes,
                counted the same way (2 * N * 4 bytes)
   cpu_baseline the sequential CPU oracle on the same input (1 host core)
+  configs      every workload the metric is stated on, with its memcpy and oracle
+  shard_8      one device's share of the headline split 8 ways: shard total,
+               seeded scan and the per-device sequence (see --shards)
 
 Step protocol: before every step (untimed) the input is restored from a
 pristine device copy and the caches (L2, MALL) are flushed by reading a 1 GiB
@@ -463,7 +466,7 @@ def run_ops(steps: int, warmup: int, with_oracle: bool = True):
     return rows
 
 
-def run_shards(steps: int, warmup: int, shards: int):
+def run_shards(steps: int, warmup: int, shards: int, x_host=None):
     """One device's share of the headline scan split into `shards` contiguous
     shards (2^28 / shards fp32 elements, exclusive, in place), cold caches:
       reduce     the shard's total (dws_reduce; 4 bytes per element read)
@@ -478,7 +481,7 @@ def run_shards(steps: int, warmup: int, shards: int):
     import device_wide_prefix_amd as dws
     w = wl.WORKLOADS["f32_2p28_excl_inplace"]
     m = w.n // shards
-    x = wl.generate_workload(w)[:m].copy()
+    x = (wl.generate_workload(w) if x_host is None else x_host)[:m].copy()
     pristine = torch.from_numpy(x).to("cuda")
     work = torch.empty_like(pristine)
     totals = torch.zeros(shards, dtype=torch.float32, device="cuda")
@@ -809,7 +812,7 @@ def main():
     ap.add_argument("--tile-index", default="auto", choices=sorted(TILE_INDEX))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="measure only the headline workload (no `configs` rows)")
+                    help="measure only the headline workload (no `configs` rows, no `shard_8`)")
     ap.add_argument("--all", action="store_true", help="also measure every workload and variant (stderr)")
     ap.add_argument("--sweep", action="store_true",
                     help="also sweep N = 2^10..2^30 for every variant against memcpy (stderr)")
@@ -922,6 +925,11 @@ def main():
             del xk
         line["configs"] = rows
         line["property_check"] = bool(line["property_check"] and all(r["property_check"] for r in rows))
+        # one device's share of the headline split 8 ways: the per-device steps
+        # of the sharded scan (the exchange of the totals is not a device's work)
+        sh = run_shards(args.steps, args.warmup, 8, x_host=x if args.workload == "f32_2p28_excl_inplace" else None)
+        line["shard_8"] = sh
+        line["property_check"] = bool(line["property_check"] and sh["property_check"] and sh["watchdog_trips"] == 0)
 
     if args.all:
         for name in ("i32_4096_incl", "f32_2p20_incl", "u32_2p26_incl", "f32_2p28_excl_inplace", "flags_2p30m12345_excl"):
@@ -939,7 +947,7 @@ def main():
         run_ops(args.steps, args.warmup, timed_oracle)
     if args.compaction:
         run_compaction(args.steps, args.warmup, timed_oracle)
-    if args.shards:
+    if args.shards and (args.headline_only or args.shards != 8):
         run_shards(args.steps, args.warmup, args.shards)
     if args.select:
         for in_place in (False, True):
