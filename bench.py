@@ -328,6 +328,30 @@ def run_select(steps: int, warmup: int, in_place: bool, with_oracle: bool = True
            "ms_min": float(np.min(times)), "gbps": algo / (mean * 1e-3) / 1e9,
            "frac_hbm_peak": algo / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, "property_check": ok}
 
+    # select-if on the same values by a predicate (x < 0, about half of
+    # uniform int32 values): the selection comes from the values, so the
+    # kernel reads 4 n bytes instead of 8 n
+    cnt_if = torch.zeros(1, dtype=torch.int64, device="cuda")
+    zero = np.zeros(1, dtype=np.int32)
+
+    def select_if():
+        st = dws.load_library().dws_select_if(work.data_ptr(), out.data_ptr(), n, dws.INT32, dws.PRED_LT,
+                                              zero.ctypes.data, cnt_if.data_ptr(), stream)
+        if st != dws.OK:
+            raise RuntimeError(f"select_if failed: {dws.status_string(st)}")
+
+    ti = time_steps(select_if, prepare, steps, warmup)
+    count_if = int(cnt_if.item())
+    neg = vals < 0
+    ok_if = count_if == int(neg.sum().item()) and bool(torch.equal(out[:count_if], vals[neg]))
+    mean_if = float(np.mean(ti))
+    algo_if = 4 * n + 4 * count_if
+    row.update({"select_if_lt0_count": count_if, "select_if_lt0_ms_mean": mean_if,
+                "select_if_lt0_gbps": algo_if / (mean_if * 1e-3) / 1e9,
+                "select_if_lt0_frac_hbm_peak": algo_if / (mean_if * 1e-3) / 1e9 / HBM_PEAK_GBPS})
+    row["property_check"] = bool(row["property_check"] and ok_if)
+    del neg
+
     def torch_select():
         torch.masked_select(work, mask)
 

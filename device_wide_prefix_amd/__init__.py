@@ -36,6 +36,8 @@ SINGLE_PASS, REDUCE_THEN_SCAN, CHAINED, SCAN_THEN_PROPAGATE = 0, 1, 2, 3
 ORDER_RELAXED, ORDER_ACQ_REL = 0, 1
 # dws_tile_index
 TILE_AUTO, TILE_DRAWN, TILE_DISPATCH = 0, 1, 2
+# dws_pred
+PRED_EQ, PRED_NE, PRED_LT, PRED_LE, PRED_GT, PRED_GE = range(6)
 # dws_options.nontemporal
 NT_AUTO, NT_ON, NT_OFF = 0, 1, 2
 
@@ -45,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "dws_release_workspaces", "dws_watchdog_trips", "dws_scan_debug", "dws_selftest_wave",
     "dws_scan_profiled", "dws_select_flagged", "dws_scan_op", "dws_partition_flagged", "dws_reduce_by_key",
     "dws_run_length_encode", "dws_device_memory_info", "dws_scan_noalloc", "dws_scan_plan", "dws_scan_seeded",
-    "dws_reduce", "dws_scan_op_seeded", "dws_reduce_op",
+    "dws_reduce", "dws_scan_op_seeded", "dws_reduce_op", "dws_select_if", "dws_partition_if",
 )
 
 
@@ -104,6 +106,10 @@ def load_library():
     lib.dws_scan_op_seeded.restype = ci
     lib.dws_reduce_op.argtypes = [vp, sz, ci, ci, vp, vp]
     lib.dws_reduce_op.restype = ci
+    for name in ("dws_select_if", "dws_partition_if"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, sz, ci, ci, vp, vp, vp]
+        f.restype = ci
     lib.dws_status_string.argtypes = [ci]
     lib.dws_status_string.restype = ctypes.c_char_p
     lib.dws_version.restype = ci
@@ -357,6 +363,17 @@ def scan_op_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: b
 def scan_op_seeded_ptr(d_in: int, d_out: int, n: int, dtype: int, op: int, exclusive: bool, d_seed: int,
                        stream: int = 0) -> int:
     return load_library().dws_scan_op_seeded(d_in, d_out, n, dtype, op, int(bool(exclusive)), d_seed, stream)
+
+
+def select_if_ptr(d_in: int, d_out: int, n: int, dtype: int, pred: int, threshold, d_count: int,
+                  stream: int = 0, partition: bool = False) -> int:
+    """dws_select_if (dws_partition_if with partition=True); ``threshold`` is a
+    Python number converted to dtype on the host."""
+    import numpy as np
+    np_t = {INT32: np.int32, UINT32: np.uint32, FLOAT32: np.float32}.get(int(dtype), np.uint32)
+    buf = np.array([threshold], dtype=np_t)
+    f = load_library().dws_partition_if if partition else load_library().dws_select_if
+    return f(d_in, d_out, n, dtype, int(pred), buf.ctypes.data, d_count, stream)
 
 
 def reduce_op_ptr(d_in: int, n: int, dtype: int, op: int, d_total: int, stream: int = 0) -> int:

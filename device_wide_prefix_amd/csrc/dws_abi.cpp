@@ -1009,13 +1009,25 @@ dws_status dws_scan_profiled(const void* d_in, void* d_out, size_t n, dws_dtype 
 namespace {
 
 // Compaction and partition by flags (one kernel, see dws_select.hip).
+// A predicate of dws_select_if / dws_partition_if: the outcomes of comparing
+// an element with the threshold (bit 0 less, 1 equal, 2 greater, 3 unordered)
+// that select it, and the comparison's element kind.
+struct SelectPredicate {
+    uint32_t mask;
+    uint32_t threshold;
+    int kind;
+};
+
+// d_flags is ignored when `pred` is given (the selection comes from the values).
 dws_status select_entry(const void* d_in, const void* d_flags, void* d_out, size_t n, int dtype,
-                        unsigned long long* d_count, bool partition, hipStream_t stream)
+                        unsigned long long* d_count, bool partition, hipStream_t stream,
+                        const SelectPredicate* pred = nullptr)
 {
     if (!valid_dtype(dtype)) return DWS_ERR_INVALID_ARG;
     if (d_count == nullptr) return DWS_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(d_count) & 7u) != 0) return DWS_ERR_MISALIGNED;
     if (n > kSelectMaxElems) return DWS_ERR_UNSUPPORTED;
+    if (pred != nullptr) d_flags = d_in;
     if (n > 0) {
         dws_status s = validate(d_in, d_out, n, dtype);
         if (s != DWS_OK) return s;
@@ -1025,7 +1037,7 @@ dws_status select_entry(const void* d_in, const void* d_flags, void* d_out, size
         const uintptr_t i = reinterpret_cast<uintptr_t>(d_in);
         const uintptr_t c = reinterpret_cast<uintptr_t>(d_count), bytes = (uintptr_t)n * kElemBytes;
         // the flags are read by later tiles while earlier ones write: no overlap with the output
-        if (f < o + bytes && o < f + bytes) return DWS_ERR_OVERLAP;
+        if (pred == nullptr && f < o + bytes && o < f + bytes) return DWS_ERR_OVERLAP;
         // a partition writes the back of the output before later tiles read their input
         if (partition && i < o + bytes && o < i + bytes) return DWS_ERR_OVERLAP;
         if ((c < o + bytes && o < c + 8) || (c < f + bytes && f < c + 8)) return DWS_ERR_OVERLAP;
@@ -1038,6 +1050,12 @@ dws_status select_entry(const void* d_in, const void* d_flags, void* d_out, size
     a.n = n;
     a.count = d_count;
     a.partition = partition;
+    if (pred != nullptr) {
+        a.pred = true;
+        a.pred_mask = pred->mask;
+        a.threshold = pred->threshold;
+        a.kind = pred->kind;
+    }
     a.aligned = ((reinterpret_cast<uintptr_t>(d_in) | reinterpret_cast<uintptr_t>(d_out) |
                   reinterpret_cast<uintptr_t>(d_flags)) & 15u) == 0;
     const uint64_t tiles = n == 0 ? 0 : ceil_div(n, select_tile_elems(n, a.aligned));
@@ -1169,6 +1187,54 @@ dws_status dws_partition_flagged(const void* d_in, const void* d_flags, void* d_
 {
     try {
         return select_entry(d_in, d_flags, d_out, n, enum_arg(dtype), d_num_selected, true, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+}  // extern "C"
+
+namespace {
+
+dws_status select_if_entry(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_pred pred,
+                           const void* h_threshold, unsigned long long* d_count, bool partition, hipStream_t stream)
+{
+    const int dt = enum_arg(dtype), pr = enum_arg(pred);
+    if (!valid_dtype(dt) || h_threshold == nullptr) return DWS_ERR_INVALID_ARG;
+    // outcome bits: 0 less, 1 equal, 2 greater, 3 unordered (a NaN: only
+    // "not equal" holds)
+    static const uint32_t kMasks[] = {0x2u, 0xDu, 0x1u, 0x3u, 0x4u, 0x6u};
+    if (pr < DWS_PRED_EQ || pr > DWS_PRED_GE) return DWS_ERR_INVALID_ARG;
+    SelectPredicate p{};
+    p.mask = kMasks[pr];
+    std::memcpy(&p.threshold, h_threshold, sizeof p.threshold);
+    p.kind = dt == DWS_FLOAT32 ? kKindF32 : (dt == DWS_INT32 ? kPredKindI32 : kKindU32);
+    return select_entry(d_in, nullptr, d_out, n, dt, d_count, partition, stream, &p);
+}
+
+}  // namespace
+
+extern "C" {
+
+dws_status dws_select_if(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_pred pred,
+                         const void* h_threshold, unsigned long long* d_count, hipStream_t stream)
+{
+    try {
+        return select_if_entry(d_in, d_out, n, dtype, pred, h_threshold, d_count, false, stream);
+    } catch (const std::bad_alloc&) {
+        return DWS_ERR_OOM;
+    } catch (...) {
+        return DWS_ERR_HIP;
+    }
+}
+
+dws_status dws_partition_if(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_pred pred,
+                            const void* h_threshold, unsigned long long* d_num_selected, hipStream_t stream)
+{
+    try {
+        return select_if_entry(d_in, d_out, n, dtype, pred, h_threshold, d_num_selected, true, stream);
     } catch (const std::bad_alloc&) {
         return DWS_ERR_OOM;
     } catch (...) {

@@ -127,7 +127,17 @@ struct SelectArgs {
     uint32_t num_tiles;
     unsigned int* epoch;     // the workspace epoch word
     bool partition;          // also write the rejected elements, reversed, at the back
+    // predicate mode (flags unused): select v when bit c of pred_mask is set,
+    // c the outcome of comparing v with threshold as `kind` (0 less, 1 equal,
+    // 2 greater, 3 unordered)
+    bool pred;
+    uint32_t pred_mask;
+    uint32_t threshold;
+    int kind;                // kKindU32, kKindF32 or kPredKindI32
 };
+// Element kind of a predicate's comparison besides kKindU32 and kKindF32:
+// signed 32-bit integers.
+constexpr int kPredKindI32 = 2;
 constexpr uint64_t kSelectLargeMin = (uint64_t)1 << 22;   // 32768-element tiles from here
 constexpr uint64_t kSelectNtMin = (uint64_t)1 << 23;      // non-temporal loads (large shape) from here
 constexpr uint64_t kSelectDrawnMin = (uint64_t)1 << 25;   // in-place select: drawn tile index from here

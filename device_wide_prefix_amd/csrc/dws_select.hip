@@ -62,9 +62,32 @@ struct SelectParams {
     uint32_t num_tiles;
     unsigned int* epoch;
     uint32_t backoff;        // pause level between blocked look-back polls (kPause*)
+    // predicate mode (PRED): element v is selected when bit c of pred_mask is
+    // set, c being the outcome of comparing v with threshold in the element
+    // type `kind` (kPredKindI32, kKindU32 or kKindF32): 0 less, 1 equal,
+    // 2 greater, 3 unordered (a NaN)
+    uint32_t pred_mask;
+    uint32_t threshold;
+    uint32_t kind;
 };
 
-template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX, bool NT = false, bool ALIAS = false>
+// The comparison outcome of v against t as 32-bit patterns of `kind`.
+__device__ __forceinline__ uint32_t compare_code(uint32_t v, uint32_t t, uint32_t kind)
+{
+    if (kind == (uint32_t)kKindF32) {
+        const float a = __uint_as_float(v), b = __uint_as_float(t);
+        if (a != a || b != b) return 3u;
+        return a < b ? 0u : (a == b ? 1u : 2u);
+    }
+    if (kind == (uint32_t)kPredKindI32) {
+        const int32_t a = (int32_t)v, b = (int32_t)t;
+        return a < b ? 0u : (a == b ? 1u : 2u);
+    }
+    return v < t ? 0u : (v == t ? 1u : 2u);
+}
+
+template <int BLOCK, int VEC, int CHUNKS, bool PARTITION, int TILE_INDEX, bool NT = false, bool ALIAS = false,
+          bool PRED = false>
 __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
 {
     static_assert(!(PARTITION && ALIAS), "a partition is never in place");
@@ -112,11 +135,16 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     const uint64_t seg_first = (uint64_t)tile * TILE + (uint64_t)wave * SEG;
     const uint32_t seg_valid = valid_bytes(seg_first, SEG, p.n);
     uint32_t x[CHUNKS][VEC], r[CHUNKS][VEC];
-    // flags first: the tile's count (its aggregate) needs only the flags, so
-    // out of place it is published and the look-back runs while the values
-    // are in flight
-    load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
-    load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    if constexpr (PRED) {
+        // the selection comes from the values themselves: no flags to load
+        load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    } else {
+        // flags first: the tile's count (its aggregate) needs only the flags,
+        // so out of place it is published and the look-back runs while the
+        // values are in flight
+        load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.flags + seg_first, seg_valid), lane, r);
+        load_segment<uint32_t, VEC, CHUNKS, NT>(make_rsrc(p.in + seg_first, seg_valid), lane, x);
+    }
     if constexpr (TILE_INDEX == kTileDispatch)
         if (multi && wave == 0) epoch_v = load_epoch_async(p.epoch);
 
@@ -126,10 +154,30 @@ __global__ void __launch_bounds__(BLOCK) k_select(SelectParams p)
     for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const uint32_t bit = r[c][e] != 0u ? 1u : 0u;
+            uint32_t bit;
+            if constexpr (PRED) {
+                bit = (p.pred_mask >> compare_code(x[c][e], p.threshold, p.kind)) & 1u;
+            } else {
+                bit = r[c][e] != 0u ? 1u : 0u;
+            }
             selected |= (Mask)bit << (c * VEC + e);
             r[c][e] = bit;
         }
+    if constexpr (PRED) {
+        // values past n load as 0, which a predicate may select: a ragged
+        // segment (the array's last, uniform test) clears their bits
+        if (seg_valid < SEG * 4u) {
+            const uint32_t valid = seg_valid / 4u;
+#pragma unroll
+            for (int c = 0; c < CHUNKS; ++c)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if ((uint32_t)(c * (int)CH + lane * VEC + e) >= valid) {
+                        selected &= ~((Mask)1 << (c * VEC + e));
+                        r[c][e] = 0u;
+                    }
+        }
+    }
     const uint32_t seg_count = scan_segment_local<uint32_t, true, VEC, CHUNKS>(r);
     pin_in_registers<uint32_t, VEC, CHUNKS>(r);
     // in place: the values must be in registers before this tile can publish
@@ -240,15 +288,32 @@ static SelectShape select_shape(uint64_t n, bool aligned)
 
 uint32_t select_tile_elems(uint64_t n, bool aligned) { return select_shape(n, aligned).elems(); }
 
-template <bool PARTITION, int TI, bool NT = false, bool ALIAS = false>
+template <bool PARTITION, int TI, bool NT = false, bool ALIAS = false, bool PRED = false>
 static const void* select_kernel(const SelectShape& s)
 {
     if (s.vec == 1) return reinterpret_cast<const void*>(
-        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION, TI, false, ALIAS>);
+        &k_select<kSelectScalar.threads, kSelectScalar.vec, kSelectScalar.chunks, PARTITION, TI, false, ALIAS, PRED>);
     if (s.threads == kSelectLarge.threads) return reinterpret_cast<const void*>(
-        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION, TI, NT, ALIAS>);
+        &k_select<kSelectLarge.threads, kSelectLarge.vec, kSelectLarge.chunks, PARTITION, TI, NT, ALIAS, PRED>);
     return reinterpret_cast<const void*>(
-        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION, TI, false, ALIAS>);
+        &k_select<kSelectSmall.threads, kSelectSmall.vec, kSelectSmall.chunks, PARTITION, TI, false, ALIAS, PRED>);
+}
+
+// The kernel for these arguments; PRED: the selection comes from a
+// predicate on the values (dws_select_if, dws_partition_if).
+template <bool PRED>
+static const void* pick_select_kernel(const SelectArgs& a, const SelectShape& s)
+{
+    const bool nt = a.n >= kSelectNtMin;
+    const bool alias = !a.partition && a.out == a.in;
+    if (a.partition)
+        return nt ? select_kernel<true, kTileDispatch, true, false, PRED>(s)
+                  : select_kernel<true, kTileDispatch, false, false, PRED>(s);
+    if (alias)
+        return a.n >= kSelectDrawnMin ? select_kernel<false, kTileDrawn, true, true, PRED>(s)
+                                      : select_kernel<false, kTileDispatch, false, true, PRED>(s);
+    return nt ? select_kernel<false, kTileDispatch, true, false, PRED>(s)
+              : select_kernel<false, kTileDispatch, false, false, PRED>(s);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
@@ -263,7 +328,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     SelectParams p{static_cast<const uint32_t*>(a.in), static_cast<const uint32_t*>(a.flags),
                    static_cast<uint32_t*>(a.out), a.n, a.desc, a.counter, a.watchdog, a.count, a.num_tiles,
                    a.epoch,
-                   select_backoff(a.n)};
+                   select_backoff(a.n), a.pred_mask, a.threshold, (uint32_t)a.kind};
     void* args[] = {&p};
     // The tile index is the workgroup index, as for the scan: no atomic on the
     // critical path; the watchdog still bounds every wait. From kSelectNtMin
@@ -278,17 +343,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream)
     // the workgroup index the in-place select of the 2^30 - 12,345 flags
     // measured 1.84 to 2.01 ms (mean 1.943) against 1.795 to 1.930 (mean
     // 1.844).
-    const bool nt = a.n >= kSelectNtMin;
-    const bool alias = !a.partition && a.out == a.in;
-    const void* fn;
-    if (a.partition) {
-        fn = nt ? select_kernel<true, kTileDispatch, true>(s) : select_kernel<true, kTileDispatch>(s);
-    } else if (alias) {
-        fn = a.n >= kSelectDrawnMin ? select_kernel<false, kTileDrawn, true, true>(s)
-                                    : select_kernel<false, kTileDispatch, false, true>(s);
-    } else {
-        fn = nt ? select_kernel<false, kTileDispatch, true>(s) : select_kernel<false, kTileDispatch>(s);
-    }
+    const void* fn = a.pred ? pick_select_kernel<true>(a, s) : pick_select_kernel<false>(a, s);
     return hipLaunchKernel(fn, dim3(a.num_tiles), dim3(s.threads), args, 0, stream);
 }
 

@@ -363,6 +363,44 @@ dws_status dws_partition_flagged(const void* d_in, const void* d_flags, void* d_
                                  dws_dtype dtype, unsigned long long* d_num_selected,
                                  hipStream_t stream);
 
+/* Predicates of dws_select_if / dws_partition_if: x[i] compared with a
+ * threshold t in the element type's order (int32 signed, uint32 unsigned,
+ * fp32 IEEE: a NaN on either side satisfies only DWS_PRED_NE, and -0.0 equals
+ * +0.0). */
+typedef enum dws_pred {
+    DWS_PRED_EQ = 0,   /* x == t */
+    DWS_PRED_NE = 1,   /* x != t */
+    DWS_PRED_LT = 2,   /* x <  t */
+    DWS_PRED_LE = 3,   /* x <= t */
+    DWS_PRED_GT = 4,   /* x >  t */
+    DWS_PRED_GE = 5    /* x >= t */
+} dws_pred;
+
+/*
+ * Select-if (Merrill & Garland, section A5, select-if): dws_select_flagged
+ * with the selection computed from the values themselves, x[i] `pred` t,
+ * where t is the element the HOST pointer h_threshold points to (one element
+ * of dtype, read during the call). The same single-pass kernel reads only the
+ * values (4 bytes per element instead of 8): no flags array is materialised.
+ * Results, in-place use (d_out == d_in allowed: a tile's count needs its values,
+ * so every earlier tile has read its input before any write), the count word,
+ * limits and errors are those of dws_select_flagged (d_flags aside); in
+ * addition an unknown pred or h_threshold == NULL gives DWS_ERR_INVALID_ARG.
+ */
+dws_status dws_select_if(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_pred pred,
+                         const void* h_threshold, unsigned long long* d_count, hipStream_t stream);
+
+/*
+ * Partition-if (Merrill & Garland, section A5, partition-if):
+ * dws_partition_flagged with the selection x[i] `pred` t computed from the
+ * values, as dws_select_if. The selected elements go to the front in input
+ * order, the others to the back in reverse input order; *d_num_selected is
+ * their count. Never in place (DWS_ERR_OVERLAP), as dws_partition_flagged.
+ */
+dws_status dws_partition_if(const void* d_in, void* d_out, size_t n, dws_dtype dtype, dws_pred pred,
+                            const void* h_threshold, unsigned long long* d_num_selected,
+                            hipStream_t stream);
+
 /*
  * Reduce by key (Merrill & Garland, section A5, reduce-by-key), one
  * single-pass launch: every maximal run of consecutive equal keys (compared

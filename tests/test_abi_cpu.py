@@ -438,6 +438,28 @@ def test_reduce_op_validation(lib):
     assert f(FAKE, 10, dws.INT32, dws.OP_SUM, FAKE + 36, None) == dws.ERR_OVERLAP
 
 
+def test_select_if_validation(lib):
+    """dws_select_if / dws_partition_if: the predicate and threshold checks,
+    then those of the flagged calls, before any HIP call."""
+    import numpy as np
+    t = np.array([3], dtype=np.int32)
+    tp = t.ctypes.data
+    cnt = FAKE + (1 << 24)
+    for f in (lib.dws_select_if, lib.dws_partition_if):
+        assert f(FAKE, FAKE + 8192, 100, dws.INT32, 6, tp, cnt, None) == dws.ERR_INVALID_ARG
+        assert f(FAKE, FAKE + 8192, 100, dws.INT32, -1, tp, cnt, None) == dws.ERR_INVALID_ARG
+        assert f(FAKE, FAKE + 8192, 100, dws.INT32, dws.PRED_LT, None, cnt, None) == dws.ERR_INVALID_ARG
+        assert f(FAKE, FAKE + 8192, 100, 7, dws.PRED_LT, tp, cnt, None) == dws.ERR_INVALID_ARG
+        assert f(FAKE, FAKE + 8192, 100, dws.INT32, dws.PRED_LT, tp, None, None) == dws.ERR_INVALID_ARG
+        assert f(FAKE, FAKE + 8192, 100, dws.INT32, dws.PRED_LT, tp, cnt + 4, None) == dws.ERR_MISALIGNED
+        assert f(FAKE + 2, FAKE + 8192, 100, dws.FLOAT32, dws.PRED_GE, tp, cnt, None) == dws.ERR_MISALIGNED
+        assert f(FAKE, FAKE + 4, 100, dws.UINT32, dws.PRED_EQ, tp, cnt, None) == dws.ERR_OVERLAP
+        assert f(FAKE, FAKE + 8192, (1 << 32), dws.INT32, dws.PRED_NE, tp, cnt, None) == dws.ERR_UNSUPPORTED
+        assert f(FAKE, FAKE + 8192, 100, dws.INT32, dws.PRED_NE, tp, FAKE + 200, None) == dws.ERR_OVERLAP
+    # a partition is never in place
+    assert lib.dws_partition_if(FAKE, FAKE, 100, dws.INT32, dws.PRED_LT, tp, cnt, None) == dws.ERR_OVERLAP
+
+
 def test_reduce_validation(lib):
     """dws_reduce: argument checks before any HIP call."""
     f = lib.dws_reduce
